@@ -1,0 +1,260 @@
+/*
+ * mlora.h - C ABI of the MI355X (gfx950) heterogeneous multi-LoRA linear.
+ *
+ * The layer computes, for every row k of a mixed batch,
+ *
+ *     Y[k] = W0 x_k + s_a * Up_a (Down_a x_k),      a = row_adapter[k]
+ *
+ * with one base weight W0 shared by the whole batch and a low-rank term of
+ * each row's own adapter (rank and scale per adapter; a row with id -1 has
+ * no adapter and keeps the base output).  This is the shared-base /
+ * per-row-delta form of the M031 card (xuujii.github.io/ai-infra-kb/details/
+ * M031.html, section 02) and the per-query formula of the airsota card
+ * (airsota.com/?p=1825, section three, derivation 1; its A is Down^T and its
+ * B is Up^T).  Rows are grouped by adapter and each group's result is
+ * written back to the rows it came from (M031 card sections 02-03; wiblog
+ * article "vLLM LoRA adapter batch scheduling", Punica section).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every function returns an mlora_status; nothing throws, aborts or
+ *    synchronises the device unless its comment says so.  On failure the
+ *    thread-local string of mlora_last_error() says why.
+ *  - "device" pointers are caller-owned device memory, only borrowed for the
+ *    call.  "host" pointers are caller-owned host memory, not retained after
+ *    the call returns.  The library never allocates device memory; it
+ *    allocates host memory (pinned staging for pool loads) only inside
+ *    mlora_pool_create.
+ *  - bf16 tensors are passed as their uint16_t bit patterns (IEEE binary32
+ *    with the low 16 bits dropped), row-major and densely packed.
+ *  - All device work is enqueued on the caller's stream (`stream` is a
+ *    hipStream_t; NULL means the default stream) and is asynchronous.
+ *    Calls on one pool must be ordered by the caller: issue them on one
+ *    stream, or synchronise between streams.
+ *  - Data-dependent errors (a row id that is not -1 and not a resident
+ *    adapter) cannot be returned without a device sync: they set bits in
+ *    the segment status word and the affected output rows become NaN.
+ *  - Full speed needs din and dout multiples of 8 and 16-byte aligned
+ *    pointers; any din, dout >= 1 is computed correctly.
+ */
+#ifndef MLORA_H
+#define MLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mlora_status {
+  MLORA_OK = 0,
+  MLORA_EINVAL = 1, /* bad argument: null pointer, shape, rank, projection, size */
+  MLORA_ENOSPC = 2, /* not enough free pages in the pool; nothing was changed   */
+  MLORA_EEXIST = 3, /* load of an adapter id that is already resident          */
+  MLORA_ENOENT = 4, /* unload of an adapter id that is not resident            */
+  MLORA_EHIP = 5    /* a HIP runtime call or kernel launch failed              */
+} mlora_status;
+
+/* Apply variants.  AUTO lets the library choose; the others force one
+ * implementation of the low-rank branch (all give the same result within
+ * the bf16 tolerance, each is bitwise deterministic). */
+typedef enum mlora_variant {
+  MLORA_VARIANT_AUTO = 0,
+  MLORA_VARIANT_SPLIT = 1, /* shrink kernel -> fp32 t in `work` -> expand kernel */
+  MLORA_VARIANT_FUSED = 2  /* one kernel per row tile: t stays on chip           */
+} mlora_variant;
+
+/* Limits. */
+#define MLORA_MAX_ROWS 16384        /* rows per batch (segment builder works in one workgroup) */
+#define MLORA_MAX_RANK 128          /* largest adapter rank a pool may hold                   */
+#define MLORA_MAX_ADAPTERS 65533    /* adapter ids are 0 .. max_adapters-1                    */
+#define MLORA_ITEM_ROWS 4           /* rows per low-rank work item                            */
+
+/* Segment status bits (header word MLORA_SEG_STATUS). */
+#define MLORA_SEG_BAD_ID 1          /* an id < -1 or >= max_adapters appeared                 */
+#define MLORA_SEG_NOT_RESIDENT 2    /* an id named an adapter with no weights loaded          */
+
+/* ---------------------------------------------------------------------------
+ * Library information
+ * ------------------------------------------------------------------------- */
+const char* mlora_version(void);
+const char* mlora_status_string(int status);
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* mlora_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Rank-stacked paged adapter pool
+ *
+ * One page holds one rank row of one adapter for one projection: the Down
+ * arena has pages of din bf16 (a row of Down), the Up arena pages of dout
+ * bf16 (a column of Up, i.e. a row of Up^T).  An adapter of rank r takes
+ * n_proj * r pages in each arena, wherever they are free: no padding to the
+ * largest rank, and adapters of different ranks share one pool.  This is
+ * the adapter half of the unified paging the M031 card (section 06) and the
+ * wiblog article (memory-cost section) point to, sized by the card's
+ * section 06 arithmetic (rank 16 over a 4096 x 4096 projection is 0.25 MiB).
+ *
+ * Device metadata (the `meta` buffer, mlora_pool_meta_bytes() long, 256-byte
+ * aligned regions in this order):
+ *   int32 rank[max_adapters]                        0 = not resident
+ *   float scale[max_adapters]
+ *   int32 down_page[max_adapters][n_proj][max_rank] page index, -1 past rank
+ *   int32 up_page  [max_adapters][n_proj][max_rank]
+ * ------------------------------------------------------------------------- */
+typedef struct mlora_pool mlora_pool; /* opaque host handle */
+
+typedef struct mlora_pool_desc {
+  int32_t din;          /* input features of the projection(s), >= 1          */
+  int32_t dout;         /* output features, >= 1                               */
+  int32_t n_proj;       /* projections (layers x modules) per adapter, >= 1    */
+  int32_t max_adapters; /* adapter ids are 0 .. max_adapters-1                 */
+  int32_t max_rank;     /* 1 .. MLORA_MAX_RANK                                 */
+  int32_t reserved;     /* must be 0                                           */
+  int64_t n_down_pages; /* pages in the Down arena                             */
+  int64_t n_up_pages;   /* pages in the Up arena                               */
+  void* down_pages;     /* device bf16 [n_down_pages][din]                     */
+  void* up_pages;       /* device bf16 [n_up_pages][dout]                      */
+  void* meta;           /* device, mlora_pool_meta_bytes() bytes, 256-aligned  */
+} mlora_pool_desc;
+
+size_t mlora_pool_meta_bytes(int32_t max_adapters, int32_t n_proj, int32_t max_rank);
+
+/* Creates the host handle, binds it to the current device and clears the
+ * device metadata on `stream` (no adapter resident).  The three device
+ * buffers stay owned by the caller and must outlive the pool. */
+mlora_status mlora_pool_create(const mlora_pool_desc* desc, void* stream, mlora_pool** out);
+mlora_status mlora_pool_destroy(mlora_pool* pool); /* waits for its own pending copies */
+
+/* Loads adapter `adapter_id` with the given rank and scale:
+ *   down: host bf16 [n_proj][rank][din]   (Down, the "lora A" layout)
+ *   up:   host bf16 [n_proj][dout][rank]  (Up,   the "lora B" layout)
+ * Pages are taken from the free lists, Up is transposed to rank-major rows
+ * on the host, and the pages plus metadata are copied on `stream` from
+ * pinned staging.  The caller's buffers may be reused when this returns.
+ * The weights are ready for any later call on the same stream (the card's
+ * lifecycle: weights must be resident before the branch runs).
+ * Errors: EINVAL (id, rank, pointers), EEXIST (already resident: no silent
+ * overwrite of a live id), ENOSPC (not enough free pages; nothing changed). */
+mlora_status mlora_pool_load(mlora_pool* pool, int32_t adapter_id, int32_t rank, float scale,
+                             const uint16_t* down, const uint16_t* up, void* stream);
+
+/* Marks the adapter not resident (rank 0, on `stream`) and returns its pages
+ * to the free lists.  Work enqueued earlier on the same stream still reads
+ * the old pages before any later load can overwrite them (evict only after
+ * the last reader).  Errors: EINVAL (id range), ENOENT (not resident). */
+mlora_status mlora_pool_unload(mlora_pool* pool, int32_t adapter_id, void* stream);
+
+/* Host-side view of the pool (no device access). */
+mlora_status mlora_pool_query(const mlora_pool* pool, int32_t adapter_id, int32_t* rank, float* scale);
+mlora_status mlora_pool_free_pages(const mlora_pool* pool, int64_t* free_down, int64_t* free_up,
+                                   int32_t* n_resident);
+
+/* ---------------------------------------------------------------------------
+ * Segment builder: groups the batch's rows by adapter (M031 card sections
+ * 02-03: group order ascending by adapter, original order inside a group,
+ * results written back to the original rows; the map is rebuilt for every
+ * batch as requests join and leave).  It is a stable sort of rows by key,
+ * key = adapter id for a row on a resident adapter, then all base-only rows
+ * (id -1), then all rows with an invalid id.  Bit-exact and deterministic.
+ *
+ * seg_ws layout (int32 words; n = n_rows; mlora_segments_bytes(n) bytes):
+ *   [0..16)            header, indices MLORA_SEG_*
+ *   perm[n]            at MLORA_SEG_PERM(n):  sorted position -> original row
+ *   inv[n]             at MLORA_SEG_INV(n):   original row -> sorted position
+ *   seg_adapter[n]     at MLORA_SEG_ADAPTER(n): adapter of segment s (nseg used)
+ *   seg_off[n+1]       at MLORA_SEG_OFF(n):   first sorted position of s;
+ *                                             seg_off[nseg] = n_act
+ *   items[2*max_items] at MLORA_SEG_ITEMS(n): work items (segment, first
+ *                      sorted position), each covering up to MLORA_ITEM_ROWS
+ *                      rows of one segment, in segment order.
+ * ------------------------------------------------------------------------- */
+#define MLORA_SEG_NSEG 0
+#define MLORA_SEG_NACT 1
+#define MLORA_SEG_NNONE 2
+#define MLORA_SEG_NBAD 3
+#define MLORA_SEG_STATUS 4
+#define MLORA_SEG_NITEMS 5
+#define MLORA_SEG_NROWS 6
+#define MLORA_SEG_MAXAD 7
+#define MLORA_SEG_HEADER 16
+#define MLORA_SEG_PERM(n) (MLORA_SEG_HEADER)
+#define MLORA_SEG_INV(n) (MLORA_SEG_HEADER + (n))
+#define MLORA_SEG_ADAPTER(n) (MLORA_SEG_HEADER + 2 * (n))
+#define MLORA_SEG_OFF(n) (MLORA_SEG_HEADER + 3 * (n))
+#define MLORA_SEG_ITEMS(n) ((MLORA_SEG_HEADER + 4 * (n) + 2) & ~1)
+#define MLORA_SEG_MAX_ITEMS(n) ((n) + ((n) + MLORA_ITEM_ROWS - 1) / MLORA_ITEM_ROWS + 1)
+
+size_t mlora_segments_bytes(int32_t n_rows);
+
+/* row_adapter: device int32 [n_rows]; seg_ws: device, mlora_segments_bytes().
+ * Reads the pool's device rank table to tell resident ids from others. */
+mlora_status mlora_build_segments(const mlora_pool* pool, const int32_t* row_adapter, int32_t n_rows,
+                                  void* seg_ws, void* stream);
+
+/* Copies the 16-word header of seg_ws to host `header` and SYNCHRONISES the
+ * stream (for tests and for callers that want to check the status word). */
+mlora_status mlora_segments_header(const void* seg_ws, int32_t* header, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * The steps of the layer, each usable on its own
+ * ------------------------------------------------------------------------- */
+
+/* Base GEMM over the whole batch, Y = X W0^T (the card's shared-base step):
+ *   X: device bf16 [n_rows][din], W0: device bf16 [dout][din],
+ *   Y: device bf16 [n_rows][dout] (overwritten).
+ * bf16 inputs, fp32 accumulation on the matrix cores, bf16 output (RNE). */
+mlora_status mlora_base_gemm(const uint16_t* X, const uint16_t* W0, uint16_t* Y, int32_t n_rows,
+                             int32_t din, int32_t dout, void* stream);
+
+/* Shrink, t = Down_a x_k for every row on a resident adapter, rows gathered
+ * through perm (each group computes its own Down product):
+ *   T: device fp32 [n_chunks][n_rows][max_rank]; row j is sorted position j,
+ *   column q < rank of its segment; chunk c holds the partial sum over the
+ *   c-th of n_chunks equal slices of din (slices are multiples of 512
+ *   elements; a slice past din contributes zeros), so t = sum over c.
+ *   Entries of rows past n_act and columns past the rank are not written.
+ *   1 <= n_chunks <= mlora_shrink_max_chunks(din). */
+int32_t mlora_shrink_max_chunks(int32_t din);
+mlora_status mlora_shrink(const mlora_pool* pool, int32_t proj, const uint16_t* X, const void* seg_ws,
+                          int32_t n_rows, float* T, int32_t n_chunks, void* stream);
+
+/* Expand, Y[perm[j]] += s_a * Up_a t_j (read-modify-write in fp32, stored as
+ * bf16 RNE; no atomics: one thread owns each output element), with t_j the
+ * sum over the n_chunks partials of T (layout as mlora_shrink).  Rows with
+ * an invalid id are set to NaN; base-only rows are untouched. */
+mlora_status mlora_expand(const mlora_pool* pool, int32_t proj, const float* T, int32_t n_chunks,
+                          const void* seg_ws, uint16_t* Y, int32_t n_rows, void* stream);
+
+/* Fused shrink + expand: Y[perm[j]] += s_a * Up_a (Down_a x_perm[j]) with t
+ * kept on chip, one workgroup per work item (for decode steps, where most
+ * groups hold one or a few tokens).  Invalid rows become NaN. */
+mlora_status mlora_fused(const mlora_pool* pool, int32_t proj, const uint16_t* X, const void* seg_ws,
+                         uint16_t* Y, int32_t n_rows, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * The whole layer for one projection of one batch:
+ *   Y = X W0^T, then every row's low-rank term added at its original row.
+ *   X: device bf16 [n_rows][din]; W0: device bf16 [dout][din] (projection
+ *   `proj`'s base weight); Y: device bf16 [n_rows][dout] (overwritten);
+ *   seg_ws from mlora_build_segments on the same rows (reusable for every
+ *   projection of the batch); work: device scratch of at least
+ *   mlora_work_bytes(pool, n_rows) bytes, 256-byte aligned.
+ * n_rows = 0 is a no-op.
+ * ------------------------------------------------------------------------- */
+size_t mlora_work_bytes(const mlora_pool* pool, int32_t n_rows);
+mlora_status mlora_apply(const mlora_pool* pool, int32_t proj, const uint16_t* X, const uint16_t* W0,
+                         const void* seg_ws, uint16_t* Y, int32_t n_rows, void* work, size_t work_bytes,
+                         int32_t variant, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Measurement helper: a plain streaming copy (dst = src, `bytes` a multiple
+ * of 16, both 16-byte aligned), used to calibrate achievable HBM bandwidth
+ * and hardware byte counters against a kernel of known traffic.
+ * ------------------------------------------------------------------------- */
+mlora_status mlora_hbm_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLORA_H */

@@ -1,0 +1,601 @@
+// Host side of the library: the C ABI of include/mlora.h - argument checks,
+// status codes, the paged adapter pool's allocator and pinned-staging loads,
+// and the launch plan of each step.  No device memory is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "internal.h"
+
+using mlora::PoolView;
+
+namespace {
+
+thread_local std::string g_err;
+
+mlora_status fail(mlora_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+mlora_status hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MLORA_OK;
+  return fail(MLORA_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(call)                                   \
+  do {                                                  \
+    mlora_status st_ = hip_check((call), #call);        \
+    if (st_ != MLORA_OK) return st_;                    \
+  } while (0)
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Free-page ranges of one arena: start -> length, merged on release.
+class RangeAlloc {
+ public:
+  typedef std::vector<std::pair<int64_t, int64_t>> Runs;
+
+  void init(int64_t n) {
+    free_.clear();
+    if (n > 0) free_[0] = n;
+    nfree_ = n;
+  }
+  int64_t nfree() const { return nfree_; }
+
+  // `count` pages as one run if some free range holds them (first fit), else
+  // gathered from the lowest free ranges.  False (nothing taken) if short.
+  bool alloc(int64_t count, Runs& runs) {
+    runs.clear();
+    if (count > nfree_) return false;
+    for (auto& kv : free_) {
+      if (kv.second >= count) {
+        const int64_t s = kv.first;
+        runs.push_back({s, count});
+        take(s, count);
+        return true;
+      }
+    }
+    int64_t need = count;
+    while (need > 0) {
+      auto it = free_.begin();
+      const int64_t s = it->first, n = std::min(need, it->second);
+      runs.push_back({s, n});
+      take(s, n);
+      need -= n;
+    }
+    return true;
+  }
+
+  void release(const Runs& runs) {
+    for (const auto& r : runs) put(r.first, r.second);
+  }
+
+ private:
+  void take(int64_t s, int64_t c) {
+    auto it = free_.find(s);
+    const int64_t len = it->second;
+    free_.erase(it);
+    if (len > c) free_[s + c] = len - c;
+    nfree_ -= c;
+  }
+  void put(int64_t s, int64_t c) {
+    auto next = free_.lower_bound(s);
+    if (next != free_.begin()) {
+      auto prev = std::prev(next);
+      if (prev->first + prev->second == s) {
+        s = prev->first;
+        c += prev->second;
+        free_.erase(prev);
+      }
+    }
+    next = free_.lower_bound(s);
+    if (next != free_.end() && s + c == next->first) {
+      c += next->second;
+      free_.erase(next);
+    }
+    free_[s] = c;
+    nfree_ += c;
+  }
+  std::map<int64_t, int64_t> free_;
+  int64_t nfree_ = 0;
+};
+
+struct MetaLayout {
+  size_t rank, scale, dpt, upt, total;
+};
+
+MetaLayout meta_layout(int32_t A, int32_t P, int32_t R) {
+  MetaLayout m;
+  const size_t pt = (size_t)A * P * R * sizeof(int32_t);
+  m.rank = 0;
+  m.scale = align256((size_t)A * 4);
+  m.dpt = m.scale + align256((size_t)A * 4);
+  m.upt = m.dpt + align256(pt);
+  m.total = m.upt + align256(pt);
+  return m;
+}
+
+constexpr size_t kStageBytes = size_t(8) << 20;  // two pinned staging buffers of 8 MiB
+constexpr int kMaxSplitChunks = 8;               // din slices used by the split variant
+
+}  // namespace
+
+struct mlora_pool {
+  int device = 0;
+  mlora_pool_desc d{};
+  MetaLayout ml{};
+  RangeAlloc dfree, ufree;
+  std::vector<int32_t> rank;
+  std::vector<float> scale;
+  std::vector<RangeAlloc::Runs> druns, uruns;
+  int32_t n_resident = 0;
+  void* stage[2] = {nullptr, nullptr};
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  bool pending[2] = {false, false};
+  int cur = 0;
+  std::mutex mu;
+
+  PoolView view() const {
+    PoolView v;
+    const char* m = static_cast<const char*>(d.meta);
+    v.rank = reinterpret_cast<const int32_t*>(m + ml.rank);
+    v.scale = reinterpret_cast<const float*>(m + ml.scale);
+    v.down_page = reinterpret_cast<const int32_t*>(m + ml.dpt);
+    v.up_page = reinterpret_cast<const int32_t*>(m + ml.upt);
+    v.down = static_cast<const uint16_t*>(d.down_pages);
+    v.up = static_cast<const uint16_t*>(d.up_pages);
+    v.din = d.din;
+    v.dout = d.dout;
+    v.n_proj = d.n_proj;
+    v.max_adapters = d.max_adapters;
+    v.max_rank = d.max_rank;
+    return v;
+  }
+};
+
+namespace {
+
+// Packs host data into pinned staging and issues stream-ordered copies to
+// the device, merging copies whose staging and device ranges are both
+// contiguous.  A staging buffer is refilled only after the event recorded
+// behind its last copies has completed.
+class Stager {
+ public:
+  Stager(mlora_pool* p, hipStream_t s) : p_(p), s_(s) {}
+
+  // reserve `bytes` of staging for a copy to device address `dst`
+  mlora_status reserve(void* dst, size_t bytes, char** host) {
+    if (bytes > kStageBytes) return fail(MLORA_EINVAL, "staging: one copy of %zu bytes exceeds %zu", bytes, kStageBytes);
+    if (used_ + bytes > kStageBytes) {
+      mlora_status st = flush();
+      if (st != MLORA_OK) return st;
+    }
+    if (!open_) {
+      const int b = p_->cur;
+      if (p_->pending[b]) {
+        HIP_TRY(hipEventSynchronize(p_->ev[b]));
+        p_->pending[b] = false;
+      }
+      open_ = true;
+      used_ = 0;
+      copies_.clear();
+    }
+    char* base = static_cast<char*>(p_->stage[p_->cur]);
+    *host = base + used_;
+    if (!copies_.empty() && copies_.back().src + copies_.back().bytes == used_ &&
+        static_cast<char*>(copies_.back().dst) + copies_.back().bytes == static_cast<char*>(dst)) {
+      copies_.back().bytes += bytes;
+    } else {
+      copies_.push_back({used_, dst, bytes});
+    }
+    used_ += bytes;
+    return MLORA_OK;
+  }
+
+  mlora_status flush() {
+    if (!open_) return MLORA_OK;
+    const int b = p_->cur;
+    char* base = static_cast<char*>(p_->stage[b]);
+    for (const auto& c : copies_) HIP_TRY(hipMemcpyAsync(c.dst, base + c.src, c.bytes, hipMemcpyHostToDevice, s_));
+    HIP_TRY(hipEventRecord(p_->ev[b], s_));
+    p_->pending[b] = true;
+    p_->cur ^= 1;
+    open_ = false;
+    used_ = 0;
+    copies_.clear();
+    return MLORA_OK;
+  }
+
+ private:
+  struct Copy {
+    size_t src;
+    void* dst;
+    size_t bytes;
+  };
+  mlora_pool* p_;
+  hipStream_t s_;
+  bool open_ = false;
+  size_t used_ = 0;
+  std::vector<Copy> copies_;
+};
+
+mlora_status check_pool(const mlora_pool* p) {
+  if (!p) return fail(MLORA_EINVAL, "pool is NULL");
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev != p->device) return fail(MLORA_EINVAL, "pool lives on device %d but device %d is current", p->device, dev);
+  return MLORA_OK;
+}
+
+// page index of the i-th page of a run list
+inline int64_t page_at(const RangeAlloc::Runs& runs, int64_t i) {
+  for (const auto& r : runs) {
+    if (i < r.second) return r.first + i;
+    i -= r.second;
+  }
+  return -1;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mlora_version(void) { return "mlora-mi355x 0.1 (gfx950)"; }
+
+const char* mlora_status_string(int s) {
+  switch (s) {
+    case MLORA_OK: return "ok";
+    case MLORA_EINVAL: return "invalid argument";
+    case MLORA_ENOSPC: return "no free pages";
+    case MLORA_EEXIST: return "adapter already resident";
+    case MLORA_ENOENT: return "adapter not resident";
+    case MLORA_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* mlora_last_error(void) { return g_err.c_str(); }
+
+size_t mlora_pool_meta_bytes(int32_t max_adapters, int32_t n_proj, int32_t max_rank) {
+  if (max_adapters < 1 || n_proj < 1 || max_rank < 1) return 0;
+  return meta_layout(max_adapters, n_proj, max_rank).total;
+}
+
+mlora_status mlora_pool_create(const mlora_pool_desc* desc, void* stream, mlora_pool** out) {
+  g_err.clear();
+  if (!desc || !out) return fail(MLORA_EINVAL, "desc and out must not be NULL");
+  *out = nullptr;
+  const mlora_pool_desc& d = *desc;
+  if (d.din < 1 || d.dout < 1 || d.n_proj < 1) return fail(MLORA_EINVAL, "din, dout and n_proj must be >= 1");
+  if (d.max_adapters < 1 || d.max_adapters > MLORA_MAX_ADAPTERS)
+    return fail(MLORA_EINVAL, "max_adapters must be in [1, %d]", MLORA_MAX_ADAPTERS);
+  if (d.max_rank < 1 || d.max_rank > MLORA_MAX_RANK) return fail(MLORA_EINVAL, "max_rank must be in [1, %d]", MLORA_MAX_RANK);
+  if (d.reserved != 0) return fail(MLORA_EINVAL, "reserved must be 0");
+  if (d.n_down_pages < 0 || d.n_up_pages < 0 || d.n_down_pages > INT32_MAX || d.n_up_pages > INT32_MAX)
+    return fail(MLORA_EINVAL, "page counts must be in [0, 2^31)");
+  if (!d.meta) return fail(MLORA_EINVAL, "meta must not be NULL");
+  if ((d.n_down_pages && !d.down_pages) || (d.n_up_pages && !d.up_pages))
+    return fail(MLORA_EINVAL, "page arenas must not be NULL");
+  if ((reinterpret_cast<uintptr_t>(d.meta) & 255u) != 0) return fail(MLORA_EINVAL, "meta must be 256-byte aligned");
+  if ((size_t)d.din * 2 > kStageBytes || (size_t)d.dout * 2 > kStageBytes) return fail(MLORA_EINVAL, "din/dout too large");
+
+  mlora_pool* p = new mlora_pool();
+  p->d = d;
+  p->ml = meta_layout(d.max_adapters, d.n_proj, d.max_rank);
+  p->dfree.init(d.n_down_pages);
+  p->ufree.init(d.n_up_pages);
+  p->rank.assign(d.max_adapters, 0);
+  p->scale.assign(d.max_adapters, 0.f);
+  p->druns.resize(d.max_adapters);
+  p->uruns.resize(d.max_adapters);
+  auto cleanup = [&](mlora_status st) {
+    for (int b = 0; b < 2; ++b) {
+      if (p->stage[b]) (void)hipHostFree(p->stage[b]);
+      if (p->ev[b]) (void)hipEventDestroy(p->ev[b]);
+    }
+    delete p;
+    return st;
+  };
+  mlora_status st = hip_check(hipGetDevice(&p->device), "hipGetDevice");
+  for (int b = 0; b < 2 && st == MLORA_OK; ++b) {
+    st = hip_check(hipHostMalloc(&p->stage[b], kStageBytes, hipHostMallocDefault), "hipHostMalloc(staging)");
+    if (st == MLORA_OK) st = hip_check(hipEventCreateWithFlags(&p->ev[b], hipEventDisableTiming), "hipEventCreate");
+  }
+  hipStream_t s = as_stream(stream);
+  char* meta = static_cast<char*>(d.meta);
+  if (st == MLORA_OK) st = hip_check(hipMemsetAsync(meta, 0, p->ml.dpt, s), "hipMemsetAsync(meta)");
+  if (st == MLORA_OK) st = hip_check(hipMemsetAsync(meta + p->ml.dpt, 0xff, p->ml.total - p->ml.dpt, s), "hipMemsetAsync(page tables)");
+  if (st != MLORA_OK) return cleanup(st);
+  *out = p;
+  return MLORA_OK;
+}
+
+mlora_status mlora_pool_destroy(mlora_pool* p) {
+  g_err.clear();
+  if (!p) return fail(MLORA_EINVAL, "pool is NULL");
+  mlora_status st = MLORA_OK;
+  for (int b = 0; b < 2; ++b) {
+    if (p->pending[b] && st == MLORA_OK) st = hip_check(hipEventSynchronize(p->ev[b]), "hipEventSynchronize");
+    if (p->stage[b]) (void)hipHostFree(p->stage[b]);
+    if (p->ev[b]) (void)hipEventDestroy(p->ev[b]);
+  }
+  delete p;
+  return st;
+}
+
+mlora_status mlora_pool_load(mlora_pool* p, int32_t id, int32_t rank, float scale, const uint16_t* down,
+                             const uint16_t* up, void* stream) {
+  g_err.clear();
+  mlora_status st = check_pool(p);
+  if (st != MLORA_OK) return st;
+  std::lock_guard<std::mutex> lock(p->mu);
+  const mlora_pool_desc& d = p->d;
+  if (id < 0 || id >= d.max_adapters) return fail(MLORA_EINVAL, "adapter id %d outside [0, %d)", id, d.max_adapters);
+  if (rank < 1 || rank > d.max_rank) return fail(MLORA_EINVAL, "rank %d outside [1, %d]", rank, d.max_rank);
+  if (!down || !up) return fail(MLORA_EINVAL, "down and up must not be NULL");
+  if (p->rank[id] != 0) return fail(MLORA_EEXIST, "adapter %d is already resident (unload it first)", id);
+  const int64_t npages = (int64_t)d.n_proj * rank;
+  RangeAlloc::Runs dr, ur;
+  if (!p->dfree.alloc(npages, dr))
+    return fail(MLORA_ENOSPC, "Down arena: %lld pages needed, %lld free", (long long)npages, (long long)p->dfree.nfree());
+  if (!p->ufree.alloc(npages, ur)) {
+    p->dfree.release(dr);
+    return fail(MLORA_ENOSPC, "Up arena: %lld pages needed, %lld free", (long long)npages, (long long)p->ufree.nfree());
+  }
+  auto undo = [&](mlora_status s) {
+    p->dfree.release(dr);
+    p->ufree.release(ur);
+    return s;
+  };
+
+  hipStream_t s = as_stream(stream);
+  Stager sg(p, s);
+  const size_t drow = (size_t)d.din * 2, urow = (size_t)d.dout * 2;
+  char* dbase = static_cast<char*>(d.down_pages);
+  char* ubase = static_cast<char*>(d.up_pages);
+  std::vector<int32_t> dpt((size_t)d.n_proj * d.max_rank, -1), upt((size_t)d.n_proj * d.max_rank, -1);
+  // Down rows: page i of the run list holds row (p, q), i = p*rank + q
+  for (int64_t i = 0; i < npages; ++i) {
+    const int64_t pg = page_at(dr, i);
+    char* h = nullptr;
+    if ((st = sg.reserve(dbase + pg * drow, drow, &h)) != MLORA_OK) return undo(st);
+    std::memcpy(h, down + (size_t)i * d.din, drow);
+    dpt[(size_t)(i / rank) * d.max_rank + (i % rank)] = (int32_t)pg;
+  }
+  // Up^T rows: page i holds column q of Up for projection p
+  for (int64_t i = 0; i < npages; ++i) {
+    const int64_t pg = page_at(ur, i);
+    const int64_t pj = i / rank, q = i % rank;
+    char* h = nullptr;
+    if ((st = sg.reserve(ubase + pg * urow, urow, &h)) != MLORA_OK) return undo(st);
+    uint16_t* row = reinterpret_cast<uint16_t*>(h);
+    const uint16_t* src = up + (size_t)pj * d.dout * rank + q;
+    for (int32_t c = 0; c < d.dout; ++c) row[c] = src[(size_t)c * rank];
+    upt[(size_t)pj * d.max_rank + q] = (int32_t)pg;
+  }
+  // metadata: page tables, scale, then rank (all ordered on the stream)
+  char* meta = static_cast<char*>(d.meta);
+  const size_t ptb = dpt.size() * sizeof(int32_t);
+  const size_t pt_off = (size_t)id * d.n_proj * d.max_rank * sizeof(int32_t);
+  char* h = nullptr;
+  if ((st = sg.reserve(meta + p->ml.dpt + pt_off, ptb, &h)) != MLORA_OK) return undo(st);
+  std::memcpy(h, dpt.data(), ptb);
+  if ((st = sg.reserve(meta + p->ml.upt + pt_off, ptb, &h)) != MLORA_OK) return undo(st);
+  std::memcpy(h, upt.data(), ptb);
+  if ((st = sg.reserve(meta + p->ml.scale + (size_t)id * 4, 4, &h)) != MLORA_OK) return undo(st);
+  std::memcpy(h, &scale, 4);
+  if ((st = sg.reserve(meta + p->ml.rank + (size_t)id * 4, 4, &h)) != MLORA_OK) return undo(st);
+  std::memcpy(h, &rank, 4);
+  if ((st = sg.flush()) != MLORA_OK) return undo(st);
+
+  p->rank[id] = rank;
+  p->scale[id] = scale;
+  p->druns[id] = dr;
+  p->uruns[id] = ur;
+  ++p->n_resident;
+  return MLORA_OK;
+}
+
+mlora_status mlora_pool_unload(mlora_pool* p, int32_t id, void* stream) {
+  g_err.clear();
+  mlora_status st = check_pool(p);
+  if (st != MLORA_OK) return st;
+  std::lock_guard<std::mutex> lock(p->mu);
+  if (id < 0 || id >= p->d.max_adapters) return fail(MLORA_EINVAL, "adapter id %d outside [0, %d)", id, p->d.max_adapters);
+  if (p->rank[id] == 0) return fail(MLORA_ENOENT, "adapter %d is not resident", id);
+  char* meta = static_cast<char*>(p->d.meta);
+  HIP_TRY(hipMemsetAsync(meta + p->ml.rank + (size_t)id * 4, 0, 4, as_stream(stream)));
+  p->dfree.release(p->druns[id]);
+  p->ufree.release(p->uruns[id]);
+  p->druns[id].clear();
+  p->uruns[id].clear();
+  p->rank[id] = 0;
+  p->scale[id] = 0.f;
+  --p->n_resident;
+  return MLORA_OK;
+}
+
+mlora_status mlora_pool_query(const mlora_pool* p, int32_t id, int32_t* rank, float* scale) {
+  g_err.clear();
+  if (!p) return fail(MLORA_EINVAL, "pool is NULL");
+  if (id < 0 || id >= p->d.max_adapters) return fail(MLORA_EINVAL, "adapter id %d outside [0, %d)", id, p->d.max_adapters);
+  std::lock_guard<std::mutex> lock(const_cast<mlora_pool*>(p)->mu);
+  if (rank) *rank = p->rank[id];
+  if (scale) *scale = p->scale[id];
+  return p->rank[id] ? MLORA_OK : fail(MLORA_ENOENT, "adapter %d is not resident", id);
+}
+
+mlora_status mlora_pool_free_pages(const mlora_pool* p, int64_t* free_down, int64_t* free_up, int32_t* n_resident) {
+  g_err.clear();
+  if (!p) return fail(MLORA_EINVAL, "pool is NULL");
+  std::lock_guard<std::mutex> lock(const_cast<mlora_pool*>(p)->mu);
+  if (free_down) *free_down = p->dfree.nfree();
+  if (free_up) *free_up = p->ufree.nfree();
+  if (n_resident) *n_resident = p->n_resident;
+  return MLORA_OK;
+}
+
+size_t mlora_segments_bytes(int32_t n) {
+  if (n < 0) return 0;
+  return align256(((size_t)MLORA_SEG_ITEMS(n) + 2 * (size_t)MLORA_SEG_MAX_ITEMS(n)) * sizeof(int32_t));
+}
+
+mlora_status mlora_build_segments(const mlora_pool* p, const int32_t* row_adapter, int32_t n, void* seg_ws,
+                                  void* stream) {
+  g_err.clear();
+  mlora_status st = check_pool(p);
+  if (st != MLORA_OK) return st;
+  if (n < 0 || n > MLORA_MAX_ROWS) return fail(MLORA_EINVAL, "n_rows %d outside [0, %d]", n, MLORA_MAX_ROWS);
+  if (!seg_ws || (n > 0 && !row_adapter)) return fail(MLORA_EINVAL, "row_adapter and seg_ws must not be NULL");
+  if ((reinterpret_cast<uintptr_t>(seg_ws) & 7u) != 0) return fail(MLORA_EINVAL, "seg_ws must be 8-byte aligned");
+  const PoolView v = p->view();
+  return hip_check(mlora::launch_seg_build(row_adapter, n, v.rank, v.max_adapters, static_cast<int32_t*>(seg_ws),
+                                           as_stream(stream)),
+                   "segment builder launch");
+}
+
+mlora_status mlora_segments_header(const void* seg_ws, int32_t* header, void* stream) {
+  g_err.clear();
+  if (!seg_ws || !header) return fail(MLORA_EINVAL, "seg_ws and header must not be NULL");
+  HIP_TRY(hipMemcpyAsync(header, seg_ws, MLORA_SEG_HEADER * sizeof(int32_t), hipMemcpyDeviceToHost, as_stream(stream)));
+  HIP_TRY(hipStreamSynchronize(as_stream(stream)));
+  return MLORA_OK;
+}
+
+mlora_status mlora_base_gemm(const uint16_t* X, const uint16_t* W0, uint16_t* Y, int32_t n, int32_t din,
+                             int32_t dout, void* stream) {
+  g_err.clear();
+  if (n < 0 || din < 1 || dout < 1) return fail(MLORA_EINVAL, "need n_rows >= 0, din >= 1, dout >= 1");
+  if (n == 0) return MLORA_OK;
+  if (!X || !W0 || !Y) return fail(MLORA_EINVAL, "X, W0 and Y must not be NULL");
+  return hip_check(mlora::launch_base_gemm(X, W0, Y, n, din, dout, as_stream(stream)), "base GEMM launch");
+}
+
+int32_t mlora_shrink_max_chunks(int32_t din) { return din < 1 ? 0 : (din + 511) / 512; }
+
+namespace {
+mlora_status check_branch_args(const mlora_pool* p, int32_t proj, const void* seg_ws, int32_t n) {
+  mlora_status st = check_pool(p);
+  if (st != MLORA_OK) return st;
+  if (proj < 0 || proj >= p->d.n_proj) return fail(MLORA_EINVAL, "proj %d outside [0, %d)", proj, p->d.n_proj);
+  if (n < 0 || n > MLORA_MAX_ROWS) return fail(MLORA_EINVAL, "n_rows %d outside [0, %d]", n, MLORA_MAX_ROWS);
+  if (!seg_ws) return fail(MLORA_EINVAL, "seg_ws must not be NULL");
+  return MLORA_OK;
+}
+int chunk_elems_for(int din, int n_chunks) {
+  const int per = (din + n_chunks - 1) / n_chunks;
+  return (per + 511) / 512 * 512;
+}
+}  // namespace
+
+mlora_status mlora_shrink(const mlora_pool* p, int32_t proj, const uint16_t* X, const void* seg_ws, int32_t n,
+                          float* T, int32_t n_chunks, void* stream) {
+  g_err.clear();
+  mlora_status st = check_branch_args(p, proj, seg_ws, n);
+  if (st != MLORA_OK) return st;
+  if (n_chunks < 1 || n_chunks > mlora_shrink_max_chunks(p->d.din))
+    return fail(MLORA_EINVAL, "n_chunks %d outside [1, %d]", n_chunks, mlora_shrink_max_chunks(p->d.din));
+  if (n == 0) return MLORA_OK;
+  if (!X || !T) return fail(MLORA_EINVAL, "X and T must not be NULL");
+  return hip_check(mlora::launch_shrink(p->view(), proj, X, static_cast<const int32_t*>(seg_ws), n, T, n_chunks,
+                                        chunk_elems_for(p->d.din, n_chunks), as_stream(stream)),
+                   "shrink launch");
+}
+
+mlora_status mlora_expand(const mlora_pool* p, int32_t proj, const float* T, int32_t n_chunks, const void* seg_ws,
+                          uint16_t* Y, int32_t n, void* stream) {
+  g_err.clear();
+  mlora_status st = check_branch_args(p, proj, seg_ws, n);
+  if (st != MLORA_OK) return st;
+  if (n_chunks < 1 || n_chunks > mlora_shrink_max_chunks(p->d.din))
+    return fail(MLORA_EINVAL, "n_chunks %d outside [1, %d]", n_chunks, mlora_shrink_max_chunks(p->d.din));
+  if (n == 0) return MLORA_OK;
+  if (!T || !Y) return fail(MLORA_EINVAL, "T and Y must not be NULL");
+  return hip_check(mlora::launch_expand(p->view(), proj, T, n_chunks, static_cast<const int32_t*>(seg_ws), Y, n,
+                                        as_stream(stream)),
+                   "expand launch");
+}
+
+mlora_status mlora_fused(const mlora_pool* p, int32_t proj, const uint16_t* X, const void* seg_ws, uint16_t* Y,
+                         int32_t n, void* stream) {
+  g_err.clear();
+  mlora_status st = check_branch_args(p, proj, seg_ws, n);
+  if (st != MLORA_OK) return st;
+  if (n == 0) return MLORA_OK;
+  if (!X || !Y) return fail(MLORA_EINVAL, "X and Y must not be NULL");
+  return hip_check(mlora::launch_fused(p->view(), proj, X, static_cast<const int32_t*>(seg_ws), Y, n,
+                                       as_stream(stream)),
+                   "fused launch");
+}
+
+namespace {
+// din slices for the split variant: enough waves to spread a small batch
+// over the chip, never more than kMaxSplitChunks
+int split_chunks(int din, int n) {
+  const int items = MLORA_SEG_MAX_ITEMS(n);
+  int c = (1024 + items - 1) / items;
+  c = std::min(c, kMaxSplitChunks);
+  c = std::min(c, mlora_shrink_max_chunks(din));
+  return std::max(c, 1);
+}
+}  // namespace
+
+size_t mlora_work_bytes(const mlora_pool* p, int32_t n) {
+  if (!p || n < 0) return 0;
+  return align256((size_t)split_chunks(p->d.din, n) * n * p->d.max_rank * sizeof(float));
+}
+
+mlora_status mlora_apply(const mlora_pool* p, int32_t proj, const uint16_t* X, const uint16_t* W0,
+                         const void* seg_ws, uint16_t* Y, int32_t n, void* work, size_t work_bytes, int32_t variant,
+                         void* stream) {
+  g_err.clear();
+  mlora_status st = check_branch_args(p, proj, seg_ws, n);
+  if (st != MLORA_OK) return st;
+  if (variant < MLORA_VARIANT_AUTO || variant > MLORA_VARIANT_FUSED) return fail(MLORA_EINVAL, "unknown variant %d", variant);
+  if (n == 0) return MLORA_OK;
+  if (!X || !W0 || !Y) return fail(MLORA_EINVAL, "X, W0 and Y must not be NULL");
+  const mlora_pool_desc& d = p->d;
+  hipStream_t s = as_stream(stream);
+  const PoolView v = p->view();
+  const int32_t* ws = static_cast<const int32_t*>(seg_ws);
+  if (variant == MLORA_VARIANT_AUTO) variant = MLORA_VARIANT_SPLIT;
+  if (variant == MLORA_VARIANT_SPLIT) {
+    const size_t need = mlora_work_bytes(p, n);
+    if (!work || work_bytes < need) return fail(MLORA_EINVAL, "work: %zu bytes given, %zu needed", work_bytes, need);
+    if (!aligned16(work)) return fail(MLORA_EINVAL, "work must be 16-byte aligned");
+  }
+  st = hip_check(mlora::launch_base_gemm(X, W0, Y, n, d.din, d.dout, s), "base GEMM launch");
+  if (st != MLORA_OK) return st;
+  if (variant == MLORA_VARIANT_FUSED)
+    return hip_check(mlora::launch_fused(v, proj, X, ws, Y, n, s), "fused launch");
+  const int chunks = split_chunks(d.din, n);
+  float* T = static_cast<float*>(work);
+  st = hip_check(mlora::launch_shrink(v, proj, X, ws, n, T, chunks, chunk_elems_for(d.din, chunks), s), "shrink launch");
+  if (st != MLORA_OK) return st;
+  return hip_check(mlora::launch_expand(v, proj, T, chunks, ws, Y, n, s), "expand launch");
+}
+
+mlora_status mlora_hbm_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  g_err.clear();
+  if (!dst || !src || bytes % 16 != 0 || !aligned16(dst) || !aligned16(src))
+    return fail(MLORA_EINVAL, "copy needs non-NULL 16-byte aligned pointers and a multiple of 16 bytes");
+  return hip_check(mlora::launch_hbm_copy(dst, src, bytes, as_stream(stream)), "copy launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,79 @@
+// Internal declarations shared by the library's translation units: device
+// helpers for bf16 data and the host-side launchers of every kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mlora.h"
+
+namespace mlora {
+
+// ----------------------------------------------------------------------------
+// device helpers
+// ----------------------------------------------------------------------------
+
+// bf16 bits -> float (exact)
+__device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// float -> bf16 bits, round to nearest even; NaN stays a quiet NaN
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// two bf16 packed in a 32-bit word -> two floats
+__device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) { return f2bf(a) | (f2bf(b) << 16); }
+
+// Eight consecutive bf16 of row `p` starting at element `i`, as floats.
+// VEC: the row base and i are 16-byte aligned and i + 8 <= limit, so one
+// 16-byte load serves; otherwise element loads, zero past `limit`.
+template <bool VEC>
+__device__ __forceinline__ void load8(const uint16_t* __restrict__ p, int i, int limit, float (&v)[8]) {
+  if (VEC) {
+    uint4 w = *reinterpret_cast<const uint4*>(p + i);
+    v[0] = lo_bf(w.x); v[1] = hi_bf(w.x); v[2] = lo_bf(w.y); v[3] = hi_bf(w.y);
+    v[4] = lo_bf(w.z); v[5] = hi_bf(w.z); v[6] = lo_bf(w.w); v[7] = hi_bf(w.w);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (i + e < limit) ? bf2f(p[i + e]) : 0.f;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// host launchers (return hipSuccess or the launch error)
+// ----------------------------------------------------------------------------
+
+// pool metadata view on the device
+struct PoolView {
+  const int32_t* rank;       // [max_adapters]
+  const float* scale;        // [max_adapters]
+  const int32_t* down_page;  // [max_adapters][n_proj][max_rank]
+  const int32_t* up_page;    // [max_adapters][n_proj][max_rank]
+  const uint16_t* down;      // [n_down_pages][din]
+  const uint16_t* up;        // [n_up_pages][dout]
+  int32_t din, dout, n_proj, max_adapters, max_rank;
+};
+
+hipError_t launch_seg_build(const int32_t* row_adapter, int n, const int32_t* pool_rank, int max_adapters,
+                            int32_t* ws, hipStream_t stream);
+
+hipError_t launch_base_gemm(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N,
+                            hipStream_t stream);
+
+hipError_t launch_shrink(const PoolView& pv, int proj, const uint16_t* X, const int32_t* ws, int n,
+                         float* T, int n_chunks, int chunk_elems, hipStream_t stream);
+
+hipError_t launch_expand(const PoolView& pv, int proj, const float* T, int n_chunks, const int32_t* ws,
+                         uint16_t* Y, int n, hipStream_t stream);
+
+hipError_t launch_fused(const PoolView& pv, int proj, const uint16_t* X, const int32_t* ws, uint16_t* Y,
+                        int n, hipStream_t stream);
+
+hipError_t launch_hbm_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+}  // namespace mlora

@@ -272,3 +272,17 @@ def random_ids(seed: int, n: int, adapters: List[int], p_none: float) -> np.ndar
     ids = g.choice(np.asarray(adapters, dtype=np.int32), size=n)
     ids[g.random(n) < p_none] = NONE
     return ids.astype(np.int32)
+
+
+def draw_t(seed: int, n: int, max_rank: int, n_chunks: int = 1) -> np.ndarray:
+    """Partial low-rank activations fed to the expand step on its own:
+    fp32 [n_chunks][n][max_rank] ~ N(0, 1/n_chunks), so each row's sum over
+    chunks is ~ N(0, 1)."""
+    g = _rng(seed, 5, n, max_rank, n_chunks)
+    return (g.standard_normal(size=(n_chunks, n, max_rank), dtype=np.float32)
+            * np.float32(1.0 / np.sqrt(n_chunks)))
+
+
+def draw_bf16(seed: int, shape, std: float = 1.0) -> np.ndarray:
+    """Any other bf16 tensor a test feeds in (e.g. the Y an expand adds to)."""
+    return round_to_bf16_bits(_normal(seed, (6,) + tuple(int(s) for s in shape), shape, std))

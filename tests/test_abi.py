@@ -1,0 +1,59 @@
+"""The C-ABI library: it loads on a machine without a GPU and exports every
+entry point include/mlora.h declares (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import lora_serving_mlora_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mlora.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mlora_[a-z0-9_]+)\s*\(", src)) - {"mlora_status"})
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("mlora_pool_load", "mlora_build_segments", "mlora_apply", "mlora_shrink", "mlora_expand",
+                 "mlora_fused", "mlora_base_gemm", "mlora_pool_create", "mlora_pool_unload"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    if not os.path.exists(M.LIB_PATH):
+        pytest.skip("libmlora.so not built")
+    L = ctypes.CDLL(M.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert set(declared_functions()) == set(M.EXPORTS)
+
+
+def test_host_only_calls():
+    """Calls that touch no device: sizes, strings, argument errors."""
+    if not os.path.exists(M.LIB_PATH):
+        pytest.skip("libmlora.so not built")
+    L = M.lib()
+    assert L.mlora_version().startswith(b"mlora")
+    assert L.mlora_status_string(M.ENOSPC) == b"no free pages"
+    # meta: 256-aligned regions rank, scale, two page tables
+    A, P, R = 100, 64, 16
+    pt = A * P * R * 4
+    al = lambda x: (x + 255) // 256 * 256
+    assert L.mlora_pool_meta_bytes(A, P, R) == al(4 * A) * 2 + al(pt) * 2
+    assert L.mlora_pool_meta_bytes(0, 1, 1) == 0
+    n = 4096
+    items0 = (16 + 4 * n + 2) & ~1
+    max_items = n + (n + 3) // 4 + 1
+    assert L.mlora_segments_bytes(n) == al((items0 + 2 * max_items) * 4)
+    assert L.mlora_shrink_max_chunks(4096) == 8 and L.mlora_shrink_max_chunks(4) == 1
+    assert L.mlora_pool_create(None, None, None) == M.EINVAL
+    assert b"NULL" in L.mlora_last_error()
+    assert L.mlora_base_gemm(None, None, None, 0, 4, 4, None) == M.OK     # n = 0 is a no-op
+    assert L.mlora_base_gemm(None, None, None, 1, 0, 4, None) == M.EINVAL
+    assert L.mlora_hbm_copy(None, None, 16, None) == M.EINVAL
