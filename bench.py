@@ -1,0 +1,340 @@
+#!/usr/bin/env python3
+"""Throughput of the heterogeneous multi-LoRA linear on one MI355X.
+
+One step = one batch through the whole layer: build the segments (group rows
+by adapter), the base GEMM Y = X W0^T, and the low-rank branch (shrink then
+expand, or the fused kernel), for the variant the library's planner picks.
+The steps of the timed region are replayed from a captured HIP graph, so the
+number is the GPU's, not the Python launcher's.  Inputs are seeded synthetic
+tensors already resident in HBM.  Consecutive steps rotate over distinct
+copies of W0 and of the adapter pages (distinct projections of one pool), at
+least 1 GiB in all, so that the 256 MB last-level cache cannot serve a step
+from the previous one.
+
+Prints ONE JSON line: tokens/s (whole batch rows per second of step time),
+the dominant kernel's roofline fraction (its algorithmic bytes or flops per
+launch over its average duration measured with HIP events on the launch
+stream inside the timed region), per-kernel averages, and the CPU oracle
+timed on the host cores as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "tokens/s per multi-LoRA linear (4096², r=16) + % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak, published
+RIDGE = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
+KERNEL_SOURCES = {"base_gemm": "base_gemm.hip", "shrink": "lora_branch.hip", "expand": "lora_branch.hip",
+                  "fused": "lora_branch.hip", "segments": "seg_build.hip"}
+DEFAULT_WORKLOAD = "decode_3"
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(synth.NAMED))
+    ap.add_argument("--variant", default="auto", choices=["auto", "split", "fused"])
+    ap.add_argument("--rotate-bytes", type=float, default=1.0, help="GiB of distinct weights to rotate over")
+    ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of from a HIP graph")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-only", action="store_true", help="only run the HBM copy calibration kernel")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work per launch (what the method must move / compute)
+# ---------------------------------------------------------------------------
+
+def segment_sizes(w):
+    ids = w.row_adapter
+    act = ids[(ids >= 0) & np.isin(ids, w.adapter_ids())]
+    counts = np.bincount(act, minlength=w.max_adapters)
+    segs = [(a, int(c), w.ranks[a]) for a, c in enumerate(counts) if c > 0]
+    return segs, int(act.size)
+
+
+def algorithmic(w, chunks):
+    """{kernel: (bytes, flops)} per launch."""
+    n, din, dout = w.n, w.din, w.dout
+    segs, n_act = segment_sizes(w)
+    sum_r = sum(r for _, _, r in segs)
+    sum_nr = sum(c * r for _, c, r in segs)
+    out = {
+        "base_gemm": (2 * (dout * din + n * din + n * dout), 2 * n * din * dout),
+        "shrink": (2 * sum_r * din + 2 * n_act * din + 4 * sum_nr * max(chunks, 1), 2 * sum_nr * din),
+        "expand": (2 * sum_r * dout + 4 * n_act * dout + 4 * sum_nr * max(chunks, 1), 2 * sum_nr * dout),
+        "fused": (2 * sum_r * (din + dout) + 2 * n_act * din + 4 * n_act * dout, 2 * sum_nr * (din + dout)),
+        "segments": (4 * n + 4 * 4 * n, 0),
+    }
+    return out
+
+
+def source_hash(kernel):
+    p = os.path.join(ROOT, "lora_serving_mlora_amd", "csrc", KERNEL_SOURCES[kernel])
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the kernel source as it is now (else None)."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        with open(p) as f:
+            rec = json.load(f).get(f"{kernel}/{workload}")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256_16") != source_hash(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(w, seconds):
+    """The oracle as it stands, in fp32, on this host: per-row loop over the
+    workload's rows (projection 0), repeated until `seconds` have passed."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    X = O.widen_bf16(w.x_bits(), np.float32)
+    W0 = O.widen_bf16(w.w0_bits(0), np.float32)
+    ad = {a: (float(w.scales[a]), O.widen_bf16(w.down_bits(a, 0), np.float32),
+              O.widen_bf16(w.up_bits(a, 0), np.float32)) for a in w.adapter_ids()}
+    rows_done, t0 = 0, time.perf_counter()
+    block = min(w.n, 64)
+    start = 0
+    while True:
+        rows = [(start + i) % w.n for i in range(block)]
+        O.linear(X, W0, w.row_adapter, ad, w.max_adapters, rows=rows, dtype=np.float32)
+        rows_done += block
+        start = (start + block) % w.n
+        el = time.perf_counter() - t0
+        if el >= seconds and rows_done >= min(w.n, 64):
+            break
+    return {"value": rows_done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows_done} rows of the {w.name} batch (projection 0), per-row fp32 numpy loop "
+                      f"of the oracle, {el:.1f} s on {os.cpu_count()} host cores"}
+
+
+# ---------------------------------------------------------------------------
+# GPU
+# ---------------------------------------------------------------------------
+
+def copy_calibration(M, torch, gib=1.0, reps=10):
+    nb = int(gib * 2 ** 30)
+    src = torch.empty(nb // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    M.hbm_copy(dst, src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        M.hbm_copy(dst, src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return {"bytes_moved": 2 * nb, "ms": ms, "gbps": 2 * nb / ms / 1e6}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no multi-GPU path; "
+              "the layer shards by adapter-affine routing or by dout columns with no exchange inside the "
+              "linear (see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import lora_serving_mlora_amd as M
+    M.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+
+    if args.copy_only:
+        cal = copy_calibration(M, torch)
+        print(json.dumps({"copy_calibration": cal}))
+        return
+
+    w = synth.NAMED[args.workload]()
+    n = w.n
+    # rotation: distinct projections of one pool, each with its own W0 copy
+    per_proj = 2 * w.din * w.dout + 2 * sum(w.ranks.values()) * (w.din + w.dout)
+    R = max(1, math.ceil(args.rotate_bytes * 2 ** 30 / per_proj))
+    if w.n_proj > 1:
+        R = w.n_proj   # the workload is a layer stack: rotate over its own projections
+    print(f"[bench] workload {w.name}: n={n} din={w.din} dout={w.dout} adapters={len(w.ranks)} "
+          f"rotation={R} projections", file=sys.stderr, flush=True)
+
+    n_pages = sum(w.ranks.values()) * R
+    pool = M.Pool(w.din, w.dout, R, w.max_adapters, w.max_rank, n_pages)
+    for a in w.adapter_ids():
+        if w.n_proj > 1:
+            d, u = w.down_all_bits(a), w.up_all_bits(a)
+        else:   # the same weights at R distinct addresses
+            d = np.repeat(w.down_bits(a, 0)[None], R, axis=0)
+            u = np.repeat(w.up_bits(a, 0)[None], R, axis=0)
+        pool.load(a, w.ranks[a], w.scales[a], d, u)
+    X = torch.from_numpy(w.x_bits().view(np.int16)).view(torch.bfloat16).cuda()
+    if w.n_proj > 1:
+        W0s = [torch.from_numpy(w.w0_bits(p).view(np.int16)).view(torch.bfloat16).cuda() for p in range(R)]
+    else:
+        W00 = torch.from_numpy(w.w0_bits(0).view(np.int16)).view(torch.bfloat16).cuda()
+        W0s = [W00.clone() for _ in range(R)]
+        del W00
+    ids = torch.from_numpy(w.row_adapter.astype(np.int32)).cuda()
+    seg_ws = M.build_segments(pool, ids)
+    Y = torch.empty((n, w.dout), dtype=torch.bfloat16, device="cuda")
+    variant, chunks = M.plan(pool, n, args.variant)
+    T = torch.zeros((max(chunks, 1), n, w.max_rank), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    print(f"[bench] plan: variant={variant} shrink_chunks={chunks}", file=sys.stderr, flush=True)
+
+    kernels = ["segments", "base_gemm"] + (["fused"] if variant == "fused" else ["shrink", "expand"])
+
+    def step(i, evs=None):
+        p = i % R
+        rec = (lambda k: evs[k].record()) if evs is not None else (lambda k: None)
+        rec(0)
+        M.build_segments(pool, ids, seg_ws)
+        rec(1)
+        M.base_gemm(X, W0s[p], Y)
+        rec(2)
+        if variant == "fused":
+            M.fused(pool, p, X, seg_ws, Y)
+        else:
+            M.shrink(pool, p, X, seg_ws, chunks, T)
+            rec(3)
+            M.expand(pool, p, T, seg_ws, Y)
+        rec(len(kernels))
+
+    K, W = args.steps, args.warmup
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps replayed from one captured HIP graph
+    use_graph = not args.no_graph
+    graph = None
+    if use_graph:
+        try:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(K):
+                    step(W + i)
+            graph.replay()           # warm replay (untimed)
+            torch.cuda.synchronize()
+        except Exception as e:  # fall back to eager launches
+            print(f"[bench] graph capture unavailable ({e}); timing eager launches", file=sys.stderr)
+            graph, use_graph = None, False
+            torch.cuda.synchronize()
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(K):
+            step(W + i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    print(f"[bench] timed {K} steps: {ms_per_step * 1e3:.2f} us/step", file=sys.stderr, flush=True)
+
+    # ---- per-kernel durations: HIP events on the launch stream around each
+    # kernel of the same K steps, launched eagerly behind a spin kernel so the
+    # queue is full and host launch gaps stay out of the intervals
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(K)]
+    spin = getattr(torch.cuda, "_sleep", None)
+    if spin is not None:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        spin(1_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        per_cycle_ms = max(a.elapsed_time(b), 1e-3) / 1_000_000
+        spin_cycles = int(min(5e9, (0.05 + 100e-6 * K) * 1e3 / per_cycle_ms))
+    torch.cuda.synchronize()
+    if spin is not None:
+        spin(spin_cycles)
+    t2 = time.perf_counter()
+    for i in range(K):
+        step(W + i, events[i])
+    host_enqueue_s = time.perf_counter() - t2
+    torch.cuda.synchronize()
+    per_kernel_ms = {}
+    for k, name in enumerate(kernels):
+        per_kernel_ms[name] = float(np.mean([events[i][k].elapsed_time(events[i][k + 1]) for i in range(K)]))
+    step_gpu_ms = float(np.mean([events[i][0].elapsed_time(events[i][len(kernels)]) for i in range(K)]))
+    queue_ok = spin is not None and host_enqueue_s * 1e3 < (0.05 + 100e-6 * K) * 1e3
+    timing = ("hip events on the launch stream, eager pass of the same steps behind a spin kernel "
+              f"({'queue stayed full' if queue_ok else 'queue may have drained'})")
+    if not bool(torch.isfinite(Y.float()).all()):
+        print("[bench] warning: non-finite outputs", file=sys.stderr)
+
+    algo = algorithmic(w, chunks)
+    timed = {k: v for k, v in per_kernel_ms.items() if v}
+    dom = max((k for k in timed if k != "segments"), key=lambda k: timed[k])
+    b, f = algo[dom]
+    t_s = timed[dom] * 1e-3
+    mfma_bound = dom == "base_gemm" and f / b > RIDGE
+    if mfma_bound:
+        ach, peak, unit = f / t_s / 1e12, MFMA_BF16_PEAK_TFS, "TFLOP/s"
+    else:
+        ach, peak, unit = b / t_s / 1e9, HBM_PEAK_GBS, "GB/s"
+    roofline = {"bound": "mfma" if mfma_bound else "hbm", "kernel": dom, "achieved": round(ach, 2),
+                "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
+                "traffic": measured_traffic(dom, args.workload),
+                "algorithmic_bytes": b, "algorithmic_flops": f, "avg_us": round(timed[dom] * 1e3, 3),
+                "timing": timing}
+
+    tokens_per_s = n / (ms_per_step * 1e-3)
+    cal = copy_calibration(M, torch)
+    result = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "n_tokens": n, "din": w.din, "dout": w.dout,
+                   "adapters": len(w.ranks), "ranks": sorted(set(w.ranks.values())),
+                   "variant": variant, "shrink_chunks": chunks, "rotation_projections": R,
+                   "launch": "hipgraph" if use_graph else "eager", "parallelism": "single-gpu"},
+        "roofline": roofline,
+        "per_kernel_us": {k: (round(v * 1e3, 3) if v else None) for k, v in per_kernel_ms.items()},
+        "step_gpu_us": round(step_gpu_ms * 1e3, 3),
+        "branch_over_base": (round((sum(timed.get(k, 0) for k in ("shrink", "expand", "fused"))) /
+                                   timed["base_gemm"], 4) if timed.get("base_gemm") else None),
+        "hbm_copy_gbps": round(cal["gbps"], 1),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

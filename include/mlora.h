@@ -221,7 +221,8 @@ mlora_status mlora_shrink(const mlora_pool* pool, int32_t proj, const uint16_t* 
 
 /* Expand, Y[perm[j]] += s_a * Up_a t_j (read-modify-write in fp32, stored as
  * bf16 RNE; no atomics: one thread owns each output element), with t_j the
- * sum over the n_chunks partials of T (layout as mlora_shrink).  Rows with
+ * sum over the n_chunks partials of T (layout as mlora_shrink; 1 <= n_chunks
+ * <= 1024, summed in slice order).  Rows with
  * an invalid id are set to NaN; base-only rows are untouched. */
 mlora_status mlora_expand(const mlora_pool* pool, int32_t proj, const float* T, int32_t n_chunks,
                           const void* seg_ws, uint16_t* Y, int32_t n_rows, void* stream);
@@ -243,6 +244,14 @@ mlora_status mlora_fused(const mlora_pool* pool, int32_t proj, const uint16_t* X
  * n_rows = 0 is a no-op.
  * ------------------------------------------------------------------------- */
 size_t mlora_work_bytes(const mlora_pool* pool, int32_t n_rows);
+
+/* The launch plan mlora_apply follows for `variant` (AUTO resolved) on a
+ * batch of n_rows: the branch variant it runs and, for SPLIT, the number of
+ * din slices of its shrink (the n_chunks of mlora_shrink/mlora_expand).
+ * Host only; lets a caller run the same steps one by one. */
+mlora_status mlora_plan(const mlora_pool* pool, int32_t n_rows, int32_t variant, int32_t* out_variant,
+                        int32_t* out_chunks);
+
 mlora_status mlora_apply(const mlora_pool* pool, int32_t proj, const uint16_t* X, const uint16_t* W0,
                          const void* seg_ws, uint16_t* Y, int32_t n_rows, void* work, size_t work_bytes,
                          int32_t variant, void* stream);

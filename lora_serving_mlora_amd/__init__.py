@@ -22,7 +22,7 @@ import numpy as np
 
 __all__ = [
     "MloraError", "lib", "Pool", "build_segments", "segments_header", "read_segments",
-    "base_gemm", "shrink", "shrink_max_chunks", "expand", "fused", "apply", "work_bytes",
+    "base_gemm", "shrink", "shrink_max_chunks", "expand", "fused", "apply", "plan", "work_bytes",
     "hbm_copy", "VARIANTS", "ITEM_ROWS", "MAX_ROWS", "MAX_RANK", "SEG", "EXPORTS", "LIB_PATH",
 ]
 
@@ -67,6 +67,7 @@ EXPORTS = {
     "mlora_expand": (ctypes.c_int, [_c_void_p, _i32, _c_void_p, _i32, _c_void_p, _c_void_p, _i32, _c_void_p]),
     "mlora_fused": (ctypes.c_int, [_c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p]),
     "mlora_work_bytes": (_sz, [_c_void_p, _i32]),
+    "mlora_plan": (ctypes.c_int, [_c_void_p, _i32, _i32, _pi32, _pi32]),
     "mlora_apply": (ctypes.c_int, [_c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p,
                                    _sz, _i32, _c_void_p]),
     "mlora_hbm_copy": (ctypes.c_int, [_c_void_p, _c_void_p, _sz, _c_void_p]),
@@ -309,6 +310,13 @@ def fused(pool: Pool, proj: int, X, seg_ws, Y):
 
 def work_bytes(pool: Pool, n: int) -> int:
     return int(lib().mlora_work_bytes(pool.handle, n))
+
+
+def plan(pool: Pool, n: int, variant: str = "auto"):
+    """(variant name, shrink slices) that apply() runs for a batch of n rows."""
+    v, c = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().mlora_plan(pool.handle, n, VARIANTS[variant], ctypes.byref(v), ctypes.byref(c)), "mlora_plan")
+    return {0: "auto", 1: "split", 2: "fused"}[v.value], c.value
 
 
 def apply(pool: Pool, proj: int, X, W0, seg_ws, Y=None, work=None, variant: str = "auto"):

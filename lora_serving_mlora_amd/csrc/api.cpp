@@ -95,6 +95,7 @@ class RangeAlloc {
     nfree_ -= c;
   }
   void put(int64_t s, int64_t c) {
+    nfree_ += c;
     auto next = free_.lower_bound(s);
     if (next != free_.begin()) {
       auto prev = std::prev(next);
@@ -110,7 +111,6 @@ class RangeAlloc {
       free_.erase(next);
     }
     free_[s] = c;
-    nfree_ += c;
   }
   std::map<int64_t, int64_t> free_;
   int64_t nfree_ = 0;
@@ -133,6 +133,7 @@ MetaLayout meta_layout(int32_t A, int32_t P, int32_t R) {
 
 constexpr size_t kStageBytes = size_t(8) << 20;  // two pinned staging buffers of 8 MiB
 constexpr int kMaxSplitChunks = 8;               // din slices used by the split variant
+constexpr int kMaxExpandChunks = 1024;           // partial-t slices an expand accepts
 
 }  // namespace
 
@@ -523,8 +524,8 @@ mlora_status mlora_expand(const mlora_pool* p, int32_t proj, const float* T, int
   g_err.clear();
   mlora_status st = check_branch_args(p, proj, seg_ws, n);
   if (st != MLORA_OK) return st;
-  if (n_chunks < 1 || n_chunks > mlora_shrink_max_chunks(p->d.din))
-    return fail(MLORA_EINVAL, "n_chunks %d outside [1, %d]", n_chunks, mlora_shrink_max_chunks(p->d.din));
+  if (n_chunks < 1 || n_chunks > kMaxExpandChunks)
+    return fail(MLORA_EINVAL, "n_chunks %d outside [1, %d]", n_chunks, kMaxExpandChunks);
   if (n == 0) return MLORA_OK;
   if (!T || !Y) return fail(MLORA_EINVAL, "T and Y must not be NULL");
   return hip_check(mlora::launch_expand(p->view(), proj, T, n_chunks, static_cast<const int32_t*>(seg_ws), Y, n,
@@ -554,11 +555,28 @@ int split_chunks(int din, int n) {
   c = std::min(c, mlora_shrink_max_chunks(din));
   return std::max(c, 1);
 }
+// AUTO: the branch variant for a batch of n rows
+int32_t auto_variant(const mlora_pool* p, int n) {
+  (void)p;
+  (void)n;
+  return MLORA_VARIANT_SPLIT;
+}
 }  // namespace
 
 size_t mlora_work_bytes(const mlora_pool* p, int32_t n) {
   if (!p || n < 0) return 0;
   return align256((size_t)split_chunks(p->d.din, n) * n * p->d.max_rank * sizeof(float));
+}
+
+mlora_status mlora_plan(const mlora_pool* p, int32_t n, int32_t variant, int32_t* out_variant, int32_t* out_chunks) {
+  g_err.clear();
+  if (!p) return fail(MLORA_EINVAL, "pool is NULL");
+  if (n < 0 || n > MLORA_MAX_ROWS) return fail(MLORA_EINVAL, "n_rows %d outside [0, %d]", n, MLORA_MAX_ROWS);
+  if (variant < MLORA_VARIANT_AUTO || variant > MLORA_VARIANT_FUSED) return fail(MLORA_EINVAL, "unknown variant %d", variant);
+  if (variant == MLORA_VARIANT_AUTO) variant = auto_variant(p, n);
+  if (out_variant) *out_variant = variant;
+  if (out_chunks) *out_chunks = variant == MLORA_VARIANT_SPLIT ? split_chunks(p->d.din, n) : 0;
+  return MLORA_OK;
 }
 
 mlora_status mlora_apply(const mlora_pool* p, int32_t proj, const uint16_t* X, const uint16_t* W0,
@@ -574,7 +592,7 @@ mlora_status mlora_apply(const mlora_pool* p, int32_t proj, const uint16_t* X, c
   hipStream_t s = as_stream(stream);
   const PoolView v = p->view();
   const int32_t* ws = static_cast<const int32_t*>(seg_ws);
-  if (variant == MLORA_VARIANT_AUTO) variant = MLORA_VARIANT_SPLIT;
+  if (variant == MLORA_VARIANT_AUTO) variant = auto_variant(p, n);
   if (variant == MLORA_VARIANT_SPLIT) {
     const size_t need = mlora_work_bytes(p, n);
     if (!work || work_bytes < need) return fail(MLORA_EINVAL, "work: %zu bytes given, %zu needed", work_bytes, need);
