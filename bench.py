@@ -39,7 +39,8 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak, published
 RIDGE = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
 KERNEL_SOURCES = {"base_gemm": "base_gemm.hip", "shrink": "lora_branch.hip", "expand": "lora_branch.hip",
-                  "fused": "lora_branch.hip", "segments": "seg_build.hip"}
+                  "fused": "lora_branch.hip", "segments": "seg_build.hip", "shrink_rows": "lora_branch.hip",
+                  "gemm_lora": "base_gemm.hip"}
 DEFAULT_WORKLOAD = "decode_3"
 
 
@@ -49,12 +50,14 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(synth.NAMED))
-    ap.add_argument("--variant", default="auto", choices=["auto", "split", "fused"])
+    ap.add_argument("--variant", default="auto", choices=["auto", "split", "fused", "rows"])
     ap.add_argument("--rotate-bytes", type=float, default=1.0, help="GiB of distinct weights to rotate over")
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of from a HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-only", action="store_true", help="only run the HBM copy calibration kernel")
+    ap.add_argument("--yardstick", action="store_true",
+                    help="also time the vendor GEMM (torch linear) on the same rotated operands, for context")
     return ap.parse_args()
 
 
@@ -83,6 +86,11 @@ def algorithmic(w, chunks):
         "fused": (2 * sum_r * (din + dout) + 2 * n_act * din + 4 * n_act * dout, 2 * sum_nr * (din + dout)),
         "segments": (4 * n + 4 * 4 * n, 0),
     }
+    # per-row decode path: the shrink moves what the grouped shrink moves; the
+    # GEMM kernel adds each distinct adapter's Up and the per-row t
+    out["shrink_rows"] = (2 * sum_r * din + 2 * n_act * din + 4 * sum_nr, 2 * sum_nr * din)
+    out["gemm_lora"] = (out["base_gemm"][0] + 2 * sum_r * dout + 4 * sum_nr,
+                        out["base_gemm"][1] + 2 * sum_nr * dout)
     return out
 
 
@@ -216,7 +224,11 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] plan: variant={variant} shrink_chunks={chunks}", file=sys.stderr, flush=True)
 
-    kernels = ["segments", "base_gemm"] + (["fused"] if variant == "fused" else ["shrink", "expand"])
+    if variant == "rows":
+        kernels = ["segments", "shrink_rows", "gemm_lora"]
+    else:
+        kernels = ["segments", "base_gemm"] + (["fused"] if variant == "fused" else ["shrink", "expand"])
+    T_rows = torch.zeros((n, w.max_rank), dtype=torch.float32, device="cuda")
 
     def step(i, evs=None):
         p = i % R
@@ -224,14 +236,19 @@ def main():
         rec(0)
         M.build_segments(pool, ids, seg_ws)
         rec(1)
-        M.base_gemm(X, W0s[p], Y)
-        rec(2)
-        if variant == "fused":
-            M.fused(pool, p, X, seg_ws, Y)
+        if variant == "rows":
+            M.shrink_rows(pool, p, X, seg_ws, T_rows)
+            rec(2)
+            M.gemm_lora(pool, p, X, W0s[p], seg_ws, T_rows, Y)
         else:
-            M.shrink(pool, p, X, seg_ws, chunks, T)
-            rec(3)
-            M.expand(pool, p, T, seg_ws, Y)
+            M.base_gemm(X, W0s[p], Y)
+            rec(2)
+            if variant == "fused":
+                M.fused(pool, p, X, seg_ws, Y)
+            else:
+                M.shrink(pool, p, X, seg_ws, chunks, T)
+                rec(3)
+                M.expand(pool, p, T, seg_ws, Y)
         rec(len(kernels))
 
     K, W = args.steps, args.warmup
@@ -303,7 +320,7 @@ def main():
     dom = max((k for k in timed if k != "segments"), key=lambda k: timed[k])
     b, f = algo[dom]
     t_s = timed[dom] * 1e-3
-    mfma_bound = dom == "base_gemm" and f / b > RIDGE
+    mfma_bound = dom in ("base_gemm", "gemm_lora") and f / b > RIDGE
     if mfma_bound:
         ach, peak, unit = f / t_s / 1e12, MFMA_BF16_PEAK_TFS, "TFLOP/s"
     else:
@@ -313,6 +330,24 @@ def main():
                 "traffic": measured_traffic(dom, args.workload),
                 "algorithmic_bytes": b, "algorithmic_flops": f, "avg_us": round(timed[dom] * 1e3, 3),
                 "timing": timing}
+
+    yardstick = None
+    if args.yardstick:
+        # the vendor library's GEMM on the same operands and rotation, as a
+        # point of comparison for the base GEMM only (not part of the path)
+        import torch.nn.functional as F
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for i in range(min(K, 2 * R)):
+            F.linear(X, W0s[i % R])
+        torch.cuda.synchronize()
+        if spin is not None:
+            spin(spin_cycles)
+        ev[0].record()
+        for i in range(K):
+            F.linear(X, W0s[i % R])
+        ev[1].record()
+        torch.cuda.synchronize()
+        yardstick = round(ev[0].elapsed_time(ev[1]) / K * 1e3, 3)
 
     tokens_per_s = n / (ms_per_step * 1e-3)
     cal = copy_calibration(M, torch)
@@ -329,8 +364,11 @@ def main():
         "step_gpu_us": round(step_gpu_ms * 1e3, 3),
         "branch_over_base": (round((sum(timed.get(k, 0) for k in ("shrink", "expand", "fused"))) /
                                    timed["base_gemm"], 4) if timed.get("base_gemm") else None),
+        "gpu_name": torch.cuda.get_device_name(0),
         "hbm_copy_gbps": round(cal["gbps"], 1),
     }
+    if yardstick is not None:
+        result["vendor_gemm_us"] = yardstick
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result))

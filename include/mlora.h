@@ -62,7 +62,10 @@ typedef enum mlora_status {
 typedef enum mlora_variant {
   MLORA_VARIANT_AUTO = 0,
   MLORA_VARIANT_SPLIT = 1, /* shrink kernel -> fp32 t in `work` -> expand kernel */
-  MLORA_VARIANT_FUSED = 2  /* one kernel per row tile: t stays on chip           */
+  MLORA_VARIANT_FUSED = 2, /* one kernel per row tile: t stays on chip           */
+  MLORA_VARIANT_ROWS = 3   /* decode batches (n_rows <= 64): per-row shrink, then
+                              the base GEMM with the expand in extra waves of the
+                              same kernel, overlapped with its K loop           */
 } mlora_variant;
 
 /* Limits. */
@@ -168,6 +171,9 @@ mlora_status mlora_pool_free_pages(const mlora_pool* pool, int64_t* free_down, i
  *   items[2*max_items] at MLORA_SEG_ITEMS(n): work items (segment, first
  *                      sorted position), each covering up to MLORA_ITEM_ROWS
  *                      rows of one segment, in segment order.
+ *   row_key[n]         at MLORA_SEG_ROWKEY(n): per original row, the
+ *                      adapter id if resident, -1 for a base-only row, -2
+ *                      for an invalid id (what the per-row kernels read).
  * ------------------------------------------------------------------------- */
 #define MLORA_SEG_NSEG 0
 #define MLORA_SEG_NACT 1
@@ -184,6 +190,7 @@ mlora_status mlora_pool_free_pages(const mlora_pool* pool, int64_t* free_down, i
 #define MLORA_SEG_OFF(n) (MLORA_SEG_HEADER + 3 * (n))
 #define MLORA_SEG_ITEMS(n) ((MLORA_SEG_HEADER + 4 * (n) + 2) & ~1)
 #define MLORA_SEG_MAX_ITEMS(n) ((n) + ((n) + MLORA_ITEM_ROWS - 1) / MLORA_ITEM_ROWS + 1)
+#define MLORA_SEG_ROWKEY(n) (MLORA_SEG_ITEMS(n) + 2 * MLORA_SEG_MAX_ITEMS(n))
 
 size_t mlora_segments_bytes(int32_t n_rows);
 
@@ -233,6 +240,21 @@ mlora_status mlora_expand(const mlora_pool* pool, int32_t proj, const float* T, 
 mlora_status mlora_fused(const mlora_pool* pool, int32_t proj, const uint16_t* X, const void* seg_ws,
                          uint16_t* Y, int32_t n_rows, void* stream);
 
+/* Per-row shrink for decode batches (rows read directly by index, as the
+ * M031 card's section 02 allows instead of regrouping): for every row k on a
+ * resident adapter a, T[k][q] = s_a * (Down_a x_k)[q] for q < rank(a), fp32
+ * [n_rows][max_rank] in ORIGINAL row order (scale folded in).  Other rows
+ * and columns are not written.  Reads the row keys of seg_ws. */
+mlora_status mlora_shrink_rows(const mlora_pool* pool, int32_t proj, const uint16_t* X, const void* seg_ws,
+                               int32_t n_rows, float* T, void* stream);
+
+/* Base GEMM with the expand of the low-rank branch in the same kernel, for
+ * n_rows <= 64: Y = X W0^T, plus for every row k on a resident adapter
+ * sum_q T[k][q] Up_a[:, q] (T from mlora_shrink_rows); rows with an invalid
+ * id become NaN; base-only rows get the plain product.  Y is written once. */
+mlora_status mlora_gemm_lora(const mlora_pool* pool, int32_t proj, const uint16_t* X, const uint16_t* W0,
+                             const void* seg_ws, const float* T, uint16_t* Y, int32_t n_rows, void* stream);
+
 /* ---------------------------------------------------------------------------
  * The whole layer for one projection of one batch:
  *   Y = X W0^T, then every row's low-rank term added at its original row.
@@ -246,8 +268,9 @@ mlora_status mlora_fused(const mlora_pool* pool, int32_t proj, const uint16_t* X
 size_t mlora_work_bytes(const mlora_pool* pool, int32_t n_rows);
 
 /* The launch plan mlora_apply follows for `variant` (AUTO resolved) on a
- * batch of n_rows: the branch variant it runs and, for SPLIT, the number of
- * din slices of its shrink (the n_chunks of mlora_shrink/mlora_expand).
+ * batch of n_rows: the variant it runs and, for SPLIT, the number of din
+ * slices of its shrink (the n_chunks of mlora_shrink/mlora_expand).  ROWS
+ * is only valid for n_rows <= 64.
  * Host only; lets a caller run the same steps one by one. */
 mlora_status mlora_plan(const mlora_pool* pool, int32_t n_rows, int32_t variant, int32_t* out_variant,
                         int32_t* out_chunks);

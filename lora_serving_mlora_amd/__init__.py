@@ -22,14 +22,14 @@ import numpy as np
 
 __all__ = [
     "MloraError", "lib", "Pool", "build_segments", "segments_header", "read_segments",
-    "base_gemm", "shrink", "shrink_max_chunks", "expand", "fused", "apply", "plan", "work_bytes",
+    "base_gemm", "shrink", "shrink_max_chunks", "expand", "fused", "shrink_rows", "gemm_lora", "apply", "plan", "work_bytes",
     "hbm_copy", "VARIANTS", "ITEM_ROWS", "MAX_ROWS", "MAX_RANK", "SEG", "EXPORTS", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmlora.so")
 
 OK, EINVAL, ENOSPC, EEXIST, ENOENT, EHIP = range(6)
-VARIANTS = {"auto": 0, "split": 1, "fused": 2}
+VARIANTS = {"auto": 0, "split": 1, "fused": 2, "rows": 3}
 ITEM_ROWS = 4
 MAX_ROWS = 16384
 MAX_RANK = 128
@@ -67,6 +67,9 @@ EXPORTS = {
     "mlora_expand": (ctypes.c_int, [_c_void_p, _i32, _c_void_p, _i32, _c_void_p, _c_void_p, _i32, _c_void_p]),
     "mlora_fused": (ctypes.c_int, [_c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p]),
     "mlora_work_bytes": (_sz, [_c_void_p, _i32]),
+    "mlora_shrink_rows": (ctypes.c_int, [_c_void_p, _i32, _c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p]),
+    "mlora_gemm_lora": (ctypes.c_int, [_c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32,
+                                       _c_void_p]),
     "mlora_plan": (ctypes.c_int, [_c_void_p, _i32, _i32, _pi32, _pi32]),
     "mlora_apply": (ctypes.c_int, [_c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p,
                                    _sz, _i32, _c_void_p]),
@@ -244,6 +247,9 @@ def read_segments(seg_ws, n: int) -> dict:
     perm0, inv0, ad0, off0 = SEG_HEADER, SEG_HEADER + n, SEG_HEADER + 2 * n, SEG_HEADER + 3 * n
     items0 = (SEG_HEADER + 4 * n + 2) & ~1
     out = dict(hdr)
+    max_items = n + (n + ITEM_ROWS - 1) // ITEM_ROWS + 1
+    rk0 = items0 + 2 * max_items
+    out["row_key"] = w[rk0:rk0 + n].copy()
     out.update(perm=w[perm0:perm0 + n].copy(), inv=w[inv0:inv0 + n].copy(),
                seg_adapter=w[ad0:ad0 + nseg].copy(), seg_off=w[off0:off0 + nseg + 1].copy(),
                items=w[items0:items0 + 2 * hdr["n_items"]].reshape(-1, 2).copy())
@@ -308,6 +314,32 @@ def fused(pool: Pool, proj: int, X, seg_ws, Y):
     return Y
 
 
+def shrink_rows(pool: Pool, proj: int, X, seg_ws, T=None):
+    """Returns T, fp32 [n][max_rank]: s * Down x per original row (decode path)."""
+    torch = _torch()
+    n = X.shape[0]
+    _rows_check(pool, X, n)
+    if T is None:
+        T = torch.zeros((n, pool.max_rank), dtype=torch.float32, device=X.device)
+    _check(lib().mlora_shrink_rows(pool.handle, proj, _ptr(X), _ptr(seg_ws), n, _ptr(T), _stream()),
+           "mlora_shrink_rows")
+    return T
+
+
+def gemm_lora(pool: Pool, proj: int, X, W0, seg_ws, T, Y=None):
+    """Y = X W0^T + per-row s * Up t (decode path, n <= 64), t from shrink_rows."""
+    torch = _torch()
+    n = X.shape[0]
+    _rows_check(pool, X, n)
+    _bf16_dev(W0, "W0")
+    if Y is None:
+        Y = torch.empty((n, pool.dout), dtype=torch.bfloat16, device=X.device)
+    _bf16_dev(Y, "Y")
+    _check(lib().mlora_gemm_lora(pool.handle, proj, _ptr(X), _ptr(W0), _ptr(seg_ws), _ptr(T), _ptr(Y), n, _stream()),
+           "mlora_gemm_lora")
+    return Y
+
+
 def work_bytes(pool: Pool, n: int) -> int:
     return int(lib().mlora_work_bytes(pool.handle, n))
 
@@ -316,7 +348,7 @@ def plan(pool: Pool, n: int, variant: str = "auto"):
     """(variant name, shrink slices) that apply() runs for a batch of n rows."""
     v, c = ctypes.c_int32(), ctypes.c_int32()
     _check(lib().mlora_plan(pool.handle, n, VARIANTS[variant], ctypes.byref(v), ctypes.byref(c)), "mlora_plan")
-    return {0: "auto", 1: "split", 2: "fused"}[v.value], c.value
+    return {0: "auto", 1: "split", 2: "fused", 3: "rows"}[v.value], c.value
 
 
 def apply(pool: Pool, proj: int, X, W0, seg_ws, Y=None, work=None, variant: str = "auto"):

@@ -134,6 +134,7 @@ MetaLayout meta_layout(int32_t A, int32_t P, int32_t R) {
 constexpr size_t kStageBytes = size_t(8) << 20;  // two pinned staging buffers of 8 MiB
 constexpr int kMaxSplitChunks = 8;               // din slices used by the split variant
 constexpr int kMaxExpandChunks = 1024;           // partial-t slices an expand accepts
+constexpr int kRowsMax = 64;                     // largest batch of the per-row decode path
 
 }  // namespace
 
@@ -454,7 +455,7 @@ mlora_status mlora_pool_free_pages(const mlora_pool* p, int64_t* free_down, int6
 
 size_t mlora_segments_bytes(int32_t n) {
   if (n < 0) return 0;
-  return align256(((size_t)MLORA_SEG_ITEMS(n) + 2 * (size_t)MLORA_SEG_MAX_ITEMS(n)) * sizeof(int32_t));
+  return align256(((size_t)MLORA_SEG_ROWKEY(n) + (size_t)n) * sizeof(int32_t));
 }
 
 mlora_status mlora_build_segments(const mlora_pool* p, const int32_t* row_adapter, int32_t n, void* seg_ws,
@@ -545,6 +546,31 @@ mlora_status mlora_fused(const mlora_pool* p, int32_t proj, const uint16_t* X, c
                    "fused launch");
 }
 
+mlora_status mlora_shrink_rows(const mlora_pool* p, int32_t proj, const uint16_t* X, const void* seg_ws, int32_t n,
+                               float* T, void* stream) {
+  g_err.clear();
+  mlora_status st = check_branch_args(p, proj, seg_ws, n);
+  if (st != MLORA_OK) return st;
+  if (n == 0) return MLORA_OK;
+  if (!X || !T) return fail(MLORA_EINVAL, "X and T must not be NULL");
+  return hip_check(mlora::launch_shrink_rows(p->view(), proj, X, static_cast<const int32_t*>(seg_ws), n, T,
+                                             as_stream(stream)),
+                   "per-row shrink launch");
+}
+
+mlora_status mlora_gemm_lora(const mlora_pool* p, int32_t proj, const uint16_t* X, const uint16_t* W0,
+                             const void* seg_ws, const float* T, uint16_t* Y, int32_t n, void* stream) {
+  g_err.clear();
+  mlora_status st = check_branch_args(p, proj, seg_ws, n);
+  if (st != MLORA_OK) return st;
+  if (n > kRowsMax) return fail(MLORA_EINVAL, "n_rows %d above %d for the per-row decode path", n, kRowsMax);
+  if (n == 0) return MLORA_OK;
+  if (!X || !W0 || !T || !Y) return fail(MLORA_EINVAL, "X, W0, T and Y must not be NULL");
+  return hip_check(mlora::launch_gemm_lora(p->view(), proj, X, W0, static_cast<const int32_t*>(seg_ws), T, Y, n,
+                                           as_stream(stream)),
+                   "GEMM + expand launch");
+}
+
 namespace {
 // din slices for the split variant: enough waves to spread a small batch
 // over the chip, never more than kMaxSplitChunks
@@ -555,25 +581,29 @@ int split_chunks(int din, int n) {
   c = std::min(c, mlora_shrink_max_chunks(din));
   return std::max(c, 1);
 }
-// AUTO: the branch variant for a batch of n rows
+// AUTO: decode-sized batches take the per-row path (shrink per row, expand
+// inside the base GEMM kernel); larger batches the grouped split path
 int32_t auto_variant(const mlora_pool* p, int n) {
   (void)p;
-  (void)n;
-  return MLORA_VARIANT_SPLIT;
+  return n <= kRowsMax ? MLORA_VARIANT_ROWS : MLORA_VARIANT_SPLIT;
 }
 }  // namespace
 
 size_t mlora_work_bytes(const mlora_pool* p, int32_t n) {
   if (!p || n < 0) return 0;
-  return align256((size_t)split_chunks(p->d.din, n) * n * p->d.max_rank * sizeof(float));
+  // the larger of the split variant's partial t and the per-row t
+  const int chunks = std::max(split_chunks(p->d.din, n), 1);
+  return align256((size_t)chunks * n * p->d.max_rank * sizeof(float));
 }
 
 mlora_status mlora_plan(const mlora_pool* p, int32_t n, int32_t variant, int32_t* out_variant, int32_t* out_chunks) {
   g_err.clear();
   if (!p) return fail(MLORA_EINVAL, "pool is NULL");
   if (n < 0 || n > MLORA_MAX_ROWS) return fail(MLORA_EINVAL, "n_rows %d outside [0, %d]", n, MLORA_MAX_ROWS);
-  if (variant < MLORA_VARIANT_AUTO || variant > MLORA_VARIANT_FUSED) return fail(MLORA_EINVAL, "unknown variant %d", variant);
+  if (variant < MLORA_VARIANT_AUTO || variant > MLORA_VARIANT_ROWS) return fail(MLORA_EINVAL, "unknown variant %d", variant);
   if (variant == MLORA_VARIANT_AUTO) variant = auto_variant(p, n);
+  if (variant == MLORA_VARIANT_ROWS && n > kRowsMax)
+    return fail(MLORA_EINVAL, "the per-row variant takes at most %d rows", kRowsMax);
   if (out_variant) *out_variant = variant;
   if (out_chunks) *out_chunks = variant == MLORA_VARIANT_SPLIT ? split_chunks(p->d.din, n) : 0;
   return MLORA_OK;
@@ -585,7 +615,9 @@ mlora_status mlora_apply(const mlora_pool* p, int32_t proj, const uint16_t* X, c
   g_err.clear();
   mlora_status st = check_branch_args(p, proj, seg_ws, n);
   if (st != MLORA_OK) return st;
-  if (variant < MLORA_VARIANT_AUTO || variant > MLORA_VARIANT_FUSED) return fail(MLORA_EINVAL, "unknown variant %d", variant);
+  if (variant < MLORA_VARIANT_AUTO || variant > MLORA_VARIANT_ROWS) return fail(MLORA_EINVAL, "unknown variant %d", variant);
+  if (variant == MLORA_VARIANT_ROWS && n > kRowsMax)
+    return fail(MLORA_EINVAL, "the per-row variant takes at most %d rows", kRowsMax);
   if (n == 0) return MLORA_OK;
   if (!X || !W0 || !Y) return fail(MLORA_EINVAL, "X, W0 and Y must not be NULL");
   const mlora_pool_desc& d = p->d;
@@ -593,10 +625,16 @@ mlora_status mlora_apply(const mlora_pool* p, int32_t proj, const uint16_t* X, c
   const PoolView v = p->view();
   const int32_t* ws = static_cast<const int32_t*>(seg_ws);
   if (variant == MLORA_VARIANT_AUTO) variant = auto_variant(p, n);
-  if (variant == MLORA_VARIANT_SPLIT) {
+  if (variant == MLORA_VARIANT_SPLIT || variant == MLORA_VARIANT_ROWS) {
     const size_t need = mlora_work_bytes(p, n);
     if (!work || work_bytes < need) return fail(MLORA_EINVAL, "work: %zu bytes given, %zu needed", work_bytes, need);
     if (!aligned16(work)) return fail(MLORA_EINVAL, "work must be 16-byte aligned");
+  }
+  if (variant == MLORA_VARIANT_ROWS) {
+    float* T = static_cast<float*>(work);
+    st = hip_check(mlora::launch_shrink_rows(v, proj, X, ws, n, T, s), "per-row shrink launch");
+    if (st != MLORA_OK) return st;
+    return hip_check(mlora::launch_gemm_lora(v, proj, X, W0, ws, T, Y, n, s), "GEMM + expand launch");
   }
   st = hip_check(mlora::launch_base_gemm(X, W0, Y, n, d.din, d.dout, s), "base GEMM launch");
   if (st != MLORA_OK) return st;

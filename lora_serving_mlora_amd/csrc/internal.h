@@ -65,6 +65,13 @@ hipError_t launch_seg_build(const int32_t* row_adapter, int n, const int32_t* po
 hipError_t launch_base_gemm(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N,
                             hipStream_t stream);
 
+// M <= 64: Y = X W^T plus the per-row expand of T (scaled t per original row)
+hipError_t launch_gemm_lora(const PoolView& pv, int proj, const uint16_t* X, const uint16_t* W, const int32_t* ws,
+                            const float* T, uint16_t* Y, int M, hipStream_t stream);
+
+hipError_t launch_shrink_rows(const PoolView& pv, int proj, const uint16_t* X, const int32_t* ws, int n, float* T,
+                              hipStream_t stream);
+
 hipError_t launch_shrink(const PoolView& pv, int proj, const uint16_t* X, const int32_t* ws, int n,
                          float* T, int n_chunks, int chunk_elems, hipStream_t stream);
 

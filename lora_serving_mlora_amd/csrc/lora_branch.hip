@@ -77,42 +77,39 @@ __device__ __forceinline__ float wave_reduce_scatter64(float (&v)[64]) {
 }
 
 // Partial dot products of one wave over din elements [k, k+8) for a rank
-// group: acc[i*G + q] += Down[g0+q][k..k+8) . x_i[k..k+8).
+// group: acc[i*G + q] += Down[g0+q][k..k+8) . x_i[k..k+8).  Ranks past the
+// adapter's rank read its last page instead (those sums are never stored),
+// so all 16 page loads are issued back to back with no tests.
 template <bool VEC>
 __device__ __forceinline__ void shrink_step(const PoolView& pv, const int32_t* __restrict__ dpage, int g0, int rank,
                                             const float (&x)[R][8], int k, float (&acc)[64]) {
+  float d[G][8];
 #pragma unroll
-  for (int q = 0; q < G; ++q) {
-    if (g0 + q < rank) {
-      float d[8];
-      load8<VEC>(pv.down + (size_t)dpage[g0 + q] * pv.din, k, pv.din, d);
+  for (int q = 0; q < G; ++q) load8<VEC>(pv.down + (size_t)dpage[min(g0 + q, rank - 1)] * pv.din, k, pv.din, d[q]);
 #pragma unroll
-      for (int i = 0; i < R; ++i) {
-        float s = acc[i * G + q];
+  for (int q = 0; q < G; ++q)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s = fmaf(d[e], x[i][e], s);
-        acc[i * G + q] = s;
-      }
+    for (int i = 0; i < R; ++i) {
+      float s = acc[i * G + q];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s = fmaf(d[q][e], x[i][e], s);
+      acc[i * G + q] = s;
     }
-  }
 }
 
+// The item's rows at din elements [k, k+8); rows past nr repeat the last
+// row (their results are never stored).
 template <bool VEC>
 __device__ __forceinline__ void load_rows(const uint16_t* __restrict__ X, const int32_t* __restrict__ perm, int din,
                                           int j0, int nr, int k, float (&x)[R][8]) {
 #pragma unroll
-  for (int i = 0; i < R; ++i) {
-    if (i < nr) {
-      load8<VEC>(X + (size_t)perm[j0 + i] * din, k, din, x[i]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
-    }
-  }
+  for (int i = 0; i < R; ++i) load8<VEC>(X + (size_t)perm[j0 + min(i, nr - 1)] * din, k, din, x[i]);
 }
 
 // y_i[c..c+8) += sum_q ts[i][q] * Up^T[q][c..c+8) for the rows of an item,
-// then read-modify-write of Y (bf16 RNE).
+// then read-modify-write of Y (bf16 RNE).  ts holds zeros from the rank up
+// to the next multiple of G, so ranks are walked in full groups of G page
+// loads (pages past the rank are clamped to the last one and weigh zero).
 template <bool VEC>
 __device__ __forceinline__ void expand_cols(const PoolView& pv, const int32_t* __restrict__ upage, int rank,
                                             const float (*ts)[MLORA_MAX_RANK], const int32_t* __restrict__ perm,
@@ -123,47 +120,40 @@ __device__ __forceinline__ void expand_cols(const PoolView& pv, const int32_t* _
   for (int i = 0; i < R; ++i)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
-  int q = 0;
-  for (; q + 4 <= rank; q += 4) {
-    float u[4][8];
+  for (int g0 = 0; g0 < rank; g0 += G) {
+    float u[G][8];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) load8<VEC>(pv.up + (size_t)upage[q + p] * dout, c, dout, u[p]);
+    for (int q = 0; q < G; ++q) load8<VEC>(pv.up + (size_t)upage[min(g0 + q, rank - 1)] * dout, c, dout, u[q]);
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
+    for (int q = 0; q < G; ++q)
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        const float t = ts[i][q + p];
+        const float t = ts[i][g0 + q];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[i][e] = fmaf(t, u[p][e], acc[i][e]);
+        for (int e = 0; e < 8; ++e) acc[i][e] = fmaf(t, u[q][e], acc[i][e]);
       }
   }
-  for (; q < rank; ++q) {
-    float u[8];
-    load8<VEC>(pv.up + (size_t)upage[q] * dout, c, dout, u);
+  float yo[R][8];
+  uint16_t* y[R];
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const float t = ts[i][q];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[i][e] = fmaf(t, u[e], acc[i][e]);
-    }
+  for (int i = 0; i < R; ++i) {
+    y[i] = Y + (size_t)perm[j0 + min(i, nr - 1)] * dout;
+    load8<VEC>(y[i], c, dout, yo[i]);
   }
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     if (i >= nr) continue;
-    uint16_t* y = Y + (size_t)perm[j0 + i] * dout;
-    float yo[8];
-    load8<VEC>(y, c, dout, yo);
     if (VEC) {
       uint4 w;
-      w.x = pack_bf2(yo[0] + acc[i][0], yo[1] + acc[i][1]);
-      w.y = pack_bf2(yo[2] + acc[i][2], yo[3] + acc[i][3]);
-      w.z = pack_bf2(yo[4] + acc[i][4], yo[5] + acc[i][5]);
-      w.w = pack_bf2(yo[6] + acc[i][6], yo[7] + acc[i][7]);
-      *reinterpret_cast<uint4*>(y + c) = w;
+      w.x = pack_bf2(yo[i][0] + acc[i][0], yo[i][1] + acc[i][1]);
+      w.y = pack_bf2(yo[i][2] + acc[i][2], yo[i][3] + acc[i][3]);
+      w.z = pack_bf2(yo[i][4] + acc[i][4], yo[i][5] + acc[i][5]);
+      w.w = pack_bf2(yo[i][6] + acc[i][6], yo[i][7] + acc[i][7]);
+      *reinterpret_cast<uint4*>(y[i] + c) = w;
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (c + e < dout) y[c + e] = (uint16_t)f2bf(yo[e] + acc[i][e]);
+        if (c + e < dout) y[i][c + e] = (uint16_t)f2bf(yo[i][e] + acc[i][e]);
     }
   }
 }
@@ -227,11 +217,16 @@ __global__ __launch_bounds__(64) void expand_kernel(PoolView pv, int proj, const
   for (int it = blockIdx.x; it < n_items + n_bad; it += gridDim.x) {
     if (it < n_items) {
       const Item m = load_item(pv, ws, n, it);
-      for (int idx = lane; idx < R * m.rank; idx += 64) {
-        const int i = idx / m.rank, q = idx % m.rank;
+      const int rpad = (m.rank + G - 1) / G * G;
+      for (int idx = lane; idx < R * rpad; idx += 64) {
+        const int i = idx / rpad, q = idx % rpad;
         float s = 0.f;
-        if (i < m.nr)
-          for (int ch = 0; ch < n_chunks; ++ch) s += T[((size_t)ch * n + m.j0 + i) * pv.max_rank + q];
+        if (i < m.nr && q < m.rank) {
+          const float* tp = T + ((size_t)(m.j0 + i)) * pv.max_rank + q;
+          const size_t cs = (size_t)n * pv.max_rank;
+#pragma unroll 8
+          for (int ch = 0; ch < n_chunks; ++ch) s += tp[ch * cs];
+        }
         ts[i][q] = m.scale * s;
       }
       __syncthreads();
@@ -284,7 +279,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_kernel(PoolView pv, int p
 #pragma unroll
           for (int w = 1; w < kFusedWaves; ++w) s += red[w][tid];
           const int i = tid / G, q = g0 + tid % G;
-          if (q < m.rank) ts[i][q] = m.scale * s;
+          ts[i][q] = (q < m.rank) ? m.scale * s : 0.f;
         }
         __syncthreads();
       }
@@ -294,6 +289,70 @@ __global__ __launch_bounds__(kFusedThreads) void fused_kernel(PoolView pv, int p
     } else {
       uint16_t* y = Y + (size_t)perm[n - n_bad + (it - n_items)] * pv.dout;
       for (int c = tid * 8; c < pv.dout; c += kFusedThreads * 8) nan_cols<VEC>(y, c, pv.dout);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// shrink_rows (decode): one 8-wave workgroup per row, rows read by index in
+// original order; T[k][q] = s_a * (Down_a x_k)[q].  Each lane holds the
+// partial dot products of its 8 din elements for a group of 16 ranks; a
+// 4-step reduce-scatter (xor 32, 16, 8, 4: 16 values -> 1 per lane) plus two
+// xor steps finishes each wave, then the 8 waves are summed in LDS in order.
+// ---------------------------------------------------------------------------
+constexpr int kRowWaves = 8;
+constexpr int kRowThreads = 64 * kRowWaves;
+
+template <bool VEC>
+__global__ __launch_bounds__(kRowThreads) void shrink_rows_kernel(PoolView pv, int proj, const uint16_t* __restrict__ X,
+                                                                  const int32_t* __restrict__ row_key, int n,
+                                                                  float* __restrict__ T) {
+  __shared__ float red[kRowWaves][G];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int k = blockIdx.x; k < n; k += gridDim.x) {
+    const int key = row_key[k];
+    if (key < 0) continue;  // base-only or invalid: no low-rank term
+    const int rank = pv.rank[key];
+    const float scale = pv.scale[key];
+    const int32_t* dpage = pv.down_page + ((size_t)key * pv.n_proj + proj) * pv.max_rank;
+    const uint16_t* xr = X + (size_t)k * pv.din;
+    for (int g0 = 0; g0 < rank; g0 += G) {
+      float v[G];
+#pragma unroll
+      for (int q = 0; q < G; ++q) v[q] = 0.f;
+      for (int kk = tid * 8; kk < pv.din; kk += kRowThreads * 8) {
+        float x[8], d[G][8];
+        load8<VEC>(xr, kk, pv.din, x);
+#pragma unroll
+        for (int q = 0; q < G; ++q) load8<VEC>(pv.down + (size_t)dpage[min(g0 + q, rank - 1)] * pv.din, kk, pv.din, d[q]);
+#pragma unroll
+        for (int q = 0; q < G; ++q)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[q] = fmaf(d[q][e], x[e], v[q]);
+      }
+      // reduce-scatter 16 -> 1: after the steps lane l holds index l >> 2
+#pragma unroll
+      for (int m = 32, len = G / 2; m >= 4; m >>= 1, len >>= 1) {
+        const bool upper = (lane & m) != 0;
+#pragma unroll
+        for (int i = 0; i < len; ++i) {
+          const float send = upper ? v[i] : v[i + len];
+          const float keep = upper ? v[i + len] : v[i];
+          v[i] = keep + __shfl_xor(send, m, 64);
+        }
+      }
+      float tot = v[0];
+      tot += __shfl_xor(tot, 2, 64);
+      tot += __shfl_xor(tot, 1, 64);
+      if ((lane & 3) == 0) red[wave][lane >> 2] = tot;
+      __syncthreads();
+      if (tid < G && g0 + tid < rank) {
+        float sum = red[0][tid];
+#pragma unroll
+        for (int w = 1; w < kRowWaves; ++w) sum += red[w][tid];
+        T[(size_t)k * pv.max_rank + g0 + tid] = scale * sum;
+      }
+      __syncthreads();
     }
   }
 }
@@ -321,6 +380,17 @@ hipError_t launch_shrink(const PoolView& pv, int proj, const uint16_t* X, const 
     hipLaunchKernelGGL((shrink_kernel<true>), grid, block, 0, stream, pv, proj, X, ws, n, T, chunk_elems);
   else
     hipLaunchKernelGGL((shrink_kernel<false>), grid, block, 0, stream, pv, proj, X, ws, n, T, chunk_elems);
+  return hipGetLastError();
+}
+
+hipError_t launch_shrink_rows(const PoolView& pv, int proj, const uint16_t* X, const int32_t* ws, int n, float* T,
+                              hipStream_t stream) {
+  const dim3 grid(n < 1024 ? n : 1024), block(kRowThreads);
+  const int32_t* row_key = ws + MLORA_SEG_ROWKEY(n);
+  if (vec_ok(pv, X, X))
+    hipLaunchKernelGGL((shrink_rows_kernel<true>), grid, block, 0, stream, pv, proj, X, row_key, n, T);
+  else
+    hipLaunchKernelGGL((shrink_rows_kernel<false>), grid, block, 0, stream, pv, proj, X, row_key, n, T);
   return hipGetLastError();
 }
 

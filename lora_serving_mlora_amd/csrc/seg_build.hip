@@ -17,13 +17,14 @@
 namespace mlora {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / 64;
 constexpr int kRadix = 256;
+constexpr int kMaxWaves = 16;
 
-// Exclusive prefix sum of one int per thread over the whole block; *total
-// gets the block sum.  Every thread of the block must call it.
+// Exclusive prefix sum of one int per thread over the whole block of NT
+// threads; *total gets the block sum.  Every thread of the block must call it.
+template <int NT>
 __device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
+  constexpr int kWaves = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
@@ -49,12 +50,16 @@ __device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
   return wave_prefix + x - v;
 }
 
-__global__ __launch_bounds__(kThreads) void seg_build_kernel(const int32_t* __restrict__ row_adapter, int n,
-                                                             const int32_t* __restrict__ pool_rank,
-                                                             int max_adapters, int passes, int cap,
-                                                             int32_t* __restrict__ ws) {
+// NT threads (1, 4 or 16 waves, picked by batch size so that small decode
+// batches do not pay for barriers across 16 waves)
+template <int NT>
+__global__ __launch_bounds__(NT) void seg_build_kernel(const int32_t* __restrict__ row_adapter, int n,
+                                                       const int32_t* __restrict__ pool_rank, int max_adapters,
+                                                       int passes, int cap, int32_t* __restrict__ ws) {
+  constexpr int kThreads = NT;
+  constexpr int kWaves = NT / 64;
   extern __shared__ uint32_t lds[];
-  __shared__ int s_wave[kWaves];
+  __shared__ int s_wave[kMaxWaves];
   __shared__ int s_cnt[3];  // base-only rows, invalid rows, status bits
 
   uint32_t* bufA = lds;
@@ -68,6 +73,7 @@ __global__ __launch_bounds__(kThreads) void seg_build_kernel(const int32_t* __re
   int32_t* seg_adapter = ws + MLORA_SEG_ADAPTER(n);
   int32_t* seg_off = ws + MLORA_SEG_OFF(n);
   int32_t* items = ws + MLORA_SEG_ITEMS(n);
+  int32_t* row_key = ws + MLORA_SEG_ROWKEY(n);
 
   if (tid < 3) s_cnt[tid] = 0;
   __syncthreads();
@@ -92,6 +98,7 @@ __global__ __launch_bounds__(kThreads) void seg_build_kernel(const int32_t* __re
       key = (uint32_t)a;
     }
     bufA[k] = (key << 16) | (uint32_t)k;
+    row_key[k] = key < A ? (int32_t)key : (key == A ? -1 : -2);
   }
   if (my_none) atomicAdd(&s_cnt[0], my_none);
   if (my_bad) atomicAdd(&s_cnt[1], my_bad);
@@ -112,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void seg_build_kernel(const int32_t* __re
     {
       const uint32_t v0 = hist[4 * tid], v1 = hist[4 * tid + 1], v2 = hist[4 * tid + 2], v3 = hist[4 * tid + 3];
       int total;
-      const uint32_t ex = (uint32_t)block_exclusive_scan((int)(v0 + v1 + v2 + v3), s_wave, &total);
+      const uint32_t ex = (uint32_t)block_exclusive_scan<NT>((int)(v0 + v1 + v2 + v3), s_wave, &total);
       hist[4 * tid] = ex;
       hist[4 * tid + 1] = ex + v0;
       hist[4 * tid + 2] = ex + v0 + v1;
@@ -169,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void seg_build_kernel(const int32_t* __re
       flag = (j == 0) || ((sorted[j - 1] >> 16) != key);
     }
     int total;
-    const int ex = block_exclusive_scan(flag, s_wave, &total);
+    const int ex = block_exclusive_scan<NT>(flag, s_wave, &total);
     if (flag) {
       offs[nseg + ex] = (uint32_t)j;
       seg_adapter[nseg + ex] = (int32_t)key;
@@ -191,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void seg_build_kernel(const int32_t* __re
     int t = 0;
     if (s < nseg) t = (int)((offs[s + 1] - offs[s] + MLORA_ITEM_ROWS - 1) / MLORA_ITEM_ROWS);
     int total;
-    const int ex = block_exclusive_scan(t, s_wave, &total);
+    const int ex = block_exclusive_scan<NT>(t, s_wave, &total);
     if (s < nseg) item_end[s] = (uint32_t)(n_items + ex + t);
     n_items += total;
   }
@@ -219,18 +226,17 @@ __global__ __launch_bounds__(kThreads) void seg_build_kernel(const int32_t* __re
   }
 }
 
-}  // namespace
-
-hipError_t launch_seg_build(const int32_t* row_adapter, int n, const int32_t* pool_rank, int max_adapters,
-                            int32_t* ws, hipStream_t stream) {
+template <int NT>
+hipError_t launch_nt(const int32_t* row_adapter, int n, const int32_t* pool_rank, int max_adapters, int32_t* ws,
+                     hipStream_t stream) {
   const int cap = ((n + 1) + 63) & ~63;
-  const size_t lds = (size_t)(2 * cap + kRadix * kWaves) * sizeof(uint32_t);
+  const size_t lds = (size_t)(2 * cap + kRadix * (NT / 64)) * sizeof(uint32_t);
   if (lds > 64 * 1024) {
     // a batch near the row limit needs most of the 160 KiB of LDS of a CU;
     // the launch itself reports an error if the device cannot provide it
     static size_t attr_bytes = 0;
     if (lds > attr_bytes) {
-      if (hipFuncSetAttribute((const void*)seg_build_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+      if (hipFuncSetAttribute((const void*)seg_build_kernel<NT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)lds) == hipSuccess)
         attr_bytes = lds;
       else
@@ -238,9 +244,18 @@ hipError_t launch_seg_build(const int32_t* row_adapter, int n, const int32_t* po
     }
   }
   const int passes = (max_adapters + 1 < 256) ? 1 : 2;
-  hipLaunchKernelGGL(seg_build_kernel, dim3(1), dim3(kThreads), lds, stream, row_adapter, n, pool_rank,
-                     max_adapters, passes, cap, ws);
+  hipLaunchKernelGGL(seg_build_kernel<NT>, dim3(1), dim3(NT), lds, stream, row_adapter, n, pool_rank, max_adapters,
+                     passes, cap, ws);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_seg_build(const int32_t* row_adapter, int n, const int32_t* pool_rank, int max_adapters,
+                            int32_t* ws, hipStream_t stream) {
+  if (n <= 64) return launch_nt<64>(row_adapter, n, pool_rank, max_adapters, ws, stream);
+  if (n <= 1024) return launch_nt<256>(row_adapter, n, pool_rank, max_adapters, ws, stream);
+  return launch_nt<1024>(row_adapter, n, pool_rank, max_adapters, ws, stream);
 }
 
 }  // namespace mlora

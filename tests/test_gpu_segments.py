@@ -46,6 +46,9 @@ def check(M, pool, ids, max_adapters, resident, what):
     assert got["n_rows"] == n and got["max_adapters"] == max_adapters
     for k in ("perm", "inv", "seg_adapter", "seg_off"):
         assert np.array_equal(got[k], ref[k]), (what, k)
+    res = set(int(a) for a in resident)
+    want_key = [int(a) if int(a) in res else (-1 if a == -1 else -2) for a in ids]
+    assert got["row_key"].tolist() == want_key, what
     # work items: every active sorted position exactly once, inside its own
     # segment, at most ITEM_ROWS rows, in segment order
     cover = np.zeros(ref["n_act"], dtype=np.int64)
