@@ -228,7 +228,7 @@ def main():
         kernels = ["segments", "shrink_rows", "gemm_lora"]
     else:
         kernels = ["segments", "base_gemm"] + (["fused"] if variant == "fused" else ["shrink", "expand"])
-    T_rows = torch.zeros((n, w.max_rank), dtype=torch.float32, device="cuda")
+    work = M.new_work(pool, n)
 
     def step(i, evs=None):
         p = i % R
@@ -237,9 +237,9 @@ def main():
         M.build_segments(pool, ids, seg_ws)
         rec(1)
         if variant == "rows":
-            M.shrink_rows(pool, p, X, seg_ws, T_rows)
+            M.shrink_rows(pool, p, X, seg_ws, work)
             rec(2)
-            M.gemm_lora(pool, p, X, W0s[p], seg_ws, T_rows, Y)
+            M.gemm_lora(pool, p, X, W0s[p], seg_ws, work, Y)
         else:
             M.base_gemm(X, W0s[p], Y)
             rec(2)

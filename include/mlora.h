@@ -63,9 +63,10 @@ typedef enum mlora_variant {
   MLORA_VARIANT_AUTO = 0,
   MLORA_VARIANT_SPLIT = 1, /* shrink kernel -> fp32 t in `work` -> expand kernel */
   MLORA_VARIANT_FUSED = 2, /* one kernel per row tile: t stays on chip           */
-  MLORA_VARIANT_ROWS = 3   /* decode batches (n_rows <= 64): per-row shrink, then
-                              the base GEMM with the expand in extra waves of the
-                              same kernel, overlapped with its K loop           */
+  MLORA_VARIANT_ROWS = 3   /* decode-sized batches (n_rows <= 1024): per-row
+                              shrink, then the base GEMM with the expand in extra
+                              waves of the same kernel, overlapped with its K
+                              loop                                               */
 } mlora_variant;
 
 /* Limits. */
@@ -240,20 +241,25 @@ mlora_status mlora_expand(const mlora_pool* pool, int32_t proj, const float* T, 
 mlora_status mlora_fused(const mlora_pool* pool, int32_t proj, const uint16_t* X, const void* seg_ws,
                          uint16_t* Y, int32_t n_rows, void* stream);
 
-/* Per-row shrink for decode batches (rows read directly by index, as the
- * M031 card's section 02 allows instead of regrouping): for every row k on a
- * resident adapter a, T[k][q] = s_a * (Down_a x_k)[q] for q < rank(a), fp32
- * [n_rows][max_rank] in ORIGINAL row order (scale folded in).  Other rows
- * and columns are not written.  Reads the row keys of seg_ws. */
+/* Per-row path (decode-sized batches, n_rows <= 1024), in two calls that
+ * share the caller's `work` buffer (mlora_work_bytes() long, 256-byte
+ * aligned).  Its first n_rows * max_rank floats hold T: T[k][q] = s_a *
+ * (Down_a x_k)[q] for every row k on a resident adapter a, q < rank(a), in
+ * ORIGINAL row order (rows read directly by index, as the M031 card's
+ * section 02 allows instead of regrouping); other entries are not written.
+ * The rest of `work` is the GEMM's scratch (split-K partials), so the two
+ * calls go in this order on one stream, and calls that share a `work` buffer
+ * must not overlap. */
 mlora_status mlora_shrink_rows(const mlora_pool* pool, int32_t proj, const uint16_t* X, const void* seg_ws,
-                               int32_t n_rows, float* T, void* stream);
+                               int32_t n_rows, void* work, size_t work_bytes, void* stream);
 
-/* Base GEMM with the expand of the low-rank branch in the same kernel, for
- * n_rows <= 64: Y = X W0^T, plus for every row k on a resident adapter
- * sum_q T[k][q] Up_a[:, q] (T from mlora_shrink_rows); rows with an invalid
+/* Base GEMM with the expand of the low-rank branch in the same kernel:
+ * Y = X W0^T, plus for every row k on a resident adapter sum_q T[k][q]
+ * Up_a[:, q] with T from mlora_shrink_rows in `work`; rows with an invalid
  * id become NaN; base-only rows get the plain product.  Y is written once. */
 mlora_status mlora_gemm_lora(const mlora_pool* pool, int32_t proj, const uint16_t* X, const uint16_t* W0,
-                             const void* seg_ws, const float* T, uint16_t* Y, int32_t n_rows, void* stream);
+                             const void* seg_ws, void* work, size_t work_bytes, uint16_t* Y, int32_t n_rows,
+                             void* stream);
 
 /* ---------------------------------------------------------------------------
  * The whole layer for one projection of one batch:
@@ -270,7 +276,7 @@ size_t mlora_work_bytes(const mlora_pool* pool, int32_t n_rows);
 /* The launch plan mlora_apply follows for `variant` (AUTO resolved) on a
  * batch of n_rows: the variant it runs and, for SPLIT, the number of din
  * slices of its shrink (the n_chunks of mlora_shrink/mlora_expand).  ROWS
- * is only valid for n_rows <= 64.
+ * is only valid for n_rows <= 1024.
  * Host only; lets a caller run the same steps one by one. */
 mlora_status mlora_plan(const mlora_pool* pool, int32_t n_rows, int32_t variant, int32_t* out_variant,
                         int32_t* out_chunks);

@@ -22,7 +22,7 @@ import numpy as np
 
 __all__ = [
     "MloraError", "lib", "Pool", "build_segments", "segments_header", "read_segments",
-    "base_gemm", "shrink", "shrink_max_chunks", "expand", "fused", "shrink_rows", "gemm_lora", "apply", "plan", "work_bytes",
+    "base_gemm", "shrink", "shrink_max_chunks", "expand", "fused", "shrink_rows", "gemm_lora", "new_work", "rows_t", "apply", "plan", "work_bytes",
     "hbm_copy", "VARIANTS", "ITEM_ROWS", "MAX_ROWS", "MAX_RANK", "SEG", "EXPORTS", "LIB_PATH",
 ]
 
@@ -67,9 +67,9 @@ EXPORTS = {
     "mlora_expand": (ctypes.c_int, [_c_void_p, _i32, _c_void_p, _i32, _c_void_p, _c_void_p, _i32, _c_void_p]),
     "mlora_fused": (ctypes.c_int, [_c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p]),
     "mlora_work_bytes": (_sz, [_c_void_p, _i32]),
-    "mlora_shrink_rows": (ctypes.c_int, [_c_void_p, _i32, _c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p]),
-    "mlora_gemm_lora": (ctypes.c_int, [_c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32,
-                                       _c_void_p]),
+    "mlora_shrink_rows": (ctypes.c_int, [_c_void_p, _i32, _c_void_p, _c_void_p, _i32, _c_void_p, _sz, _c_void_p]),
+    "mlora_gemm_lora": (ctypes.c_int, [_c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p,
+                                       _i32, _c_void_p]),
     "mlora_plan": (ctypes.c_int, [_c_void_p, _i32, _i32, _pi32, _pi32]),
     "mlora_apply": (ctypes.c_int, [_c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p,
                                    _sz, _i32, _c_void_p]),
@@ -314,20 +314,32 @@ def fused(pool: Pool, proj: int, X, seg_ws, Y):
     return Y
 
 
-def shrink_rows(pool: Pool, proj: int, X, seg_ws, T=None):
-    """Returns T, fp32 [n][max_rank]: s * Down x per original row (decode path)."""
+def new_work(pool: Pool, n: int, device=None):
+    """A zeroed work buffer for apply / the per-row path (mlora_work_bytes)."""
     torch = _torch()
+    return torch.zeros(max(work_bytes(pool, n), 256), dtype=torch.uint8,
+                       device=device if device is not None else torch.device("cuda", torch.cuda.current_device()))
+
+
+def rows_t(pool: Pool, work, n: int):
+    """The T region of a per-row work buffer: fp32 [n][max_rank] view."""
+    torch = _torch()
+    return work[: n * pool.max_rank * 4].view(torch.float32).view(n, pool.max_rank)
+
+
+def shrink_rows(pool: Pool, proj: int, X, seg_ws, work=None):
+    """Per-row shrink; returns the work buffer (T = rows_t(pool, work, n))."""
     n = X.shape[0]
     _rows_check(pool, X, n)
-    if T is None:
-        T = torch.zeros((n, pool.max_rank), dtype=torch.float32, device=X.device)
-    _check(lib().mlora_shrink_rows(pool.handle, proj, _ptr(X), _ptr(seg_ws), n, _ptr(T), _stream()),
-           "mlora_shrink_rows")
-    return T
+    if work is None:
+        work = new_work(pool, n, X.device)
+    _check(lib().mlora_shrink_rows(pool.handle, proj, _ptr(X), _ptr(seg_ws), n, _ptr(work),
+                                   work.numel() * work.element_size(), _stream()), "mlora_shrink_rows")
+    return work
 
 
-def gemm_lora(pool: Pool, proj: int, X, W0, seg_ws, T, Y=None):
-    """Y = X W0^T + per-row s * Up t (decode path, n <= 64), t from shrink_rows."""
+def gemm_lora(pool: Pool, proj: int, X, W0, seg_ws, work, Y=None):
+    """Y = X W0^T + per-row s * Up t, t from shrink_rows in `work`."""
     torch = _torch()
     n = X.shape[0]
     _rows_check(pool, X, n)
@@ -335,8 +347,8 @@ def gemm_lora(pool: Pool, proj: int, X, W0, seg_ws, T, Y=None):
     if Y is None:
         Y = torch.empty((n, pool.dout), dtype=torch.bfloat16, device=X.device)
     _bf16_dev(Y, "Y")
-    _check(lib().mlora_gemm_lora(pool.handle, proj, _ptr(X), _ptr(W0), _ptr(seg_ws), _ptr(T), _ptr(Y), n, _stream()),
-           "mlora_gemm_lora")
+    _check(lib().mlora_gemm_lora(pool.handle, proj, _ptr(X), _ptr(W0), _ptr(seg_ws), _ptr(work),
+                                 work.numel() * work.element_size(), _ptr(Y), n, _stream()), "mlora_gemm_lora")
     return Y
 
 
@@ -362,9 +374,8 @@ def apply(pool: Pool, proj: int, X, W0, seg_ws, Y=None, work=None, variant: str 
     if Y is None:
         Y = torch.empty((n, pool.dout), dtype=torch.bfloat16, device=X.device)
     _bf16_dev(Y, "Y")
-    wb = work_bytes(pool, n)
     if work is None:
-        work = torch.empty(max(wb, 256), dtype=torch.uint8, device=X.device)
+        work = new_work(pool, n, X.device)
     _check(lib().mlora_apply(pool.handle, proj, _ptr(X), _ptr(W0), _ptr(seg_ws), _ptr(Y), n, _ptr(work),
                              work.numel() * work.element_size(), VARIANTS[variant], _stream()), "mlora_apply")
     return Y

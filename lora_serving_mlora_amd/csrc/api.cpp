@@ -134,7 +134,7 @@ MetaLayout meta_layout(int32_t A, int32_t P, int32_t R) {
 constexpr size_t kStageBytes = size_t(8) << 20;  // two pinned staging buffers of 8 MiB
 constexpr int kMaxSplitChunks = 8;               // din slices used by the split variant
 constexpr int kMaxExpandChunks = 1024;           // partial-t slices an expand accepts
-constexpr int kRowsMax = 64;                     // largest batch of the per-row decode path
+constexpr int kRowsMax = 1024;                   // largest batch of the per-row path
 
 }  // namespace
 
@@ -546,28 +546,57 @@ mlora_status mlora_fused(const mlora_pool* p, int32_t proj, const uint16_t* X, c
                    "fused launch");
 }
 
+namespace {
+// work layout of the per-row path: T [n][max_rank] fp32 | split-K partials
+struct RowsWork {
+  float* T;
+  float* part;
+};
+size_t rows_work_bytes(const mlora_pool* p, int n) {
+  return align256((size_t)n * p->d.max_rank * sizeof(float)) +
+         align256(mlora::gemm_lora_part_floats(n, p->d.dout, p->d.din) * sizeof(float));
+}
+RowsWork rows_work(const mlora_pool* p, int n, void* work) {
+  char* w = static_cast<char*>(work);
+  RowsWork r;
+  r.T = reinterpret_cast<float*>(w);
+  r.part = reinterpret_cast<float*>(w + align256((size_t)n * p->d.max_rank * sizeof(float)));
+  return r;
+}
+mlora_status check_rows_work(const mlora_pool* p, int n, const void* work, size_t work_bytes) {
+  if (n > kRowsMax) return fail(MLORA_EINVAL, "n_rows %d above %d for the per-row path", n, kRowsMax);
+  const size_t need = rows_work_bytes(p, n);
+  if (!work || work_bytes < need) return fail(MLORA_EINVAL, "work: %zu bytes given, %zu needed", work_bytes, need);
+  if ((reinterpret_cast<uintptr_t>(work) & 255u) != 0) return fail(MLORA_EINVAL, "work must be 256-byte aligned");
+  return MLORA_OK;
+}
+}  // namespace
+
 mlora_status mlora_shrink_rows(const mlora_pool* p, int32_t proj, const uint16_t* X, const void* seg_ws, int32_t n,
-                               float* T, void* stream) {
+                               void* work, size_t work_bytes, void* stream) {
   g_err.clear();
   mlora_status st = check_branch_args(p, proj, seg_ws, n);
   if (st != MLORA_OK) return st;
   if (n == 0) return MLORA_OK;
-  if (!X || !T) return fail(MLORA_EINVAL, "X and T must not be NULL");
-  return hip_check(mlora::launch_shrink_rows(p->view(), proj, X, static_cast<const int32_t*>(seg_ws), n, T,
+  if (!X) return fail(MLORA_EINVAL, "X must not be NULL");
+  if ((st = check_rows_work(p, n, work, work_bytes)) != MLORA_OK) return st;
+  const RowsWork w = rows_work(p, n, work);
+  return hip_check(mlora::launch_shrink_rows(p->view(), proj, X, static_cast<const int32_t*>(seg_ws), n, w.T,
                                              as_stream(stream)),
                    "per-row shrink launch");
 }
 
 mlora_status mlora_gemm_lora(const mlora_pool* p, int32_t proj, const uint16_t* X, const uint16_t* W0,
-                             const void* seg_ws, const float* T, uint16_t* Y, int32_t n, void* stream) {
+                             const void* seg_ws, void* work, size_t work_bytes, uint16_t* Y, int32_t n, void* stream) {
   g_err.clear();
   mlora_status st = check_branch_args(p, proj, seg_ws, n);
   if (st != MLORA_OK) return st;
-  if (n > kRowsMax) return fail(MLORA_EINVAL, "n_rows %d above %d for the per-row decode path", n, kRowsMax);
   if (n == 0) return MLORA_OK;
-  if (!X || !W0 || !T || !Y) return fail(MLORA_EINVAL, "X, W0, T and Y must not be NULL");
-  return hip_check(mlora::launch_gemm_lora(p->view(), proj, X, W0, static_cast<const int32_t*>(seg_ws), T, Y, n,
-                                           as_stream(stream)),
+  if (!X || !W0 || !Y) return fail(MLORA_EINVAL, "X, W0 and Y must not be NULL");
+  if ((st = check_rows_work(p, n, work, work_bytes)) != MLORA_OK) return st;
+  const RowsWork w = rows_work(p, n, work);
+  return hip_check(mlora::launch_gemm_lora(p->view(), proj, X, W0, static_cast<const int32_t*>(seg_ws), w.T, w.part,
+                                           Y, n, as_stream(stream)),
                    "GEMM + expand launch");
 }
 
@@ -591,9 +620,11 @@ int32_t auto_variant(const mlora_pool* p, int n) {
 
 size_t mlora_work_bytes(const mlora_pool* p, int32_t n) {
   if (!p || n < 0) return 0;
-  // the larger of the split variant's partial t and the per-row t
+  // the larger of the split variant's partial t and the per-row path's layout
   const int chunks = std::max(split_chunks(p->d.din, n), 1);
-  return align256((size_t)chunks * n * p->d.max_rank * sizeof(float));
+  size_t b = align256((size_t)chunks * n * p->d.max_rank * sizeof(float));
+  if (n <= kRowsMax) b = std::max(b, rows_work_bytes(p, n));
+  return b;
 }
 
 mlora_status mlora_plan(const mlora_pool* p, int32_t n, int32_t variant, int32_t* out_variant, int32_t* out_chunks) {
@@ -631,10 +662,11 @@ mlora_status mlora_apply(const mlora_pool* p, int32_t proj, const uint16_t* X, c
     if (!aligned16(work)) return fail(MLORA_EINVAL, "work must be 16-byte aligned");
   }
   if (variant == MLORA_VARIANT_ROWS) {
-    float* T = static_cast<float*>(work);
-    st = hip_check(mlora::launch_shrink_rows(v, proj, X, ws, n, T, s), "per-row shrink launch");
+    if ((st = check_rows_work(p, n, work, work_bytes)) != MLORA_OK) return st;
+    const RowsWork w = rows_work(p, n, work);
+    st = hip_check(mlora::launch_shrink_rows(v, proj, X, ws, n, w.T, s), "per-row shrink launch");
     if (st != MLORA_OK) return st;
-    return hip_check(mlora::launch_gemm_lora(v, proj, X, W0, ws, T, Y, n, s), "GEMM + expand launch");
+    return hip_check(mlora::launch_gemm_lora(v, proj, X, W0, ws, w.T, w.part, Y, n, s), "GEMM + expand launch");
   }
   st = hip_check(mlora::launch_base_gemm(X, W0, Y, n, d.din, d.dout, s), "base GEMM launch");
   if (st != MLORA_OK) return st;

@@ -56,7 +56,6 @@ __device__ __forceinline__ uint4 load_chunk(const uint16_t* __restrict__ row, in
 // fill a whole 32-wide step takes element loads.
 // ---------------------------------------------------------------------------
 constexpr int kSkinnyWaves = 8;
-constexpr int kSkinnyUnroll = 4;
 
 template <int MB>
 __device__ __forceinline__ void skinny_step(const uint16_t* __restrict__ wrow, const uint16_t* const (&xrow)[MB],
@@ -83,47 +82,41 @@ __device__ __forceinline__ void skinny_kloop(const uint16_t* __restrict__ X, con
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  // Each wave owns a contiguous range of 32-wide K steps.  In batches of 16
+  // steps, all 16 W0 loads of the batch are issued at once (the HBM stream:
+  // one round trip per batch instead of one per step), then the X fragments
+  // (L2-resident, tiny) follow in groups of 4 steps, the next group issued
+  // before the MFMAs of the current one.
   const int nfull = VEC ? K / 32 : 0;  // steps whose 32 K values all exist
-  int s = wave;
+  const int per = (nfull + kSkinnyWaves - 1) / kSkinnyWaves;
+  const int s_beg = min(nfull, wave * per), s_end = min(nfull, s_beg + per);
+  int s = VEC ? s_beg : wave;  // without VEC every step is a tail step, shared round-robin
   if (VEC) {
-    // groups of kSkinnyUnroll steps, two groups in flight: the loads of group
-    // g+1 are issued before the MFMAs of group g, so W0 keeps streaming
-    constexpr int kGroup = kSkinnyWaves * kSkinnyUnroll;  // steps spanned by one group
-    uint4 b0[kSkinnyUnroll], a0[kSkinnyUnroll][MB], b1[kSkinnyUnroll], a1[kSkinnyUnroll][MB];
-    auto load_group = [&](int s_, uint4 (&b)[kSkinnyUnroll], uint4 (&a)[kSkinnyUnroll][MB]) {
+    for (; s + 16 <= s_end; s += 16) {
+      uint4 wv[16];
 #pragma unroll
-      for (int u = 0; u < kSkinnyUnroll; ++u) {
-        const int k = (s_ + u * kSkinnyWaves) * 32;
-        b[u] = *reinterpret_cast<const uint4*>(wrow + k);
+      for (int j = 0; j < 16; ++j) wv[j] = *reinterpret_cast<const uint4*>(wrow + (s + j) * 32);
+      uint4 xa[2][4][MB];
+      auto xload = [&](int g, uint4 (&x)[4][MB]) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) a[u][mb] = *reinterpret_cast<const uint4*>(xrow[mb] + k);
-      }
-    };
-    auto mma_group = [&](const uint4 (&b)[kSkinnyUnroll], const uint4 (&a)[kSkinnyUnroll][MB]) {
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int u = 0; u < kSkinnyUnroll; ++u)
+          for (int mb = 0; mb < MB; ++mb) x[u][mb] = *reinterpret_cast<const uint4*>(xrow[mb] + (s + 4 * g + u) * 32);
+      };
+      xload(0, xa[0]);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u][mb]), as_bf16x8(b[u]), acc[mb], 0, 0, 0);
-    };
-    // number of whole groups this wave owns
-    const int ngroups = (nfull - wave + kGroup - kSkinnyWaves * (kSkinnyUnroll - 1) - 1) / kGroup;
-    if (ngroups > 0) {
-      load_group(s, b0, a0);
-      int g = 0;
-      for (; g + 2 <= ngroups; g += 2) {
-        load_group(s + kGroup, b1, a1);
-        mma_group(b0, a0);
-        if (g + 2 < ngroups) load_group(s + 2 * kGroup, b0, a0);
-        mma_group(b1, a1);
-        s += 2 * kGroup;
-      }
-      if (g < ngroups) {
-        mma_group(b0, a0);
-        s += kGroup;
+      for (int g = 0; g < 4; ++g) {
+        if (g + 1 < 4) xload(g + 1, xa[(g + 1) & 1]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[g & 1][u][mb]), as_bf16x8(wv[4 * g + u]),
+                                                              acc[mb], 0, 0, 0);
       }
     }
-    for (; s < nfull; s += kSkinnyWaves) skinny_step<MB>(wrow, xrow, s * 32, acc);
+    for (; s < s_end; ++s) skinny_step<MB>(wrow, xrow, s * 32, acc);
+    s = nfull + wave;  // the K tail below is shared round-robin
   }
   // K tail (and every step when rows are not 16-byte aligned): element loads
   const int nsteps = (K + 31) / 32;
@@ -178,6 +171,50 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void gemm_skinny(const uint16_t*
 // ---------------------------------------------------------------------------
 constexpr int kLoraWaves = 2;
 
+// The low-rank term of row r at columns [c0, c0+8): sum_q T[r][q] Up_a[c][q]
+// (T carries the scale).  Zero for a base-only row or a row past M, NaN for
+// a row with an invalid id.  Ranks past the adapter's rank read its last
+// column with weight 0, so each group of 8 page loads goes out at once.
+template <bool VEC>
+__device__ __forceinline__ void lora_delta8(const PoolView& pv, int proj, const int32_t* __restrict__ row_key,
+                                            const float* __restrict__ T, int r, int M, int c0, int N,
+                                            float (&acc8)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc8[e] = 0.f;
+  const int key = (r < M && c0 < N) ? row_key[r] : -1;
+  if (key >= 0) {
+    const int rank = pv.rank[key];
+    const int32_t* upage = pv.up_page + ((size_t)key * pv.n_proj + proj) * pv.max_rank;
+    const float* tr = T + (size_t)r * pv.max_rank;
+    // page indices and t are read without waiting for the rank: entries past
+    // it fall back to the group's first page and weigh zero (a select, so an
+    // unwritten t past the rank never reaches the sum)
+    int q0 = 0;
+    do {
+      float u8[8][8], tq[8];
+      int pg[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) pg[q] = upage[min(q0 + q, pv.max_rank - 1)];
+#pragma unroll
+      for (int q = 1; q < 8; ++q) pg[q] = pg[q] < 0 ? pg[0] : pg[q];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        load8<VEC>(pv.up + (size_t)pg[q] * pv.dout, c0, N, u8[q]);
+        const float tv = tr[min(q0 + q, pv.max_rank - 1)];
+        tq[q] = (q0 + q < rank) ? tv : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc8[e] = fmaf(tq[q], u8[q][e], acc8[e]);
+      q0 += 8;
+    } while (q0 < rank);
+  } else if (key == -2) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc8[e] = __uint_as_float(0x7fc00000u);
+  }
+}
+
 template <int MB, bool VEC>
 __global__ __launch_bounds__(64 * (kSkinnyWaves + kLoraWaves)) void gemm_skinny_lora(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y, int M, int K, int N,
@@ -196,34 +233,8 @@ __global__ __launch_bounds__(64 * (kSkinnyWaves + kLoraWaves)) void gemm_skinny_
     const int u = threadIdx.x - 64 * kSkinnyWaves;
     for (int task = u; task < MB * 16 * 2; task += 64 * kLoraWaves) {
       const int r = task >> 1, h = task & 1;
-      const int c0 = n0 + 8 * h;
       float acc8[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc8[e] = 0.f;
-      const int key = (r < M && c0 < N) ? row_key[r] : -1;
-      if (key >= 0) {
-        const int rank = pv.rank[key];
-        const int32_t* upage = pv.up_page + ((size_t)key * pv.n_proj + proj) * pv.max_rank;
-        const float* tr = T + (size_t)r * pv.max_rank;
-        for (int q0 = 0; q0 < rank; q0 += 8) {
-          // ranks past the adapter's rank read its last column with weight 0
-          float u8[8][8], tq[8];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const int qq = min(q0 + q, rank - 1);
-            load8<VEC>(pv.up + (size_t)upage[qq] * pv.dout, c0, N, u8[q]);
-            const float tv = tr[qq];
-            tq[q] = (q0 + q < rank) ? tv : 0.f;
-          }
-#pragma unroll
-          for (int q = 0; q < 8; ++q)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc8[e] = fmaf(tq[q], u8[q][e], acc8[e]);
-        }
-      } else if (key == -2) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc8[e] = __uint_as_float(0x7fc00000u);
-      }
+      lora_delta8<VEC>(pv, proj, row_key, T, r, M, n0 + 8 * h, N, acc8);
 #pragma unroll
       for (int e = 0; e < 8; ++e) delta[r][8 * h + e] = acc8[e];
     }
@@ -246,6 +257,130 @@ __global__ __launch_bounds__(64 * (kSkinnyWaves + kLoraWaves)) void gemm_skinny_
 }
 
 // ---------------------------------------------------------------------------
+// ksplit: medium batches (65 .. 1024 rows).  A 128 x 32 output tile per
+// workgroup, so even a 256-row batch launches 256+ workgroups; its 4 waves
+// split K (steps of 16, interleaved), each computing the whole tile over its
+// share with MFMA 32x32x16 on operands loaded straight into registers, two
+// groups of 4 steps in flight; the 4 partial tiles are summed in LDS in a
+// fixed order.  Rows past M / columns past N read clamped rows (never
+// stored); a K tail shorter than a 16-wide step takes element loads.
+// ---------------------------------------------------------------------------
+constexpr int kKsWaves = 4;
+constexpr int kKsLoraWaves = 8;  // one (row, 8-column) task of the 128 x 32 tile per thread
+constexpr int KS_MB = 4;         // 32-row blocks per tile (128 rows)
+
+template <bool VEC, bool LORA>
+__global__ __launch_bounds__(64 * (kKsWaves + (LORA ? kKsLoraWaves : 0))) void gemm_ksplit(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y, int M, int K, int N,
+    PoolView pv, int proj, const int32_t* __restrict__ row_key, const float* __restrict__ T) {
+  __shared__ float red[kKsWaves - 1][KS_MB][16][64];  // partials of waves 1..3, [mb][v][lane]
+  __shared__ float delta[LORA ? 32 * KS_MB : 1][32];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * 32, m0 = blockIdx.y * (32 * KS_MB);
+  if (LORA && wave >= kKsWaves) {
+    // the tile's low-rank term: task (row, 8-column quarter) per thread
+    const int u = threadIdx.x - 64 * kKsWaves;
+    for (int task = u; task < 32 * KS_MB * 4; task += 64 * kKsLoraWaves) {
+      const int r = task >> 2, h = task & 3;
+      float acc8[8];
+      lora_delta8<VEC>(pv, proj, row_key, T, m0 + r, M, n0 + 8 * h, N, acc8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) delta[r][8 * h + e] = acc8[e];
+    }
+    __syncthreads();
+    return;
+  }
+  const int kl = (lane >> 5) * 8;
+  const uint16_t* wrow = W + (size_t)min(n0 + (lane & 31), N - 1) * K + kl;
+  const uint16_t* xrow[KS_MB];
+#pragma unroll
+  for (int mb = 0; mb < KS_MB; ++mb) xrow[mb] = X + (size_t)min(m0 + mb * 32 + (lane & 31), M - 1) * K + kl;
+  floatx16 acc[KS_MB];
+#pragma unroll
+  for (int mb = 0; mb < KS_MB; ++mb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[mb][v] = 0.f;
+
+  // Each wave owns a contiguous range of 16-wide K steps.  In batches of 16
+  // steps, the 16 W0 loads of the batch go out at once (the HBM stream);
+  // the X fragments (4 per step, L2-resident) follow in groups of 2 steps,
+  // the next group issued before the MFMAs of the current one.
+  const int nfull = VEC ? K / 16 : 0;
+  const int per = (nfull + kKsWaves - 1) / kKsWaves;
+  const int s_beg = min(nfull, wave * per), s_end = min(nfull, s_beg + per);
+  int s = VEC ? s_beg : wave;  // without VEC every step is a tail step, shared round-robin
+  if (VEC) {
+    for (; s + 16 <= s_end; s += 16) {
+      uint4 wv[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) wv[j] = *reinterpret_cast<const uint4*>(wrow + (s + j) * 16);
+      uint4 xa[2][2][KS_MB];
+      auto xload = [&](int g, uint4 (&x)[2][KS_MB]) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int mb = 0; mb < KS_MB; ++mb) x[u][mb] = *reinterpret_cast<const uint4*>(xrow[mb] + (s + 2 * g + u) * 16);
+      };
+      xload(0, xa[0]);
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        if (g + 1 < 8) xload(g + 1, xa[(g + 1) & 1]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int mb = 0; mb < KS_MB; ++mb)
+            acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xa[g & 1][u][mb]), as_bf16x8(wv[2 * g + u]),
+                                                              acc[mb], 0, 0, 0);
+      }
+    }
+    for (; s < s_end; ++s) {
+      const int k = s * 16;
+      const uint4 b = *reinterpret_cast<const uint4*>(wrow + k);
+#pragma unroll
+      for (int mb = 0; mb < KS_MB; ++mb) {
+        const uint4 a = *reinterpret_cast<const uint4*>(xrow[mb] + k);
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), acc[mb], 0, 0, 0);
+      }
+    }
+    s = nfull + wave;  // the K tail below is shared round-robin
+  }
+  const int nsteps = (K + 15) / 16;
+  for (; s < nsteps; s += kKsWaves) {
+    const int k = s * 16;
+    const int lim = K - k - kl;
+    const uint4 b = load_chunk<false>(wrow + k, 0, lim);
+#pragma unroll
+    for (int mb = 0; mb < KS_MB; ++mb) {
+      const uint4 a = load_chunk<false>(xrow[mb] + k, 0, lim);
+      acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), acc[mb], 0, 0, 0);
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int mb = 0; mb < KS_MB; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) red[wave - 1][mb][v][lane] = acc[mb][v];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // C layout of a 32x32 tile: lane l holds column l%32, rows 8*(v/4) + 4*(l/32) + v%4
+    const int c = n0 + (lane & 31);
+#pragma unroll
+    for (int mb = 0; mb < KS_MB; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float sum = acc[mb][v];
+#pragma unroll
+        for (int w = 0; w < kKsWaves - 1; ++w) sum += red[w][mb][v][lane];
+        const int rl = mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int r = m0 + rl;
+        if (LORA) sum += delta[rl][lane & 31];
+        if (r < M && c < N) Y[(size_t)r * N + c] = (uint16_t)f2bf(sum);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // tiled: 128 x 128 x 64 tiles, 4 waves, MFMA 32x32x16
 // ---------------------------------------------------------------------------
 constexpr int BM = 128, BN = 128, BK = 64;
@@ -256,10 +391,13 @@ constexpr int kLoadsB = BN * kChunksPerRow / kTiledThreads;    // 4
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
 
-template <bool VEC>
+// PART: split-K form - workgroup z covers K tiles [z*kt_per, (z+1)*kt_per)
+// and stores its fp32 partial tile to part[z][M][N] (summed by finish_part).
+template <bool VEC, bool PART = false>
 __global__ __launch_bounds__(kTiledThreads) void gemm_tiled(const uint16_t* __restrict__ X,
                                                             const uint16_t* __restrict__ W,
-                                                            uint16_t* __restrict__ Y, int M, int K, int N) {
+                                                            uint16_t* __restrict__ Y, int M, int K, int N,
+                                                            float* __restrict__ part = nullptr, int kt_per = 0) {
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * BK];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * BK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -324,14 +462,16 @@ __global__ __launch_bounds__(kTiledThreads) void gemm_tiled(const uint16_t* __re
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int nk = (K + BK - 1) / BK;
-  gload(0);
+  const int nk_all = (K + BK - 1) / BK;
+  const int kt0 = PART ? blockIdx.z * kt_per : 0;
+  const int nk = PART ? min(nk_all, kt0 + kt_per) : nk_all;
+  gload(kt0);
   sstore(0);
   __syncthreads();
   const int fr = lane & 31;        // fragment row (A) / column (B) inside a 32-wide tile
   const int fk = lane >> 5;        // which 8-wide half of a 16-wide k step
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
+  for (int kt = kt0; kt < nk; ++kt) {
+    const int buf = (kt - kt0) & 1;
     if (kt + 1 < nk) gload(kt + 1);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
@@ -367,7 +507,12 @@ __global__ __launch_bounds__(kTiledThreads) void gemm_tiled(const uint16_t* __re
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (r < M) Y[(size_t)r * N + c] = (uint16_t)f2bf(acc[i][j][v]);
+        if (r < M) {
+          if (PART)
+            part[((size_t)blockIdx.z * M + r) * N + c] = acc[i][j][v];
+          else
+            Y[(size_t)r * N + c] = (uint16_t)f2bf(acc[i][j][v]);
+        }
       }
     }
 }
@@ -502,6 +647,36 @@ __global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(1, 
     }
 }
 
+// MLORA_DECODE_SPLITK=0 keeps decode batches on the one-pass skinny kernel (A/B timing)
+bool decode_splitk_enabled() {
+  static int on = -1;
+  if (on < 0) {
+    const char* e = getenv("MLORA_DECODE_SPLITK");
+    on = (e && e[0] == '0') ? 0 : 1;
+  }
+  return on == 1;
+}
+
+// MLORA_GEMM_MID=0 keeps medium per-row batches on the K-split kernel (A/B timing)
+bool mid_enabled() {
+  static int on = -1;
+  if (on < 0) {
+    const char* e = getenv("MLORA_GEMM_MID");
+    on = (e && e[0] == '0') ? 0 : 1;
+  }
+  return on == 1;
+}
+
+// MLORA_GEMM_KSPLIT=0 keeps medium batches on the 128x128 kernel (A/B timing)
+bool ksplit_enabled() {
+  static int on = -1;
+  if (on < 0) {
+    const char* e = getenv("MLORA_GEMM_KSPLIT");
+    on = (e && e[0] == '0') ? 0 : 1;
+  }
+  return on == 1;
+}
+
 // MLORA_GEMM_BIG=0 keeps large products on the 128x128 kernel (for A/B timing)
 bool big_gemm_enabled() {
   static int on = -1;
@@ -529,6 +704,10 @@ hipError_t launch_gemm(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M,
     else if (M <= 32) hipLaunchKernelGGL((gemm_skinny<2, VEC>), grid, block, 0, st, X, W, Y, M, K, N);
     else if (M <= 48) hipLaunchKernelGGL((gemm_skinny<3, VEC>), grid, block, 0, st, X, W, Y, M, K, N);
     else hipLaunchKernelGGL((gemm_skinny<4, VEC>), grid, block, 0, st, X, W, Y, M, K, N);
+  } else if (M <= 1024 && (long)((M + 127) / 128) * ((N + 31) / 32) >= 128 && ksplit_enabled()) {
+    const dim3 grid((N + 31) / 32, (M + 32 * KS_MB - 1) / (32 * KS_MB)), block(64 * kKsWaves);
+    hipLaunchKernelGGL((gemm_ksplit<VEC, false>), grid, block, 0, st, X, W, Y, M, K, N, PoolView{}, 0, nullptr,
+                       nullptr);
   } else if (VEC && K % GBK == 0 && (long)M * N >= 2048L * 2048L && (long)M * K * 2 < (1L << 31) &&
              (long)N * K * 2 < (1L << 31) && big_gemm_enabled()) {
     return launch_big(X, W, Y, M, K, N, st);
@@ -539,9 +718,208 @@ hipError_t launch_gemm(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// decode: split-K skinny GEMM with the low-rank expand, for M <= 64.
+//
+// Every workgroup reading all of X made X (L2-resident, but read 256 times)
+// cost as much as streaming W0 from HBM.  Here a workgroup owns 64 columns
+// and one quarter of K: its X slice (M x K/4) is brought into LDS once by
+// LDS DMA and shared by the 4 column-group waves, so each X byte is read by 64
+// workgroups instead of 256, while the 256 workgroups still cover the chip.
+// 8 GEMM waves = 4 column groups x 2 halves of the quarter; each wave issues
+// all 16 of its W0 loads at once.  2 more waves compute the low-rank term of
+// the rows r with r % 4 == quarter (so the 4 quarters split that work).  The
+// quarter's fp32 partial goes to `part`; the last workgroup of a column block
+// to finish (atomic counter, zeroed by the per-row shrink and reset here)
+// sums the 4 partials in quarter order and writes Y: deterministic.
+// LDS: X slice [M][K/4] in 1 KiB blocks whose 16-byte chunks are XOR-swizzled
+// by (row & 15), so the 16 rows an MFMA fragment read touches hit 16
+// different chunk positions.
+// ---------------------------------------------------------------------------
+constexpr int kDecCols = 64, kDecSplit = 4, kDecWaves = 8, kDecLoraWaves = 2;
+constexpr int kMidMaxSplit = 8;
+
+template <int MB>
+__global__ __launch_bounds__(64 * (kDecWaves + kDecLoraWaves)) void gemm_decode(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y, int M, int K, int N,
+    PoolView pv, int proj, const int32_t* __restrict__ row_key, const float* __restrict__ T,
+    float* __restrict__ part) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t dec_lds[];
+  const int Kq = K / kDecSplit;
+  uint16_t* xs = dec_lds;                                               // [M][Kq]
+  floatx4* red = reinterpret_cast<floatx4*>(dec_lds + (size_t)M * Kq);  // [4][MB][64]
+  float* delta = reinterpret_cast<float*>(red + 4 * MB * 64);           // [16][64]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cb = blockIdx.x, kq = blockIdx.y;
+  const int n0 = cb * kDecCols;
+  const bool gemm_wave = wave < kDecWaves;
+  const int cg = wave & 3, kh = (wave >> 2) & 1;
+  const int steps = Kq / 64;  // 32-wide steps in a wave's half of the quarter (<= 16)
+  uint4 wv[16];
+
+  if (gemm_wave) {
+    // X slice -> LDS: instruction (row r, 1 KiB block b); lane l fetches
+    // logical chunk l ^ (r & 15) of the block into physical chunk l
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X), (short)0, M * K * 2, 0x00020000);
+    const int blocks = Kq / 512;
+    for (int i = wave; i < M * blocks; i += kDecWaves) {
+      const int r = i / blocks, b = i % blocks;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, xs + (size_t)r * Kq + b * 512, 16, (lane ^ (r & 15)) * 16,
+                                               (r * K + kq * Kq + b * 512) * 2, 0, 0);
+    }
+    // all of this wave's W0 fragments at once (column group cg, half kh)
+    const uint16_t* wrow =
+        W + (size_t)min(n0 + 16 * cg + (lane & 15), N - 1) * K + kq * Kq + kh * (Kq / 2) + (lane >> 4) * 8;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) wv[j] = *reinterpret_cast<const uint4*>(wrow + (size_t)min(j, steps - 1) * 32);
+    __builtin_amdgcn_s_waitcnt(0);
+  } else {
+    // low-rank term of rows r = kq, kq+4, ... over the block's 64 columns
+    const int u = tid - 64 * kDecWaves;
+    const int rr = u >> 3, h = u & 7;
+    float acc8[8];
+    lora_delta8<true>(pv, proj, row_key, T, kq + 4 * rr, M, n0 + 8 * h, N, acc8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) delta[rr * 64 + 8 * h + e] = acc8[e];
+  }
+  __syncthreads();  // X slice in LDS, delta written
+
+  floatx4 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (gemm_wave) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j < steps) {
+        const int c = kh * (Kq / 16) + j * 4 + (lane >> 4);  // logical 16-byte chunk in the slice row
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int r = min(mb * 16 + (lane & 15), M - 1);
+          const uint4 a = *reinterpret_cast<const uint4*>(xs + (size_t)r * Kq + (c >> 6) * 512 +
+                                                          (((c & 63) ^ (r & 15)) << 3));
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(wv[j]), acc[mb], 0, 0, 0);
+        }
+      }
+    }
+    if (kh == 1) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) red[(cg * MB + mb) * 64 + lane] = acc[mb];
+    }
+  }
+  __syncthreads();
+  if (gemm_wave && kh == 0) {
+    // the quarter's partial: both halves + this quarter's share of the delta
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const floatx4 o = red[(cg * MB + mb) * 64 + lane];
+      const int c = 16 * cg + (lane & 15);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = mb * 16 + (lane >> 4) * 4 + v;
+        float y = acc[mb][v] + o[v];
+        if ((r & 3) == kq) y += delta[(r >> 2) * 64 + c];
+        if (r < M && n0 + c < N) part[((size_t)kq * M + r) * N + n0 + c] = y;
+      }
+    }
+  }
+}
+
+// Sums the S split-K partials of a tile in split order, adds the row's
+// low-rank term when LORA (sum_q T[r][q] Up_a[c][q], Up streamed here), and
+// writes Y (bf16 RNE); 8 columns per thread, so each Up page row is read as
+// coalesced 16-byte pieces.
+template <bool LORA>
+__global__ __launch_bounds__(256) void finish_part(const float* __restrict__ part, int S, uint16_t* __restrict__ Y,
+                                                   int M, int N, PoolView pv, int proj,
+                                                   const int32_t* __restrict__ row_key, const float* __restrict__ T) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int per_row = N / 8;
+  if (t >= M * per_row) return;
+  const int r = t / per_row, c0 = (t % per_row) * 8;
+  float y[8];
+  if (LORA) {
+    lora_delta8<true>(pv, proj, row_key, T, r, M, c0, N, y);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = 0.f;
+  }
+  float sum[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sum[e] = 0.f;
+  for (int q = 0; q < S; ++q) {
+    const float* pp = part + ((size_t)q * M + r) * N + c0;
+    const float4 p0 = *reinterpret_cast<const float4*>(pp);
+    const float4 p1 = *reinterpret_cast<const float4*>(pp + 4);
+    sum[0] += p0.x; sum[1] += p0.y; sum[2] += p0.z; sum[3] += p0.w;
+    sum[4] += p1.x; sum[5] += p1.y; sum[6] += p1.z; sum[7] += p1.w;
+  }
+  uint4 w;
+  w.x = pack_bf2(sum[0] + y[0], sum[1] + y[1]);
+  w.y = pack_bf2(sum[2] + y[2], sum[3] + y[3]);
+  w.z = pack_bf2(sum[4] + y[4], sum[5] + y[5]);
+  w.w = pack_bf2(sum[6] + y[6], sum[7] + y[7]);
+  *reinterpret_cast<uint4*>(Y + (size_t)r * N + c0) = w;
+}
+
+size_t decode_lds_bytes(int M, int K, int MB) {
+  return (size_t)M * (K / kDecSplit) * 2 + (size_t)4 * MB * 64 * 16 + 16 * 64 * 4;
+}
+
+template <int MB>
+hipError_t launch_decode(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N, const PoolView& pv,
+                         int proj, const int32_t* row_key, const float* T, float* part, hipStream_t st) {
+  const size_t lds = decode_lds_bytes(M, K, MB);
+  static size_t attr = 0;
+  if (lds > attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_decode<MB>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+    attr = lds;
+  }
+  const dim3 grid((N + kDecCols - 1) / kDecCols, kDecSplit), block(64 * (kDecWaves + kDecLoraWaves));
+  hipLaunchKernelGGL(gemm_decode<MB>, grid, block, lds, st, X, W, Y, M, K, N, pv, proj, row_key, T, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int threads = M * (N / 8);
+  hipLaunchKernelGGL(finish_part<false>, dim3((threads + 255) / 256), dim3(256), 0, st, part, kDecSplit, Y, M, N,
+                     PoolView{}, 0, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+// medium batches: 128x128 tiles with split-K over S workgroups, then the
+// finish pass (partials + low-rank term)
+int mid_split(int M, int N, int K) {
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  int S = 1;
+  while (S < kMidMaxSplit && tiles * S < 256 && K % (BK * S * 2) == 0) S *= 2;
+  return S;
+}
+
+hipError_t launch_mid_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N, const PoolView& pv,
+                           int proj, const int32_t* row_key, const float* T, float* part, hipStream_t st) {
+  const int S = mid_split(M, N, K);
+  const int kt_per = K / BK / S;
+  const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM, S), block(kTiledThreads);
+  hipLaunchKernelGGL((gemm_tiled<true, true>), grid, block, 0, st, X, W, Y, M, K, N, part, kt_per);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int threads = M * (N / 8);
+  hipLaunchKernelGGL(finish_part<true>, dim3((threads + 255) / 256), dim3(256), 0, st, part, S, Y, M, N, pv, proj,
+                     row_key, T);
+  return hipGetLastError();
+}
+
 template <bool VEC>
 hipError_t launch_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N, const PoolView& pv,
                        int proj, const int32_t* row_key, const float* T, hipStream_t st) {
+  if (M > 64) {
+    const dim3 g((N + 31) / 32, (M + 32 * KS_MB - 1) / (32 * KS_MB)), b(64 * (kKsWaves + kKsLoraWaves));
+    hipLaunchKernelGGL((gemm_ksplit<VEC, true>), g, b, 0, st, X, W, Y, M, K, N, pv, proj, row_key, T);
+    return hipGetLastError();
+  }
   const dim3 grid((N + 15) / 16), block(64 * (kSkinnyWaves + kLoraWaves));
   if (M <= 16)
     hipLaunchKernelGGL((gemm_skinny_lora<1, VEC>), grid, block, 0, st, X, W, Y, M, K, N, pv, proj, row_key, T);
@@ -556,16 +934,33 @@ hipError_t launch_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M,
 
 }  // namespace
 
+bool decode_splitk_ok(int M, int K, int N, bool vec) {
+  // X slice in 1 KiB blocks, each wave's half of a quarter in <= 16 steps
+  return vec && M <= 64 && K % (kDecSplit * 512) == 0 && K <= kDecSplit * 1024 && (long)M * K * 2 < (1L << 31);
+}
+
 hipError_t launch_gemm_lora(const PoolView& pv, int proj, const uint16_t* X, const uint16_t* W, const int32_t* ws,
-                            const float* T, uint16_t* Y, int M, hipStream_t stream) {
+                            const float* T, float* part, uint16_t* Y, int M, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
   const int K = pv.din, N = pv.dout;
   const int32_t* row_key = ws + MLORA_SEG_ROWKEY(M);
   const uintptr_t al = reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(W) |
-                       reinterpret_cast<uintptr_t>(pv.up);
+                       reinterpret_cast<uintptr_t>(pv.up) | reinterpret_cast<uintptr_t>(Y);
   const bool vec = (K % 8 == 0) && (N % 8 == 0) && (al % 16 == 0);
+  if (decode_splitk_ok(M, K, N, vec) && decode_splitk_enabled()) {
+    if (M <= 16) return launch_decode<1>(X, W, Y, M, K, N, pv, proj, row_key, T, part, stream);
+    if (M <= 32) return launch_decode<2>(X, W, Y, M, K, N, pv, proj, row_key, T, part, stream);
+    if (M <= 48) return launch_decode<3>(X, W, Y, M, K, N, pv, proj, row_key, T, part, stream);
+    return launch_decode<4>(X, W, Y, M, K, N, pv, proj, row_key, T, part, stream);
+  }
+  if (M > 64 && vec && K % BK == 0 && mid_enabled())
+    return launch_mid_lora(X, W, Y, M, K, N, pv, proj, row_key, T, part, stream);
   return vec ? launch_lora<true>(X, W, Y, M, K, N, pv, proj, row_key, T, stream)
              : launch_lora<false>(X, W, Y, M, K, N, pv, proj, row_key, T, stream);
+}
+
+size_t gemm_lora_part_floats(int M, int N, int K) {
+  return (size_t)(M > 64 ? mid_split(M, N, K) : kDecSplit) * M * N;
 }
 
 hipError_t launch_base_gemm(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N,

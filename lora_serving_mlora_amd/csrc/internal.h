@@ -65,9 +65,12 @@ hipError_t launch_seg_build(const int32_t* row_adapter, int n, const int32_t* po
 hipError_t launch_base_gemm(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N,
                             hipStream_t stream);
 
-// M <= 64: Y = X W^T plus the per-row expand of T (scaled t per original row)
+// Y = X W^T plus the per-row expand of T (scaled t per original row).  The
+// decode (M <= 64) and medium (M <= 1024) forms split K over workgroups and
+// need gemm_lora_part_floats() of fp32 scratch for the partials.
 hipError_t launch_gemm_lora(const PoolView& pv, int proj, const uint16_t* X, const uint16_t* W, const int32_t* ws,
-                            const float* T, uint16_t* Y, int M, hipStream_t stream);
+                            const float* T, float* part, uint16_t* Y, int M, hipStream_t stream);
+size_t gemm_lora_part_floats(int M, int N, int K);
 
 hipError_t launch_shrink_rows(const PoolView& pv, int proj, const uint16_t* X, const int32_t* ws, int n, float* T,
                               hipStream_t stream);

@@ -316,7 +316,16 @@ __global__ __launch_bounds__(kRowThreads) void shrink_rows_kernel(PoolView pv, i
     const float scale = pv.scale[key];
     const int32_t* dpage = pv.down_page + ((size_t)key * pv.n_proj + proj) * pv.max_rank;
     const uint16_t* xr = X + (size_t)k * pv.din;
-    for (int g0 = 0; g0 < rank; g0 += G) {
+    // The page table is read without waiting for the rank: entries past the
+    // rank hold -1 and are replaced by the group's first page (their sums are
+    // never stored), and the first group runs before the rank is known.
+    int g0 = 0;
+    do {
+      int pg[G];
+#pragma unroll
+      for (int q = 0; q < G; ++q) pg[q] = dpage[min(g0 + q, pv.max_rank - 1)];
+#pragma unroll
+      for (int q = 1; q < G; ++q) pg[q] = pg[q] < 0 ? pg[0] : pg[q];
       float v[G];
 #pragma unroll
       for (int q = 0; q < G; ++q) v[q] = 0.f;
@@ -324,7 +333,7 @@ __global__ __launch_bounds__(kRowThreads) void shrink_rows_kernel(PoolView pv, i
         float x[8], d[G][8];
         load8<VEC>(xr, kk, pv.din, x);
 #pragma unroll
-        for (int q = 0; q < G; ++q) load8<VEC>(pv.down + (size_t)dpage[min(g0 + q, rank - 1)] * pv.din, kk, pv.din, d[q]);
+        for (int q = 0; q < G; ++q) load8<VEC>(pv.down + (size_t)pg[q] * pv.din, kk, pv.din, d[q]);
 #pragma unroll
         for (int q = 0; q < G; ++q)
 #pragma unroll
@@ -353,7 +362,8 @@ __global__ __launch_bounds__(kRowThreads) void shrink_rows_kernel(PoolView pv, i
         T[(size_t)k * pv.max_rank + g0 + tid] = scale * sum;
       }
       __syncthreads();
-    }
+      g0 += G;
+    } while (g0 < rank);
   }
 }
 

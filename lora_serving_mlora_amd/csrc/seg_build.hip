@@ -226,6 +226,99 @@ __global__ __launch_bounds__(NT) void seg_build_kernel(const int32_t* __restrict
   }
 }
 
+// ---------------------------------------------------------------------------
+// Batches of at most 64 rows (decode steps): one wave, one row per lane.  A
+// row's sorted position is the number of rows with a smaller (key, row) pair,
+// counted against every other lane's key broadcast from registers; the
+// result is the same stable order as the radix path, with no LDS passes and
+// no barriers across waves.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void seg_build_small(const int32_t* __restrict__ row_adapter, int n,
+                                                      const int32_t* __restrict__ pool_rank, int max_adapters,
+                                                      int32_t* __restrict__ ws) {
+  __shared__ int s_sorted[65];  // sorted keys, then segment offsets
+  const int lane = threadIdx.x;
+  const bool valid = lane < n;
+  const int A = max_adapters;
+  int key = A + 2, status = 0;  // lanes past n sort after everything
+  if (valid) {
+    const int a = row_adapter[lane];
+    if (a == -1) {
+      key = A;
+    } else if (a < -1 || a >= A) {
+      key = A + 1;
+      status = MLORA_SEG_BAD_ID;
+    } else if (pool_rank[a] <= 0) {
+      key = A + 1;
+      status = MLORA_SEG_NOT_RESIDENT;
+    } else {
+      key = a;
+    }
+    ws[MLORA_SEG_ROWKEY(n) + lane] = key < A ? key : (key == A ? -1 : -2);
+  }
+  int pos = 0;
+  for (int j = 0; j < 64; ++j) {
+    const int kj = __builtin_amdgcn_readlane(key, j);
+    pos += (kj < key) || (kj == key && j < lane);
+  }
+  if (valid) {
+    ws[MLORA_SEG_PERM(n) + pos] = lane;
+    ws[MLORA_SEG_INV(n) + lane] = pos;
+    s_sorted[pos] = key;
+  }
+  const unsigned long long act = __ballot(valid && key < A);
+  const unsigned long long none = __ballot(valid && key == A);
+  const unsigned long long bad = __ballot(valid && key == A + 1);
+  int st = status;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) st |= __shfl_xor(st, m, 64);
+  const int n_act = __popcll(act);
+  __syncthreads();
+  // segment starts among the active sorted positions
+  const int kj = lane < n_act ? s_sorted[lane] : -1;
+  const bool start = lane < n_act && (lane == 0 || s_sorted[lane - 1] != kj);
+  const unsigned long long starts = __ballot(start);
+  const int nseg = __popcll(starts);
+  const int sidx = __popcll(starts & ((1ull << lane) - 1ull));
+  __syncthreads();
+  if (start) {
+    ws[MLORA_SEG_ADAPTER(n) + sidx] = kj;
+    ws[MLORA_SEG_OFF(n) + sidx] = lane;
+    s_sorted[sidx] = lane;
+  }
+  if (lane == 0) {
+    ws[MLORA_SEG_OFF(n) + nseg] = n_act;
+    s_sorted[nseg] = n_act;
+  }
+  __syncthreads();
+  // work items: ceil(len / ITEM_ROWS) per segment, in segment order
+  int tiles = 0;
+  if (lane < nseg) tiles = (s_sorted[lane + 1] - s_sorted[lane] + MLORA_ITEM_ROWS - 1) / MLORA_ITEM_ROWS;
+  int incl = tiles;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += y;
+  }
+  const int n_items = __shfl(incl, 63, 64);
+  int32_t* items = ws + MLORA_SEG_ITEMS(n);
+  for (int t = 0; t < tiles; ++t) {
+    items[2 * (incl - tiles + t)] = lane;
+    items[2 * (incl - tiles + t) + 1] = s_sorted[lane] + t * MLORA_ITEM_ROWS;
+  }
+  if (lane == 0) {
+    ws[MLORA_SEG_NSEG] = nseg;
+    ws[MLORA_SEG_NACT] = n_act;
+    ws[MLORA_SEG_NNONE] = __popcll(none);
+    ws[MLORA_SEG_NBAD] = __popcll(bad);
+    ws[MLORA_SEG_STATUS] = st;
+    ws[MLORA_SEG_NITEMS] = n_items;
+    ws[MLORA_SEG_NROWS] = n;
+    ws[MLORA_SEG_MAXAD] = max_adapters;
+  }
+  if (lane >= 8 && lane < MLORA_SEG_HEADER) ws[lane] = 0;
+}
+
 template <int NT>
 hipError_t launch_nt(const int32_t* row_adapter, int n, const int32_t* pool_rank, int max_adapters, int32_t* ws,
                      hipStream_t stream) {
@@ -253,7 +346,10 @@ hipError_t launch_nt(const int32_t* row_adapter, int n, const int32_t* pool_rank
 
 hipError_t launch_seg_build(const int32_t* row_adapter, int n, const int32_t* pool_rank, int max_adapters,
                             int32_t* ws, hipStream_t stream) {
-  if (n <= 64) return launch_nt<64>(row_adapter, n, pool_rank, max_adapters, ws, stream);
+  if (n <= 64 && max_adapters <= 65533) {
+    hipLaunchKernelGGL(seg_build_small, dim3(1), dim3(64), 0, stream, row_adapter, n, pool_rank, max_adapters, ws);
+    return hipGetLastError();
+  }
   if (n <= 1024) return launch_nt<256>(row_adapter, n, pool_rank, max_adapters, ws, stream);
   return launch_nt<1024>(row_adapter, n, pool_rank, max_adapters, ws, stream);
 }

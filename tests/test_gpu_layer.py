@@ -25,7 +25,9 @@ def M():
 
 GEMM_SHAPES = [(1, 4, 4), (4, 4, 4), (3, 5, 7), (16, 64, 16), (17, 72, 33), (32, 4096, 4096), (33, 1000, 520),
                (48, 40, 1000), (64, 520, 1000), (65, 4096, 300), (200, 136, 136), (300, 1000, 777),
-               (256, 4096, 4096), (513, 264, 392)]
+               (256, 4096, 4096), (513, 264, 392),
+               # medium batches on the K-split kernel, incl. K tails and unaligned K
+               (65, 4096, 4096), (129, 520, 4104), (700, 1000, 2000), (100, 20, 4096), (512, 4096, 4096)]
 
 
 @pytest.mark.parametrize("m,k,n", GEMM_SHAPES)
@@ -110,7 +112,8 @@ def test_shrink_rows(M, case):
     ad = oracle_adapters(w)
     ref = O.shrink_rows(O.widen_bf16(X), w.row_adapter, ad, w.max_adapters)
     say(f"shrink_rows {w.name}")
-    T = M.shrink_rows(pool, 0, to_dev_bf16(X), seg_ws).cpu().numpy().astype(np.float64)
+    work = M.shrink_rows(pool, 0, to_dev_bf16(X), seg_ws)
+    T = M.rows_t(pool, work, w.n).cpu().numpy().astype(np.float64)
     for k, t in ref.items():
         a = int(w.row_adapter[k])
         assert_close(T[k, : len(t)], w.scales[a] * t, f"shrink_rows {w.name} row {k}")
@@ -154,7 +157,7 @@ def test_fused(M, case):
 
 def check_apply(M, w, projs=(0,), rows=None, variants=None, pool=None, w0_zero=False):
     if variants is None:
-        variants = ("split", "fused", "rows") if w.n <= 64 else ("split", "fused")
+        variants = ("split", "fused", "rows") if w.n <= 1024 else ("split", "fused")
     pool = pool or make_pool(M, w)
     X = w.x_bits()
     Xd = to_dev_bf16(X)
@@ -216,15 +219,24 @@ def test_delta_only(M, name):
     check_apply(M, synth.NAMED[name](), w0_zero=True)
 
 
-def test_gemm_lora_with_synthetic_t(M):
-    """The GEMM-with-expand kernel alone, fed a synthetic per-row T."""
+@pytest.mark.parametrize("n,din,dout", [(40, 520, 264), (300, 520, 4104), (1024, 520, 1000),
+                                        # split-K decode form: K multiple of 2048, up to 64 rows
+                                        (1, 4096, 4096), (17, 2048, 1000), (32, 4096, 136), (48, 2048, 4096),
+                                        (64, 4096, 4104),
+                                        # medium batches on the split-K tiled kernel + finish pass
+                                        (130, 512, 1000), (700, 1024, 2000), (256, 4096, 4096)])
+def test_gemm_lora_with_synthetic_t(M, n, din, dout):
+    """The GEMM-with-expand kernel alone (skinny, split-K decode and K-split
+    forms), fed a synthetic per-row T."""
     torch = torch_cuda()
-    w = small_workload(61, 520, 264, 40, {0: 16, 1: 3, 2: 64}, p_none=0.2)
+    w = small_workload(61 + n, din, dout, n, {0: 16, 1: 3, 2: 64}, p_none=0.2)
     pool, X, seg, seg_ws = _prepare(M, w)
     Tn = synth.draw_t(w.seed, w.n, w.max_rank, 1)[0]
     W0 = w.w0_bits()
-    say("gemm_lora synthetic T")
-    Y = M.gemm_lora(pool, 0, to_dev_bf16(X), to_dev_bf16(W0), seg_ws, torch.from_numpy(Tn).cuda())
+    say(f"gemm_lora synthetic T n={n} dout={dout}")
+    work = M.new_work(pool, w.n)
+    M.rows_t(pool, work, w.n).copy_(torch.from_numpy(Tn))
+    Y = M.gemm_lora(pool, 0, to_dev_bf16(X), to_dev_bf16(W0), seg_ws, work)
     base = O.widen_bf16(X) @ O.widen_bf16(W0).T
     ad = oracle_adapters(w)
     # T already carries the scale: expand with unit scale
