@@ -2,8 +2,8 @@
 """Throughput of the heterogeneous multi-LoRA linear on one MI355X.
 
 One step = one batch through the whole layer: build the segments (group rows
-by adapter), the base GEMM Y = X W0^T, and the low-rank branch (shrink then
-expand, or the fused kernel), for the variant the library's planner picks.
+by adapter), then mlora_apply (the base GEMM Y = X W0^T and the low-rank
+branch, shrink and expand), for the variant the library's planner picks.
 The steps of the timed region are replayed from a captured HIP graph, so the
 number is the GPU's, not the Python launcher's.  Inputs are seeded synthetic
 tensors already resident in HBM.  Consecutive steps rotate over distinct
@@ -13,9 +13,9 @@ from the previous one.
 
 Prints ONE JSON line: tokens/s (whole batch rows per second of step time),
 the dominant kernel's roofline fraction (its algorithmic bytes or flops per
-launch over its average duration measured with HIP events on the launch
-stream inside the timed region), per-kernel averages, and the CPU oracle
-timed on the host cores as a reported baseline.
+launch over its average duration, from HIP events the library records on the
+launch stream right after each of its kernel launches), per-kernel averages,
+and the CPU oracle timed on the host cores as a reported baseline.
 """
 from __future__ import annotations
 
@@ -38,9 +38,12 @@ METRIC = "tokens/s per multi-LoRA linear (4096², r=16) + % HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak, published
 RIDGE = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
-KERNEL_SOURCES = {"base_gemm": "base_gemm.hip", "shrink": "lora_branch.hip", "expand": "lora_branch.hip",
-                  "fused": "lora_branch.hip", "segments": "seg_build.hip", "shrink_rows": "lora_branch.hip",
-                  "gemm_lora": "base_gemm.hip"}
+KERNEL_SOURCES = {"seg_build": "seg_build.hip", "gemm_skinny": "base_gemm.hip", "gemm_ksplit": "base_gemm.hip",
+                  "gemm_tiled": "base_gemm.hip", "gemm_big": "base_gemm.hip", "gemm_decode": "base_gemm.hip",
+                  "gemm_decode+shrink_rows": "base_gemm.hip", "finish_part": "base_gemm.hip",
+                  "gemm_mid": "base_gemm.hip", "gemm_skinny_lora": "base_gemm.hip",
+                  "gemm_ksplit_lora": "base_gemm.hip", "shrink": "lora_branch.hip", "expand": "lora_branch.hip",
+                  "fused": "lora_branch.hip", "shrink_rows": "lora_branch.hip"}
 DEFAULT_WORKLOAD = "decode_3"
 
 
@@ -74,30 +77,46 @@ def segment_sizes(w):
 
 
 def algorithmic(w, chunks):
-    """{kernel: (bytes, flops)} per launch."""
+    """{kernel: (bytes, flops)} per launch: what the step must move and
+    compute, split over the library's kernels (scratch such as split-K
+    partials is not counted)."""
     n, din, dout = w.n, w.din, w.dout
     segs, n_act = segment_sizes(w)
     sum_r = sum(r for _, _, r in segs)
     sum_nr = sum(c * r for _, c, r in segs)
+    base = (2 * (dout * din + n * din + n * dout), 2 * n * din * dout)
+    shrink_rows = (2 * sum_r * din + 2 * n_act * din + 4 * sum_nr, 2 * sum_nr * din)
+    split_dense = (2 * (dout * din + n * din), 2 * n * din * dout)   # Y comes from the finish pass
+    finish = (2 * sum_r * dout + 4 * sum_nr + 2 * n * dout, 2 * sum_nr * dout)
+    gemm_lora = (base[0] + 2 * sum_r * dout + 4 * sum_nr, base[1] + 2 * sum_nr * dout)
     out = {
-        "base_gemm": (2 * (dout * din + n * din + n * dout), 2 * n * din * dout),
+        "seg_build": (4 * n + 4 * 4 * n, 0),
         "shrink": (2 * sum_r * din + 2 * n_act * din + 4 * sum_nr * max(chunks, 1), 2 * sum_nr * din),
         "expand": (2 * sum_r * dout + 4 * n_act * dout + 4 * sum_nr * max(chunks, 1), 2 * sum_nr * dout),
         "fused": (2 * sum_r * (din + dout) + 2 * n_act * din + 4 * n_act * dout, 2 * sum_nr * (din + dout)),
-        "segments": (4 * n + 4 * 4 * n, 0),
+        "shrink_rows": shrink_rows,
+        "gemm_decode": split_dense, "gemm_mid": split_dense,
+        "gemm_decode+shrink_rows": (split_dense[0] + shrink_rows[0], split_dense[1] + shrink_rows[1]),
+        "finish_part": finish,
+        "gemm_skinny_lora": gemm_lora, "gemm_ksplit_lora": gemm_lora,
     }
-    # per-row decode path: the shrink moves what the grouped shrink moves; the
-    # GEMM kernel adds each distinct adapter's Up and the per-row t
-    out["shrink_rows"] = (2 * sum_r * din + 2 * n_act * din + 4 * sum_nr, 2 * sum_nr * din)
-    out["gemm_lora"] = (out["base_gemm"][0] + 2 * sum_r * dout + 4 * sum_nr,
-                        out["base_gemm"][1] + 2 * sum_nr * dout)
+    for k in ("gemm_skinny", "gemm_ksplit", "gemm_tiled", "gemm_big"):
+        out[k] = base
     return out
 
 
+DENSE = ("gemm_skinny", "gemm_ksplit", "gemm_tiled", "gemm_big", "gemm_decode", "gemm_mid",
+         "gemm_decode+shrink_rows", "gemm_skinny_lora", "gemm_ksplit_lora")
+
+
 def source_hash(kernel):
-    p = os.path.join(ROOT, "lora_serving_mlora_amd", "csrc", KERNEL_SOURCES[kernel])
-    with open(p, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel's source file and the headers every kernel shares."""
+    h = hashlib.sha256()
+    base = os.path.join(ROOT, "lora_serving_mlora_amd", "csrc")
+    for f in (KERNEL_SOURCES[kernel.split("#")[0]], "internal.h", "row_kernels.h"):
+        with open(os.path.join(base, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel, workload):
@@ -220,36 +239,15 @@ def main():
     seg_ws = M.build_segments(pool, ids)
     Y = torch.empty((n, w.dout), dtype=torch.bfloat16, device="cuda")
     variant, chunks = M.plan(pool, n, args.variant)
-    T = torch.zeros((max(chunks, 1), n, w.max_rank), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     print(f"[bench] plan: variant={variant} shrink_chunks={chunks}", file=sys.stderr, flush=True)
 
-    if variant == "rows":
-        kernels = ["segments", "shrink_rows", "gemm_lora"]
-    else:
-        kernels = ["segments", "base_gemm"] + (["fused"] if variant == "fused" else ["shrink", "expand"])
     work = M.new_work(pool, n)
 
-    def step(i, evs=None):
+    def step(i):
         p = i % R
-        rec = (lambda k: evs[k].record()) if evs is not None else (lambda k: None)
-        rec(0)
         M.build_segments(pool, ids, seg_ws)
-        rec(1)
-        if variant == "rows":
-            M.shrink_rows(pool, p, X, seg_ws, work)
-            rec(2)
-            M.gemm_lora(pool, p, X, W0s[p], seg_ws, work, Y)
-        else:
-            M.base_gemm(X, W0s[p], Y)
-            rec(2)
-            if variant == "fused":
-                M.fused(pool, p, X, seg_ws, Y)
-            else:
-                M.shrink(pool, p, X, seg_ws, chunks, T)
-                rec(3)
-                M.expand(pool, p, T, seg_ws, Y)
-        rec(len(kernels))
+        M.apply(pool, p, X, W0s[p], seg_ws, Y=Y, work=work, variant=variant)
 
     K, W = args.steps, args.warmup
     for i in range(W):
@@ -284,10 +282,10 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / K
     print(f"[bench] timed {K} steps: {ms_per_step * 1e3:.2f} us/step", file=sys.stderr, flush=True)
 
-    # ---- per-kernel durations: HIP events on the launch stream around each
-    # kernel of the same K steps, launched eagerly behind a spin kernel so the
-    # queue is full and host launch gaps stay out of the intervals
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(K)]
+    # ---- per-kernel durations: the library records a HIP event on the launch
+    # stream right after each of its kernel launches; the same K steps are
+    # launched eagerly behind a spin kernel so the queue is full and host
+    # launch gaps stay out of the intervals
     spin = getattr(torch.cuda, "_sleep", None)
     if spin is not None:
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -300,27 +298,34 @@ def main():
     torch.cuda.synchronize()
     if spin is not None:
         spin(spin_cycles)
+    KT = min(K, 2048 // 8)
+    M.timing_arm(2048)
     t2 = time.perf_counter()
-    for i in range(K):
-        step(W + i, events[i])
+    for i in range(KT):
+        step(W + i)
     host_enqueue_s = time.perf_counter() - t2
+    marks = M.timing_read()
     torch.cuda.synchronize()
+    per_step = len(marks) // KT
+    kernels = [marks[j][0] for j in range(per_step)]
     per_kernel_ms = {}
-    for k, name in enumerate(kernels):
-        per_kernel_ms[name] = float(np.mean([events[i][k].elapsed_time(events[i][k + 1]) for i in range(K)]))
-    step_gpu_ms = float(np.mean([events[i][0].elapsed_time(events[i][len(kernels)]) for i in range(K)]))
+    for j, name in enumerate(kernels):
+        key = name if name not in per_kernel_ms else f"{name}#{j}"
+        per_kernel_ms[key] = float(np.mean([marks[i * per_step + j][1] for i in range(KT)]))
+    kernel_sum_ms = float(np.mean([sum(m[1] for m in marks[i * per_step:(i + 1) * per_step]) for i in range(KT)]))
     queue_ok = spin is not None and host_enqueue_s * 1e3 < (0.05 + 100e-6 * K) * 1e3
-    timing = ("hip events on the launch stream, eager pass of the same steps behind a spin kernel "
+    timing = ("kernel start/end HIP events stamped by the runtime on each library launch (hipExtLaunchKernel), "
+              f"eager pass of {KT} steps behind a spin kernel "
               f"({'queue stayed full' if queue_ok else 'queue may have drained'})")
     if not bool(torch.isfinite(Y.float()).all()):
         print("[bench] warning: non-finite outputs", file=sys.stderr)
 
     algo = algorithmic(w, chunks)
     timed = {k: v for k, v in per_kernel_ms.items() if v}
-    dom = max((k for k in timed if k != "segments"), key=lambda k: timed[k])
-    b, f = algo[dom]
+    dom = max((k for k in timed if k != "seg_build"), key=lambda k: timed[k])
+    b, f = algo[dom.split("#")[0]]
     t_s = timed[dom] * 1e-3
-    mfma_bound = dom in ("base_gemm", "gemm_lora") and f / b > RIDGE
+    mfma_bound = dom.split("#")[0] in DENSE and f / b > RIDGE
     if mfma_bound:
         ach, peak, unit = f / t_s / 1e12, MFMA_BF16_PEAK_TFS, "TFLOP/s"
     else:
@@ -361,9 +366,7 @@ def main():
                    "launch": "hipgraph" if use_graph else "eager", "parallelism": "single-gpu"},
         "roofline": roofline,
         "per_kernel_us": {k: (round(v * 1e3, 3) if v else None) for k, v in per_kernel_ms.items()},
-        "step_gpu_us": round(step_gpu_ms * 1e3, 3),
-        "branch_over_base": (round((sum(timed.get(k, 0) for k in ("shrink", "expand", "fused"))) /
-                                   timed["base_gemm"], 4) if timed.get("base_gemm") else None),
+        "kernel_sum_us": round(kernel_sum_ms * 1e3, 3),
         "gpu_name": torch.cuda.get_device_name(0),
         "hbm_copy_gbps": round(cal["gbps"], 1),
     }

@@ -249,7 +249,9 @@ mlora_status mlora_fused(const mlora_pool* pool, int32_t proj, const uint16_t* X
  * section 02 allows instead of regrouping); other entries are not written.
  * The rest of `work` is the GEMM's scratch (split-K partials), so the two
  * calls go in this order on one stream, and calls that share a `work` buffer
- * must not overlap. */
+ * must not overlap.  mlora_apply with ROWS computes the same T and Y; for
+ * decode shapes it runs the per-row shrink as extra workgroups of the GEMM
+ * launch (two kernels in all: GEMM + shrink, then partial sums + expand). */
 mlora_status mlora_shrink_rows(const mlora_pool* pool, int32_t proj, const uint16_t* X, const void* seg_ws,
                                int32_t n_rows, void* work, size_t work_bytes, void* stream);
 
@@ -291,6 +293,22 @@ mlora_status mlora_apply(const mlora_pool* pool, int32_t proj, const uint16_t* X
  * and hardware byte counters against a kernel of known traffic.
  * ------------------------------------------------------------------------- */
 mlora_status mlora_hbm_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Launch timing, a measurement aid that changes no result.
+ * mlora_timing_arm(n) arms the library's next n kernel launches (1..2048),
+ * from any entry point: each is made with a pair of HIP events that the
+ * runtime stamps when that kernel starts and ends on the GPU.
+ * mlora_timing_read disarms, sets *out_n to the number of launches marked,
+ * and, if `capacity` holds them, waits for their events and writes ms[i],
+ * launch i's kernel duration in milliseconds; otherwise it fails with
+ * MLORA_EINVAL.  mlora_timing_name(i) is the kernel of launch i (a static
+ * string; NULL past the marked launches).  Not for use while a stream is
+ * captured into a graph; one armed sequence per process at a time.
+ * ------------------------------------------------------------------------- */
+mlora_status mlora_timing_arm(int32_t n_launches);
+mlora_status mlora_timing_read(float* ms, int32_t capacity, int32_t* out_n);
+const char* mlora_timing_name(int32_t i);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,7 @@ import numpy as np
 __all__ = [
     "MloraError", "lib", "Pool", "build_segments", "segments_header", "read_segments",
     "base_gemm", "shrink", "shrink_max_chunks", "expand", "fused", "shrink_rows", "gemm_lora", "new_work", "rows_t", "apply", "plan", "work_bytes",
-    "hbm_copy", "VARIANTS", "ITEM_ROWS", "MAX_ROWS", "MAX_RANK", "SEG", "EXPORTS", "LIB_PATH",
+    "hbm_copy", "timing_arm", "timing_read", "VARIANTS", "ITEM_ROWS", "MAX_ROWS", "MAX_RANK", "SEG", "EXPORTS", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmlora.so")
@@ -74,6 +74,10 @@ EXPORTS = {
     "mlora_apply": (ctypes.c_int, [_c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p,
                                    _sz, _i32, _c_void_p]),
     "mlora_hbm_copy": (ctypes.c_int, [_c_void_p, _c_void_p, _sz, _c_void_p]),
+    "mlora_timing_arm": (ctypes.c_int, [ctypes.c_int32]),
+    "mlora_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float), ctypes.c_int32,
+                                         ctypes.POINTER(ctypes.c_int32)]),
+    "mlora_timing_name": (ctypes.c_char_p, [ctypes.c_int32]),
 }
 
 _lib = None
@@ -385,3 +389,23 @@ def hbm_copy(dst, src, nbytes: Optional[int] = None):
     nb = src.numel() * src.element_size() if nbytes is None else nbytes
     _check(lib().mlora_hbm_copy(_ptr(dst), _ptr(src), nb, _stream()), "mlora_hbm_copy")
     return dst
+
+
+_timing_armed = [0]
+
+
+def timing_arm(n_launches: int):
+    """Arms kernel start/end events on the library's next n_launches kernel
+    launches (a measurement aid)."""
+    _check(lib().mlora_timing_arm(n_launches), "mlora_timing_arm")
+    _timing_armed[0] = n_launches
+
+
+def timing_read() -> list:
+    """Waits for the armed events: [(kernel name, milliseconds)] per marked
+    launch, in launch order."""
+    cap = max(_timing_armed[0], 1)
+    ms = (ctypes.c_float * cap)()
+    n = ctypes.c_int32(0)
+    _check(lib().mlora_timing_read(ms, cap, ctypes.byref(n)), "mlora_timing_read")
+    return [(lib().mlora_timing_name(i).decode(), float(ms[i])) for i in range(n.value)]

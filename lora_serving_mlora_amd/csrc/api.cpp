@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -30,6 +31,18 @@ mlora_status fail(mlora_status s, const char* fmt, ...) {
   g_err = buf;
   return s;
 }
+
+// armed launch timing: launch i gets events ev[2i] (kernel start) and
+// ev[2i+1] (kernel end)
+constexpr int kTimingMax = 2048;
+struct Timing {
+  std::mutex mu;
+  std::atomic<int> armed{0};  // launches still to mark
+  int used = 0;               // launches marked so far
+  std::vector<hipEvent_t> ev;
+  std::vector<const char*> name;  // name[i]: kernel of launch i
+};
+Timing g_timing;
 
 mlora_status hip_check(hipError_t e, const char* what) {
   if (e == hipSuccess) return MLORA_OK;
@@ -596,7 +609,7 @@ mlora_status mlora_gemm_lora(const mlora_pool* p, int32_t proj, const uint16_t* 
   if ((st = check_rows_work(p, n, work, work_bytes)) != MLORA_OK) return st;
   const RowsWork w = rows_work(p, n, work);
   return hip_check(mlora::launch_gemm_lora(p->view(), proj, X, W0, static_cast<const int32_t*>(seg_ws), w.T, w.part,
-                                           Y, n, as_stream(stream)),
+                                           Y, n, false, as_stream(stream)),
                    "GEMM + expand launch");
 }
 
@@ -664,9 +677,8 @@ mlora_status mlora_apply(const mlora_pool* p, int32_t proj, const uint16_t* X, c
   if (variant == MLORA_VARIANT_ROWS) {
     if ((st = check_rows_work(p, n, work, work_bytes)) != MLORA_OK) return st;
     const RowsWork w = rows_work(p, n, work);
-    st = hip_check(mlora::launch_shrink_rows(v, proj, X, ws, n, w.T, s), "per-row shrink launch");
-    if (st != MLORA_OK) return st;
-    return hip_check(mlora::launch_gemm_lora(v, proj, X, W0, ws, w.T, w.part, Y, n, s), "GEMM + expand launch");
+    return hip_check(mlora::launch_gemm_lora(v, proj, X, W0, ws, w.T, w.part, Y, n, true, s),
+                     "per-row shrink + GEMM + expand launch");
   }
   st = hip_check(mlora::launch_base_gemm(X, W0, Y, n, d.din, d.dout, s), "base GEMM launch");
   if (st != MLORA_OK) return st;
@@ -679,6 +691,43 @@ mlora_status mlora_apply(const mlora_pool* p, int32_t proj, const uint16_t* X, c
   return hip_check(mlora::launch_expand(v, proj, T, chunks, ws, Y, n, s), "expand launch");
 }
 
+mlora_status mlora_timing_arm(int32_t n_launches) {
+  g_err.clear();
+  if (n_launches < 1 || n_launches > kTimingMax) return fail(MLORA_EINVAL, "n_launches %d outside [1, %d]", n_launches, kTimingMax);
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  while ((int)g_timing.ev.size() < 2 * n_launches) {
+    hipEvent_t e;
+    mlora_status st = hip_check(hipEventCreate(&e), "hipEventCreate(timing)");
+    if (st != MLORA_OK) return st;
+    g_timing.ev.push_back(e);
+  }
+  g_timing.name.assign(n_launches, nullptr);
+  g_timing.used = 0;
+  g_timing.armed.store(n_launches);
+  return MLORA_OK;
+}
+
+mlora_status mlora_timing_read(float* ms, int32_t capacity, int32_t* out_n) {
+  g_err.clear();
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  g_timing.armed.store(0);
+  const int used = g_timing.used;
+  if (out_n) *out_n = used;
+  if (!ms || capacity < used) return fail(MLORA_EINVAL, "room for %d intervals, %d launches marked", capacity, used);
+  mlora_status st = MLORA_OK;
+  for (int i = 0; i < used && st == MLORA_OK; ++i) {
+    st = hip_check(hipEventSynchronize(g_timing.ev[2 * i + 1]), "hipEventSynchronize(timing)");
+    if (st == MLORA_OK)
+      st = hip_check(hipEventElapsedTime(&ms[i], g_timing.ev[2 * i], g_timing.ev[2 * i + 1]), "hipEventElapsedTime");
+  }
+  return st;
+}
+
+const char* mlora_timing_name(int32_t i) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  return (i >= 0 && i < g_timing.used) ? g_timing.name[i] : nullptr;
+}
+
 mlora_status mlora_hbm_copy(void* dst, const void* src, size_t bytes, void* stream) {
   g_err.clear();
   if (!dst || !src || bytes % 16 != 0 || !aligned16(dst) || !aligned16(src))
@@ -687,3 +736,19 @@ mlora_status mlora_hbm_copy(void* dst, const void* src, size_t bytes, void* stre
 }
 
 }  // extern "C"
+
+namespace mlora {
+TimingSlot timing_next(const char* kernel) {
+  TimingSlot t;
+  if (g_timing.armed.load(std::memory_order_relaxed) <= 0) return t;
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  if (g_timing.armed.load() <= 0) return t;
+  g_timing.armed.fetch_sub(1);
+  const int i = g_timing.used++;
+  g_timing.name[i] = kernel;
+  t.start = g_timing.ev[2 * i];
+  t.stop = g_timing.ev[2 * i + 1];
+  t.on = true;
+  return t;
+}
+}  // namespace mlora

@@ -21,6 +21,7 @@
 #include <stdlib.h>
 
 #include "internal.h"
+#include "row_kernels.h"
 
 namespace mlora {
 namespace {
@@ -170,50 +171,6 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void gemm_skinny(const uint16_t*
 // so Y is written once and the branch costs no extra pass over Y.
 // ---------------------------------------------------------------------------
 constexpr int kLoraWaves = 2;
-
-// The low-rank term of row r at columns [c0, c0+8): sum_q T[r][q] Up_a[c][q]
-// (T carries the scale).  Zero for a base-only row or a row past M, NaN for
-// a row with an invalid id.  Ranks past the adapter's rank read its last
-// column with weight 0, so each group of 8 page loads goes out at once.
-template <bool VEC>
-__device__ __forceinline__ void lora_delta8(const PoolView& pv, int proj, const int32_t* __restrict__ row_key,
-                                            const float* __restrict__ T, int r, int M, int c0, int N,
-                                            float (&acc8)[8]) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc8[e] = 0.f;
-  const int key = (r < M && c0 < N) ? row_key[r] : -1;
-  if (key >= 0) {
-    const int rank = pv.rank[key];
-    const int32_t* upage = pv.up_page + ((size_t)key * pv.n_proj + proj) * pv.max_rank;
-    const float* tr = T + (size_t)r * pv.max_rank;
-    // page indices and t are read without waiting for the rank: entries past
-    // it fall back to the group's first page and weigh zero (a select, so an
-    // unwritten t past the rank never reaches the sum)
-    int q0 = 0;
-    do {
-      float u8[8][8], tq[8];
-      int pg[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) pg[q] = upage[min(q0 + q, pv.max_rank - 1)];
-#pragma unroll
-      for (int q = 1; q < 8; ++q) pg[q] = pg[q] < 0 ? pg[0] : pg[q];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        load8<VEC>(pv.up + (size_t)pg[q] * pv.dout, c0, N, u8[q]);
-        const float tv = tr[min(q0 + q, pv.max_rank - 1)];
-        tq[q] = (q0 + q < rank) ? tv : 0.f;
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc8[e] = fmaf(tq[q], u8[q][e], acc8[e]);
-      q0 += 8;
-    } while (q0 < rank);
-  } else if (key == -2) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc8[e] = __uint_as_float(0x7fc00000u);
-  }
-}
 
 template <int MB, bool VEC>
 __global__ __launch_bounds__(64 * (kSkinnyWaves + kLoraWaves)) void gemm_skinny_lora(
@@ -691,31 +648,32 @@ hipError_t launch_big(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, 
   const int tiles_m = (M + GB - 1) / GB, tiles_n = (N + GB - 1) / GB;
   const int n_tiles = tiles_m * tiles_n;
   const int per_xcd = (n_tiles + 7) / 8;
-  hipLaunchKernelGGL(gemm_big, dim3(per_xcd * 8), dim3(kBigThreads), 0, st, X, W, Y, M, K, N, tiles_n, n_tiles,
+  MLORA_LAUNCH("gemm_big", gemm_big, dim3(per_xcd * 8), dim3(kBigThreads), 0, st, X, W, Y, M, K, N, tiles_n, n_tiles,
                      per_xcd);
-  return hipGetLastError();
+  return launched();
 }
 
 template <bool VEC>
 hipError_t launch_gemm(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N, hipStream_t st) {
   if (M <= 64) {
     const dim3 grid((N + 15) / 16), block(64 * kSkinnyWaves);
-    if (M <= 16) hipLaunchKernelGGL((gemm_skinny<1, VEC>), grid, block, 0, st, X, W, Y, M, K, N);
-    else if (M <= 32) hipLaunchKernelGGL((gemm_skinny<2, VEC>), grid, block, 0, st, X, W, Y, M, K, N);
-    else if (M <= 48) hipLaunchKernelGGL((gemm_skinny<3, VEC>), grid, block, 0, st, X, W, Y, M, K, N);
-    else hipLaunchKernelGGL((gemm_skinny<4, VEC>), grid, block, 0, st, X, W, Y, M, K, N);
+    if (M <= 16) MLORA_LAUNCH("gemm_skinny", (gemm_skinny<1, VEC>), grid, block, 0, st, X, W, Y, M, K, N);
+    else if (M <= 32) MLORA_LAUNCH("gemm_skinny", (gemm_skinny<2, VEC>), grid, block, 0, st, X, W, Y, M, K, N);
+    else if (M <= 48) MLORA_LAUNCH("gemm_skinny", (gemm_skinny<3, VEC>), grid, block, 0, st, X, W, Y, M, K, N);
+    else MLORA_LAUNCH("gemm_skinny", (gemm_skinny<4, VEC>), grid, block, 0, st, X, W, Y, M, K, N);
   } else if (M <= 1024 && (long)((M + 127) / 128) * ((N + 31) / 32) >= 128 && ksplit_enabled()) {
     const dim3 grid((N + 31) / 32, (M + 32 * KS_MB - 1) / (32 * KS_MB)), block(64 * kKsWaves);
-    hipLaunchKernelGGL((gemm_ksplit<VEC, false>), grid, block, 0, st, X, W, Y, M, K, N, PoolView{}, 0, nullptr,
+    MLORA_LAUNCH("gemm_ksplit", (gemm_ksplit<VEC, false>), grid, block, 0, st, X, W, Y, M, K, N, PoolView{}, 0, nullptr,
                        nullptr);
   } else if (VEC && K % GBK == 0 && (long)M * N >= 2048L * 2048L && (long)M * K * 2 < (1L << 31) &&
              (long)N * K * 2 < (1L << 31) && big_gemm_enabled()) {
     return launch_big(X, W, Y, M, K, N, st);
   } else {
     const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM), block(kTiledThreads);
-    hipLaunchKernelGGL((gemm_tiled<VEC>), grid, block, 0, st, X, W, Y, M, K, N);
+    MLORA_LAUNCH("gemm_tiled", (gemm_tiled<VEC>), grid, block, 0, st, X, W, Y, M, K, N, nullptr, 0);
+    return launched();
   }
-  return hipGetLastError();
+  return launched();
 }
 
 // ---------------------------------------------------------------------------
@@ -727,101 +685,96 @@ hipError_t launch_gemm(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M,
 // LDS DMA and shared by the 4 column-group waves, so each X byte is read by 64
 // workgroups instead of 256, while the 256 workgroups still cover the chip.
 // 8 GEMM waves = 4 column groups x 2 halves of the quarter; each wave issues
-// all 16 of its W0 loads at once.  2 more waves compute the low-rank term of
-// the rows r with r % 4 == quarter (so the 4 quarters split that work).  The
-// quarter's fp32 partial goes to `part`; the last workgroup of a column block
-// to finish (atomic counter, zeroed by the per-row shrink and reset here)
-// sums the 4 partials in quarter order and writes Y: deterministic.
+// all 16 of its W0 loads at once.  The quarter's fp32 partial goes to `part`
+// and a second kernel (finish_part) sums the 4 partials in quarter order,
+// adds the low-rank term and writes Y: deterministic.  (Finishing in the last
+// workgroup of a column block behind an atomic counter cost more: the
+// device-scope release/acquire writes back and invalidates the L2s.)  The
+// per-row shrink of the batch rides along as extra workgroups of the launch:
+// independent work, and one launch less per step.
 // LDS: X slice [M][K/4] in 1 KiB blocks whose 16-byte chunks are XOR-swizzled
 // by (row & 15), so the 16 rows an MFMA fragment read touches hit 16
 // different chunk positions.
 // ---------------------------------------------------------------------------
-constexpr int kDecCols = 64, kDecSplit = 4, kDecWaves = 8, kDecLoraWaves = 2;
+constexpr int kDecCols = 64, kDecSplit = 4, kDecWaves = 8;
 constexpr int kMidMaxSplit = 8;
 
 template <int MB>
-__global__ __launch_bounds__(64 * (kDecWaves + kDecLoraWaves)) void gemm_decode(
-    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y, int M, int K, int N,
-    PoolView pv, int proj, const int32_t* __restrict__ row_key, const float* __restrict__ T,
-    float* __restrict__ part) {
+__global__ __launch_bounds__(64 * kDecWaves) void gemm_decode(const uint16_t* __restrict__ X,
+                                                             const uint16_t* __restrict__ W, int M, int K, int N,
+                                                             PoolView pv, int proj,
+                                                             const int32_t* __restrict__ row_key, float* __restrict__ T,
+                                                             float* __restrict__ part, int n_shrink) {
+  // the first n_shrink workgroups are the per-row shrink of the batch
+  // (independent work that shares the launch)
+  if ((int)blockIdx.x < n_shrink) {
+    shrink_row_body<true>(pv, proj, X, row_key, blockIdx.x, T);
+    return;
+  }
   extern __shared__ __attribute__((aligned(16))) uint16_t dec_lds[];
   const int Kq = K / kDecSplit;
   uint16_t* xs = dec_lds;                                               // [M][Kq]
   floatx4* red = reinterpret_cast<floatx4*>(dec_lds + (size_t)M * Kq);  // [4][MB][64]
-  float* delta = reinterpret_cast<float*>(red + 4 * MB * 64);           // [16][64]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int cb = blockIdx.x, kq = blockIdx.y;
+  const int ncb = (N + kDecCols - 1) / kDecCols;
+  const int b = blockIdx.x - n_shrink;
+  const int cb = b % ncb, kq = b / ncb;
   const int n0 = cb * kDecCols;
-  const bool gemm_wave = wave < kDecWaves;
-  const int cg = wave & 3, kh = (wave >> 2) & 1;
+  const int cg = wave & 3, kh = wave >> 2;
   const int steps = Kq / 64;  // 32-wide steps in a wave's half of the quarter (<= 16)
-  uint4 wv[16];
 
-  if (gemm_wave) {
-    // X slice -> LDS: instruction (row r, 1 KiB block b); lane l fetches
-    // logical chunk l ^ (r & 15) of the block into physical chunk l
-    const __amdgpu_buffer_rsrc_t rx =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X), (short)0, M * K * 2, 0x00020000);
-    const int blocks = Kq / 512;
-    for (int i = wave; i < M * blocks; i += kDecWaves) {
-      const int r = i / blocks, b = i % blocks;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, xs + (size_t)r * Kq + b * 512, 16, (lane ^ (r & 15)) * 16,
-                                               (r * K + kq * Kq + b * 512) * 2, 0, 0);
-    }
-    // all of this wave's W0 fragments at once (column group cg, half kh)
-    const uint16_t* wrow =
-        W + (size_t)min(n0 + 16 * cg + (lane & 15), N - 1) * K + kq * Kq + kh * (Kq / 2) + (lane >> 4) * 8;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) wv[j] = *reinterpret_cast<const uint4*>(wrow + (size_t)min(j, steps - 1) * 32);
-    __builtin_amdgcn_s_waitcnt(0);
-  } else {
-    // low-rank term of rows r = kq, kq+4, ... over the block's 64 columns
-    const int u = tid - 64 * kDecWaves;
-    const int rr = u >> 3, h = u & 7;
-    float acc8[8];
-    lora_delta8<true>(pv, proj, row_key, T, kq + 4 * rr, M, n0 + 8 * h, N, acc8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) delta[rr * 64 + 8 * h + e] = acc8[e];
+  // X slice -> LDS: instruction (row r, 1 KiB block b); lane l fetches
+  // logical chunk l ^ (r & 15) of the block into physical chunk l
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X), (short)0, M * K * 2, 0x00020000);
+  const int blocks = Kq / 512;
+  for (int i = wave; i < M * blocks; i += kDecWaves) {
+    const int r = i / blocks, bl = i % blocks;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, xs + (size_t)r * Kq + bl * 512, 16, (lane ^ (r & 15)) * 16,
+                                             (r * K + kq * Kq + bl * 512) * 2, 0, 0);
   }
-  __syncthreads();  // X slice in LDS, delta written
+  // all of this wave's W0 fragments at once (column group cg, half kh)
+  const uint16_t* wrow =
+      W + (size_t)min(n0 + 16 * cg + (lane & 15), N - 1) * K + kq * Kq + kh * (Kq / 2) + (lane >> 4) * 8;
+  uint4 wv[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) wv[j] = *reinterpret_cast<const uint4*>(wrow + (size_t)min(j, steps - 1) * 32);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // X slice in LDS
 
   floatx4 acc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
-  if (gemm_wave) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (j < steps) {
-        const int c = kh * (Kq / 16) + j * 4 + (lane >> 4);  // logical 16-byte chunk in the slice row
+  for (int j = 0; j < 16; ++j) {
+    if (j < steps) {
+      const int c = kh * (Kq / 16) + j * 4 + (lane >> 4);  // logical 16-byte chunk in the slice row
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const int r = min(mb * 16 + (lane & 15), M - 1);
-          const uint4 a = *reinterpret_cast<const uint4*>(xs + (size_t)r * Kq + (c >> 6) * 512 +
-                                                          (((c & 63) ^ (r & 15)) << 3));
-          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(wv[j]), acc[mb], 0, 0, 0);
-        }
+      for (int mb = 0; mb < MB; ++mb) {
+        const int r = min(mb * 16 + (lane & 15), M - 1);
+        const uint4 a =
+            *reinterpret_cast<const uint4*>(xs + (size_t)r * Kq + (c >> 6) * 512 + (((c & 63) ^ (r & 15)) << 3));
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(wv[j]), acc[mb], 0, 0, 0);
       }
     }
-    if (kh == 1) {
+  }
+  if (kh == 1) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) red[(cg * MB + mb) * 64 + lane] = acc[mb];
-    }
+    for (int mb = 0; mb < MB; ++mb) red[(cg * MB + mb) * 64 + lane] = acc[mb];
   }
   __syncthreads();
-  if (gemm_wave && kh == 0) {
-    // the quarter's partial: both halves + this quarter's share of the delta
+  if (kh == 0) {
+    // the quarter's partial: both halves
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const floatx4 o = red[(cg * MB + mb) * 64 + lane];
-      const int c = 16 * cg + (lane & 15);
+      const int c = n0 + 16 * cg + (lane & 15);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int r = mb * 16 + (lane >> 4) * 4 + v;
-        float y = acc[mb][v] + o[v];
-        if ((r & 3) == kq) y += delta[(r >> 2) * 64 + c];
-        if (r < M && n0 + c < N) part[((size_t)kq * M + r) * N + n0 + c] = y;
+        if (r < M && c < N) part[((size_t)kq * M + r) * N + c] = acc[mb][v] + o[v];
       }
     }
   }
@@ -831,21 +784,18 @@ __global__ __launch_bounds__(64 * (kDecWaves + kDecLoraWaves)) void gemm_decode(
 // low-rank term when LORA (sum_q T[r][q] Up_a[c][q], Up streamed here), and
 // writes Y (bf16 RNE); 8 columns per thread, so each Up page row is read as
 // coalesced 16-byte pieces.
+constexpr int kFinishThreads = 64;  // one wave per workgroup: the decode grid spreads over every CU
+
 template <bool LORA>
-__global__ __launch_bounds__(256) void finish_part(const float* __restrict__ part, int S, uint16_t* __restrict__ Y,
-                                                   int M, int N, PoolView pv, int proj,
-                                                   const int32_t* __restrict__ row_key, const float* __restrict__ T) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
+__global__ __launch_bounds__(kFinishThreads) void finish_part(const float* __restrict__ part, int S,
+                                                              uint16_t* __restrict__ Y, int M, int N, PoolView pv,
+                                                              int proj, const int32_t* __restrict__ row_key,
+                                                              const float* __restrict__ T) {
+  const int t = blockIdx.x * kFinishThreads + threadIdx.x;
   const int per_row = N / 8;
   if (t >= M * per_row) return;
   const int r = t / per_row, c0 = (t % per_row) * 8;
-  float y[8];
-  if (LORA) {
-    lora_delta8<true>(pv, proj, row_key, T, r, M, c0, N, y);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = 0.f;
-  }
+  // the partials' loads go out before the low-rank term's dependent chain
   float sum[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) sum[e] = 0.f;
@@ -856,6 +806,13 @@ __global__ __launch_bounds__(256) void finish_part(const float* __restrict__ par
     sum[0] += p0.x; sum[1] += p0.y; sum[2] += p0.z; sum[3] += p0.w;
     sum[4] += p1.x; sum[5] += p1.y; sum[6] += p1.z; sum[7] += p1.w;
   }
+  float y[8];
+  if (LORA) {
+    lora_delta8<true>(pv, proj, row_key, T, r, M, c0, N, y);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = 0.f;
+  }
   uint4 w;
   w.x = pack_bf2(sum[0] + y[0], sum[1] + y[1]);
   w.y = pack_bf2(sum[2] + y[2], sum[3] + y[3]);
@@ -864,13 +821,14 @@ __global__ __launch_bounds__(256) void finish_part(const float* __restrict__ par
   *reinterpret_cast<uint4*>(Y + (size_t)r * N + c0) = w;
 }
 
-size_t decode_lds_bytes(int M, int K, int MB) {
-  return (size_t)M * (K / kDecSplit) * 2 + (size_t)4 * MB * 64 * 16 + 16 * 64 * 4;
-}
+size_t decode_lds_bytes(int M, int K, int MB) { return (size_t)M * (K / kDecSplit) * 2 + (size_t)4 * MB * 64 * 16; }
 
+// n_shrink > 0: the per-row shrink of the batch runs as extra workgroups of
+// the same launch (T must not be read by the GEMM itself: the finish pass
+// adds the low-rank term).
 template <int MB>
 hipError_t launch_decode(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N, const PoolView& pv,
-                         int proj, const int32_t* row_key, const float* T, float* part, hipStream_t st) {
+                         int proj, const int32_t* row_key, float* T, float* part, int n_shrink, hipStream_t st) {
   const size_t lds = decode_lds_bytes(M, K, MB);
   static size_t attr = 0;
   if (lds > attr) {
@@ -879,14 +837,15 @@ hipError_t launch_decode(const uint16_t* X, const uint16_t* W, uint16_t* Y, int 
     if (e != hipSuccess) return e;
     attr = lds;
   }
-  const dim3 grid((N + kDecCols - 1) / kDecCols, kDecSplit), block(64 * (kDecWaves + kDecLoraWaves));
-  hipLaunchKernelGGL(gemm_decode<MB>, grid, block, lds, st, X, W, Y, M, K, N, pv, proj, row_key, T, part);
-  hipError_t e = hipGetLastError();
+  const int ncb = (N + kDecCols - 1) / kDecCols;
+  MLORA_LAUNCH(n_shrink ? "gemm_decode+shrink_rows" : "gemm_decode", gemm_decode<MB>, dim3(n_shrink + ncb * kDecSplit), dim3(64 * kDecWaves), lds, st, X, W, M, K, N,
+                     pv, proj, row_key, T, part, n_shrink);
+  hipError_t e = launched();
   if (e != hipSuccess) return e;
   const int threads = M * (N / 8);
-  hipLaunchKernelGGL(finish_part<false>, dim3((threads + 255) / 256), dim3(256), 0, st, part, kDecSplit, Y, M, N,
-                     PoolView{}, 0, nullptr, nullptr);
-  return hipGetLastError();
+  MLORA_LAUNCH("finish_part", finish_part<true>, dim3((threads + kFinishThreads - 1) / kFinishThreads), dim3(kFinishThreads),
+                     0, st, part, kDecSplit, Y, M, N, pv, proj, row_key, T);
+  return launched();
 }
 
 // medium batches: 128x128 tiles with split-K over S workgroups, then the
@@ -903,13 +862,13 @@ hipError_t launch_mid_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, in
   const int S = mid_split(M, N, K);
   const int kt_per = K / BK / S;
   const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM, S), block(kTiledThreads);
-  hipLaunchKernelGGL((gemm_tiled<true, true>), grid, block, 0, st, X, W, Y, M, K, N, part, kt_per);
-  hipError_t e = hipGetLastError();
+  MLORA_LAUNCH("gemm_mid", (gemm_tiled<true, true>), grid, block, 0, st, X, W, Y, M, K, N, part, kt_per);
+  hipError_t e = launched();
   if (e != hipSuccess) return e;
   const int threads = M * (N / 8);
-  hipLaunchKernelGGL(finish_part<true>, dim3((threads + 255) / 256), dim3(256), 0, st, part, S, Y, M, N, pv, proj,
-                     row_key, T);
-  return hipGetLastError();
+  MLORA_LAUNCH("finish_part", finish_part<true>, dim3((threads + kFinishThreads - 1) / kFinishThreads), dim3(kFinishThreads),
+                     0, st, part, S, Y, M, N, pv, proj, row_key, T);
+  return launched();
 }
 
 template <bool VEC>
@@ -917,19 +876,19 @@ hipError_t launch_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M,
                        int proj, const int32_t* row_key, const float* T, hipStream_t st) {
   if (M > 64) {
     const dim3 g((N + 31) / 32, (M + 32 * KS_MB - 1) / (32 * KS_MB)), b(64 * (kKsWaves + kKsLoraWaves));
-    hipLaunchKernelGGL((gemm_ksplit<VEC, true>), g, b, 0, st, X, W, Y, M, K, N, pv, proj, row_key, T);
-    return hipGetLastError();
+    MLORA_LAUNCH("gemm_ksplit_lora", (gemm_ksplit<VEC, true>), g, b, 0, st, X, W, Y, M, K, N, pv, proj, row_key, T);
+    return launched();
   }
   const dim3 grid((N + 15) / 16), block(64 * (kSkinnyWaves + kLoraWaves));
   if (M <= 16)
-    hipLaunchKernelGGL((gemm_skinny_lora<1, VEC>), grid, block, 0, st, X, W, Y, M, K, N, pv, proj, row_key, T);
+    MLORA_LAUNCH("gemm_skinny_lora", (gemm_skinny_lora<1, VEC>), grid, block, 0, st, X, W, Y, M, K, N, pv, proj, row_key, T);
   else if (M <= 32)
-    hipLaunchKernelGGL((gemm_skinny_lora<2, VEC>), grid, block, 0, st, X, W, Y, M, K, N, pv, proj, row_key, T);
+    MLORA_LAUNCH("gemm_skinny_lora", (gemm_skinny_lora<2, VEC>), grid, block, 0, st, X, W, Y, M, K, N, pv, proj, row_key, T);
   else if (M <= 48)
-    hipLaunchKernelGGL((gemm_skinny_lora<3, VEC>), grid, block, 0, st, X, W, Y, M, K, N, pv, proj, row_key, T);
+    MLORA_LAUNCH("gemm_skinny_lora", (gemm_skinny_lora<3, VEC>), grid, block, 0, st, X, W, Y, M, K, N, pv, proj, row_key, T);
   else
-    hipLaunchKernelGGL((gemm_skinny_lora<4, VEC>), grid, block, 0, st, X, W, Y, M, K, N, pv, proj, row_key, T);
-  return hipGetLastError();
+    MLORA_LAUNCH("gemm_skinny_lora", (gemm_skinny_lora<4, VEC>), grid, block, 0, st, X, W, Y, M, K, N, pv, proj, row_key, T);
+  return launched();
 }
 
 }  // namespace
@@ -940,18 +899,25 @@ bool decode_splitk_ok(int M, int K, int N, bool vec) {
 }
 
 hipError_t launch_gemm_lora(const PoolView& pv, int proj, const uint16_t* X, const uint16_t* W, const int32_t* ws,
-                            const float* T, float* part, uint16_t* Y, int M, hipStream_t stream) {
+                            float* T, float* part, uint16_t* Y, int M, bool shrink, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
   const int K = pv.din, N = pv.dout;
   const int32_t* row_key = ws + MLORA_SEG_ROWKEY(M);
   const uintptr_t al = reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(W) |
                        reinterpret_cast<uintptr_t>(pv.up) | reinterpret_cast<uintptr_t>(Y);
   const bool vec = (K % 8 == 0) && (N % 8 == 0) && (al % 16 == 0);
-  if (decode_splitk_ok(M, K, N, vec) && decode_splitk_enabled()) {
-    if (M <= 16) return launch_decode<1>(X, W, Y, M, K, N, pv, proj, row_key, T, part, stream);
-    if (M <= 32) return launch_decode<2>(X, W, Y, M, K, N, pv, proj, row_key, T, part, stream);
-    if (M <= 48) return launch_decode<3>(X, W, Y, M, K, N, pv, proj, row_key, T, part, stream);
-    return launch_decode<4>(X, W, Y, M, K, N, pv, proj, row_key, T, part, stream);
+  const bool down_vec = reinterpret_cast<uintptr_t>(pv.down) % 16 == 0;  // the in-launch shrink's loads
+  if (decode_splitk_ok(M, K, N, vec) && (down_vec || !shrink) && decode_splitk_enabled()) {
+    // the per-row shrink shares the GEMM launch
+    const int ns = shrink ? M : 0;
+    if (M <= 16) return launch_decode<1>(X, W, Y, M, K, N, pv, proj, row_key, T, part, ns, stream);
+    if (M <= 32) return launch_decode<2>(X, W, Y, M, K, N, pv, proj, row_key, T, part, ns, stream);
+    if (M <= 48) return launch_decode<3>(X, W, Y, M, K, N, pv, proj, row_key, T, part, ns, stream);
+    return launch_decode<4>(X, W, Y, M, K, N, pv, proj, row_key, T, part, ns, stream);
+  }
+  if (shrink) {
+    hipError_t e = launch_shrink_rows(pv, proj, X, ws, M, T, stream);
+    if (e != hipSuccess) return e;
   }
   if (M > 64 && vec && K % BK == 0 && mid_enabled())
     return launch_mid_lora(X, W, Y, M, K, N, pv, proj, row_key, T, part, stream);

@@ -26,9 +26,9 @@ hipError_t launch_hbm_copy(void* dst, const void* src, size_t bytes, hipStream_t
   if (n16 == 0) return hipSuccess;
   size_t blocks = (n16 + 255) / 256;
   if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(hbm_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, static_cast<uint4*>(dst),
+  MLORA_LAUNCH("hbm_copy", hbm_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, static_cast<uint4*>(dst),
                      static_cast<const uint4*>(src), n16);
-  return hipGetLastError();
+  return launched();
 }
 
 }  // namespace mlora

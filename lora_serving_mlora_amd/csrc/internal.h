@@ -2,6 +2,7 @@
 // helpers for bf16 data and the host-side launchers of every kernel.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -67,9 +68,11 @@ hipError_t launch_base_gemm(const uint16_t* X, const uint16_t* W, uint16_t* Y, i
 
 // Y = X W^T plus the per-row expand of T (scaled t per original row).  The
 // decode (M <= 64) and medium (M <= 1024) forms split K over workgroups and
-// need gemm_lora_part_floats() of fp32 scratch for the partials.
+// need gemm_lora_part_floats() of fp32 scratch for the partials.  shrink:
+// compute T first (the per-row shrink), in the GEMM's own launch where the
+// decode form applies.
 hipError_t launch_gemm_lora(const PoolView& pv, int proj, const uint16_t* X, const uint16_t* W, const int32_t* ws,
-                            const float* T, float* part, uint16_t* Y, int M, hipStream_t stream);
+                            float* T, float* part, uint16_t* Y, int M, bool shrink, hipStream_t stream);
 size_t gemm_lora_part_floats(int M, int N, int K);
 
 hipError_t launch_shrink_rows(const PoolView& pv, int proj, const uint16_t* X, const int32_t* ws, int n, float* T,
@@ -85,5 +88,28 @@ hipError_t launch_fused(const PoolView& pv, int proj, const uint16_t* X, const i
                         int n, hipStream_t stream);
 
 hipError_t launch_hbm_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+// Launch timing: while armed, each kernel launch of the library takes the
+// next pair of events, which the runtime stamps with the kernel's own start
+// and end (hipExtLaunchKernel); `on` is false when nothing is armed.
+struct TimingSlot {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool on = false;
+};
+TimingSlot timing_next(const char* kernel);
+
+// Every kernel launch goes through this: a plain launch, or one that stamps
+// the armed timing events.
+#define MLORA_LAUNCH(name, kernel, grid, block, lds, stream, ...)                                       \
+  do {                                                                                                  \
+    const ::mlora::TimingSlot ts_ = ::mlora::timing_next(name);                                         \
+    if (ts_.on)                                                                                         \
+      hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, ts_.start, ts_.stop, 0u, __VA_ARGS__);    \
+    else                                                                                                \
+      hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);                                \
+  } while (0)
+
+// the error of the launch just made
+inline hipError_t launched() { return hipGetLastError(); }
 
 }  // namespace mlora

@@ -31,6 +31,7 @@
 // Rows with an invalid adapter id are set to NaN by the expand and fused
 // kernels (after the items).
 #include "internal.h"
+#include "row_kernels.h"
 
 namespace mlora {
 namespace {
@@ -294,77 +295,13 @@ __global__ __launch_bounds__(kFusedThreads) void fused_kernel(PoolView pv, int p
 }
 
 // ---------------------------------------------------------------------------
-// shrink_rows (decode): one 8-wave workgroup per row, rows read by index in
-// original order; T[k][q] = s_a * (Down_a x_k)[q].  Each lane holds the
-// partial dot products of its 8 din elements for a group of 16 ranks; a
-// 4-step reduce-scatter (xor 32, 16, 8, 4: 16 values -> 1 per lane) plus two
-// xor steps finishes each wave, then the 8 waves are summed in LDS in order.
+// shrink_rows (decode): one 8-wave workgroup per row (body in row_kernels.h)
 // ---------------------------------------------------------------------------
-constexpr int kRowWaves = 8;
-constexpr int kRowThreads = 64 * kRowWaves;
-
 template <bool VEC>
 __global__ __launch_bounds__(kRowThreads) void shrink_rows_kernel(PoolView pv, int proj, const uint16_t* __restrict__ X,
                                                                   const int32_t* __restrict__ row_key, int n,
                                                                   float* __restrict__ T) {
-  __shared__ float red[kRowWaves][G];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int k = blockIdx.x; k < n; k += gridDim.x) {
-    const int key = row_key[k];
-    if (key < 0) continue;  // base-only or invalid: no low-rank term
-    const int rank = pv.rank[key];
-    const float scale = pv.scale[key];
-    const int32_t* dpage = pv.down_page + ((size_t)key * pv.n_proj + proj) * pv.max_rank;
-    const uint16_t* xr = X + (size_t)k * pv.din;
-    // The page table is read without waiting for the rank: entries past the
-    // rank hold -1 and are replaced by the group's first page (their sums are
-    // never stored), and the first group runs before the rank is known.
-    int g0 = 0;
-    do {
-      int pg[G];
-#pragma unroll
-      for (int q = 0; q < G; ++q) pg[q] = dpage[min(g0 + q, pv.max_rank - 1)];
-#pragma unroll
-      for (int q = 1; q < G; ++q) pg[q] = pg[q] < 0 ? pg[0] : pg[q];
-      float v[G];
-#pragma unroll
-      for (int q = 0; q < G; ++q) v[q] = 0.f;
-      for (int kk = tid * 8; kk < pv.din; kk += kRowThreads * 8) {
-        float x[8], d[G][8];
-        load8<VEC>(xr, kk, pv.din, x);
-#pragma unroll
-        for (int q = 0; q < G; ++q) load8<VEC>(pv.down + (size_t)pg[q] * pv.din, kk, pv.din, d[q]);
-#pragma unroll
-        for (int q = 0; q < G; ++q)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[q] = fmaf(d[q][e], x[e], v[q]);
-      }
-      // reduce-scatter 16 -> 1: after the steps lane l holds index l >> 2
-#pragma unroll
-      for (int m = 32, len = G / 2; m >= 4; m >>= 1, len >>= 1) {
-        const bool upper = (lane & m) != 0;
-#pragma unroll
-        for (int i = 0; i < len; ++i) {
-          const float send = upper ? v[i] : v[i + len];
-          const float keep = upper ? v[i + len] : v[i];
-          v[i] = keep + __shfl_xor(send, m, 64);
-        }
-      }
-      float tot = v[0];
-      tot += __shfl_xor(tot, 2, 64);
-      tot += __shfl_xor(tot, 1, 64);
-      if ((lane & 3) == 0) red[wave][lane >> 2] = tot;
-      __syncthreads();
-      if (tid < G && g0 + tid < rank) {
-        float sum = red[0][tid];
-#pragma unroll
-        for (int w = 1; w < kRowWaves; ++w) sum += red[w][tid];
-        T[(size_t)k * pv.max_rank + g0 + tid] = scale * sum;
-      }
-      __syncthreads();
-      g0 += G;
-    } while (g0 < rank);
-  }
+  for (int k = blockIdx.x; k < n; k += gridDim.x) shrink_row_body<VEC>(pv, proj, X, row_key, k, T);
 }
 
 bool vec_ok(const PoolView& pv, const void* a, const void* b) {
@@ -387,10 +324,10 @@ hipError_t launch_shrink(const PoolView& pv, int proj, const uint16_t* X, const 
                          int n_chunks, int chunk_elems, hipStream_t stream) {
   const dim3 grid(item_grid(n), n_chunks), block(64);
   if (vec_ok(pv, X, X))
-    hipLaunchKernelGGL((shrink_kernel<true>), grid, block, 0, stream, pv, proj, X, ws, n, T, chunk_elems);
+    MLORA_LAUNCH("shrink", (shrink_kernel<true>), grid, block, 0, stream, pv, proj, X, ws, n, T, chunk_elems);
   else
-    hipLaunchKernelGGL((shrink_kernel<false>), grid, block, 0, stream, pv, proj, X, ws, n, T, chunk_elems);
-  return hipGetLastError();
+    MLORA_LAUNCH("shrink", (shrink_kernel<false>), grid, block, 0, stream, pv, proj, X, ws, n, T, chunk_elems);
+  return launched();
 }
 
 hipError_t launch_shrink_rows(const PoolView& pv, int proj, const uint16_t* X, const int32_t* ws, int n, float* T,
@@ -398,30 +335,30 @@ hipError_t launch_shrink_rows(const PoolView& pv, int proj, const uint16_t* X, c
   const dim3 grid(n < 1024 ? n : 1024), block(kRowThreads);
   const int32_t* row_key = ws + MLORA_SEG_ROWKEY(n);
   if (vec_ok(pv, X, X))
-    hipLaunchKernelGGL((shrink_rows_kernel<true>), grid, block, 0, stream, pv, proj, X, row_key, n, T);
+    MLORA_LAUNCH("shrink_rows", (shrink_rows_kernel<true>), grid, block, 0, stream, pv, proj, X, row_key, n, T);
   else
-    hipLaunchKernelGGL((shrink_rows_kernel<false>), grid, block, 0, stream, pv, proj, X, row_key, n, T);
-  return hipGetLastError();
+    MLORA_LAUNCH("shrink_rows", (shrink_rows_kernel<false>), grid, block, 0, stream, pv, proj, X, row_key, n, T);
+  return launched();
 }
 
 hipError_t launch_expand(const PoolView& pv, int proj, const float* T, int n_chunks, const int32_t* ws, uint16_t* Y,
                          int n, hipStream_t stream) {
   const dim3 grid(item_grid(n), (pv.dout + 511) / 512), block(64);
   if (vec_ok(pv, Y, Y))
-    hipLaunchKernelGGL((expand_kernel<true>), grid, block, 0, stream, pv, proj, T, n_chunks, ws, Y, n);
+    MLORA_LAUNCH("expand", (expand_kernel<true>), grid, block, 0, stream, pv, proj, T, n_chunks, ws, Y, n);
   else
-    hipLaunchKernelGGL((expand_kernel<false>), grid, block, 0, stream, pv, proj, T, n_chunks, ws, Y, n);
-  return hipGetLastError();
+    MLORA_LAUNCH("expand", (expand_kernel<false>), grid, block, 0, stream, pv, proj, T, n_chunks, ws, Y, n);
+  return launched();
 }
 
 hipError_t launch_fused(const PoolView& pv, int proj, const uint16_t* X, const int32_t* ws, uint16_t* Y, int n,
                         hipStream_t stream) {
   const dim3 grid(item_grid(n)), block(kFusedThreads);
   if (vec_ok(pv, X, Y))
-    hipLaunchKernelGGL((fused_kernel<true>), grid, block, 0, stream, pv, proj, X, ws, Y, n);
+    MLORA_LAUNCH("fused", (fused_kernel<true>), grid, block, 0, stream, pv, proj, X, ws, Y, n);
   else
-    hipLaunchKernelGGL((fused_kernel<false>), grid, block, 0, stream, pv, proj, X, ws, Y, n);
-  return hipGetLastError();
+    MLORA_LAUNCH("fused", (fused_kernel<false>), grid, block, 0, stream, pv, proj, X, ws, Y, n);
+  return launched();
 }
 
 }  // namespace mlora

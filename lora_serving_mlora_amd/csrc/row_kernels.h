@@ -1,0 +1,132 @@
+// Device code shared by the per-row kernels: the per-row shrink body and the
+// per-row low-rank term of 8 output columns.
+#pragma once
+
+#include "internal.h"
+
+namespace mlora {
+namespace {
+
+// The low-rank term of row r at columns [c0, c0+8): sum_q T[r][q] Up_a[c][q]
+// (T carries the scale).  Zero for a base-only row or a row past M, NaN for
+// a row with an invalid id.  Ranks past the adapter's rank read its last
+// column with weight 0, so each group of 8 page loads goes out at once.
+template <bool VEC>
+__device__ __forceinline__ void lora_delta8(const PoolView& pv, int proj, const int32_t* __restrict__ row_key,
+                                            const float* __restrict__ T, int r, int M, int c0, int N,
+                                            float (&acc8)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc8[e] = 0.f;
+  const int key = (r < M && c0 < N) ? row_key[r] : -1;
+  if (key >= 0) {
+    const int rank = pv.rank[key];
+    const int32_t* upage = pv.up_page + ((size_t)key * pv.n_proj + proj) * pv.max_rank;
+    const float* tr = T + (size_t)r * pv.max_rank;
+    // page indices and t are read without waiting for the rank: entries past
+    // it fall back to the group's first page and weigh zero (a select, so an
+    // unwritten t past the rank never reaches the sum)
+    int q0 = 0;
+    do {
+      float u8[8][8], tq[8];
+      int pg[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) pg[q] = upage[min(q0 + q, pv.max_rank - 1)];
+#pragma unroll
+      for (int q = 1; q < 8; ++q) pg[q] = pg[q] < 0 ? pg[0] : pg[q];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        load8<VEC>(pv.up + (size_t)pg[q] * pv.dout, c0, N, u8[q]);
+        const float tv = tr[min(q0 + q, pv.max_rank - 1)];
+        tq[q] = (q0 + q < rank) ? tv : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc8[e] = fmaf(tq[q], u8[q][e], acc8[e]);
+      q0 += 8;
+    } while (q0 < rank);
+  } else if (key == -2) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc8[e] = __uint_as_float(0x7fc00000u);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// shrink_rows (decode): one 8-wave workgroup per row, rows read by index in
+// original order; T[k][q] = s_a * (Down_a x_k)[q].  Each lane holds the
+// partial dot products of its 8 din elements for a group of 16 ranks; a
+// 4-step reduce-scatter (xor 32, 16, 8, 4: 16 values -> 1 per lane) plus two
+// xor steps finishes each wave, then the 8 waves are summed in LDS in order.
+// ---------------------------------------------------------------------------
+constexpr int kRowWaves = 8;
+constexpr int kRowThreads = 64 * kRowWaves;
+constexpr int kRowGroup = 16;  // ranks per reduction group
+
+// One row k: T[k][q] = s_a (Down_a x_k)[q]; called by all kRowThreads threads
+// of a workgroup (uniform control flow, block barriers inside).
+template <bool VEC>
+__device__ __forceinline__ void shrink_row_body(const PoolView& pv, int proj, const uint16_t* __restrict__ X,
+                                                const int32_t* __restrict__ row_key, int k, float* __restrict__ T) {
+  __shared__ float red[kRowWaves][kRowGroup];
+  constexpr int G = kRowGroup;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  {
+    const int key = row_key[k];
+    if (key < 0) return;  // base-only or invalid: no low-rank term
+    const int rank = pv.rank[key];
+    const float scale = pv.scale[key];
+    const int32_t* dpage = pv.down_page + ((size_t)key * pv.n_proj + proj) * pv.max_rank;
+    const uint16_t* xr = X + (size_t)k * pv.din;
+    // The page table is read without waiting for the rank: entries past the
+    // rank hold -1 and are replaced by the group's first page (their sums are
+    // never stored), and the first group runs before the rank is known.
+    int g0 = 0;
+    do {
+      int pg[G];
+#pragma unroll
+      for (int q = 0; q < G; ++q) pg[q] = dpage[min(g0 + q, pv.max_rank - 1)];
+#pragma unroll
+      for (int q = 1; q < G; ++q) pg[q] = pg[q] < 0 ? pg[0] : pg[q];
+      float v[G];
+#pragma unroll
+      for (int q = 0; q < G; ++q) v[q] = 0.f;
+      for (int kk = tid * 8; kk < pv.din; kk += kRowThreads * 8) {
+        float x[8], d[G][8];
+        load8<VEC>(xr, kk, pv.din, x);
+#pragma unroll
+        for (int q = 0; q < G; ++q) load8<VEC>(pv.down + (size_t)pg[q] * pv.din, kk, pv.din, d[q]);
+#pragma unroll
+        for (int q = 0; q < G; ++q)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[q] = fmaf(d[q][e], x[e], v[q]);
+      }
+      // reduce-scatter 16 -> 1: after the steps lane l holds index l >> 2
+#pragma unroll
+      for (int m = 32, len = G / 2; m >= 4; m >>= 1, len >>= 1) {
+        const bool upper = (lane & m) != 0;
+#pragma unroll
+        for (int i = 0; i < len; ++i) {
+          const float send = upper ? v[i] : v[i + len];
+          const float keep = upper ? v[i + len] : v[i];
+          v[i] = keep + __shfl_xor(send, m, 64);
+        }
+      }
+      float tot = v[0];
+      tot += __shfl_xor(tot, 2, 64);
+      tot += __shfl_xor(tot, 1, 64);
+      if ((lane & 3) == 0) red[wave][lane >> 2] = tot;
+      __syncthreads();
+      if (tid < G && g0 + tid < rank) {
+        float sum = red[0][tid];
+#pragma unroll
+        for (int w = 1; w < kRowWaves; ++w) sum += red[w][tid];
+        T[(size_t)k * pv.max_rank + g0 + tid] = scale * sum;
+      }
+      __syncthreads();
+      g0 += G;
+    } while (g0 < rank);
+  }
+}
+
+}  // namespace
+}  // namespace mlora

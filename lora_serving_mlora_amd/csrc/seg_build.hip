@@ -337,9 +337,9 @@ hipError_t launch_nt(const int32_t* row_adapter, int n, const int32_t* pool_rank
     }
   }
   const int passes = (max_adapters + 1 < 256) ? 1 : 2;
-  hipLaunchKernelGGL(seg_build_kernel<NT>, dim3(1), dim3(NT), lds, stream, row_adapter, n, pool_rank, max_adapters,
+  MLORA_LAUNCH("seg_build", seg_build_kernel<NT>, dim3(1), dim3(NT), lds, stream, row_adapter, n, pool_rank, max_adapters,
                      passes, cap, ws);
-  return hipGetLastError();
+  return launched();
 }
 
 }  // namespace
@@ -347,8 +347,8 @@ hipError_t launch_nt(const int32_t* row_adapter, int n, const int32_t* pool_rank
 hipError_t launch_seg_build(const int32_t* row_adapter, int n, const int32_t* pool_rank, int max_adapters,
                             int32_t* ws, hipStream_t stream) {
   if (n <= 64 && max_adapters <= 65533) {
-    hipLaunchKernelGGL(seg_build_small, dim3(1), dim3(64), 0, stream, row_adapter, n, pool_rank, max_adapters, ws);
-    return hipGetLastError();
+    MLORA_LAUNCH("seg_build", seg_build_small, dim3(1), dim3(64), 0, stream, row_adapter, n, pool_rank, max_adapters, ws);
+    return launched();
   }
   if (n <= 1024) return launch_nt<256>(row_adapter, n, pool_rank, max_adapters, ws, stream);
   return launch_nt<1024>(row_adapter, n, pool_rank, max_adapters, ws, stream);

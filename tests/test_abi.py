@@ -57,3 +57,10 @@ def test_host_only_calls():
     assert L.mlora_base_gemm(None, None, None, 0, 4, 4, None) == M.OK     # n = 0 is a no-op
     assert L.mlora_base_gemm(None, None, None, 1, 0, 4, None) == M.EINVAL
     assert L.mlora_hbm_copy(None, None, 16, None) == M.EINVAL
+    # launch timing: argument checks and an empty read touch no device
+    assert L.mlora_timing_arm(0) == M.EINVAL
+    assert L.mlora_timing_arm(2049) == M.EINVAL
+    n_marked = ctypes.c_int32(-1)
+    ms = (ctypes.c_float * 4)()
+    assert L.mlora_timing_read(ms, 4, ctypes.byref(n_marked)) == M.OK and n_marked.value == 0
+    assert L.mlora_timing_name(0) is None

@@ -246,6 +246,40 @@ def test_gemm_lora_with_synthetic_t(M, n, din, dout):
     assert_close(dev_to_f64(Y), ref, "gemm_lora")
 
 
+@pytest.mark.parametrize("n,din,dout", [(1, 2048, 1000), (17, 2048, 1000), (33, 4096, 136), (48, 4096, 4104),
+                                        (64, 4096, 4096), (65, 4096, 4096)])
+def test_apply_rows_decode_forms(M, n, din, dout):
+    """The per-row variant end to end where the per-row shrink shares the
+    split-K GEMM launch (K a multiple of 2048, up to 64 rows; 65 rows takes
+    the separate shrink), mixed ranks up to 64 and base-only rows."""
+    w = small_workload(71 + n, din, dout, n, {0: 16, 1: 3, 2: 64}, p_none=0.2)
+    check_apply(M, w, variants=("rows",))
+
+
+def test_launch_timing_marks_every_launch(M):
+    """The timing hook names and times each kernel launch of an apply call
+    (two for the decode form: GEMM with the shrink, then the finish pass)."""
+    torch = torch_cuda()
+    w = synth.decode_3_adapters()
+    pool = make_pool(M, w)
+    Xd, W0d = to_dev_bf16(w.x_bits()), to_dev_bf16(w.w0_bits())
+    seg = M.build_segments(pool, ids_dev(w.row_adapter))
+    work = M.new_work(pool, w.n)
+    Y = torch.empty((w.n, w.dout), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    say("launch timing")
+    M.timing_arm(8)
+    M.build_segments(pool, ids_dev(w.row_adapter), seg)
+    M.apply(pool, 0, Xd, W0d, seg, Y=Y, work=work, variant="rows")
+    marks = M.timing_read()
+    assert [m[0] for m in marks] == ["seg_build", "gemm_decode+shrink_rows", "finish_part"], marks
+    assert all(0.0 < ms < 100.0 for _, ms in marks), marks
+    # disarmed after the read: further launches are not marked
+    M.apply(pool, 0, Xd, W0d, seg, Y=Y, work=work, variant="rows")
+    torch.cuda.synchronize()
+    assert [m[0] for m in M.timing_read()] == [m[0] for m in marks]
+
+
 @pytest.mark.parametrize("variant", ["split", "fused", "rows"])
 def test_base_only_rows_bitwise_and_deterministic(M, variant):
     torch = torch_cuda()
