@@ -565,15 +565,18 @@ struct RowsWork {
   float* T;
   float* part;
 };
+// T region: room for the decode form's K-quarter partials of T as well
+size_t rows_t_bytes(const mlora_pool* p, int n) {
+  return align256((size_t)mlora::kRowsTParts * n * p->d.max_rank * sizeof(float));
+}
 size_t rows_work_bytes(const mlora_pool* p, int n) {
-  return align256((size_t)n * p->d.max_rank * sizeof(float)) +
-         align256(mlora::gemm_lora_part_floats(n, p->d.dout, p->d.din) * sizeof(float));
+  return rows_t_bytes(p, n) + align256(mlora::gemm_lora_part_floats(n, p->d.dout, p->d.din) * sizeof(float));
 }
 RowsWork rows_work(const mlora_pool* p, int n, void* work) {
   char* w = static_cast<char*>(work);
   RowsWork r;
   r.T = reinterpret_cast<float*>(w);
-  r.part = reinterpret_cast<float*>(w + align256((size_t)n * p->d.max_rank * sizeof(float)));
+  r.part = reinterpret_cast<float*>(w + rows_t_bytes(p, n));
   return r;
 }
 mlora_status check_rows_work(const mlora_pool* p, int n, const void* work, size_t work_bytes) {

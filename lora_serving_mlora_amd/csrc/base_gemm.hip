@@ -703,14 +703,9 @@ template <int MB>
 __global__ __launch_bounds__(64 * kDecWaves) void gemm_decode(const uint16_t* __restrict__ X,
                                                              const uint16_t* __restrict__ W, int M, int K, int N,
                                                              PoolView pv, int proj,
-                                                             const int32_t* __restrict__ row_key, float* __restrict__ T,
-                                                             float* __restrict__ part, int n_shrink) {
-  // the first n_shrink workgroups are the per-row shrink of the batch
-  // (independent work that shares the launch)
-  if ((int)blockIdx.x < n_shrink) {
-    shrink_row_body<true>(pv, proj, X, row_key, blockIdx.x, T);
-    return;
-  }
+                                                             const int32_t* __restrict__ row_key,
+                                                             float* __restrict__ Tp, float* __restrict__ part,
+                                                             int shrink) {
   extern __shared__ __attribute__((aligned(16))) uint16_t dec_lds[];
   const int Kq = K / kDecSplit;
   uint16_t* xs = dec_lds;                                               // [M][Kq]
@@ -719,12 +714,23 @@ __global__ __launch_bounds__(64 * kDecWaves) void gemm_decode(const uint16_t* __
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ncb = (N + kDecCols - 1) / kDecCols;
-  const int b = blockIdx.x - n_shrink;
-  const int cb = b % ncb, kq = b / ncb;
+  const int cb = blockIdx.x % ncb, kq = blockIdx.x / ncb;
   const int n0 = cb * kDecCols;
   const int cg = wave & 3, kh = wave >> 2;
-  const int steps = Kq / 64;  // 32-wide steps in a wave's half of the quarter (<= 16)
+  const int nseg = Kq / 128;  // 64-element K segments in a wave's half of the quarter (<= 8)
 
+  // W0 first, all 16 loads of the wave at once.  Instruction 2s+h reads rows
+  // 8h + (l & 7) of the column group, 16-byte chunk l >> 3 of K segment s:
+  // 128 contiguous bytes per row (64-byte row pieces cost 30 % more HBM time).
+  const size_t kbase = (size_t)kq * Kq + kh * (Kq / 2) + (lane >> 3) * 8;
+  const uint16_t* w0p = W + (size_t)min(n0 + 16 * cg + (lane & 7), N - 1) * K + kbase;
+  const uint16_t* w1p = W + (size_t)min(n0 + 16 * cg + 8 + (lane & 7), N - 1) * K + kbase;
+  uint4 wv[16];
+#pragma unroll
+  for (int sg = 0; sg < 8; ++sg) {
+    wv[2 * sg] = *reinterpret_cast<const uint4*>(w0p + min(sg, nseg - 1) * 64);
+    wv[2 * sg + 1] = *reinterpret_cast<const uint4*>(w1p + min(sg, nseg - 1) * 64);
+  }
   // X slice -> LDS: instruction (row r, 1 KiB block b); lane l fetches
   // logical chunk l ^ (r & 15) of the block into physical chunk l
   const __amdgpu_buffer_rsrc_t rx =
@@ -735,12 +741,30 @@ __global__ __launch_bounds__(64 * kDecWaves) void gemm_decode(const uint16_t* __
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, xs + (size_t)r * Kq + bl * 512, 16, (lane ^ (r & 15)) * 16,
                                              (r * K + kq * Kq + bl * 512) * 2, 0, 0);
   }
-  // all of this wave's W0 fragments at once (column group cg, half kh)
-  const uint16_t* wrow =
-      W + (size_t)min(n0 + 16 * cg + (lane & 15), N - 1) * K + kq * Kq + kh * (Kq / 2) + (lane >> 4) * 8;
-  uint4 wv[16];
+  // The per-row shrink rides along: this workgroup computes the quarter-kq
+  // partial of T for rows cb, cb + ncb, ... from the X slice it already
+  // holds.  Key, rank and pages are uniform (scalar loads, which do not wait
+  // for the vector loads in flight); the first 16 ranks of the first row
+  // are fetched now: each wave takes ranks wave and wave + 8, each lane
+  // Kq / 64 consecutive elements (cpl 16-byte chunks).
+  const int cpl = Kq / 512;  // 1 or 2
+  int key0 = -1, rank0 = 0;
+  uint4 dn[2][2];
+  if (shrink && cb < M) {
+    key0 = __builtin_amdgcn_readfirstlane(row_key[cb]);
+    if (key0 >= 0) {
+      rank0 = __builtin_amdgcn_readfirstlane(pv.rank[key0]);
+      const int32_t* dpage = pv.down_page + ((size_t)key0 * pv.n_proj + proj) * pv.max_rank;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) wv[j] = *reinterpret_cast<const uint4*>(wrow + (size_t)min(j, steps - 1) * 32);
+      for (int i = 0; i < 2; ++i) {
+        int pg = dpage[min(wave + 8 * i, pv.max_rank - 1)];
+        pg = pg < 0 ? dpage[0] : pg;
+        const uint16_t* dr = pv.down + (size_t)pg * pv.din + (size_t)kq * Kq + lane * cpl * 8;
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) dn[i][cc] = *reinterpret_cast<const uint4*>(dr + min(cc, cpl - 1) * 8);
+      }
+    }
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();  // X slice in LDS
 
@@ -748,18 +772,99 @@ __global__ __launch_bounds__(64 * kDecWaves) void gemm_decode(const uint16_t* __
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    if (j < steps) {
-      const int c = kh * (Kq / 16) + j * 4 + (lane >> 4);  // logical 16-byte chunk in the slice row
+  for (int sg = 0; sg < 8; ++sg) {
+    if (sg < nseg) {
+      // two MFMA B fragments from the pair of loads of segment sg, with one
+      // DPP move per dword: f0 = K chunks 0,2,4,6 of the segment (lane group
+      // g = l >> 4 takes chunk 2g), f1 = chunks 1,3,5,7.  Column n < 8 is
+      // row n (first load), n >= 8 row n (second load), as MFMA wants.
+      const uint4 A = wv[2 * sg], B = wv[2 * sg + 1];
+      uint4 f0, f1;
+      f0.x = __builtin_amdgcn_update_dpp((int)A.x, (int)B.x, 0x118, 0xf, 0xc, false);  // row_shr:8 into lanes 8-15
+      f0.y = __builtin_amdgcn_update_dpp((int)A.y, (int)B.y, 0x118, 0xf, 0xc, false);
+      f0.z = __builtin_amdgcn_update_dpp((int)A.z, (int)B.z, 0x118, 0xf, 0xc, false);
+      f0.w = __builtin_amdgcn_update_dpp((int)A.w, (int)B.w, 0x118, 0xf, 0xc, false);
+      f1.x = __builtin_amdgcn_update_dpp((int)B.x, (int)A.x, 0x108, 0xf, 0x3, false);  // row_shl:8 into lanes 0-7
+      f1.y = __builtin_amdgcn_update_dpp((int)B.y, (int)A.y, 0x108, 0xf, 0x3, false);
+      f1.z = __builtin_amdgcn_update_dpp((int)B.z, (int)A.z, 0x108, 0xf, 0x3, false);
+      f1.w = __builtin_amdgcn_update_dpp((int)B.w, (int)A.w, 0x108, 0xf, 0x3, false);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int r = min(mb * 16 + (lane & 15), M - 1);
-        const uint4 a =
-            *reinterpret_cast<const uint4*>(xs + (size_t)r * Kq + (c >> 6) * 512 + (((c & 63) ^ (r & 15)) << 3));
-        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(wv[j]), acc[mb], 0, 0, 0);
+      for (int odd = 0; odd < 2; ++odd) {
+        const int c = kh * (Kq / 16) + sg * 8 + 2 * (lane >> 4) + odd;  // logical 16-byte chunk in the slice row
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int r = min(mb * 16 + (lane & 15), M - 1);
+          const uint4 a =
+              *reinterpret_cast<const uint4*>(xs + (size_t)r * Kq + (c >> 6) * 512 + (((c & 63) ^ (r & 15)) << 3));
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(odd ? f1 : f0), acc[mb], 0, 0, 0);
+        }
       }
     }
   }
+
+  if (shrink) {
+    for (int r = cb; r < M; r += ncb) {
+      const bool first = r == cb;
+      const int key = first ? key0 : __builtin_amdgcn_readfirstlane(row_key[r]);
+      if (key < 0) continue;
+      const int rank = first ? rank0 : __builtin_amdgcn_readfirstlane(pv.rank[key]);
+      const int32_t* dpage = pv.down_page + ((size_t)key * pv.n_proj + proj) * pv.max_rank;
+      uint4 d[2][2];
+      // Down chunks of ranks q0 + wave and q0 + wave + 8 (the first group of
+      // the first row came in with the W0 loads)
+      auto fetch = [&](int q0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          int pg = dpage[min(q0 + wave + 8 * i, pv.max_rank - 1)];
+          pg = pg < 0 ? dpage[0] : pg;
+          const uint16_t* dr = pv.down + (size_t)pg * pv.din + (size_t)kq * Kq + lane * cpl * 8;
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) d[i][cc] = *reinterpret_cast<const uint4*>(dr + min(cc, cpl - 1) * 8);
+        }
+      };
+      if (first) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) d[i][cc] = dn[i][cc];
+      } else {
+        fetch(0);
+      }
+      for (int q0 = 0; q0 < rank; q0 += 16) {
+        float v[2] = {0.f, 0.f};
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          if (cc < cpl) {
+            const int c = lane * cpl + cc;  // logical chunk of row r's slice
+            const uint4 xa = *reinterpret_cast<const uint4*>(xs + (size_t)r * Kq + (c >> 6) * 512 +
+                                                             (((c & 63) ^ (r & 15)) << 3));
+            const uint32_t xw[4] = {xa.x, xa.y, xa.z, xa.w};
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              const uint32_t dw[4] = {d[i][cc].x, d[i][cc].y, d[i][cc].z, d[i][cc].w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                v[i] = fmaf(lo_bf(dw[e]), lo_bf(xw[e]), v[i]);
+                v[i] = fmaf(hi_bf(dw[e]), hi_bf(xw[e]), v[i]);
+              }
+            }
+          }
+        }
+        if (q0 + 16 < rank) fetch(q0 + 16);
+        // lanes 0-31 finish rank q0 + wave, lanes 32-63 rank q0 + wave + 8
+        const bool up = (lane & 32) != 0;
+        float t = (up ? v[1] : v[0]) + __shfl_xor(up ? v[0] : v[1], 32, 64);
+        t += __shfl_xor(t, 16, 64);
+        t += __shfl_xor(t, 8, 64);
+        t += __shfl_xor(t, 4, 64);
+        t += __shfl_xor(t, 2, 64);
+        t += __shfl_xor(t, 1, 64);
+        const int q = q0 + wave + (up ? 8 : 0);
+        if ((lane & 31) == 0 && q < rank) Tp[((size_t)kq * M + r) * pv.max_rank + q] = t;
+      }
+    }
+  }
+
   if (kh == 1) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) red[(cg * MB + mb) * 64 + lane] = acc[mb];
@@ -786,7 +891,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void gemm_decode(const uint16_t* __
 // coalesced 16-byte pieces.
 constexpr int kFinishThreads = 64;  // one wave per workgroup: the decode grid spreads over every CU
 
-template <bool LORA>
+template <bool LORA, int TP>
 __global__ __launch_bounds__(kFinishThreads) void finish_part(const float* __restrict__ part, int S,
                                                               uint16_t* __restrict__ Y, int M, int N, PoolView pv,
                                                               int proj, const int32_t* __restrict__ row_key,
@@ -808,7 +913,7 @@ __global__ __launch_bounds__(kFinishThreads) void finish_part(const float* __res
   }
   float y[8];
   if (LORA) {
-    lora_delta8<true>(pv, proj, row_key, T, r, M, c0, N, y);
+    lora_delta8<true, TP>(pv, proj, row_key, T, r, M, c0, N, y);
   } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = 0.f;
@@ -823,12 +928,13 @@ __global__ __launch_bounds__(kFinishThreads) void finish_part(const float* __res
 
 size_t decode_lds_bytes(int M, int K, int MB) { return (size_t)M * (K / kDecSplit) * 2 + (size_t)4 * MB * 64 * 16; }
 
-// n_shrink > 0: the per-row shrink of the batch runs as extra workgroups of
-// the same launch (T must not be read by the GEMM itself: the finish pass
-// adds the low-rank term).
+// shrink: the workgroups also compute T as K-quarter partials (kRowsTParts
+// slices of [M][max_rank] in T), which the finish pass sums and scales;
+// otherwise T holds the finished t (scale folded).
 template <int MB>
 hipError_t launch_decode(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N, const PoolView& pv,
-                         int proj, const int32_t* row_key, float* T, float* part, int n_shrink, hipStream_t st) {
+                         int proj, const int32_t* row_key, float* T, float* part, bool shrink, hipStream_t st) {
+  static_assert(kDecSplit == kRowsTParts, "T partial slices are the K quarters");
   const size_t lds = decode_lds_bytes(M, K, MB);
   static size_t attr = 0;
   if (lds > attr) {
@@ -838,13 +944,17 @@ hipError_t launch_decode(const uint16_t* X, const uint16_t* W, uint16_t* Y, int 
     attr = lds;
   }
   const int ncb = (N + kDecCols - 1) / kDecCols;
-  MLORA_LAUNCH(n_shrink ? "gemm_decode+shrink_rows" : "gemm_decode", gemm_decode<MB>, dim3(n_shrink + ncb * kDecSplit), dim3(64 * kDecWaves), lds, st, X, W, M, K, N,
-                     pv, proj, row_key, T, part, n_shrink);
+  MLORA_LAUNCH(shrink ? "gemm_decode+shrink_rows" : "gemm_decode", gemm_decode<MB>, dim3(ncb * kDecSplit),
+               dim3(64 * kDecWaves), lds, st, X, W, M, K, N, pv, proj, row_key, T, part, shrink ? 1 : 0);
   hipError_t e = launched();
   if (e != hipSuccess) return e;
   const int threads = M * (N / 8);
-  MLORA_LAUNCH("finish_part", finish_part<true>, dim3((threads + kFinishThreads - 1) / kFinishThreads), dim3(kFinishThreads),
-                     0, st, part, kDecSplit, Y, M, N, pv, proj, row_key, T);
+  if (shrink)
+    MLORA_LAUNCH("finish_part", (finish_part<true, kRowsTParts>), dim3((threads + kFinishThreads - 1) / kFinishThreads),
+                 dim3(kFinishThreads), 0, st, part, kDecSplit, Y, M, N, pv, proj, row_key, T);
+  else
+    MLORA_LAUNCH("finish_part", (finish_part<true, 1>), dim3((threads + kFinishThreads - 1) / kFinishThreads),
+                 dim3(kFinishThreads), 0, st, part, kDecSplit, Y, M, N, pv, proj, row_key, T);
   return launched();
 }
 
@@ -866,8 +976,8 @@ hipError_t launch_mid_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, in
   hipError_t e = launched();
   if (e != hipSuccess) return e;
   const int threads = M * (N / 8);
-  MLORA_LAUNCH("finish_part", finish_part<true>, dim3((threads + kFinishThreads - 1) / kFinishThreads), dim3(kFinishThreads),
-                     0, st, part, S, Y, M, N, pv, proj, row_key, T);
+  MLORA_LAUNCH("finish_part", (finish_part<true, 1>), dim3((threads + kFinishThreads - 1) / kFinishThreads),
+               dim3(kFinishThreads), 0, st, part, S, Y, M, N, pv, proj, row_key, T);
   return launched();
 }
 
@@ -909,11 +1019,10 @@ hipError_t launch_gemm_lora(const PoolView& pv, int proj, const uint16_t* X, con
   const bool down_vec = reinterpret_cast<uintptr_t>(pv.down) % 16 == 0;  // the in-launch shrink's loads
   if (decode_splitk_ok(M, K, N, vec) && (down_vec || !shrink) && decode_splitk_enabled()) {
     // the per-row shrink shares the GEMM launch
-    const int ns = shrink ? M : 0;
-    if (M <= 16) return launch_decode<1>(X, W, Y, M, K, N, pv, proj, row_key, T, part, ns, stream);
-    if (M <= 32) return launch_decode<2>(X, W, Y, M, K, N, pv, proj, row_key, T, part, ns, stream);
-    if (M <= 48) return launch_decode<3>(X, W, Y, M, K, N, pv, proj, row_key, T, part, ns, stream);
-    return launch_decode<4>(X, W, Y, M, K, N, pv, proj, row_key, T, part, ns, stream);
+    if (M <= 16) return launch_decode<1>(X, W, Y, M, K, N, pv, proj, row_key, T, part, shrink, stream);
+    if (M <= 32) return launch_decode<2>(X, W, Y, M, K, N, pv, proj, row_key, T, part, shrink, stream);
+    if (M <= 48) return launch_decode<3>(X, W, Y, M, K, N, pv, proj, row_key, T, part, shrink, stream);
+    return launch_decode<4>(X, W, Y, M, K, N, pv, proj, row_key, T, part, shrink, stream);
   }
   if (shrink) {
     hipError_t e = launch_shrink_rows(pv, proj, X, ws, M, T, stream);

@@ -73,6 +73,9 @@ hipError_t launch_base_gemm(const uint16_t* X, const uint16_t* W, uint16_t* Y, i
 // decode form applies.
 hipError_t launch_gemm_lora(const PoolView& pv, int proj, const uint16_t* X, const uint16_t* W, const int32_t* ws,
                             float* T, float* part, uint16_t* Y, int M, bool shrink, hipStream_t stream);
+// T's region in the per-row work holds up to this many [M][max_rank] slices
+// (the decode form computes T as K-quarter partials inside its GEMM launch)
+constexpr int kRowsTParts = 4;
 size_t gemm_lora_part_floats(int M, int N, int K);
 
 hipError_t launch_shrink_rows(const PoolView& pv, int proj, const uint16_t* X, const int32_t* ws, int n, float* T,

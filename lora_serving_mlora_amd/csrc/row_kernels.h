@@ -7,11 +7,14 @@
 namespace mlora {
 namespace {
 
-// The low-rank term of row r at columns [c0, c0+8): sum_q T[r][q] Up_a[c][q]
-// (T carries the scale).  Zero for a base-only row or a row past M, NaN for
-// a row with an invalid id.  Ranks past the adapter's rank read its last
-// column with weight 0, so each group of 8 page loads goes out at once.
-template <bool VEC>
+// The low-rank term of row r at columns [c0, c0+8): sum_q t_q Up_a[c][q].
+// TP == 1: T [M][max_rank] holds t with the scale folded in; TP > 1: T
+// holds TP partial slices [TP][M][max_rank] (K ranges of the shrink),
+// summed here in slice order and then scaled.  Zero for a
+// base-only row or a row past M, NaN for a row with an invalid id.  Ranks
+// past the adapter's rank read its last column with weight 0, so each group
+// of 8 page loads goes out at once.
+template <bool VEC, int TP = 1>
 __device__ __forceinline__ void lora_delta8(const PoolView& pv, int proj, const int32_t* __restrict__ row_key,
                                             const float* __restrict__ T, int r, int M, int c0, int N,
                                             float (&acc8)[8]) {
@@ -20,25 +23,47 @@ __device__ __forceinline__ void lora_delta8(const PoolView& pv, int proj, const 
   const int key = (r < M && c0 < N) ? row_key[r] : -1;
   if (key >= 0) {
     const int rank = pv.rank[key];
+    const float tscale = TP > 1 ? pv.scale[key] : 1.f;
     const int32_t* upage = pv.up_page + ((size_t)key * pv.n_proj + proj) * pv.max_rank;
     const float* tr = T + (size_t)r * pv.max_rank;
+    const size_t tstride = (size_t)M * pv.max_rank;
+    // t rows of 8 ranks as two 16-byte loads per slice when they are aligned
+    const bool tvec = (pv.max_rank & 7) == 0;
     // page indices and t are read without waiting for the rank: entries past
     // it fall back to the group's first page and weigh zero (a select, so an
     // unwritten t past the rank never reaches the sum)
     int q0 = 0;
     do {
-      float u8[8][8], tq[8];
+      float u8[8][8], tv[8], tq[8];
       int pg[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) pg[q] = upage[min(q0 + q, pv.max_rank - 1)];
 #pragma unroll
       for (int q = 1; q < 8; ++q) pg[q] = pg[q] < 0 ? pg[0] : pg[q];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        load8<VEC>(pv.up + (size_t)pg[q] * pv.dout, c0, N, u8[q]);
-        const float tv = tr[min(q0 + q, pv.max_rank - 1)];
-        tq[q] = (q0 + q < rank) ? tv : 0.f;
+      for (int q = 0; q < 8; ++q) load8<VEC>(pv.up + (size_t)pg[q] * pv.dout, c0, N, u8[q]);
+      if (tvec) {
+        // q0 + 7 < max_rank here: q0 < rank <= max_rank and both multiples of 8
+#pragma unroll
+        for (int q = 0; q < 8; ++q) tv[q] = 0.f;
+#pragma unroll
+        for (int p = 0; p < TP; ++p) {
+          const float4 a = *reinterpret_cast<const float4*>(tr + p * tstride + q0);
+          const float4 b = *reinterpret_cast<const float4*>(tr + p * tstride + q0 + 4);
+          tv[0] += a.x; tv[1] += a.y; tv[2] += a.z; tv[3] += a.w;
+          tv[4] += b.x; tv[5] += b.y; tv[6] += b.z; tv[7] += b.w;
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int qq = min(q0 + q, pv.max_rank - 1);
+          tv[q] = tr[qq];
+#pragma unroll
+          for (int p = 1; p < TP; ++p) tv[q] += tr[p * tstride + qq];
+        }
       }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) tq[q] = (q0 + q < rank) ? tscale * tv[q] : 0.f;
 #pragma unroll
       for (int q = 0; q < 8; ++q)
 #pragma unroll
