@@ -74,6 +74,7 @@ typedef enum mlora_variant {
 #define MLORA_MAX_RANK 128          /* largest adapter rank a pool may hold                   */
 #define MLORA_MAX_ADAPTERS 65533    /* adapter ids are 0 .. max_adapters-1                    */
 #define MLORA_ITEM_ROWS 4           /* rows per low-rank work item                            */
+#define MLORA_TILE_ROWS 64          /* rows per segment tile (matrix-core shrink of big groups) */
 
 /* Segment status bits (header word MLORA_SEG_STATUS). */
 #define MLORA_SEG_BAD_ID 1          /* an id < -1 or >= max_adapters appeared                 */
@@ -175,6 +176,11 @@ mlora_status mlora_pool_free_pages(const mlora_pool* pool, int64_t* free_down, i
  *   row_key[n]         at MLORA_SEG_ROWKEY(n): per original row, the
  *                      adapter id if resident, -1 for a base-only row, -2
  *                      for an invalid id (what the per-row kernels read).
+ *   tiles[2*n]         at MLORA_SEG_TILES(n): (segment, first sorted
+ *                      position) of every MLORA_TILE_ROWS-row tile of every
+ *                      segment, in segment order: tile t of segment s
+ *                      starts at seg_off[s] + t * MLORA_TILE_ROWS; header
+ *                      word MLORA_SEG_NTILES holds the count.
  * ------------------------------------------------------------------------- */
 #define MLORA_SEG_NSEG 0
 #define MLORA_SEG_NACT 1
@@ -184,6 +190,7 @@ mlora_status mlora_pool_free_pages(const mlora_pool* pool, int64_t* free_down, i
 #define MLORA_SEG_NITEMS 5
 #define MLORA_SEG_NROWS 6
 #define MLORA_SEG_MAXAD 7
+#define MLORA_SEG_NTILES 8
 #define MLORA_SEG_HEADER 16
 #define MLORA_SEG_PERM(n) (MLORA_SEG_HEADER)
 #define MLORA_SEG_INV(n) (MLORA_SEG_HEADER + (n))
@@ -192,6 +199,7 @@ mlora_status mlora_pool_free_pages(const mlora_pool* pool, int64_t* free_down, i
 #define MLORA_SEG_ITEMS(n) ((MLORA_SEG_HEADER + 4 * (n) + 2) & ~1)
 #define MLORA_SEG_MAX_ITEMS(n) ((n) + ((n) + MLORA_ITEM_ROWS - 1) / MLORA_ITEM_ROWS + 1)
 #define MLORA_SEG_ROWKEY(n) (MLORA_SEG_ITEMS(n) + 2 * MLORA_SEG_MAX_ITEMS(n))
+#define MLORA_SEG_TILES(n) (MLORA_SEG_ROWKEY(n) + (n))
 
 size_t mlora_segments_bytes(int32_t n_rows);
 

@@ -23,7 +23,7 @@ import numpy as np
 __all__ = [
     "MloraError", "lib", "Pool", "build_segments", "segments_header", "read_segments",
     "base_gemm", "shrink", "shrink_max_chunks", "expand", "fused", "shrink_rows", "gemm_lora", "new_work", "rows_t", "apply", "plan", "work_bytes",
-    "hbm_copy", "timing_arm", "timing_read", "VARIANTS", "ITEM_ROWS", "MAX_ROWS", "MAX_RANK", "SEG", "EXPORTS", "LIB_PATH",
+    "hbm_copy", "timing_arm", "timing_read", "VARIANTS", "ITEM_ROWS", "TILE_ROWS", "MAX_ROWS", "MAX_RANK", "SEG", "EXPORTS", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmlora.so")
@@ -31,9 +31,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmlora.so
 OK, EINVAL, ENOSPC, EEXIST, ENOENT, EHIP = range(6)
 VARIANTS = {"auto": 0, "split": 1, "fused": 2, "rows": 3}
 ITEM_ROWS = 4
+TILE_ROWS = 64
 MAX_ROWS = 16384
 MAX_RANK = 128
-SEG = dict(nseg=0, n_act=1, n_none=2, n_bad=3, status=4, n_items=5, n_rows=6, max_adapters=7)
+SEG = dict(nseg=0, n_act=1, n_none=2, n_bad=3, status=4, n_items=5, n_rows=6, max_adapters=7, n_tiles=8)
 SEG_HEADER = 16
 
 _c_void_p, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -254,6 +255,8 @@ def read_segments(seg_ws, n: int) -> dict:
     max_items = n + (n + ITEM_ROWS - 1) // ITEM_ROWS + 1
     rk0 = items0 + 2 * max_items
     out["row_key"] = w[rk0:rk0 + n].copy()
+    tl0 = rk0 + n
+    out["tiles"] = w[tl0:tl0 + 2 * hdr["n_tiles"]].reshape(-1, 2).copy()
     out.update(perm=w[perm0:perm0 + n].copy(), inv=w[inv0:inv0 + n].copy(),
                seg_adapter=w[ad0:ad0 + nseg].copy(), seg_off=w[off0:off0 + nseg + 1].copy(),
                items=w[items0:items0 + 2 * hdr["n_items"]].reshape(-1, 2).copy())

@@ -468,7 +468,7 @@ mlora_status mlora_pool_free_pages(const mlora_pool* p, int64_t* free_down, int6
 
 size_t mlora_segments_bytes(int32_t n) {
   if (n < 0) return 0;
-  return align256(((size_t)MLORA_SEG_ROWKEY(n) + (size_t)n) * sizeof(int32_t));
+  return align256(((size_t)MLORA_SEG_TILES(n) + 2 * (size_t)n) * sizeof(int32_t));
 }
 
 mlora_status mlora_build_segments(const mlora_pool* p, const int32_t* row_adapter, int32_t n, void* seg_ws,
@@ -619,9 +619,17 @@ mlora_status mlora_gemm_lora(const mlora_pool* p, int32_t proj, const uint16_t* 
 namespace {
 // din slices for the split variant: enough waves to spread a small batch
 // over the chip, never more than kMaxSplitChunks
-int split_chunks(int din, int n) {
-  const int items = MLORA_SEG_MAX_ITEMS(n);
-  int c = (1024 + items - 1) / items;
+int split_chunks(const mlora_pool* p, int n) {
+  const int din = p->d.din;
+  int c;
+  if (n >= mlora::kShrinkTilesMinRows && din % 32 == 0) {
+    // matrix-core shrink: enough (tile, slice) workgroups to cover the chip
+    const int cap = mlora::shrink_tile_cap(p->view(), n);
+    c = (256 + cap - 1) / cap;
+  } else {
+    const int items = MLORA_SEG_MAX_ITEMS(n);
+    c = (1024 + items - 1) / items;
+  }
   c = std::min(c, kMaxSplitChunks);
   c = std::min(c, mlora_shrink_max_chunks(din));
   return std::max(c, 1);
@@ -637,7 +645,7 @@ int32_t auto_variant(const mlora_pool* p, int n) {
 size_t mlora_work_bytes(const mlora_pool* p, int32_t n) {
   if (!p || n < 0) return 0;
   // the larger of the split variant's partial t and the per-row path's layout
-  const int chunks = std::max(split_chunks(p->d.din, n), 1);
+  const int chunks = std::max(split_chunks(p, n), 1);
   size_t b = align256((size_t)chunks * n * p->d.max_rank * sizeof(float));
   if (n <= kRowsMax) b = std::max(b, rows_work_bytes(p, n));
   return b;
@@ -652,7 +660,7 @@ mlora_status mlora_plan(const mlora_pool* p, int32_t n, int32_t variant, int32_t
   if (variant == MLORA_VARIANT_ROWS && n > kRowsMax)
     return fail(MLORA_EINVAL, "the per-row variant takes at most %d rows", kRowsMax);
   if (out_variant) *out_variant = variant;
-  if (out_chunks) *out_chunks = variant == MLORA_VARIANT_SPLIT ? split_chunks(p->d.din, n) : 0;
+  if (out_chunks) *out_chunks = variant == MLORA_VARIANT_SPLIT ? split_chunks(p, n) : 0;
   return MLORA_OK;
 }
 
@@ -687,7 +695,7 @@ mlora_status mlora_apply(const mlora_pool* p, int32_t proj, const uint16_t* X, c
   if (st != MLORA_OK) return st;
   if (variant == MLORA_VARIANT_FUSED)
     return hip_check(mlora::launch_fused(v, proj, X, ws, Y, n, s), "fused launch");
-  const int chunks = split_chunks(d.din, n);
+  const int chunks = split_chunks(p, n);
   float* T = static_cast<float*>(work);
   st = hip_check(mlora::launch_shrink(v, proj, X, ws, n, T, chunks, chunk_elems_for(d.din, chunks), s), "shrink launch");
   if (st != MLORA_OK) return st;

@@ -475,95 +475,153 @@ __global__ __launch_bounds__(kTiledThreads) void gemm_tiled(const uint16_t* __re
 }
 
 // ---------------------------------------------------------------------------
-// big: 256 x 256 x 64 tiles for large batches (prefill), 4 waves of 128x128
-// (4 x 4 MFMA 32x32x16 tiles, 256 fp32 accumulators per lane).  Tiles are
-// moved global -> LDS by the gfx950 LDS DMA (global_load_lds_dwordx4: each
-// lane's 16 bytes land at a fixed LDS slot, so the XOR swizzle is applied by
-// choosing which global chunk each lane fetches), double-buffered, so no
-// registers are spent on staging.  Workgroups are mapped to tiles so that
+// big: 256 x 256 output tiles for large batches (prefill), 4 waves of
+// 128x128 (4 x 4 MFMA 32x32x16 tiles, 256 fp32 accumulators per lane).  K
+// advances in 32-deep tiles through a 4-stage LDS ring (4 x 32 KiB): tiles
+// are moved global -> LDS by LDS DMA (buffer_load ... lds: each lane's 16
+// bytes land at a fixed LDS slot, so the XOR swizzle is applied by choosing
+// which global chunk each lane fetches), and the DMA of tile kt+3 is issued
+// while tile kt is consumed, so a tile has three stages (~3000 MFMA cycles)
+// to arrive.  Inside a stage the fragment reads of the second 16-deep step
+// overlap the MFMAs of the first.  Workgroups are mapped to tiles so that
 // the tiles dispatched to one XCD (block ids congruent mod 8) are contiguous
 // along N within one or two 256-row bands of X: they share X rows in that
-// XCD's L2.  Needs K % 64 == 0 and 16-byte aligned rows.
+// XCD's L2.  Needs K % 128 == 0 and 16-byte aligned rows.
 // ---------------------------------------------------------------------------
-constexpr int GB = 256, GBK = 64;
+constexpr int GB = 256, GBK = 32, kBigStages = 4;
 constexpr int kBigThreads = 256;
 constexpr int kTileElems = GB * GBK;
 
-// Four separate LDS arrays (A and B, two stages): with the stage fixed at
-// compile time in each half of the unrolled K loop, the compiler can tell
-// the DMA target from the buffer being read and does not wait for the DMA
-// before every LDS read.
+// one array per (operand, stage): the main loop takes them as distinct
+// restrict pointers, so the compiler knows a DMA into one stage does not
+// write the stage being read
 __shared__ __attribute__((aligned(16))) uint16_t big_a0[kTileElems];
 __shared__ __attribute__((aligned(16))) uint16_t big_a1[kTileElems];
+__shared__ __attribute__((aligned(16))) uint16_t big_a2[kTileElems];
+__shared__ __attribute__((aligned(16))) uint16_t big_a3[kTileElems];
 __shared__ __attribute__((aligned(16))) uint16_t big_b0[kTileElems];
 __shared__ __attribute__((aligned(16))) uint16_t big_b1[kTileElems];
+__shared__ __attribute__((aligned(16))) uint16_t big_b2[kTileElems];
+__shared__ __attribute__((aligned(16))) uint16_t big_b3[kTileElems];
 
-// DMA of one K tile (byte offset kb) into (as, bs): instruction j of this
-// wave covers rows 8i..8i+7 of the tile, i = wave + 4j, 16 bytes per lane.
-#define BIG_ISSUE(kb, as, bs)                                                                  \
-  do {                                                                                         \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                            \
-      const int i_ = wave + 4 * j;                                                             \
-      const int so_ = i_ * 8 * row_bytes + (kb);                                               \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (as) + i_ * 8 * GBK, 16, voff, so_, 0, 0); \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (bs) + i_ * 8 * GBK, 16, voff, so_, 0, 0); \
-    }                                                                                          \
-  } while (0)
+// LDS element offset of 16-byte chunk `chunk` (0..3) of tile row `row`:
+// 64-byte rows, chunks XOR-swizzled by (row >> 2) & 3.  The LDS serves a
+// 128-bit read 16 lanes (256 bytes) per cycle; the 16 lanes of a fragment
+// read are 16 consecutive rows at one logical chunk, which this swizzle
+// spreads over all 16 slots of a 256-byte window (with (row >> 1) & 3 rows
+// r and r + 8 collided: 2-way conflicts, 4 extra cycles per read).
+__device__ __forceinline__ int swz4(int row, int chunk) { return row * GBK + ((chunk ^ ((row >> 2) & 3)) << 3); }
 
-// fragments of 16-wide K step kk from (as, bs)
-#define BIG_FRAGS(as, bs, kk, fa, fb)                                                           \
-  do {                                                                                          \
-    const int kc_ = (kk) * 2 + fk;                                                              \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) fa[i] =                                       \
-        *reinterpret_cast<const uint4*>((as) + swz(wm * 128 + i * 32 + fr, kc_));               \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j) fb[j] =                                       \
-        *reinterpret_cast<const uint4*>((bs) + swz(wn * 128 + j * 32 + fr, kc_));               \
-  } while (0)
+// Workgroup barrier without the release/acquire fences of __syncthreads():
+// those make every wave wait for all of its outstanding DMAs (vmcnt(0)),
+// which would expose the latency the stage ring is there to hide.  Each
+// wave waits for exactly the DMA it needs before arriving (explicit
+// s_waitcnt), and LDS is coherent inside the CU; the empty asm statements
+// keep the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
-// One 64-deep K tile: all 32 fragments of the tile are read from LDS first,
-// then the DMA of the next tile is issued (NEXT), then the 64 MFMAs run.  No
-// LDS read ever follows an outstanding DMA, so the compiler's conservative
-// wait for DMA completion before LDS reads never stalls the pipeline.
-#define BIG_STAGE(as, bs, NEXT)                                                                 \
-  do {                                                                                          \
-    uint4 fa0[4], fb0[4], fa1[4], fb1[4], fa2[4], fb2[4], fa3[4], fb3[4];                       \
-    BIG_FRAGS(as, bs, 0, fa0, fb0);                                                             \
-    BIG_FRAGS(as, bs, 1, fa1, fb1);                                                             \
-    BIG_FRAGS(as, bs, 2, fa2, fb2);                                                             \
-    BIG_FRAGS(as, bs, 3, fa3, fb3);                                                             \
-    NEXT;                                                                                       \
-    __builtin_amdgcn_sched_barrier(0); /* keep reads + DMA issue ahead of the MFMAs */          \
-    BIG_MMA(fa0, fb0);                                                                          \
-    BIG_MMA(fa1, fb1);                                                                          \
-    BIG_MMA(fa2, fb2);                                                                          \
-    BIG_MMA(fa3, fb3);                                                                          \
-    __builtin_amdgcn_sched_barrier(0); /* the MFMAs stay ahead of the stage's closing wait */   \
-  } while (0)
+struct BigCtx {
+  __amdgpu_buffer_rsrc_t rsa, rsb;
+  int voff, row_bytes, wave, wm, wn, fr, fk;
+};
 
-#define BIG_MMA(fa, fb)                                                                                         \
-  do {                                                                                                          \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[i][j] =     \
-        __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[i]), as_bf16x8(fb[j]), acc[i][j], 0, 0, 0);        \
-  } while (0)
+// DMA of K tile kt (32 deep) into (da, db): instruction j of this wave
+// covers tile rows 16i..16i+15, i = wave + 4j; lane L fills row L >> 2,
+// physical chunk L & 3
+__device__ __forceinline__ void big_issue(const BigCtx& c, uint16_t* __restrict__ da, uint16_t* __restrict__ db,
+                                          int kt) {
+#pragma unroll
+  for (int j = 0; j < GB / 16 / 4; ++j) {
+    const int i = c.wave + 4 * j;
+    const int so = i * 16 * c.row_bytes + kt * GBK * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsa, da + i * 16 * GBK, 16, c.voff, so, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsb, db + i * 16 * GBK, 16, c.voff, so, 0, 0);
+  }
+}
 
-__global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_big(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
-                                                        uint16_t* __restrict__ Y, int M, int K, int N, int tiles_n,
-                                                        int n_tiles, int per_xcd) {
+// Consumes K tile kt from stage (ra, rb) while tile kt+3 is sent to stage
+// (na, nb), then waits for tile kt+1 and syncs the workgroup.  Past the end
+// of K the DMA re-fetches the last tile into a stage nobody reads again, so
+// every step issues the same number of DMAs and the wait count is constant.
+__device__ __forceinline__ void big_step(const BigCtx& c, const uint16_t* __restrict__ ra,
+                                         const uint16_t* __restrict__ rb, uint16_t* __restrict__ na,
+                                         uint16_t* __restrict__ nb, int kt, int nk, floatx16 (&acc)[4][4]) {
+  uint4 fa0[4], fb0[4], fa1[4], fb1[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fa0[i] = *reinterpret_cast<const uint4*>(ra + swz4(c.wm * 128 + i * 32 + c.fr, c.fk));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) fb0[j] = *reinterpret_cast<const uint4*>(rb + swz4(c.wn * 128 + j * 32 + c.fr, c.fk));
+  big_issue(c, na, nb, min(kt + 3, nk - 1));
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    fa1[i] = *reinterpret_cast<const uint4*>(ra + swz4(c.wm * 128 + i * 32 + c.fr, 2 + c.fk));
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    fb1[j] = *reinterpret_cast<const uint4*>(rb + swz4(c.wn * 128 + j * 32 + c.fr, 2 + c.fk));
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa0[i]), as_bf16x8(fb0[j]), acc[i][j], 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa1[i]), as_bf16x8(fb1[j]), acc[i][j], 0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  // tile kt+1 has landed once only the DMAs issued after it (tiles kt+2 and
+  // kt+3, 8 instructions each per wave) may still be in flight
+  __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16)
+  ring_barrier();
+}
+
+// K tiles in groups of 4 (K % 128 == 0), one stage each
+__device__ __forceinline__ void big_mainloop(const BigCtx& c, uint16_t* __restrict__ a0, uint16_t* __restrict__ a1,
+                                             uint16_t* __restrict__ a2, uint16_t* __restrict__ a3,
+                                             uint16_t* __restrict__ b0, uint16_t* __restrict__ b1,
+                                             uint16_t* __restrict__ b2, uint16_t* __restrict__ b3, int nk,
+                                             floatx16 (&acc)[4][4]) {
+  big_issue(c, a0, b0, 0);
+  big_issue(c, a1, b1, 1);
+  big_issue(c, a2, b2, 2);
+  __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): tile 0 has landed
+  ring_barrier();
+  for (int kt = 0; kt < nk; kt += kBigStages) {
+    big_step(c, a0, b0, a3, b3, kt, nk, acc);
+    big_step(c, a1, b1, a0, b0, kt + 1, nk, acc);
+    big_step(c, a2, b2, a1, b1, kt + 2, nk, acc);
+    big_step(c, a3, b3, a2, b2, kt + 3, nk, acc);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // drain the trailing re-fetches before the workgroup ends
+}
+
+__global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_big(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y, int M, int K, int N,
+    int tiles_n, int n_tiles, int per_xcd) {
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: DMA offsets stay scalar
   const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (t >= n_tiles) return;
   const int m0 = (t / tiles_n) * GB, n0 = (t % tiles_n) * GB;
-  const int fr = lane & 31, fk = lane >> 5, wm = wave >> 1, wn = wave & 1;
-  const int row_bytes = K * 2;
+  BigCtx c;
+  c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: DMA offsets stay scalar
+  c.fr = lane & 31;
+  c.fk = lane >> 5;
+  c.wm = c.wave >> 1;
+  c.wn = c.wave & 1;
+  c.row_bytes = K * 2;
   // X rows m0.. and W rows n0..; loads past the end of either return zeros
-  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(X + (size_t)m0 * K), (short)0, (M - m0) * row_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(W + (size_t)n0 * K), (short)0, (N - n0) * row_bytes, 0x00020000);
-  // lane L fills LDS chunk slot (row L/8 of its 8-row group, physical chunk
-  // L%8), which holds logical chunk (L%8) ^ (L/8) of that row
-  const int voff = (lane >> 3) * row_bytes + (((lane & 7) ^ (lane >> 3)) << 4);
+  c.rsa = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X + (size_t)m0 * K), (short)0,
+                                            (M - m0) * c.row_bytes, 0x00020000);
+  c.rsb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(W + (size_t)n0 * K), (short)0,
+                                            (N - n0) * c.row_bytes, 0x00020000);
+  // lane L fills LDS slot (row L >> 2 of its 16-row group, physical chunk
+  // L & 3), which holds logical chunk (L & 3) ^ ((row >> 2) & 3)
+  c.voff = (lane >> 2) * c.row_bytes + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
 
   floatx16 acc[4][4];
 #pragma unroll
@@ -573,32 +631,17 @@ __global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(1, 
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int nk = K / GBK;
-  BIG_ISSUE(0, big_a0, big_b0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  int kt = 0;
-  for (; kt + 2 <= nk; kt += 2) {
-    // stage 0 holds tile kt; fetch tile kt+1 into stage 1
-    BIG_STAGE(big_a0, big_b0, BIG_ISSUE((kt + 1) * GBK * 2, big_a1, big_b1));
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    // stage 1 holds tile kt+1; fetch tile kt+2 (if any) into stage 0
-    BIG_STAGE(big_a1, big_b1, if (kt + 2 < nk) BIG_ISSUE((kt + 2) * GBK * 2, big_a0, big_b0));
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-  if (kt < nk) BIG_STAGE(big_a0, big_b0, (void)0);  // odd tile count: the last tile sits in stage 0
+  big_mainloop(c, big_a0, big_a1, big_a2, big_a3, big_b0, big_b1, big_b2, big_b3, K / GBK, acc);
 
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int col = n0 + wn * 128 + j * 32 + (lane & 31);
+      const int col = n0 + c.wn * 128 + j * 32 + (lane & 31);
       if (col >= N) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int r = m0 + wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int r = m0 + c.wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (r < M) Y[(size_t)r * N + col] = (uint16_t)f2bf(acc[i][j][v]);
       }
     }
@@ -665,7 +708,7 @@ hipError_t launch_gemm(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M,
     const dim3 grid((N + 31) / 32, (M + 32 * KS_MB - 1) / (32 * KS_MB)), block(64 * kKsWaves);
     MLORA_LAUNCH("gemm_ksplit", (gemm_ksplit<VEC, false>), grid, block, 0, st, X, W, Y, M, K, N, PoolView{}, 0, nullptr,
                        nullptr);
-  } else if (VEC && K % GBK == 0 && (long)M * N >= 2048L * 2048L && (long)M * K * 2 < (1L << 31) &&
+  } else if (VEC && K % (GBK * kBigStages) == 0 && (long)M * N >= 2048L * 2048L && (long)M * K * 2 < (1L << 31) &&
              (long)N * K * 2 < (1L << 31) && big_gemm_enabled()) {
     return launch_big(X, W, Y, M, K, N, st);
   } else {

@@ -83,6 +83,11 @@ hipError_t launch_shrink_rows(const PoolView& pv, int proj, const uint16_t* X, c
 
 hipError_t launch_shrink(const PoolView& pv, int proj, const uint16_t* X, const int32_t* ws, int n,
                          float* T, int n_chunks, int chunk_elems, hipStream_t stream);
+// Batches of at least this many rows run the shrink on the matrix cores per
+// 64-row segment tile (when din allows); shrink_tile_cap bounds the tiles.
+constexpr int kShrinkTilesMinRows = 256;
+bool shrink_uses_tiles(const PoolView& pv, int n, const void* X);
+int shrink_tile_cap(const PoolView& pv, int n);
 
 hipError_t launch_expand(const PoolView& pv, int proj, const float* T, int n_chunks, const int32_t* ws,
                          uint16_t* Y, int n, hipStream_t stream);

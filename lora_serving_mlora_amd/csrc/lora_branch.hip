@@ -304,6 +304,167 @@ __global__ __launch_bounds__(kRowThreads) void shrink_rows_kernel(PoolView pv, i
   for (int k = blockIdx.x; k < n; k += gridDim.x) shrink_row_body<VEC>(pv, proj, X, row_key, k, T);
 }
 
+// ---------------------------------------------------------------------------
+// shrink_tiles (large groups): one 4-wave workgroup per (64-row segment
+// tile, din slice).  At prefill sizes a group holds hundreds of rows and the
+// shrink is a real contraction (ranks up to 64 and more need more flops per
+// byte than the vector ALU gives at HBM speed), so it runs on the matrix
+// cores: v_mfma_f32_16x16x32_bf16 with A = 16 gathered X rows and B = 16
+// Down rank rows.  Each wave takes all 64 rows of the tile and up to 64
+// ranks over its own quarter of the slice, so every X element and every
+// Down element of the slice is read exactly once by the workgroup, straight
+// from global memory into MFMA operands; the four quarters are summed
+// through LDS in a fixed order.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+constexpr int kTileWaves = 4;
+constexpr int kTileRB = MLORA_TILE_ROWS / 16;  // 16-row MFMA blocks per tile
+
+// Two MFMA operand fragments from 128-byte row pieces: `lo` holds rows
+// l & 7, `hi` rows 8 + (l & 7), 16-byte chunk l >> 3 of a 64-element K
+// segment.  f0 takes chunk 2g for lane group g = l >> 4 (the even chunks),
+// f1 the odd chunks; lanes 0-7 of each 16-lane row carry rows 0-7 and lanes
+// 8-15 rows 8-15, as the MFMA operand layout wants.  One DPP move per dword.
+__device__ __forceinline__ void frag_pair(const uint4& lo, const uint4& hi, uint4& f0, uint4& f1) {
+  f0.x = __builtin_amdgcn_update_dpp((int)lo.x, (int)hi.x, 0x118, 0xf, 0xc, false);  // row_shr:8 into lanes 8-15
+  f0.y = __builtin_amdgcn_update_dpp((int)lo.y, (int)hi.y, 0x118, 0xf, 0xc, false);
+  f0.z = __builtin_amdgcn_update_dpp((int)lo.z, (int)hi.z, 0x118, 0xf, 0xc, false);
+  f0.w = __builtin_amdgcn_update_dpp((int)lo.w, (int)hi.w, 0x118, 0xf, 0xc, false);
+  f1.x = __builtin_amdgcn_update_dpp((int)hi.x, (int)lo.x, 0x108, 0xf, 0x3, false);  // row_shl:8 into lanes 0-7
+  f1.y = __builtin_amdgcn_update_dpp((int)hi.y, (int)lo.y, 0x108, 0xf, 0x3, false);
+  f1.z = __builtin_amdgcn_update_dpp((int)hi.z, (int)lo.z, 0x108, 0xf, 0x3, false);
+  f1.w = __builtin_amdgcn_update_dpp((int)hi.w, (int)lo.w, 0x108, 0xf, 0x3, false);
+}
+
+template <int NG>  // rank groups of 16 in this pass
+__device__ __forceinline__ void shrink_tile_pass(const PoolView& pv, const uint16_t* __restrict__ X,
+                                                 const int32_t* __restrict__ perm, int j0, int jend, int q0,
+                                                 int rank, const int32_t* __restrict__ dpage, int k0, int k1,
+                                                 float* __restrict__ Tc, floatx4* __restrict__ red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int din = pv.din;
+  // this wave's quarter of the slice in 64-wide segments; the last wave also
+  // takes a trailing 32-wide step
+  const int segs = (k1 - k0) / 64;
+  const int kb = k0 + 64 * ((segs * wave) / kTileWaves);
+  const int km = k0 + 64 * ((segs * (wave + 1)) / kTileWaves);
+  const int ke = wave == kTileWaves - 1 ? k1 : km;
+  // X: 128-byte pieces of rows 8h + (l & 7) of each 16-row block (for the
+  // segment loop) and the plain fragment rows l & 15 (for the 32-wide tail)
+  const uint16_t* xp[kTileRB][2];
+  const uint16_t* xt[kTileRB];
+#pragma unroll
+  for (int rb = 0; rb < kTileRB; ++rb) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int j = min(j0 + 16 * rb + 8 * h + (lane & 7), jend - 1);  // rows past the tile repeat its last row
+      xp[rb][h] = X + (size_t)perm[j] * din + (lane >> 3) * 8;
+    }
+    xt[rb] = X + (size_t)perm[min(j0 + 16 * rb + (lane & 15), jend - 1)] * din + (lane >> 4) * 8;
+  }
+  // Down: rank rows q0 + 16g + (l & 15); ranks past the adapter's repeat its last
+  const uint16_t* dr[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int pg = dpage[min(q0 + 16 * g + (lane & 15), rank - 1)];
+    dr[g] = pv.down + (size_t)pg * din + (lane >> 4) * 8;
+  }
+  floatx4 acc[kTileRB][NG];
+#pragma unroll
+  for (int rb = 0; rb < kTileRB; ++rb)
+#pragma unroll
+    for (int g = 0; g < NG; ++g) acc[rb][g] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int k = kb; k < km; k += 64) {
+    uint4 xa[kTileRB][2], d0[NG], d1[NG];
+#pragma unroll
+    for (int rb = 0; rb < kTileRB; ++rb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) xa[rb][h] = *reinterpret_cast<const uint4*>(xp[rb][h] + k);
+    // B chunks matching f0 (chunk 2g of the segment) and f1 (chunk 2g + 1)
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      d0[g] = *reinterpret_cast<const uint4*>(dr[g] + k + (lane >> 4) * 8);
+      d1[g] = *reinterpret_cast<const uint4*>(dr[g] + k + (lane >> 4) * 8 + 8);
+    }
+#pragma unroll
+    for (int rb = 0; rb < kTileRB; ++rb) {
+      uint4 f0, f1;
+      frag_pair(xa[rb][0], xa[rb][1], f0, f1);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        acc[rb][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f0), as_bf16x8(d0[g]), acc[rb][g], 0, 0, 0);
+        acc[rb][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(f1), as_bf16x8(d1[g]), acc[rb][g], 0, 0, 0);
+      }
+    }
+  }
+  for (int k = km; k < ke; k += 32) {
+    uint4 a[kTileRB], b[NG];
+#pragma unroll
+    for (int rb = 0; rb < kTileRB; ++rb) a[rb] = *reinterpret_cast<const uint4*>(xt[rb] + k);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) b[g] = *reinterpret_cast<const uint4*>(dr[g] + k);
+#pragma unroll
+    for (int rb = 0; rb < kTileRB; ++rb)
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+        acc[rb][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[rb]), as_bf16x8(b[g]), acc[rb][g], 0, 0, 0);
+  }
+  // quarters -> LDS, then wave w sums row block w over the quarters in order
+#pragma unroll
+  for (int rb = 0; rb < kTileRB; ++rb)
+#pragma unroll
+    for (int g = 0; g < NG; ++g) red[((wave * kTileRB + rb) * NG + g) * 64 + lane] = acc[rb][g];
+  __syncthreads();
+  const int rb = wave;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    floatx4 sum = red[((0 * kTileRB + rb) * NG + g) * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < kTileWaves; ++w) sum += red[((w * kTileRB + rb) * NG + g) * 64 + lane];
+    // C[(l >> 4) * 4 + v][l & 15]: row of the block, rank of the group
+    const int q = q0 + 16 * g + (lane & 15);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int jj = j0 + 16 * rb + (lane >> 4) * 4 + v;
+      if (jj < jend && q < rank) Tc[(size_t)jj * pv.max_rank + q] = sum[v];
+    }
+  }
+  __syncthreads();  // red is reused by the next pass
+}
+
+__global__ __launch_bounds__(64 * kTileWaves) void shrink_tiles_kernel(PoolView pv, int proj,
+                                                                       const uint16_t* __restrict__ X,
+                                                                       const int32_t* __restrict__ ws, int n,
+                                                                       float* __restrict__ T, int chunk_elems) {
+  __shared__ floatx4 red[kTileWaves * kTileRB * 4 * 64];  // 64 KiB
+  const int n_tiles = ws[MLORA_SEG_NTILES];
+  const int32_t* tiles = ws + MLORA_SEG_TILES(n);
+  const int32_t* perm = ws + MLORA_SEG_PERM(n);
+  const int c = blockIdx.y;
+  const int k0 = min(c * chunk_elems, pv.din), k1 = min(k0 + chunk_elems, pv.din);
+  float* Tc = T + (size_t)c * n * pv.max_rank;
+  for (int t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+    const int seg = __builtin_amdgcn_readfirstlane(tiles[2 * t]);
+    const int j0 = __builtin_amdgcn_readfirstlane(tiles[2 * t + 1]);
+    const int jend = min(j0 + MLORA_TILE_ROWS, __builtin_amdgcn_readfirstlane(ws[MLORA_SEG_OFF(n) + seg + 1]));
+    const int adapter = __builtin_amdgcn_readfirstlane(ws[MLORA_SEG_ADAPTER(n) + seg]);
+    const int rank = __builtin_amdgcn_readfirstlane(pv.rank[adapter]);
+    const int32_t* dpage = pv.down_page + ((size_t)adapter * pv.n_proj + proj) * pv.max_rank;
+    for (int q0 = 0; q0 < rank; q0 += 64) {
+      const int rem = rank - q0;
+      if (rem > 32)
+        shrink_tile_pass<4>(pv, X, perm, j0, jend, q0, rank, dpage, k0, k1, Tc, red);
+      else if (rem > 16)
+        shrink_tile_pass<2>(pv, X, perm, j0, jend, q0, rank, dpage, k0, k1, Tc, red);
+      else
+        shrink_tile_pass<1>(pv, X, perm, j0, jend, q0, rank, dpage, k0, k1, Tc, red);
+    }
+  }
+}
+
 bool vec_ok(const PoolView& pv, const void* a, const void* b) {
   const uintptr_t p = reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b) |
                       reinterpret_cast<uintptr_t>(pv.down) | reinterpret_cast<uintptr_t>(pv.up);
@@ -320,8 +481,23 @@ int item_grid(int n) {
 
 }  // namespace
 
+bool shrink_uses_tiles(const PoolView& pv, int n, const void* X) {
+  return n >= kShrinkTilesMinRows && pv.din % 32 == 0 && vec_ok(pv, X, X);
+}
+
+int shrink_tile_cap(const PoolView& pv, int n) {
+  // tiles <= ceil(n_act / TILE_ROWS) + nseg, nseg <= min(n, max_adapters)
+  return (n + MLORA_TILE_ROWS - 1) / MLORA_TILE_ROWS + (n < pv.max_adapters ? n : pv.max_adapters);
+}
+
 hipError_t launch_shrink(const PoolView& pv, int proj, const uint16_t* X, const int32_t* ws, int n, float* T,
                          int n_chunks, int chunk_elems, hipStream_t stream) {
+  if (shrink_uses_tiles(pv, n, X)) {
+    const int cap = shrink_tile_cap(pv, n);
+    const dim3 grid(cap < 4096 ? cap : 4096, n_chunks), block(64 * kTileWaves);
+    MLORA_LAUNCH("shrink_tiles", shrink_tiles_kernel, grid, block, 0, stream, pv, proj, X, ws, n, T, chunk_elems);
+    return launched();
+  }
   const dim3 grid(item_grid(n), n_chunks), block(64);
   if (vec_ok(pv, X, X))
     MLORA_LAUNCH("shrink", (shrink_kernel<true>), grid, block, 0, stream, pv, proj, X, ws, n, T, chunk_elems);

@@ -213,6 +213,32 @@ __global__ __launch_bounds__(NT) void seg_build_kernel(const int32_t* __restrict
     items[2 * i] = lo;
     items[2 * i + 1] = (int)offs[lo] + (i - first) * MLORA_ITEM_ROWS;
   }
+  __syncthreads();
+
+  // 6. tiles: ceil(len / TILE_ROWS) per segment, in segment order
+  int32_t* tiles = ws + MLORA_SEG_TILES(n);
+  uint32_t* tile_end = sorted;
+  int n_tiles = 0;
+  for (int base = 0; base < nseg; base += kThreads) {
+    const int s = base + tid;
+    int t = 0;
+    if (s < nseg) t = (int)((offs[s + 1] - offs[s] + MLORA_TILE_ROWS - 1) / MLORA_TILE_ROWS);
+    int total;
+    const int ex = block_exclusive_scan<NT>(t, s_wave, &total);
+    if (s < nseg) tile_end[s] = (uint32_t)(n_tiles + ex + t);
+    n_tiles += total;
+  }
+  __syncthreads();
+  for (int i = tid; i < n_tiles; i += kThreads) {
+    int lo = 0, hi = nseg - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if ((int)tile_end[mid] > i) hi = mid; else lo = mid + 1;
+    }
+    const int first = lo ? (int)tile_end[lo - 1] : 0;
+    tiles[2 * i] = lo;
+    tiles[2 * i + 1] = (int)offs[lo] + (i - first) * MLORA_TILE_ROWS;
+  }
   if (tid == 0) {
     ws[MLORA_SEG_NSEG] = nseg;
     ws[MLORA_SEG_NACT] = n_act;
@@ -223,6 +249,7 @@ __global__ __launch_bounds__(NT) void seg_build_kernel(const int32_t* __restrict
     ws[MLORA_SEG_NROWS] = n;
     ws[MLORA_SEG_MAXAD] = max_adapters;
     for (int h = 8; h < MLORA_SEG_HEADER; ++h) ws[h] = 0;
+    ws[MLORA_SEG_NTILES] = n_tiles;
   }
 }
 
@@ -316,7 +343,12 @@ __global__ __launch_bounds__(64) void seg_build_small(const int32_t* __restrict_
     ws[MLORA_SEG_NROWS] = n;
     ws[MLORA_SEG_MAXAD] = max_adapters;
   }
-  if (lane >= 8 && lane < MLORA_SEG_HEADER) ws[lane] = 0;
+  // one tile per segment (a segment here has at most 64 rows)
+  if (lane < nseg) {
+    ws[MLORA_SEG_TILES(n) + 2 * lane] = lane;
+    ws[MLORA_SEG_TILES(n) + 2 * lane + 1] = s_sorted[lane];
+  }
+  if (lane >= 8 && lane < MLORA_SEG_HEADER) ws[lane] = lane == MLORA_SEG_NTILES ? nseg : 0;
 }
 
 template <int NT>

@@ -50,7 +50,7 @@ def test_host_only_calls():
     n = 4096
     items0 = (16 + 4 * n + 2) & ~1
     max_items = n + (n + 3) // 4 + 1
-    assert L.mlora_segments_bytes(n) == al((items0 + 2 * max_items + n) * 4)
+    assert L.mlora_segments_bytes(n) == al((items0 + 2 * max_items + n + 2 * n) * 4)
     assert L.mlora_shrink_max_chunks(4096) == 8 and L.mlora_shrink_max_chunks(4) == 1
     assert L.mlora_pool_create(None, None, None) == M.EINVAL
     assert b"NULL" in L.mlora_last_error()

@@ -27,7 +27,9 @@ GEMM_SHAPES = [(1, 4, 4), (4, 4, 4), (3, 5, 7), (16, 64, 16), (17, 72, 33), (32,
                (48, 40, 1000), (64, 520, 1000), (65, 4096, 300), (200, 136, 136), (300, 1000, 777),
                (256, 4096, 4096), (513, 264, 392),
                # medium batches on the K-split kernel, incl. K tails and unaligned K
-               (65, 4096, 4096), (129, 520, 4104), (700, 1000, 2000), (100, 20, 4096), (512, 4096, 4096)]
+               (65, 4096, 4096), (129, 520, 4104), (700, 1000, 2000), (100, 20, 4096), (512, 4096, 4096),
+               # 256x256 LDS-DMA kernel (M*N >= 2048^2): full tiles, ragged M and N, odd K-tile count
+               (2048, 1024, 2048), (2100, 640, 2200), (1030, 4096, 4104)]
 
 
 @pytest.mark.parametrize("m,k,n", GEMM_SHAPES)
@@ -69,6 +71,10 @@ SMALL = [
     (4, 12, 20, 23, {0: 4, 1: 7}),                    # din, dout not multiples of 8: element-wise path
     (5, 4104, 136, 70, {i: 16 for i in range(20)}),   # many one/two-row groups
     (6, 256, 11008, 40, {0: 64, 1: 128}),              # rank up to the limit, wide dout
+    # >= 256 rows: the matrix-core shrink over 64-row segment tiles
+    (7, 4128, 264, 300, {0: 1, 1: 8, 2: 17, 3: 64, 4: 128}),   # din = 32 * 129: K tail, empty slices
+    (8, 512, 1000, 700, {i: (16 if i % 3 else 64) for i in range(40)}),
+    (9, 1000, 520, 260, {0: 16, 1: 3, 2: 64}),        # din not a multiple of 32: vector-ALU shrink
 ]
 
 

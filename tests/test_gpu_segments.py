@@ -60,6 +60,12 @@ def check(M, pool, ids, max_adapters, resident, what):
         last = j0
         cover[j0:min(j0 + M.ITEM_ROWS, hi)] += 1
     assert np.all(cover == 1), what
+    # tiles: fixed by the segments, (s, seg_off[s] + t * TILE_ROWS) in order
+    want = [(s, int(ref["seg_off"][s]) + t)
+            for s in range(ref["nseg"])
+            for t in range(0, int(ref["seg_off"][s + 1] - ref["seg_off"][s]), M.TILE_ROWS)]
+    assert got["n_tiles"] == len(want), (what, got["n_tiles"], len(want))
+    assert [tuple(int(v) for v in t) for t in got["tiles"]] == want, what
     return got
 
 
