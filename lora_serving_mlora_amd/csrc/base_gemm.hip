@@ -16,7 +16,7 @@
 //    waves (2x2, 64x64 each = 2x2 MFMA 32x32x16 tiles), K in steps of 64
 //    staged through LDS with a register-staged double buffer; LDS rows are
 //    XOR-swizzled in 16-byte chunks so that the 128-bit fragment reads of
-//    eight consecutive lanes hit eight different chunk positions (no bank
+//    sixteen consecutive lanes hit sixteen different bank groups (no bank
 //    conflicts).
 #include <stdlib.h>
 
@@ -346,7 +346,11 @@ constexpr int kChunksPerRow = BK / 8;                          // 16-byte chunks
 constexpr int kLoadsA = BM * kChunksPerRow / kTiledThreads;    // 4
 constexpr int kLoadsB = BN * kChunksPerRow / kTiledThreads;    // 4
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 3); }
+// 128-byte LDS rows, chunks XOR-swizzled by (row >> 1) & 7: a 128-bit LDS
+// read is served 16 lanes (256 bytes) per cycle, and the 16 consecutive
+// rows of a fragment read then land in 16 distinct 16-byte slots of the
+// 256-byte window (row & 7 would put rows r and r + 8 on the same banks).
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ ((row >> 1) & 7)) << 3); }
 
 // PART: split-K form - workgroup z covers K tiles [z*kt_per, (z+1)*kt_per)
 // and stores its fp32 partial tile to part[z][M][N] (summed by finish_part).
@@ -475,34 +479,53 @@ __global__ __launch_bounds__(kTiledThreads) void gemm_tiled(const uint16_t* __re
 }
 
 // ---------------------------------------------------------------------------
-// big: 256 x 256 output tiles for large batches (prefill), 4 waves of
-// 128x128 (4 x 4 MFMA 32x32x16 tiles, 256 fp32 accumulators per lane).  K
-// advances in 32-deep tiles through a 4-stage LDS ring (4 x 32 KiB): tiles
-// are moved global -> LDS by LDS DMA (buffer_load ... lds: each lane's 16
-// bytes land at a fixed LDS slot, so the XOR swizzle is applied by choosing
-// which global chunk each lane fetches), and the DMA of tile kt+3 is issued
-// while tile kt is consumed, so a tile has three stages (~3000 MFMA cycles)
-// to arrive.  Inside a stage the fragment reads of the second 16-deep step
-// overlap the MFMAs of the first.  Workgroups are mapped to tiles so that
-// the tiles dispatched to one XCD (block ids congruent mod 8) are contiguous
-// along N within one or two 256-row bands of X: they share X rows in that
-// XCD's L2.  Needs K % 128 == 0 and 16-byte aligned rows.
+// ring: TM x TN output tiles (256 x 256 for large batches, 128 x 128 with
+// split-K for medium ones), 4 waves of (TM/2) x (TN/2), MFMA 32x32x16.  K
+// advances in 32-deep tiles through an LDS ring of NS stages (4 of 32 KiB
+// for 256 x 256, 8 of 16 KiB for 128 x 128).  Tiles are moved global -> LDS
+// by LDS DMA (buffer_load ... lds: each lane's 16 bytes land at a fixed LDS
+// slot, so the XOR swizzle is applied by choosing which global chunk each
+// lane fetches), and the DMA of tile kt+NS-1 is issued while tile kt is
+// consumed, so NS-1 tiles are always in flight.  Inside a stage the
+// fragment reads of the second 16-deep step overlap the MFMAs of the first.
+// Workgroups are mapped to tiles so that the tiles dispatched to one XCD
+// (block ids congruent mod 8) are contiguous: along N within one or two
+// bands of X rows for large products (they share X rows in that XCD's L2),
+// along M within a W column block for split-K medium ones (W is then read
+// from HBM once and X, a few MiB, is what each XCD re-reads).  Needs K a
+// multiple of 32 * NS (per split) and 16-byte aligned rows; rows past M or
+// N read zeros (buffer bounds).
 // ---------------------------------------------------------------------------
-constexpr int GB = 256, GBK = 32, kBigStages = 4;
-constexpr int kBigThreads = 256;
-constexpr int kTileElems = GB * GBK;
+constexpr int GBK = 32, kRingStages = 4, kMidStages = 8;  // stages: 256x256 tiles, 128x128 tiles
+constexpr int kRingThreads = 256;
 
-// one array per (operand, stage): the main loop takes them as distinct
-// restrict pointers, so the compiler knows a DMA into one stage does not
-// write the stage being read
-__shared__ __attribute__((aligned(16))) uint16_t big_a0[kTileElems];
-__shared__ __attribute__((aligned(16))) uint16_t big_a1[kTileElems];
-__shared__ __attribute__((aligned(16))) uint16_t big_a2[kTileElems];
-__shared__ __attribute__((aligned(16))) uint16_t big_a3[kTileElems];
-__shared__ __attribute__((aligned(16))) uint16_t big_b0[kTileElems];
-__shared__ __attribute__((aligned(16))) uint16_t big_b1[kTileElems];
-__shared__ __attribute__((aligned(16))) uint16_t big_b2[kTileElems];
-__shared__ __attribute__((aligned(16))) uint16_t big_b3[kTileElems];
+// one array per (operand, stage, tile size): the main loop takes them as
+// distinct restrict pointers, so the compiler knows a DMA into one stage
+// does not write the stage being read
+__shared__ __attribute__((aligned(16))) uint16_t big_a0[256 * GBK];
+__shared__ __attribute__((aligned(16))) uint16_t big_a1[256 * GBK];
+__shared__ __attribute__((aligned(16))) uint16_t big_a2[256 * GBK];
+__shared__ __attribute__((aligned(16))) uint16_t big_a3[256 * GBK];
+__shared__ __attribute__((aligned(16))) uint16_t big_b0[256 * GBK];
+__shared__ __attribute__((aligned(16))) uint16_t big_b1[256 * GBK];
+__shared__ __attribute__((aligned(16))) uint16_t big_b2[256 * GBK];
+__shared__ __attribute__((aligned(16))) uint16_t big_b3[256 * GBK];
+__shared__ __attribute__((aligned(16))) uint16_t mid_a0[128 * GBK];
+__shared__ __attribute__((aligned(16))) uint16_t mid_a1[128 * GBK];
+__shared__ __attribute__((aligned(16))) uint16_t mid_a2[128 * GBK];
+__shared__ __attribute__((aligned(16))) uint16_t mid_a3[128 * GBK];
+__shared__ __attribute__((aligned(16))) uint16_t mid_a4[128 * GBK];
+__shared__ __attribute__((aligned(16))) uint16_t mid_a5[128 * GBK];
+__shared__ __attribute__((aligned(16))) uint16_t mid_a6[128 * GBK];
+__shared__ __attribute__((aligned(16))) uint16_t mid_a7[128 * GBK];
+__shared__ __attribute__((aligned(16))) uint16_t mid_b0[128 * GBK];
+__shared__ __attribute__((aligned(16))) uint16_t mid_b1[128 * GBK];
+__shared__ __attribute__((aligned(16))) uint16_t mid_b2[128 * GBK];
+__shared__ __attribute__((aligned(16))) uint16_t mid_b3[128 * GBK];
+__shared__ __attribute__((aligned(16))) uint16_t mid_b4[128 * GBK];
+__shared__ __attribute__((aligned(16))) uint16_t mid_b5[128 * GBK];
+__shared__ __attribute__((aligned(16))) uint16_t mid_b6[128 * GBK];
+__shared__ __attribute__((aligned(16))) uint16_t mid_b7[128 * GBK];
 
 // LDS element offset of 16-byte chunk `chunk` (0..3) of tile row `row`:
 // 64-byte rows, chunks XOR-swizzled by (row >> 2) & 3.  The LDS serves a
@@ -524,7 +547,10 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("" ::: "memory");
 }
 
-struct BigCtx {
+// s_waitcnt immediate for "vmcnt <= v" (expcnt and lgkmcnt not waited)
+constexpr int vmcnt_imm(int v) { return (v & 15) | ((v >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+struct RingCtx {
   __amdgpu_buffer_rsrc_t rsa, rsb;
   int voff, row_bytes, wave, wm, wn, fr, fk;
 };
@@ -532,89 +558,140 @@ struct BigCtx {
 // DMA of K tile kt (32 deep) into (da, db): instruction j of this wave
 // covers tile rows 16i..16i+15, i = wave + 4j; lane L fills row L >> 2,
 // physical chunk L & 3
-__device__ __forceinline__ void big_issue(const BigCtx& c, uint16_t* __restrict__ da, uint16_t* __restrict__ db,
-                                          int kt) {
+template <int TM, int TN>
+__device__ __forceinline__ void ring_issue(const RingCtx& c, uint16_t* __restrict__ da, uint16_t* __restrict__ db,
+                                           int kt) {
 #pragma unroll
-  for (int j = 0; j < GB / 16 / 4; ++j) {
+  for (int j = 0; j < TM / 64; ++j) {
     const int i = c.wave + 4 * j;
-    const int so = i * 16 * c.row_bytes + kt * GBK * 2;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsa, da + i * 16 * GBK, 16, c.voff, so, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsb, db + i * 16 * GBK, 16, c.voff, so, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsa, da + i * 16 * GBK, 16, c.voff,
+                                             i * 16 * c.row_bytes + kt * GBK * 2, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < TN / 64; ++j) {
+    const int i = c.wave + 4 * j;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsb, db + i * 16 * GBK, 16, c.voff,
+                                             i * 16 * c.row_bytes + kt * GBK * 2, 0, 0);
   }
 }
 
-// Consumes K tile kt from stage (ra, rb) while tile kt+3 is sent to stage
-// (na, nb), then waits for tile kt+1 and syncs the workgroup.  Past the end
-// of K the DMA re-fetches the last tile into a stage nobody reads again, so
-// every step issues the same number of DMAs and the wait count is constant.
-__device__ __forceinline__ void big_step(const BigCtx& c, const uint16_t* __restrict__ ra,
-                                         const uint16_t* __restrict__ rb, uint16_t* __restrict__ na,
-                                         uint16_t* __restrict__ nb, int kt, int nk, floatx16 (&acc)[4][4]) {
-  uint4 fa0[4], fb0[4], fa1[4], fb1[4];
+// Consumes K tile kt from stage (ra, rb) while tile kt+NS-1 is sent to
+// stage (na, nb), then waits for tile kt+1 and syncs the workgroup.  Past
+// the end of the K range the DMA re-fetches its last tile into a stage
+// nobody reads again, so every step issues the same number of DMAs and the
+// wait count is constant.
+template <int TM, int TN, int NS>
+__device__ __forceinline__ void ring_step(const RingCtx& c, const uint16_t* __restrict__ ra,
+                                          const uint16_t* __restrict__ rb, uint16_t* __restrict__ na,
+                                          uint16_t* __restrict__ nb, int kt, int kend,
+                                          floatx16 (&acc)[TM / 64][TN / 64]) {
+  constexpr int MI = TM / 64, NJ = TN / 64;
+  uint4 fa0[MI], fb0[NJ], fa1[MI], fb1[NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) fa0[i] = *reinterpret_cast<const uint4*>(ra + swz4(c.wm * 128 + i * 32 + c.fr, c.fk));
+  for (int i = 0; i < MI; ++i)
+    fa0[i] = *reinterpret_cast<const uint4*>(ra + swz4(c.wm * (TM / 2) + i * 32 + c.fr, c.fk));
 #pragma unroll
-  for (int j = 0; j < 4; ++j) fb0[j] = *reinterpret_cast<const uint4*>(rb + swz4(c.wn * 128 + j * 32 + c.fr, c.fk));
-  big_issue(c, na, nb, min(kt + 3, nk - 1));
+  for (int j = 0; j < NJ; ++j)
+    fb0[j] = *reinterpret_cast<const uint4*>(rb + swz4(c.wn * (TN / 2) + j * 32 + c.fr, c.fk));
+  ring_issue<TM, TN>(c, na, nb, min(kt + NS - 1, kend - 1));
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    fa1[i] = *reinterpret_cast<const uint4*>(ra + swz4(c.wm * 128 + i * 32 + c.fr, 2 + c.fk));
+  for (int i = 0; i < MI; ++i)
+    fa1[i] = *reinterpret_cast<const uint4*>(ra + swz4(c.wm * (TM / 2) + i * 32 + c.fr, 2 + c.fk));
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    fb1[j] = *reinterpret_cast<const uint4*>(rb + swz4(c.wn * 128 + j * 32 + c.fr, 2 + c.fk));
+  for (int j = 0; j < NJ; ++j)
+    fb1[j] = *reinterpret_cast<const uint4*>(rb + swz4(c.wn * (TN / 2) + j * 32 + c.fr, 2 + c.fk));
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa0[i]), as_bf16x8(fb0[j]), acc[i][j], 0, 0, 0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa1[i]), as_bf16x8(fb1[j]), acc[i][j], 0, 0, 0);
   __builtin_amdgcn_sched_barrier(0);
-  // tile kt+1 has landed once only the DMAs issued after it (tiles kt+2 and
-  // kt+3, 8 instructions each per wave) may still be in flight
-  __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16)
+  // tile kt+1 has landed once only the DMAs issued after it (tiles kt+2 ..
+  // kt+NS-1) may still be in flight
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * (MI + NJ)));
   ring_barrier();
 }
 
-// K tiles in groups of 4 (K % 128 == 0), one stage each
-__device__ __forceinline__ void big_mainloop(const BigCtx& c, uint16_t* __restrict__ a0, uint16_t* __restrict__ a1,
-                                             uint16_t* __restrict__ a2, uint16_t* __restrict__ a3,
-                                             uint16_t* __restrict__ b0, uint16_t* __restrict__ b1,
-                                             uint16_t* __restrict__ b2, uint16_t* __restrict__ b3, int nk,
-                                             floatx16 (&acc)[4][4]) {
-  big_issue(c, a0, b0, 0);
-  big_issue(c, a1, b1, 1);
-  big_issue(c, a2, b2, 2);
-  __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16): tile 0 has landed
+// K tiles [kt0, kend) in groups of 4 ((kend - kt0) % 4 == 0), one stage each
+template <int TM, int TN>
+__device__ __forceinline__ void ring_mainloop4(const RingCtx& c, uint16_t* __restrict__ a0, uint16_t* __restrict__ a1,
+                                               uint16_t* __restrict__ a2, uint16_t* __restrict__ a3,
+                                               uint16_t* __restrict__ b0, uint16_t* __restrict__ b1,
+                                               uint16_t* __restrict__ b2, uint16_t* __restrict__ b3, int kt0,
+                                               int kend, floatx16 (&acc)[TM / 64][TN / 64]) {
+  ring_issue<TM, TN>(c, a0, b0, kt0);
+  ring_issue<TM, TN>(c, a1, b1, kt0 + 1);
+  ring_issue<TM, TN>(c, a2, b2, kt0 + 2);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (TM / 64 + TN / 64)));  // tile kt0 has landed
   ring_barrier();
-  for (int kt = 0; kt < nk; kt += kBigStages) {
-    big_step(c, a0, b0, a3, b3, kt, nk, acc);
-    big_step(c, a1, b1, a0, b0, kt + 1, nk, acc);
-    big_step(c, a2, b2, a1, b1, kt + 2, nk, acc);
-    big_step(c, a3, b3, a2, b2, kt + 3, nk, acc);
+  for (int kt = kt0; kt < kend; kt += 4) {
+    ring_step<TM, TN, 4>(c, a0, b0, a3, b3, kt, kend, acc);
+    ring_step<TM, TN, 4>(c, a1, b1, a0, b0, kt + 1, kend, acc);
+    ring_step<TM, TN, 4>(c, a2, b2, a1, b1, kt + 2, kend, acc);
+    ring_step<TM, TN, 4>(c, a3, b3, a2, b2, kt + 3, kend, acc);
   }
   __builtin_amdgcn_s_waitcnt(0);  // drain the trailing re-fetches before the workgroup ends
 }
 
-__global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_big(
-    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y, int M, int K, int N,
-    int tiles_n, int n_tiles, int per_xcd) {
+// K tiles [kt0, kend) in groups of 8 ((kend - kt0) % 8 == 0), one stage each
+template <int TM, int TN>
+__device__ __forceinline__ void ring_mainloop8(
+    const RingCtx& c, uint16_t* __restrict__ a0, uint16_t* __restrict__ a1, uint16_t* __restrict__ a2,
+    uint16_t* __restrict__ a3, uint16_t* __restrict__ a4, uint16_t* __restrict__ a5, uint16_t* __restrict__ a6,
+    uint16_t* __restrict__ a7, uint16_t* __restrict__ b0, uint16_t* __restrict__ b1, uint16_t* __restrict__ b2,
+    uint16_t* __restrict__ b3, uint16_t* __restrict__ b4, uint16_t* __restrict__ b5, uint16_t* __restrict__ b6,
+    uint16_t* __restrict__ b7, int kt0, int kend, floatx16 (&acc)[TM / 64][TN / 64]) {
+  ring_issue<TM, TN>(c, a0, b0, kt0);
+  ring_issue<TM, TN>(c, a1, b1, kt0 + 1);
+  ring_issue<TM, TN>(c, a2, b2, kt0 + 2);
+  ring_issue<TM, TN>(c, a3, b3, kt0 + 3);
+  ring_issue<TM, TN>(c, a4, b4, kt0 + 4);
+  ring_issue<TM, TN>(c, a5, b5, kt0 + 5);
+  ring_issue<TM, TN>(c, a6, b6, kt0 + 6);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(6 * (TM / 64 + TN / 64)));  // tile kt0 has landed
+  ring_barrier();
+  for (int kt = kt0; kt < kend; kt += 8) {
+    ring_step<TM, TN, 8>(c, a0, b0, a7, b7, kt, kend, acc);
+    ring_step<TM, TN, 8>(c, a1, b1, a0, b0, kt + 1, kend, acc);
+    ring_step<TM, TN, 8>(c, a2, b2, a1, b1, kt + 2, kend, acc);
+    ring_step<TM, TN, 8>(c, a3, b3, a2, b2, kt + 3, kend, acc);
+    ring_step<TM, TN, 8>(c, a4, b4, a3, b3, kt + 4, kend, acc);
+    ring_step<TM, TN, 8>(c, a5, b5, a4, b4, kt + 5, kend, acc);
+    ring_step<TM, TN, 8>(c, a6, b6, a5, b5, kt + 6, kend, acc);
+    ring_step<TM, TN, 8>(c, a7, b7, a6, b6, kt + 7, kend, acc);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // drain the trailing re-fetches before the workgroup ends
+}
+
+// PART: workgroup z covers K tiles [z * kt_per, (z + 1) * kt_per) and
+// stores its fp32 partial tile to part[z][M][N] (summed by finish_part);
+// otherwise the whole K range and a bf16 (RNE) store to Y.
+template <int TM, int TN, bool PART>
+__global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_ring(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y,
+    float* __restrict__ part, int M, int K, int N, int tiles_n, int n_tiles, int per_xcd, int kt_per) {
+  constexpr int MI = TM / 64, NJ = TN / 64;
   const int tid = threadIdx.x, lane = tid & 63;
   const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (t >= n_tiles) return;
-  const int m0 = (t / tiles_n) * GB, n0 = (t % tiles_n) * GB;
-  BigCtx c;
+  // large: row-band major (an XCD's tiles share X rows); split-K medium:
+  // column major, so the few row tiles of a W column block run on one XCD
+  // and W crosses HBM once
+  const int tiles_m = n_tiles / tiles_n;
+  const int m0 = (PART ? t % tiles_m : t / tiles_n) * TM, n0 = (PART ? t / tiles_m : t % tiles_n) * TN;
+  RingCtx c;
   c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: DMA offsets stay scalar
   c.fr = lane & 31;
   c.fk = lane >> 5;
   c.wm = c.wave >> 1;
   c.wn = c.wave & 1;
   c.row_bytes = K * 2;
-  // X rows m0.. and W rows n0..; loads past the end of either return zeros
   c.rsa = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X + (size_t)m0 * K), (short)0,
                                             (M - m0) * c.row_bytes, 0x00020000);
   c.rsb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(W + (size_t)n0 * K), (short)0,
@@ -623,26 +700,38 @@ __global__ __launch_bounds__(kBigThreads) __attribute__((amdgpu_waves_per_eu(1, 
   // L & 3), which holds logical chunk (L & 3) ^ ((row >> 2) & 3)
   c.voff = (lane >> 2) * c.row_bytes + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
 
-  floatx16 acc[4][4];
+  floatx16 acc[MI][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  big_mainloop(c, big_a0, big_a1, big_a2, big_a3, big_b0, big_b1, big_b2, big_b3, K / GBK, acc);
+  const int kt0 = PART ? blockIdx.y * kt_per : 0;
+  const int kend = PART ? kt0 + kt_per : K / GBK;
+  if (TM == 256)
+    ring_mainloop4<TM, TN>(c, big_a0, big_a1, big_a2, big_a3, big_b0, big_b1, big_b2, big_b3, kt0, kend, acc);
+  else
+    ring_mainloop8<TM, TN>(c, mid_a0, mid_a1, mid_a2, mid_a3, mid_a4, mid_a5, mid_a6, mid_a7, mid_b0, mid_b1, mid_b2,
+                           mid_b3, mid_b4, mid_b5, mid_b6, mid_b7, kt0, kend, acc);
 
+  // C layout of a 32x32 tile: lane l holds column l%32, rows 8*(v/4) + 4*(l/32) + v%4
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + c.wn * 128 + j * 32 + (lane & 31);
+    for (int j = 0; j < NJ; ++j) {
+      const int col = n0 + c.wn * (TN / 2) + j * 32 + (lane & 31);
       if (col >= N) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int r = m0 + c.wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (r < M) Y[(size_t)r * N + col] = (uint16_t)f2bf(acc[i][j][v]);
+        const int r = m0 + c.wm * (TM / 2) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (r < M) {
+          if (PART)
+            part[((size_t)blockIdx.y * M + r) * N + col] = acc[i][j][v];
+          else
+            Y[(size_t)r * N + col] = (uint16_t)f2bf(acc[i][j][v]);
+        }
       }
     }
 }
@@ -688,11 +777,11 @@ bool big_gemm_enabled() {
 }
 
 hipError_t launch_big(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N, hipStream_t st) {
-  const int tiles_m = (M + GB - 1) / GB, tiles_n = (N + GB - 1) / GB;
+  const int tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
   const int n_tiles = tiles_m * tiles_n;
   const int per_xcd = (n_tiles + 7) / 8;
-  MLORA_LAUNCH("gemm_big", gemm_big, dim3(per_xcd * 8), dim3(kBigThreads), 0, st, X, W, Y, M, K, N, tiles_n, n_tiles,
-                     per_xcd);
+  MLORA_LAUNCH("gemm_big", (gemm_ring<256, 256, false>), dim3(per_xcd * 8), dim3(kRingThreads), 0, st, X, W, Y,
+               (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0);
   return launched();
 }
 
@@ -708,7 +797,7 @@ hipError_t launch_gemm(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M,
     const dim3 grid((N + 31) / 32, (M + 32 * KS_MB - 1) / (32 * KS_MB)), block(64 * kKsWaves);
     MLORA_LAUNCH("gemm_ksplit", (gemm_ksplit<VEC, false>), grid, block, 0, st, X, W, Y, M, K, N, PoolView{}, 0, nullptr,
                        nullptr);
-  } else if (VEC && K % (GBK * kBigStages) == 0 && (long)M * N >= 2048L * 2048L && (long)M * K * 2 < (1L << 31) &&
+  } else if (VEC && K % (GBK * kRingStages) == 0 && (long)M * N >= 2048L * 2048L && (long)M * K * 2 < (1L << 31) &&
              (long)N * K * 2 < (1L << 31) && big_gemm_enabled()) {
     return launch_big(X, W, Y, M, K, N, st);
   } else {
@@ -1004,18 +1093,21 @@ hipError_t launch_decode(const uint16_t* X, const uint16_t* W, uint16_t* Y, int 
 // medium batches: 128x128 tiles with split-K over S workgroups, then the
 // finish pass (partials + low-rank term)
 int mid_split(int M, int N, int K) {
-  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
   int S = 1;
-  while (S < kMidMaxSplit && tiles * S < 256 && K % (BK * S * 2) == 0) S *= 2;
+  while (S < kMidMaxSplit && tiles * S < 256 && K % (GBK * kMidStages * S * 2) == 0) S *= 2;
   return S;
 }
+
+bool mid_ring_ok(int M, int K) { return K % (GBK * kMidStages) == 0 && (long)M * K * 2 < (1L << 31); }
 
 hipError_t launch_mid_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N, const PoolView& pv,
                            int proj, const int32_t* row_key, const float* T, float* part, hipStream_t st) {
   const int S = mid_split(M, N, K);
-  const int kt_per = K / BK / S;
-  const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM, S), block(kTiledThreads);
-  MLORA_LAUNCH("gemm_mid", (gemm_tiled<true, true>), grid, block, 0, st, X, W, Y, M, K, N, part, kt_per);
+  const int tiles_n = (N + 127) / 128, n_tiles = ((M + 127) / 128) * tiles_n;
+  const int per_xcd = (n_tiles + 7) / 8;
+  MLORA_LAUNCH("gemm_mid", (gemm_ring<128, 128, true>), dim3(per_xcd * 8, S), dim3(kRingThreads), 0, st, X, W, Y,
+               part, M, K, N, tiles_n, n_tiles, per_xcd, K / GBK / S);
   hipError_t e = launched();
   if (e != hipSuccess) return e;
   const int threads = M * (N / 8);
@@ -1071,7 +1163,7 @@ hipError_t launch_gemm_lora(const PoolView& pv, int proj, const uint16_t* X, con
     hipError_t e = launch_shrink_rows(pv, proj, X, ws, M, T, stream);
     if (e != hipSuccess) return e;
   }
-  if (M > 64 && vec && K % BK == 0 && mid_enabled())
+  if (M > 64 && vec && mid_ring_ok(M, K) && (long)N * K * 2 < (1L << 31) && mid_enabled())
     return launch_mid_lora(X, W, Y, M, K, N, pv, proj, row_key, T, part, stream);
   return vec ? launch_lora<true>(X, W, Y, M, K, N, pv, proj, row_key, T, stream)
              : launch_lora<false>(X, W, Y, M, K, N, pv, proj, row_key, T, stream);
