@@ -4,9 +4,11 @@
 // base-only rows, then rows with an invalid id), keeping the original order
 // inside each key, which yields the group order and write-back rows of the
 // M031 card's worked example (sections 02-03: P, R, Q; A's result to rows 0
-// and 2, B's to row 1).  The whole batch is handled by one 1024-thread
-// workgroup in LDS: an LSD radix sort on 8-bit digits of the key (one pass
-// when every key fits in 8 bits, two otherwise).  Each pass is stable by
+// and 2, B's to row 1).  The whole batch is handled by one workgroup in LDS.
+// Up to 256 rows, each row's place is counted directly: the number of
+// smaller (key, row) pairs, all of which are distinct.  Larger batches take
+// an LSD radix sort on 8-bit digits of the key (one pass when every key fits
+// in 8 bits, two otherwise).  Each radix pass is stable by
 // construction: every wave owns a contiguous range of entries, per-(digit,
 // wave) counts are scanned digit-major, and inside a 64-entry slice a lane's
 // place among equal digits is the popcount of the lower lanes holding the
@@ -105,11 +107,29 @@ __global__ __launch_bounds__(NT) void seg_build_kernel(const int32_t* __restrict
   if (my_status) atomicOr(&s_cnt[2], my_status);
   __syncthreads();
 
-  // 2. stable LSD radix passes over the key's 8-bit digits
-  const int per = (((n + kWaves - 1) / kWaves) + 63) & ~63;
-  const int beg = min(n, wave * per), end = min(n, wave * per + per);
+  // 2. stable sort of the packed (key, row) values, which are all distinct.
+  // passes == 0 (at most one row per thread, up to 256 rows): a row's sorted
+  // position is the number of smaller packed values.  Each wave reads 64 of
+  // them at a time (one per lane) and broadcasts them lane by lane from
+  // registers, so a comparison costs no LDS access.  Otherwise stable LSD
+  // radix passes over the key's 8-bit digits.
   uint32_t* src = bufA;
   uint32_t* dst = bufB;
+  if (passes == 0) {
+    const uint32_t me = tid < n ? bufA[tid] : 0xffffffffu;
+    int pos = 0;
+    for (int base = 0; base < n; base += 64) {
+      const uint32_t other = base + lane < n ? bufA[base + lane] : 0xffffffffu;  // above every packed value
+#pragma unroll 16
+      for (int l = 0; l < 64; ++l) pos += (int)(__builtin_amdgcn_readlane(other, l) < me);
+    }
+    if (tid < n) bufB[pos] = me;
+    __syncthreads();
+    src = bufB;
+    dst = bufA;
+  }
+  const int per = (((n + kWaves - 1) / kWaves) + 63) & ~63;
+  const int beg = min(n, wave * per), end = min(n, wave * per + per);
   for (int pass = 0; pass < passes; ++pass) {
     const int shift = 16 + 8 * pass;
     for (int i = tid; i < kRadix * kWaves; i += kThreads) hist[i] = 0;
@@ -368,7 +388,7 @@ hipError_t launch_nt(const int32_t* row_adapter, int n, const int32_t* pool_rank
         (void)hipGetLastError();
     }
   }
-  const int passes = (max_adapters + 1 < 256) ? 1 : 2;
+  const int passes = n <= NT ? 0 : ((max_adapters + 1 < 256) ? 1 : 2);
   MLORA_LAUNCH("seg_build", seg_build_kernel<NT>, dim3(1), dim3(NT), lds, stream, row_adapter, n, pool_rank, max_adapters,
                      passes, cap, ws);
   return launched();
