@@ -43,7 +43,8 @@ KERNEL_SOURCES = {"seg_build": "seg_build.hip", "gemm_skinny": "base_gemm.hip", 
                   "gemm_decode+shrink_rows": "base_gemm.hip", "finish_part": "base_gemm.hip",
                   "gemm_mid": "base_gemm.hip", "gemm_skinny_lora": "base_gemm.hip",
                   "gemm_ksplit_lora": "base_gemm.hip", "shrink": "lora_branch.hip", "expand": "lora_branch.hip",
-                  "fused": "lora_branch.hip", "shrink_rows": "lora_branch.hip"}
+                  "fused": "lora_branch.hip", "shrink_rows": "lora_branch.hip", "shrink_tiles": "lora_branch.hip",
+                  "gemm_big_lora": "base_gemm.hip", "lora_prep": "lora_branch.hip"}
 DEFAULT_WORKLOAD = "decode_3"
 
 
@@ -98,7 +99,11 @@ def algorithmic(w, chunks):
         "gemm_decode": split_dense, "gemm_mid": split_dense,
         "gemm_decode+shrink_rows": (split_dense[0] + shrink_rows[0], split_dense[1] + shrink_rows[1]),
         "finish_part": finish,
-        "gemm_skinny_lora": gemm_lora, "gemm_ksplit_lora": gemm_lora,
+        "gemm_skinny_lora": gemm_lora, "gemm_ksplit_lora": gemm_lora, "gemm_big_lora": gemm_lora,
+        # the epilogue's operands: chunk partials in, bf16 t per row out; Up
+        # pages in, the same Up with ranks contiguous out
+        "lora_prep": (4 * sum_nr * max(chunks, 1) + 2 * sum_nr + 4 * sum_r * dout, sum_nr * max(chunks, 1)),
+        "shrink_tiles": (2 * sum_r * din + 2 * n_act * din + 4 * sum_nr * max(chunks, 1), 2 * sum_nr * din),
     }
     for k in ("gemm_skinny", "gemm_ksplit", "gemm_tiled", "gemm_big"):
         out[k] = base
@@ -106,7 +111,7 @@ def algorithmic(w, chunks):
 
 
 DENSE = ("gemm_skinny", "gemm_ksplit", "gemm_tiled", "gemm_big", "gemm_decode", "gemm_mid",
-         "gemm_decode+shrink_rows", "gemm_skinny_lora", "gemm_ksplit_lora")
+         "gemm_decode+shrink_rows", "gemm_skinny_lora", "gemm_ksplit_lora", "gemm_big_lora")
 
 
 def source_hash(kernel):

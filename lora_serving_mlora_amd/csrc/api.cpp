@@ -619,6 +619,22 @@ mlora_status mlora_gemm_lora(const mlora_pool* p, int32_t proj, const uint16_t* 
 namespace {
 // din slices for the split variant: enough waves to spread a small batch
 // over the chip, never more than kMaxSplitChunks
+// the large-batch epilogue's operands (t per row in bf16, adapter offsets,
+// Up blocks with ranks contiguous)
+size_t lora_operands_bytes(const mlora_pool* p, int n) {
+  const int wt = mlora::t_rows_width(p->d.max_rank);
+  return align256((size_t)n * wt * 2) + align256((size_t)p->d.max_adapters * 4) +
+         align256(mlora::lora_upt_bytes(n, p->d.max_adapters, p->d.max_rank, p->d.dout));
+}
+// The GEMM epilogue takes the low-rank term of batches with at most 256
+// adapters (one prep block per adapter and column chunk) whose operands
+// stay within 256 MiB; others take the separate expand.
+constexpr size_t kMaxEpilogueBytes = 256u << 20;
+bool big_epilogue_fits(const mlora_pool* p, int n) {
+  return std::min(n, p->d.max_adapters) <= 256 && lora_operands_bytes(p, n) <= kMaxEpilogueBytes &&
+         (size_t)p->d.n_up_pages * p->d.dout < (1u << 31);
+}
+
 int split_chunks(const mlora_pool* p, int n) {
   const int din = p->d.din;
   int c;
@@ -646,7 +662,10 @@ size_t mlora_work_bytes(const mlora_pool* p, int32_t n) {
   if (!p || n < 0) return 0;
   // the larger of the split variant's partial t and the per-row path's layout
   const int chunks = std::max(split_chunks(p, n), 1);
+  // split: the shrink's partial t, then t per row for a GEMM that adds the
+  // low-rank term in its epilogue (large batches)
   size_t b = align256((size_t)chunks * n * p->d.max_rank * sizeof(float));
+  if (big_epilogue_fits(p, n)) b += lora_operands_bytes(p, n);
   if (n <= kRowsMax) b = std::max(b, rows_work_bytes(p, n));
   return b;
 }
@@ -690,6 +709,25 @@ mlora_status mlora_apply(const mlora_pool* p, int32_t proj, const uint16_t* X, c
     const RowsWork w = rows_work(p, n, work);
     return hip_check(mlora::launch_gemm_lora(v, proj, X, W0, ws, w.T, w.part, Y, n, true, s),
                      "per-row shrink + GEMM + expand launch");
+  }
+  if (variant == MLORA_VARIANT_SPLIT && big_epilogue_fits(p, n) && mlora::big_lora_ok(v, X, W0, n)) {
+    // large batch: shrink, the epilogue's operands, then one GEMM that adds
+    // the low-rank term in its epilogue (Y written once)
+    const int chunks = split_chunks(p, n);
+    float* T = static_cast<float*>(work);
+    char* w = static_cast<char*>(work) + align256((size_t)chunks * n * d.max_rank * sizeof(float));
+    const int wt = mlora::t_rows_width(d.max_rank);
+    uint16_t* tb = reinterpret_cast<uint16_t*>(w);
+    w += align256((size_t)n * wt * 2);
+    int32_t* koff = reinterpret_cast<int32_t*>(w);
+    w += align256((size_t)d.max_adapters * 4);
+    uint16_t* upt = reinterpret_cast<uint16_t*>(w);
+    st = hip_check(mlora::launch_shrink(v, proj, X, ws, n, T, chunks, chunk_elems_for(d.din, chunks), s), "shrink launch");
+    if (st != MLORA_OK) return st;
+    st = hip_check(mlora::launch_lora_prep(v, proj, ws, n, T, chunks, tb, wt, koff, upt, s), "low-rank operand launch");
+    if (st != MLORA_OK) return st;
+    const mlora::LoraOperands lo{tb, koff, upt, wt};
+    return hip_check(mlora::launch_big_lora(v, X, W0, ws, lo, Y, n, s), "GEMM + low-rank epilogue launch");
   }
   st = hip_check(mlora::launch_base_gemm(X, W0, Y, n, d.din, d.dout, s), "base GEMM launch");
   if (st != MLORA_OK) return st;

@@ -669,13 +669,140 @@ __device__ __forceinline__ void ring_mainloop8(
   __builtin_amdgcn_s_waitcnt(0);  // drain the trailing re-fetches before the workgroup ends
 }
 
-// PART: workgroup z covers K tiles [z * kt_per, (z + 1) * kt_per) and
-// stores its fp32 partial tile to part[z][M][N] (summed by finish_part);
-// otherwise the whole K range and a bf16 (RNE) store to Y.
-template <int TM, int TN, bool PART>
+// The low-rank term added in the GEMM's registers (prefill): for every row
+// of the tile on a resident adapter a, acc[row][col] += sum_q t[row][q] *
+// Up_a[col][q].  Rows of one tile carry different adapters, so each wave
+// walks the distinct adapters among its own rows (smallest first, a wave
+// min-reduction per step) and, per 16 ranks, runs one more 32x32x16 MFMA
+// step per accumulator with A = t of the rows on that adapter (zero for the
+// others) and B = the adapter's Up columns.  Both operands are prepared per
+// batch in MFMA-friendly form (lora_prep): t as bf16 [M][wt] per original
+// row, Up as a [dout][r_pad] block per adapter (ranks contiguous), so each
+// fragment is one 16-byte load.  The expand then costs a few percent more
+// MFMA work instead of a read-modify-write of all of Y.
+// A uniform read of pool metadata that the kernel never writes, through the
+// constant address space, so it becomes a scalar load (it does not wait on
+// the vector loads in flight).
+__device__ __forceinline__ int32_t uniform_load(const int32_t* p, size_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void ring_lora_epilogue(const RingCtx& c, int m0, int n0, int M, int N, const PoolView& pv,
+                                                   const int32_t* __restrict__ row_key, const LoraOperands& lo,
+                                                   floatx16 (&acc)[TM / 64][TN / 64], int (&key)[TM / 64]) {
+  constexpr int MI = TM / 64, NJ = TN / 64;
+  // kBad: the pseudo adapter of rows with an invalid id, walked after the
+  // real ones; its step multiplies NaN into those rows' accumulators
+  constexpr int kNone = 0x7fffffff, kBad = 0x7ffffffe, kBatch = 4;
+  const int lane = threadIdx.x & 63, half = lane >> 5;
+  int pend[MI];
+  int trow[MI];  // element offset of the lane's t piece (rows past M read row M-1: never stored)
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int r = m0 + c.wm * (TM / 2) + i * 32 + (lane & 31);
+    key[i] = r < M ? row_key[r] : -1;
+    if (key[i] == -2) key[i] = kBad;
+    pend[i] = (key[i] >= 0) ? key[i] : kNone;
+    trow[i] = min(r, M - 1) * lo.wt + 8 * half;
+  }
+  int col[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) col[j] = min(n0 + c.wn * (TN / 2) + j * 32 + (lane & 31), N - 1);
+  // the wave's next adapter (smallest pending key), taken off the pending set
+  auto next_key = [&]() {
+    int a = pend[0];
+#pragma unroll
+    for (int i = 1; i < MI; ++i) a = min(a, pend[i]);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) a = min(a, __shfl_xor(a, m, 64));
+    a = __builtin_amdgcn_readfirstlane(a);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) pend[i] = pend[i] == a ? kNone : pend[i];
+    return a;
+  };
+  int a = next_key(), rank = 0, koff = 0, q0 = 0;
+  auto adapter_meta = [&]() {
+    if (a == kBad) {
+      rank = 16;  // one step, no memory of its own
+      koff = 0;
+    } else if (a != kNone) {
+      rank = uniform_load(pv.rank, a);
+      koff = uniform_load(lo.koff, a);
+    }
+  };
+  adapter_meta();
+  // Steps (adapter, 16 ranks) in batches of kBatch: all loads of a batch go
+  // out together, then its MFMAs run.  A batch is always full: slots past
+  // the last step load valid addresses and are zeroed (branch-free), so the
+  // loads of the whole batch can be issued back to back.  (One flat loop: a
+  // nested loop made the register allocator move the accumulators out of
+  // the AGPRs.)
+  while (a != kNone) {
+    int sa[kBatch], sq[kBatch], sb[kBatch], sr[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      sa[k] = a;  // kNone for an empty slot: matches no row
+      sq[k] = 0;
+      sb[k] = 0;
+      sr[k] = 16;
+      if (a != kNone) {
+        const int rp = (rank + 15) & ~15;
+        sq[k] = q0;
+        sr[k] = rp;
+        sb[k] = koff * N + q0;  // element offset of (col 0, rank q0) in the adapter's block
+        q0 += 16;
+        if (q0 >= rank) {
+          a = next_key();
+          q0 = 0;
+          adapter_meta();
+        }
+      }
+    }
+    uint4 fa[kBatch][MI], fb[kBatch][NJ];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i) fa[k][i] = *reinterpret_cast<const uint4*>(lo.tb + trow[i] + sq[k]);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        fb[k][j] = *reinterpret_cast<const uint4*>(lo.upt + sb[k] + col[j] * sr[k] + 8 * half);
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      // A = t of the rows on this step's adapter, zero for the others (NaN
+      // for the invalid rows' step); B of an empty or invalid-row slot is
+      // zeroed (its memory may hold anything; NaN times zero stays NaN)
+      const bool bad = sa[k] == kBad;
+      const uint32_t live = (sa[k] != kNone && !bad) ? 0xffffffffu : 0u;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const uint32_t m = key[i] == sa[k] ? 0xffffffffu : 0u;
+        const uint32_t nan = bad ? 0x7fc07fc0u : 0u;
+        fa[k][i] = make_uint4(((fa[k][i].x & live) | nan) & m, ((fa[k][i].y & live) | nan) & m,
+                              ((fa[k][i].z & live) | nan) & m, ((fa[k][i].w & live) | nan) & m);
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        fb[k][j] = make_uint4(fb[k][j].x & live, fb[k][j].y & live, fb[k][j].z & live, fb[k][j].w & live);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[k][i]), as_bf16x8(fb[k][j]), acc[i][j],
+                                                              0, 0, 0);
+    }
+  }
+}
+
+// LORA (whole-K form only): the low-rank term of every row is added in the
+// epilogue (ring_lora_epilogue) and rows with an invalid id become NaN.
+template <int TM, int TN, bool PART, bool LORA>
 __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_ring(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y,
-    float* __restrict__ part, int M, int K, int N, int tiles_n, int n_tiles, int per_xcd, int kt_per) {
+    float* __restrict__ part, int M, int K, int N, int tiles_n, int n_tiles, int per_xcd, int kt_per, PoolView pv,
+    const int32_t* __restrict__ row_key, LoraOperands lo) {
+  static_assert(!(PART && LORA), "the low-rank epilogue needs the whole K range");
   constexpr int MI = TM / 64, NJ = TN / 64;
   const int tid = threadIdx.x, lane = tid & 63;
   const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
@@ -716,17 +843,22 @@ __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(1,
     ring_mainloop8<TM, TN>(c, mid_a0, mid_a1, mid_a2, mid_a3, mid_a4, mid_a5, mid_a6, mid_a7, mid_b0, mid_b1, mid_b2,
                            mid_b3, mid_b4, mid_b5, mid_b6, mid_b7, kt0, kend, acc);
 
+  int key[MI];  // low-rank epilogue: the keys of the lane's A-fragment rows
+  if (LORA) {
+    __builtin_amdgcn_sched_barrier(0);
+    ring_lora_epilogue<TM, TN>(c, m0, n0, M, N, pv, row_key, lo, acc, key);
+  }
+
   // C layout of a 32x32 tile: lane l holds column l%32, rows 8*(v/4) + 4*(l/32) + v%4
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int col = n0 + c.wn * (TN / 2) + j * 32 + (lane & 31);
-      if (col >= N) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = m0 + c.wm * (TM / 2) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (r < M) {
+        if (r < M && col < N) {
           if (PART)
             part[((size_t)blockIdx.y * M + r) * N + col] = acc[i][j][v];
           else
@@ -780,8 +912,9 @@ hipError_t launch_big(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, 
   const int tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
   const int n_tiles = tiles_m * tiles_n;
   const int per_xcd = (n_tiles + 7) / 8;
-  MLORA_LAUNCH("gemm_big", (gemm_ring<256, 256, false>), dim3(per_xcd * 8), dim3(kRingThreads), 0, st, X, W, Y,
-               (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0);
+  MLORA_LAUNCH("gemm_big", (gemm_ring<256, 256, false, false>), dim3(per_xcd * 8), dim3(kRingThreads), 0, st, X, W,
+               Y, (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, PoolView{}, (const int32_t*)nullptr,
+               LoraOperands{});
   return launched();
 }
 
@@ -1106,8 +1239,9 @@ hipError_t launch_mid_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, in
   const int S = mid_split(M, N, K);
   const int tiles_n = (N + 127) / 128, n_tiles = ((M + 127) / 128) * tiles_n;
   const int per_xcd = (n_tiles + 7) / 8;
-  MLORA_LAUNCH("gemm_mid", (gemm_ring<128, 128, true>), dim3(per_xcd * 8, S), dim3(kRingThreads), 0, st, X, W, Y,
-               part, M, K, N, tiles_n, n_tiles, per_xcd, K / GBK / S);
+  MLORA_LAUNCH("gemm_mid", (gemm_ring<128, 128, true, false>), dim3(per_xcd * 8, S), dim3(kRingThreads), 0, st, X,
+               W, Y, part, M, K, N, tiles_n, n_tiles, per_xcd, K / GBK / S, PoolView{}, (const int32_t*)nullptr,
+               LoraOperands{});
   hipError_t e = launched();
   if (e != hipSuccess) return e;
   const int threads = M * (N / 8);
@@ -1171,6 +1305,35 @@ hipError_t launch_gemm_lora(const PoolView& pv, int proj, const uint16_t* X, con
 
 size_t gemm_lora_part_floats(int M, int N, int K) {
   return (size_t)(M > 64 ? mid_split(M, N, K) : kDecSplit) * M * N;
+}
+
+// MLORA_BIG_EPILOGUE=0 keeps large batches on base GEMM + separate expand (A/B timing)
+bool big_epilogue_enabled() {
+  static int on = -1;
+  if (on < 0) {
+    const char* e = getenv("MLORA_BIG_EPILOGUE");
+    on = (e && e[0] == '0') ? 0 : 1;
+  }
+  return on == 1;
+}
+
+bool big_lora_ok(const PoolView& pv, const uint16_t* X, const uint16_t* W, int M) {
+  if (!big_epilogue_enabled()) return false;
+  const int K = pv.din, N = pv.dout;
+  const bool vec = (K % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(W)) % 16 == 0);
+  return vec && K % (GBK * kRingStages) == 0 && (long)M * N >= 2048L * 2048L && (long)M * K * 2 < (1L << 31) &&
+         (long)N * K * 2 < (1L << 31) && big_gemm_enabled();
+}
+
+hipError_t launch_big_lora(const PoolView& pv, const uint16_t* X, const uint16_t* W, const int32_t* ws,
+                           const LoraOperands& lo, uint16_t* Y, int M, hipStream_t st) {
+  const int K = pv.din, N = pv.dout;
+  const int tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
+  const int n_tiles = tiles_m * tiles_n;
+  const int per_xcd = (n_tiles + 7) / 8;
+  MLORA_LAUNCH("gemm_big_lora", (gemm_ring<256, 256, false, true>), dim3(per_xcd * 8), dim3(kRingThreads), 0, st, X,
+               W, Y, (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, pv, ws + MLORA_SEG_ROWKEY(M), lo);
+  return launched();
 }
 
 hipError_t launch_base_gemm(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N,

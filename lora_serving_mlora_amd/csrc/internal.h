@@ -30,6 +30,14 @@ __device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w <<
 __device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ uint32_t pack_bf2(float a, float b) { return f2bf(a) | (f2bf(b) << 16); }
 
+// the same rounding (RNE) by the gfx950 conversion instruction
+// (v_cvt_pk_bf16_f32), branch-free: for MFMA operands built in registers
+__device__ __forceinline__ uint32_t pack_bf2_hw(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // Eight consecutive bf16 of row `p` starting at element `i`, as floats.
 // VEC: the row base and i are 16-byte aligned and i + 8 <= limit, so one
 // 16-byte load serves; otherwise element loads, zero past `limit`.
@@ -80,6 +88,39 @@ size_t gemm_lora_part_floats(int M, int N, int K);
 
 hipError_t launch_shrink_rows(const PoolView& pv, int proj, const uint16_t* X, const int32_t* ws, int n, float* T,
                               hipStream_t stream);
+
+// Operands of the large-batch GEMM's low-rank epilogue, prepared per batch
+// and projection by launch_lora_prep from the shrink's slices and the pool:
+//   tb   bf16 [M][wt]: s_a * t per original row (ranks past the adapter's
+//        are zero; rows not on a resident adapter are not written),
+//   koff int32 [max_adapters]: for each adapter of the batch, the first
+//        rank row of its block in upt (other entries are not written),
+//   upt  bf16: per adapter a block [dout][r_pad(a)] at element koff[a] * dout
+//        (Up with ranks contiguous, r_pad = rank rounded up to 16, zeros
+//        past the rank).
+struct LoraOperands {
+  const uint16_t* tb;
+  const int32_t* koff;
+  const uint16_t* upt;
+  int wt;
+};
+inline int t_rows_width(int max_rank) { return (max_rank + 15) / 16 * 16; }
+// Bytes of upt for a batch of n rows: every adapter of the batch padded to
+// the largest rank.
+inline size_t lora_upt_bytes(int n, int max_adapters, int max_rank, int dout) {
+  return (size_t)(n < max_adapters ? n : max_adapters) * t_rows_width(max_rank) * dout * 2;
+}
+
+// Large batches: Y = X W^T plus every row's low-rank term, added in the
+// 256x256 GEMM's epilogue (no read-modify-write of Y); invalid rows become
+// NaN.  big_lora_ok: the shapes and pointers this kernel takes.
+bool big_lora_ok(const PoolView& pv, const uint16_t* X, const uint16_t* W, int M);
+hipError_t launch_big_lora(const PoolView& pv, const uint16_t* X, const uint16_t* W, const int32_t* ws,
+                           const LoraOperands& lo, uint16_t* Y, int M, hipStream_t stream);
+// Writes tb, koff and upt (see LoraOperands) from the shrink's slices Ts
+// [n_chunks][n][max_rank] (sorted positions; t = sum over slices in order).
+hipError_t launch_lora_prep(const PoolView& pv, int proj, const int32_t* ws, int n, const float* Ts, int n_chunks,
+                            uint16_t* tb, int wt, int32_t* koff, uint16_t* upt, hipStream_t stream);
 
 hipError_t launch_shrink(const PoolView& pv, int proj, const uint16_t* X, const int32_t* ws, int n,
                          float* T, int n_chunks, int chunk_elems, hipStream_t stream);

@@ -243,18 +243,72 @@ __global__ __launch_bounds__(64) void expand_kernel(PoolView pv, int proj, const
 }
 
 // ---------------------------------------------------------------------------
-// fused: one 512-thread workgroup per item
+// fused: one 512-thread workgroup per item.  The shrink runs one row of the
+// item at a time with the per-row body (8 waves over din, 16 ranks per
+// reduction group: few live registers, so nothing spills), the scaled t of
+// the item's rows stays in LDS, then the expand runs over all of dout.
 // ---------------------------------------------------------------------------
-constexpr int kFusedWaves = 8;
-constexpr int kFusedThreads = 64 * kFusedWaves;
+constexpr int kFusedThreads = kRowThreads;
+
+// The first expand pass of a thread (columns c..c+8, ranks below G) with its
+// Up pieces already in registers (bf16 pairs as loaded); later rank groups
+// are loaded here.  Then read-modify-write of Y, as expand_cols.
+__device__ __forceinline__ void expand_cols_pre(const PoolView& pv, const int32_t* __restrict__ upage, int rank,
+                                                const float (*ts)[MLORA_MAX_RANK], const int32_t* __restrict__ perm,
+                                                int j0, int nr, int c, const uint4 (&u0)[G],
+                                                uint16_t* __restrict__ Y) {
+  const int dout = pv.dout;
+  float acc[R][8];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
+#pragma unroll
+  for (int q = 0; q < G; ++q) {
+    const uint32_t w[4] = {u0[q].x, u0[q].y, u0[q].z, u0[q].w};
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const float t = ts[i][q];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        acc[i][2 * h] = fmaf(t, lo_bf(w[h]), acc[i][2 * h]);
+        acc[i][2 * h + 1] = fmaf(t, hi_bf(w[h]), acc[i][2 * h + 1]);
+      }
+    }
+  }
+  for (int g0 = G; g0 < rank; g0 += G) {
+    float u[G][8];
+#pragma unroll
+    for (int q = 0; q < G; ++q) load8<true>(pv.up + (size_t)upage[min(g0 + q, rank - 1)] * dout, c, dout, u[q]);
+#pragma unroll
+    for (int q = 0; q < G; ++q)
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const float t = ts[i][g0 + q];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[i][e] = fmaf(t, u[q][e], acc[i][e]);
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    if (i >= nr) continue;
+    uint16_t* y = Y + (size_t)perm[j0 + i] * dout;
+    const uint4 o = *reinterpret_cast<const uint4*>(y + c);
+    uint4 w;
+    w.x = pack_bf2(lo_bf(o.x) + acc[i][0], hi_bf(o.x) + acc[i][1]);
+    w.y = pack_bf2(lo_bf(o.y) + acc[i][2], hi_bf(o.y) + acc[i][3]);
+    w.z = pack_bf2(lo_bf(o.z) + acc[i][4], hi_bf(o.z) + acc[i][5]);
+    w.w = pack_bf2(lo_bf(o.w) + acc[i][6], hi_bf(o.w) + acc[i][7]);
+    *reinterpret_cast<uint4*>(y + c) = w;
+  }
+}
 
 template <bool VEC>
 __global__ __launch_bounds__(kFusedThreads) void fused_kernel(PoolView pv, int proj, const uint16_t* __restrict__ X,
                                                               const int32_t* __restrict__ ws,
                                                               uint16_t* __restrict__ Y, int n) {
-  __shared__ float red[kFusedWaves][64];
   __shared__ float ts[R][MLORA_MAX_RANK];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int n_items = ws[MLORA_SEG_NITEMS];
   const int n_bad = ws[MLORA_SEG_NBAD];
   const int32_t* perm = ws + MLORA_SEG_PERM(n);
@@ -262,30 +316,36 @@ __global__ __launch_bounds__(kFusedThreads) void fused_kernel(PoolView pv, int p
     if (it < n_items) {
       const Item m = load_item(pv, ws, n, it);
       const size_t pt = ((size_t)m.adapter * pv.n_proj + proj) * pv.max_rank;
-      const int32_t* dpage = pv.down_page + pt;
       const int32_t* upage = pv.up_page + pt;
-      for (int g0 = 0; g0 < m.rank; g0 += G) {
-        float acc[64];
+      const int rpad = (m.rank + G - 1) / G * G;
+      // VEC: the Up pieces of this thread's first columns and first 16 ranks
+      // do not depend on t, so they are fetched before the shrink and arrive
+      // while it runs (pages past the rank fall back to the first one and
+      // weigh zero)
+      const int c0 = tid * 8;
+      uint4 u0[G];
+      if (VEC && c0 < pv.dout) {
+        int pg[G];
 #pragma unroll
-        for (int v = 0; v < 64; ++v) acc[v] = 0.f;
-        for (int k = tid * 8; k < pv.din; k += kFusedThreads * 8) {
-          float x[R][8];
-          load_rows<VEC>(X, perm, pv.din, m.j0, m.nr, k, x);
-          shrink_step<VEC>(pv, dpage, g0, m.rank, x, k, acc);
-        }
-        red[wave][lane] = wave_reduce_scatter64(acc);
-        __syncthreads();
-        if (tid < 64) {
-          float s = red[0][tid];
+        for (int q = 0; q < G; ++q) pg[q] = upage[min(q, pv.max_rank - 1)];
 #pragma unroll
-          for (int w = 1; w < kFusedWaves; ++w) s += red[w][tid];
-          const int i = tid / G, q = g0 + tid % G;
-          ts[i][q] = (q < m.rank) ? m.scale * s : 0.f;
-        }
-        __syncthreads();
+        for (int q = 1; q < G; ++q) pg[q] = pg[q] < 0 ? pg[0] : pg[q];
+#pragma unroll
+        for (int q = 0; q < G; ++q) u0[q] = *reinterpret_cast<const uint4*>(pv.up + (size_t)pg[q] * pv.dout + c0);
       }
-      for (int c = tid * 8; c < pv.dout; c += kFusedThreads * 8)
-        expand_cols<VEC>(pv, upage, m.rank, ts, perm, m.j0, m.nr, c, Y);
+      for (int i = 0; i < R; ++i) {
+        if (i < m.nr)
+          shrink_row_to<VEC>(pv, pv.down_page + pt, m.rank, m.scale, X + (size_t)perm[m.j0 + i] * pv.din, ts[i]);
+        // zeros past the rank up to the group size the expand walks
+        for (int q = m.rank + tid; q < rpad; q += kFusedThreads) ts[i][q] = 0.f;
+      }
+      __syncthreads();
+      int c = c0;
+      if (VEC && c < pv.dout) {
+        expand_cols_pre(pv, upage, m.rank, ts, perm, m.j0, m.nr, c, u0, Y);
+        c += kFusedThreads * 8;
+      }
+      for (; c < pv.dout; c += kFusedThreads * 8) expand_cols<VEC>(pv, upage, m.rank, ts, perm, m.j0, m.nr, c, Y);
       __syncthreads();
     } else {
       uint16_t* y = Y + (size_t)perm[n - n_bad + (it - n_items)] * pv.dout;
@@ -465,6 +525,95 @@ __global__ __launch_bounds__(64 * kTileWaves) void shrink_tiles_kernel(PoolView 
   }
 }
 
+// ---------------------------------------------------------------------------
+// lora_prep: the operands of the large-batch GEMM's low-rank epilogue.
+// (Columns per gather block: small enough that the LDS tile lets the
+// launch's blocks all be resident at once.)
+// Blocks [0, nt): t per original row, the scaled sum of the shrink's din
+// slices in slice order (the same arithmetic the expand applies), rounded
+// to bf16 and zero-padded to wt.  Blocks [nt, ...): one per (segment,
+// kPrepCols columns): the adapter's Up columns as a [dout][r_pad] block (ranks
+// contiguous, zeros past the rank) at koff * dout, koff = the sum of r_pad
+// over the segments before it, and koff recorded per adapter id.
+// ---------------------------------------------------------------------------
+constexpr int kPrepCols = 64;
+
+__global__ __launch_bounds__(256) void lora_prep_kernel(PoolView pv, int proj, const int32_t* __restrict__ ws, int n,
+                                                        const float* __restrict__ Ts, int n_chunks,
+                                                        uint16_t* __restrict__ tb, int wt, int nt,
+                                                        int32_t* __restrict__ koff_out, uint16_t* __restrict__ upt) {
+  const int tid = threadIdx.x;
+  if ((int)blockIdx.x < nt) {
+    const int n_act = ws[MLORA_SEG_NACT];
+    const int32_t* perm = ws + MLORA_SEG_PERM(n);
+    const int32_t* row_key = ws + MLORA_SEG_ROWKEY(n);
+    const size_t cs = (size_t)n * pv.max_rank;
+    for (int idx = blockIdx.x * 256 + tid; idx < n_act * wt; idx += nt * 256) {
+      const int j = idx / wt, q = idx % wt;
+      const int row = perm[j];
+      const int key = row_key[row];  // >= 0: sorted positions below n_act are rows on resident adapters
+      float s = 0.f;
+      if (q < pv.rank[key]) {
+        const float* tp = Ts + (size_t)j * pv.max_rank + q;
+        for (int ch = 0; ch < n_chunks; ++ch) s += tp[ch * cs];
+        s *= pv.scale[key];
+      }
+      tb[(size_t)row * wt + q] = (uint16_t)f2bf(s);
+    }
+    return;
+  }
+  __shared__ __attribute__((aligned(16))) uint16_t tile[MLORA_MAX_RANK][kPrepCols];  // Up rows of the block's columns
+  const int chunks = (pv.dout + kPrepCols - 1) / kPrepCols;
+  const int sidx = (blockIdx.x - nt) / chunks, cc = (blockIdx.x - nt) % chunks;
+  const int nseg = ws[MLORA_SEG_NSEG];
+  if (sidx >= nseg) return;
+  const int32_t* seg_adapter = ws + MLORA_SEG_ADAPTER(n);
+  // koff = sum of r_pad over the segments before this one (at most 255 of
+  // them: one per thread, then a block sum)
+  __shared__ int part[4];
+  int mine = tid < sidx ? (pv.rank[seg_adapter[tid]] + 15) & ~15 : 0;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) mine += __shfl_xor(mine, m, 64);
+  if ((tid & 63) == 0) part[tid >> 6] = mine;
+  __syncthreads();
+  const int koff = part[0] + part[1] + part[2] + part[3];
+  const int a = seg_adapter[sidx];
+  const int rank = pv.rank[a], rp = (rank + 15) & ~15;
+  if (cc == 0 && tid == 0) koff_out[a] = koff;
+  const int c0 = cc * kPrepCols, ncol = min(kPrepCols, pv.dout - c0);
+  const int32_t* upage = pv.up_page + ((size_t)a * pv.n_proj + proj) * pv.max_rank;
+  // rank rows in: 8 columns per thread-chunk (one 16-byte load when the
+  // row pieces are aligned and whole), rows past the rank are zero
+  const bool vec = (pv.dout % 8) == 0 && (reinterpret_cast<uintptr_t>(pv.up) % 16) == 0;
+  for (int idx = tid; idx < rp * (kPrepCols / 8); idx += 256) {
+    const int q = idx / (kPrepCols / 8), cl = (idx % (kPrepCols / 8)) * 8;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (q < rank && cl < ncol) {
+      const uint16_t* src = pv.up + (size_t)upage[q] * pv.dout + c0 + cl;
+      if (vec && cl + 8 <= ncol) {
+        v = *reinterpret_cast<const uint4*>(src);
+      } else {
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = cl + e < ncol ? src[e] : 0u;
+        v = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+      }
+    }
+    *reinterpret_cast<uint4*>(&tile[q][cl]) = v;
+  }
+  __syncthreads();
+  // columns out: the block [dout][rp] at koff * dout, 8 ranks per 16-byte store
+  uint16_t* dst = upt + (size_t)koff * pv.dout + (size_t)c0 * rp;
+  for (int idx = tid; idx < ncol * (rp / 8); idx += 256) {
+    const int cl = idx / (rp / 8), q0 = (idx % (rp / 8)) * 8;
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = tile[q0 + e][cl];
+    *reinterpret_cast<uint4*>(dst + (size_t)cl * rp + q0) =
+        make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+  }
+}
+
 bool vec_ok(const PoolView& pv, const void* a, const void* b) {
   const uintptr_t p = reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b) |
                       reinterpret_cast<uintptr_t>(pv.down) | reinterpret_cast<uintptr_t>(pv.up);
@@ -534,6 +683,17 @@ hipError_t launch_fused(const PoolView& pv, int proj, const uint16_t* X, const i
     MLORA_LAUNCH("fused", (fused_kernel<true>), grid, block, 0, stream, pv, proj, X, ws, Y, n);
   else
     MLORA_LAUNCH("fused", (fused_kernel<false>), grid, block, 0, stream, pv, proj, X, ws, Y, n);
+  return launched();
+}
+
+hipError_t launch_lora_prep(const PoolView& pv, int proj, const int32_t* ws, int n, const float* Ts, int n_chunks,
+                            uint16_t* tb, int wt, int32_t* koff, uint16_t* upt, hipStream_t stream) {
+  const long total = (long)n * wt;
+  const int nt = (int)((total + 255) / 256 < 1024 ? (total + 255) / 256 : 1024);
+  const int segs = n < pv.max_adapters ? n : pv.max_adapters;  // segments of the batch, at most
+  const int blocks = (nt > 0 ? nt : 1) + segs * ((pv.dout + kPrepCols - 1) / kPrepCols);
+  MLORA_LAUNCH("lora_prep", lora_prep_kernel, dim3(blocks), dim3(256), 0, stream, pv, proj, ws, n, Ts, n_chunks, tb,
+               wt, nt > 0 ? nt : 1, koff, upt);
   return launched();
 }
 

@@ -87,70 +87,75 @@ constexpr int kRowWaves = 8;
 constexpr int kRowThreads = 64 * kRowWaves;
 constexpr int kRowGroup = 16;  // ranks per reduction group
 
+// One row: out[q] = scale * (Down x)[q] for q < rank, with x the row at xr
+// and Down reached through the page table dpage (rank >= 1).  Called by all
+// kRowThreads threads of a workgroup (uniform control flow, block barriers
+// inside); `out` may be global or LDS memory.
+template <bool VEC>
+__device__ __forceinline__ void shrink_row_to(const PoolView& pv, const int32_t* __restrict__ dpage, int rank,
+                                              float scale, const uint16_t* __restrict__ xr, float* __restrict__ out) {
+  __shared__ float red[kRowWaves][kRowGroup];
+  constexpr int G = kRowGroup;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The page table is read without waiting for the rank: entries past the
+  // rank hold -1 and are replaced by the group's first page (their sums are
+  // never stored), and the first group runs before the rank is known.
+  int g0 = 0;
+  do {
+    int pg[G];
+#pragma unroll
+    for (int q = 0; q < G; ++q) pg[q] = dpage[min(g0 + q, pv.max_rank - 1)];
+#pragma unroll
+    for (int q = 1; q < G; ++q) pg[q] = pg[q] < 0 ? pg[0] : pg[q];
+    float v[G];
+#pragma unroll
+    for (int q = 0; q < G; ++q) v[q] = 0.f;
+    for (int kk = tid * 8; kk < pv.din; kk += kRowThreads * 8) {
+      float x[8], d[G][8];
+      load8<VEC>(xr, kk, pv.din, x);
+#pragma unroll
+      for (int q = 0; q < G; ++q) load8<VEC>(pv.down + (size_t)pg[q] * pv.din, kk, pv.din, d[q]);
+#pragma unroll
+      for (int q = 0; q < G; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[q] = fmaf(d[q][e], x[e], v[q]);
+    }
+    // reduce-scatter 16 -> 1: after the steps lane l holds index l >> 2
+#pragma unroll
+    for (int m = 32, len = G / 2; m >= 4; m >>= 1, len >>= 1) {
+      const bool upper = (lane & m) != 0;
+#pragma unroll
+      for (int i = 0; i < len; ++i) {
+        const float send = upper ? v[i] : v[i + len];
+        const float keep = upper ? v[i + len] : v[i];
+        v[i] = keep + __shfl_xor(send, m, 64);
+      }
+    }
+    float tot = v[0];
+    tot += __shfl_xor(tot, 2, 64);
+    tot += __shfl_xor(tot, 1, 64);
+    if ((lane & 3) == 0) red[wave][lane >> 2] = tot;
+    __syncthreads();
+    if (tid < G && g0 + tid < rank) {
+      float sum = red[0][tid];
+#pragma unroll
+      for (int w = 1; w < kRowWaves; ++w) sum += red[w][tid];
+      out[g0 + tid] = scale * sum;
+    }
+    __syncthreads();
+    g0 += G;
+  } while (g0 < rank);
+}
+
 // One row k: T[k][q] = s_a (Down_a x_k)[q]; called by all kRowThreads threads
 // of a workgroup (uniform control flow, block barriers inside).
 template <bool VEC>
 __device__ __forceinline__ void shrink_row_body(const PoolView& pv, int proj, const uint16_t* __restrict__ X,
                                                 const int32_t* __restrict__ row_key, int k, float* __restrict__ T) {
-  __shared__ float red[kRowWaves][kRowGroup];
-  constexpr int G = kRowGroup;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  {
-    const int key = row_key[k];
-    if (key < 0) return;  // base-only or invalid: no low-rank term
-    const int rank = pv.rank[key];
-    const float scale = pv.scale[key];
-    const int32_t* dpage = pv.down_page + ((size_t)key * pv.n_proj + proj) * pv.max_rank;
-    const uint16_t* xr = X + (size_t)k * pv.din;
-    // The page table is read without waiting for the rank: entries past the
-    // rank hold -1 and are replaced by the group's first page (their sums are
-    // never stored), and the first group runs before the rank is known.
-    int g0 = 0;
-    do {
-      int pg[G];
-#pragma unroll
-      for (int q = 0; q < G; ++q) pg[q] = dpage[min(g0 + q, pv.max_rank - 1)];
-#pragma unroll
-      for (int q = 1; q < G; ++q) pg[q] = pg[q] < 0 ? pg[0] : pg[q];
-      float v[G];
-#pragma unroll
-      for (int q = 0; q < G; ++q) v[q] = 0.f;
-      for (int kk = tid * 8; kk < pv.din; kk += kRowThreads * 8) {
-        float x[8], d[G][8];
-        load8<VEC>(xr, kk, pv.din, x);
-#pragma unroll
-        for (int q = 0; q < G; ++q) load8<VEC>(pv.down + (size_t)pg[q] * pv.din, kk, pv.din, d[q]);
-#pragma unroll
-        for (int q = 0; q < G; ++q)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[q] = fmaf(d[q][e], x[e], v[q]);
-      }
-      // reduce-scatter 16 -> 1: after the steps lane l holds index l >> 2
-#pragma unroll
-      for (int m = 32, len = G / 2; m >= 4; m >>= 1, len >>= 1) {
-        const bool upper = (lane & m) != 0;
-#pragma unroll
-        for (int i = 0; i < len; ++i) {
-          const float send = upper ? v[i] : v[i + len];
-          const float keep = upper ? v[i + len] : v[i];
-          v[i] = keep + __shfl_xor(send, m, 64);
-        }
-      }
-      float tot = v[0];
-      tot += __shfl_xor(tot, 2, 64);
-      tot += __shfl_xor(tot, 1, 64);
-      if ((lane & 3) == 0) red[wave][lane >> 2] = tot;
-      __syncthreads();
-      if (tid < G && g0 + tid < rank) {
-        float sum = red[0][tid];
-#pragma unroll
-        for (int w = 1; w < kRowWaves; ++w) sum += red[w][tid];
-        T[(size_t)k * pv.max_rank + g0 + tid] = scale * sum;
-      }
-      __syncthreads();
-      g0 += G;
-    } while (g0 < rank);
-  }
+  const int key = row_key[k];
+  if (key < 0) return;  // base-only or invalid: no low-rank term
+  shrink_row_to<VEC>(pv, pv.down_page + ((size_t)key * pv.n_proj + proj) * pv.max_rank, pv.rank[key], pv.scale[key],
+                     X + (size_t)k * pv.din, T + (size_t)k * pv.max_rank);
 }
 
 }  // namespace
