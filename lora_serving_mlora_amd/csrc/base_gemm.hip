@@ -498,6 +498,7 @@ __global__ __launch_bounds__(kTiledThreads) void gemm_tiled(const uint16_t* __re
 // ---------------------------------------------------------------------------
 constexpr int GBK = 32, kRingStages = 4, kMidStages = 8;  // stages: 256x256 tiles, 128x128 tiles
 constexpr int kRingThreads = 256;
+constexpr int kGroupM = 4;  // row bands per tile group (large products)
 
 // one array per (operand, stage, tile size): the main loop takes them as
 // distinct restrict pointers, so the compiler knows a DMA into one stage
@@ -807,11 +808,23 @@ __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(1,
   const int tid = threadIdx.x, lane = tid & 63;
   const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (t >= n_tiles) return;
-  // large: row-band major (an XCD's tiles share X rows); split-K medium:
-  // column major, so the few row tiles of a W column block run on one XCD
-  // and W crosses HBM once
+  // large: groups of kGroupM row bands walked column by column, so the
+  // ~32 tiles an XCD runs at once form a kGroupM x 8 block that shares X and
+  // W slices in its L2 (row-band major order re-fetched every W tile for
+  // each band); split-K medium: column major, so the few row tiles of a W
+  // column block run on one XCD and W crosses HBM once
   const int tiles_m = n_tiles / tiles_n;
-  const int m0 = (PART ? t % tiles_m : t / tiles_n) * TM, n0 = (PART ? t / tiles_m : t % tiles_n) * TN;
+  int mt, nt;
+  if (PART) {
+    mt = t % tiles_m;
+    nt = t / tiles_m;
+  } else {
+    const int g = t / (kGroupM * tiles_n), r = t % (kGroupM * tiles_n);
+    const int gm = min(kGroupM, tiles_m - g * kGroupM);
+    mt = g * kGroupM + r % gm;
+    nt = r / gm;
+  }
+  const int m0 = mt * TM, n0 = nt * TN;
   RingCtx c;
   c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: DMA offsets stay scalar
   c.fr = lane & 31;
