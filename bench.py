@@ -41,6 +41,7 @@ RIDGE = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
 KERNEL_SOURCES = {"seg_build": "seg_build.hip", "gemm_skinny": "base_gemm.hip", "gemm_ksplit": "base_gemm.hip",
                   "gemm_tiled": "base_gemm.hip", "gemm_big": "base_gemm.hip", "gemm_decode": "base_gemm.hip",
                   "gemm_decode+shrink_rows": "base_gemm.hip", "finish_part": "base_gemm.hip",
+                  "gemm_mid+shrink_rows": "base_gemm.hip",
                   "gemm_mid": "base_gemm.hip", "gemm_skinny_lora": "base_gemm.hip",
                   "gemm_ksplit_lora": "base_gemm.hip", "shrink": "lora_branch.hip", "expand": "lora_branch.hip",
                   "fused": "lora_branch.hip", "shrink_rows": "lora_branch.hip", "shrink_tiles": "lora_branch.hip",
@@ -98,6 +99,7 @@ def algorithmic(w, chunks):
         "shrink_rows": shrink_rows,
         "gemm_decode": split_dense, "gemm_mid": split_dense,
         "gemm_decode+shrink_rows": (split_dense[0] + shrink_rows[0], split_dense[1] + shrink_rows[1]),
+        "gemm_mid+shrink_rows": (split_dense[0] + shrink_rows[0], split_dense[1] + shrink_rows[1]),
         "finish_part": finish,
         "gemm_skinny_lora": gemm_lora, "gemm_ksplit_lora": gemm_lora, "gemm_big_lora": gemm_lora,
         # the epilogue's operands: chunk partials in, bf16 t per row out; Up
@@ -110,7 +112,7 @@ def algorithmic(w, chunks):
     return out
 
 
-DENSE = ("gemm_skinny", "gemm_ksplit", "gemm_tiled", "gemm_big", "gemm_decode", "gemm_mid",
+DENSE = ("gemm_skinny", "gemm_ksplit", "gemm_tiled", "gemm_big", "gemm_decode", "gemm_mid", "gemm_mid+shrink_rows",
          "gemm_decode+shrink_rows", "gemm_skinny_lora", "gemm_ksplit_lora", "gemm_big_lora")
 
 

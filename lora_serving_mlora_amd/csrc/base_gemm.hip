@@ -481,8 +481,9 @@ __global__ __launch_bounds__(kTiledThreads) void gemm_tiled(const uint16_t* __re
 // ---------------------------------------------------------------------------
 // ring: TM x TN output tiles (256 x 256 for large batches, 128 x 128 with
 // split-K for medium ones), 4 waves of (TM/2) x (TN/2), MFMA 32x32x16.  K
-// advances in 32-deep tiles through an LDS ring of NS stages (4 of 32 KiB
-// for 256 x 256, 8 of 16 KiB for 128 x 128).  Tiles are moved global -> LDS
+// advances in 32-deep tiles through an LDS ring of NS = 4 stages (32 KiB
+// each for 256 x 256, 16 KiB for 128 x 128, so two medium workgroups fit a
+// CU).  Tiles are moved global -> LDS
 // by LDS DMA (buffer_load ... lds: each lane's 16 bytes land at a fixed LDS
 // slot, so the XOR swizzle is applied by choosing which global chunk each
 // lane fetches), and the DMA of tile kt+NS-1 is issued while tile kt is
@@ -496,7 +497,7 @@ __global__ __launch_bounds__(kTiledThreads) void gemm_tiled(const uint16_t* __re
 // multiple of 32 * NS (per split) and 16-byte aligned rows; rows past M or
 // N read zeros (buffer bounds).
 // ---------------------------------------------------------------------------
-constexpr int GBK = 32, kRingStages = 4, kMidStages = 8;  // stages: 256x256 tiles, 128x128 tiles
+constexpr int GBK = 32, kRingStages = 4;  // 32-deep K tiles, 4 stages (32 KiB / 16 KiB for 256x256 / 128x128)
 constexpr int kRingThreads = 256;
 constexpr int kGroupM = 4;  // row bands per tile group (large products)
 
@@ -515,18 +516,10 @@ __shared__ __attribute__((aligned(16))) uint16_t mid_a0[128 * GBK];
 __shared__ __attribute__((aligned(16))) uint16_t mid_a1[128 * GBK];
 __shared__ __attribute__((aligned(16))) uint16_t mid_a2[128 * GBK];
 __shared__ __attribute__((aligned(16))) uint16_t mid_a3[128 * GBK];
-__shared__ __attribute__((aligned(16))) uint16_t mid_a4[128 * GBK];
-__shared__ __attribute__((aligned(16))) uint16_t mid_a5[128 * GBK];
-__shared__ __attribute__((aligned(16))) uint16_t mid_a6[128 * GBK];
-__shared__ __attribute__((aligned(16))) uint16_t mid_a7[128 * GBK];
 __shared__ __attribute__((aligned(16))) uint16_t mid_b0[128 * GBK];
 __shared__ __attribute__((aligned(16))) uint16_t mid_b1[128 * GBK];
 __shared__ __attribute__((aligned(16))) uint16_t mid_b2[128 * GBK];
 __shared__ __attribute__((aligned(16))) uint16_t mid_b3[128 * GBK];
-__shared__ __attribute__((aligned(16))) uint16_t mid_b4[128 * GBK];
-__shared__ __attribute__((aligned(16))) uint16_t mid_b5[128 * GBK];
-__shared__ __attribute__((aligned(16))) uint16_t mid_b6[128 * GBK];
-__shared__ __attribute__((aligned(16))) uint16_t mid_b7[128 * GBK];
 
 // LDS element offset of 16-byte chunk `chunk` (0..3) of tile row `row`:
 // 64-byte rows, chunks XOR-swizzled by (row >> 2) & 3.  The LDS serves a
@@ -636,36 +629,6 @@ __device__ __forceinline__ void ring_mainloop4(const RingCtx& c, uint16_t* __res
     ring_step<TM, TN, 4>(c, a1, b1, a0, b0, kt + 1, kend, acc);
     ring_step<TM, TN, 4>(c, a2, b2, a1, b1, kt + 2, kend, acc);
     ring_step<TM, TN, 4>(c, a3, b3, a2, b2, kt + 3, kend, acc);
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // drain the trailing re-fetches before the workgroup ends
-}
-
-// K tiles [kt0, kend) in groups of 8 ((kend - kt0) % 8 == 0), one stage each
-template <int TM, int TN>
-__device__ __forceinline__ void ring_mainloop8(
-    const RingCtx& c, uint16_t* __restrict__ a0, uint16_t* __restrict__ a1, uint16_t* __restrict__ a2,
-    uint16_t* __restrict__ a3, uint16_t* __restrict__ a4, uint16_t* __restrict__ a5, uint16_t* __restrict__ a6,
-    uint16_t* __restrict__ a7, uint16_t* __restrict__ b0, uint16_t* __restrict__ b1, uint16_t* __restrict__ b2,
-    uint16_t* __restrict__ b3, uint16_t* __restrict__ b4, uint16_t* __restrict__ b5, uint16_t* __restrict__ b6,
-    uint16_t* __restrict__ b7, int kt0, int kend, floatx16 (&acc)[TM / 64][TN / 64]) {
-  ring_issue<TM, TN>(c, a0, b0, kt0);
-  ring_issue<TM, TN>(c, a1, b1, kt0 + 1);
-  ring_issue<TM, TN>(c, a2, b2, kt0 + 2);
-  ring_issue<TM, TN>(c, a3, b3, kt0 + 3);
-  ring_issue<TM, TN>(c, a4, b4, kt0 + 4);
-  ring_issue<TM, TN>(c, a5, b5, kt0 + 5);
-  ring_issue<TM, TN>(c, a6, b6, kt0 + 6);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(6 * (TM / 64 + TN / 64)));  // tile kt0 has landed
-  ring_barrier();
-  for (int kt = kt0; kt < kend; kt += 8) {
-    ring_step<TM, TN, 8>(c, a0, b0, a7, b7, kt, kend, acc);
-    ring_step<TM, TN, 8>(c, a1, b1, a0, b0, kt + 1, kend, acc);
-    ring_step<TM, TN, 8>(c, a2, b2, a1, b1, kt + 2, kend, acc);
-    ring_step<TM, TN, 8>(c, a3, b3, a2, b2, kt + 3, kend, acc);
-    ring_step<TM, TN, 8>(c, a4, b4, a3, b3, kt + 4, kend, acc);
-    ring_step<TM, TN, 8>(c, a5, b5, a4, b4, kt + 5, kend, acc);
-    ring_step<TM, TN, 8>(c, a6, b6, a5, b5, kt + 6, kend, acc);
-    ring_step<TM, TN, 8>(c, a7, b7, a6, b6, kt + 7, kend, acc);
   }
   __builtin_amdgcn_s_waitcnt(0);  // drain the trailing re-fetches before the workgroup ends
 }
@@ -798,15 +761,27 @@ __device__ __forceinline__ void ring_lora_epilogue(const RingCtx& c, int m0, int
 
 // LORA (whole-K form only): the low-rank term of every row is added in the
 // epilogue (ring_lora_epilogue) and rows with an invalid id become NaN.
+// n_shrink > 0 (split-K form): the first n_shrink workgroups of the launch
+// (blockIdx.y == 0) compute the per-row shrink T[k] = s_a Down_a x_k for
+// rows k < M instead (independent work that shares the launch).
 template <int TM, int TN, bool PART, bool LORA>
 __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_ring(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y,
     float* __restrict__ part, int M, int K, int N, int tiles_n, int n_tiles, int per_xcd, int kt_per, PoolView pv,
-    const int32_t* __restrict__ row_key, LoraOperands lo) {
+    const int32_t* __restrict__ row_key, LoraOperands lo, int proj, float* __restrict__ Trows, int n_shrink) {
   static_assert(!(PART && LORA), "the low-rank epilogue needs the whole K range");
   constexpr int MI = TM / 64, NJ = TN / 64;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if constexpr (PART) {
+    if ((int)blockIdx.x < n_shrink) {
+      if (blockIdx.y == 0)
+        for (int k = blockIdx.x; k < M; k += n_shrink)
+          shrink_row_body<true, kRingThreads / 64>(pv, proj, X, row_key, k, Trows);
+      return;
+    }
+  }
+  const int bx = (int)blockIdx.x - n_shrink;
+  const int t = (bx & 7) * per_xcd + (bx >> 3);
   if (t >= n_tiles) return;
   // large: groups of kGroupM row bands walked column by column, so the
   // ~32 tiles an XCD runs at once form a kGroupM x 8 block that shares X and
@@ -850,14 +825,13 @@ __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(1,
 
   const int kt0 = PART ? blockIdx.y * kt_per : 0;
   const int kend = PART ? kt0 + kt_per : K / GBK;
-  if (TM == 256)
+  if constexpr (TM == 256)
     ring_mainloop4<TM, TN>(c, big_a0, big_a1, big_a2, big_a3, big_b0, big_b1, big_b2, big_b3, kt0, kend, acc);
   else
-    ring_mainloop8<TM, TN>(c, mid_a0, mid_a1, mid_a2, mid_a3, mid_a4, mid_a5, mid_a6, mid_a7, mid_b0, mid_b1, mid_b2,
-                           mid_b3, mid_b4, mid_b5, mid_b6, mid_b7, kt0, kend, acc);
+    ring_mainloop4<TM, TN>(c, mid_a0, mid_a1, mid_a2, mid_a3, mid_b0, mid_b1, mid_b2, mid_b3, kt0, kend, acc);
 
   int key[MI];  // low-rank epilogue: the keys of the lane's A-fragment rows
-  if (LORA) {
+  if constexpr (LORA) {
     __builtin_amdgcn_sched_barrier(0);
     ring_lora_epilogue<TM, TN>(c, m0, n0, M, N, pv, row_key, lo, acc, key);
   }
@@ -927,7 +901,7 @@ hipError_t launch_big(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, 
   const int per_xcd = (n_tiles + 7) / 8;
   MLORA_LAUNCH("gemm_big", (gemm_ring<256, 256, false, false>), dim3(per_xcd * 8), dim3(kRingThreads), 0, st, X, W,
                Y, (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, PoolView{}, (const int32_t*)nullptr,
-               LoraOperands{});
+               LoraOperands{}, 0, (float*)nullptr, 0);
   return launched();
 }
 
@@ -1241,20 +1215,25 @@ hipError_t launch_decode(const uint16_t* X, const uint16_t* W, uint16_t* Y, int 
 int mid_split(int M, int N, int K) {
   const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
   int S = 1;
-  while (S < kMidMaxSplit && tiles * S < 256 && K % (GBK * kMidStages * S * 2) == 0) S *= 2;
+  while (S < kMidMaxSplit && tiles * S < 256 && K % (GBK * kRingStages * S * 2) == 0) S *= 2;
   return S;
 }
 
-bool mid_ring_ok(int M, int K) { return K % (GBK * kMidStages) == 0 && (long)M * K * 2 < (1L << 31); }
+bool mid_ring_ok(int M, int K) { return K % (GBK * kRingStages) == 0 && (long)M * K * 2 < (1L << 31); }
 
+// shrink: the per-row shrink (T, one slice) runs as extra workgroups of the
+// GEMM launch
 hipError_t launch_mid_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N, const PoolView& pv,
-                           int proj, const int32_t* row_key, const float* T, float* part, hipStream_t st) {
+                           int proj, const int32_t* row_key, float* T, float* part, bool shrink, hipStream_t st) {
   const int S = mid_split(M, N, K);
   const int tiles_n = (N + 127) / 128, n_tiles = ((M + 127) / 128) * tiles_n;
   const int per_xcd = (n_tiles + 7) / 8;
-  MLORA_LAUNCH("gemm_mid", (gemm_ring<128, 128, true, false>), dim3(per_xcd * 8, S), dim3(kRingThreads), 0, st, X,
-               W, Y, part, M, K, N, tiles_n, n_tiles, per_xcd, K / GBK / S, PoolView{}, (const int32_t*)nullptr,
-               LoraOperands{});
+  // shrink workgroups: one per row, a multiple of 8 so the GEMM blocks keep
+  // their XCD mapping
+  const int ns = shrink ? (M + 7) / 8 * 8 : 0;
+  MLORA_LAUNCH(shrink ? "gemm_mid+shrink_rows" : "gemm_mid", (gemm_ring<128, 128, true, false>),
+               dim3(ns + per_xcd * 8, S), dim3(kRingThreads), 0, st, X, W, Y, part, M, K, N, tiles_n, n_tiles,
+               per_xcd, K / GBK / S, pv, row_key, LoraOperands{}, proj, T, ns);
   hipError_t e = launched();
   if (e != hipSuccess) return e;
   const int threads = M * (N / 8);
@@ -1306,12 +1285,12 @@ hipError_t launch_gemm_lora(const PoolView& pv, int proj, const uint16_t* X, con
     if (M <= 48) return launch_decode<3>(X, W, Y, M, K, N, pv, proj, row_key, T, part, shrink, stream);
     return launch_decode<4>(X, W, Y, M, K, N, pv, proj, row_key, T, part, shrink, stream);
   }
+  if (M > 64 && vec && down_vec && mid_ring_ok(M, K) && (long)N * K * 2 < (1L << 31) && mid_enabled())
+    return launch_mid_lora(X, W, Y, M, K, N, pv, proj, row_key, T, part, shrink, stream);
   if (shrink) {
     hipError_t e = launch_shrink_rows(pv, proj, X, ws, M, T, stream);
     if (e != hipSuccess) return e;
   }
-  if (M > 64 && vec && mid_ring_ok(M, K) && (long)N * K * 2 < (1L << 31) && mid_enabled())
-    return launch_mid_lora(X, W, Y, M, K, N, pv, proj, row_key, T, part, stream);
   return vec ? launch_lora<true>(X, W, Y, M, K, N, pv, proj, row_key, T, stream)
              : launch_lora<false>(X, W, Y, M, K, N, pv, proj, row_key, T, stream);
 }
@@ -1345,7 +1324,8 @@ hipError_t launch_big_lora(const PoolView& pv, const uint16_t* X, const uint16_t
   const int n_tiles = tiles_m * tiles_n;
   const int per_xcd = (n_tiles + 7) / 8;
   MLORA_LAUNCH("gemm_big_lora", (gemm_ring<256, 256, false, true>), dim3(per_xcd * 8), dim3(kRingThreads), 0, st, X,
-               W, Y, (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, pv, ws + MLORA_SEG_ROWKEY(M), lo);
+               W, Y, (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, pv, ws + MLORA_SEG_ROWKEY(M), lo, 0,
+               (float*)nullptr, 0);
   return launched();
 }
 

@@ -89,12 +89,12 @@ constexpr int kRowGroup = 16;  // ranks per reduction group
 
 // One row: out[q] = scale * (Down x)[q] for q < rank, with x the row at xr
 // and Down reached through the page table dpage (rank >= 1).  Called by all
-// kRowThreads threads of a workgroup (uniform control flow, block barriers
+// 64 * NW threads of a workgroup (uniform control flow, block barriers
 // inside); `out` may be global or LDS memory.
-template <bool VEC>
+template <bool VEC, int NW = kRowWaves>
 __device__ __forceinline__ void shrink_row_to(const PoolView& pv, const int32_t* __restrict__ dpage, int rank,
                                               float scale, const uint16_t* __restrict__ xr, float* __restrict__ out) {
-  __shared__ float red[kRowWaves][kRowGroup];
+  __shared__ float red[NW][kRowGroup];
   constexpr int G = kRowGroup;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // The page table is read without waiting for the rank: entries past the
@@ -110,7 +110,7 @@ __device__ __forceinline__ void shrink_row_to(const PoolView& pv, const int32_t*
     float v[G];
 #pragma unroll
     for (int q = 0; q < G; ++q) v[q] = 0.f;
-    for (int kk = tid * 8; kk < pv.din; kk += kRowThreads * 8) {
+    for (int kk = tid * 8; kk < pv.din; kk += 64 * NW * 8) {
       float x[8], d[G][8];
       load8<VEC>(xr, kk, pv.din, x);
 #pragma unroll
@@ -139,7 +139,7 @@ __device__ __forceinline__ void shrink_row_to(const PoolView& pv, const int32_t*
     if (tid < G && g0 + tid < rank) {
       float sum = red[0][tid];
 #pragma unroll
-      for (int w = 1; w < kRowWaves; ++w) sum += red[w][tid];
+      for (int w = 1; w < NW; ++w) sum += red[w][tid];
       out[g0 + tid] = scale * sum;
     }
     __syncthreads();
@@ -147,15 +147,15 @@ __device__ __forceinline__ void shrink_row_to(const PoolView& pv, const int32_t*
   } while (g0 < rank);
 }
 
-// One row k: T[k][q] = s_a (Down_a x_k)[q]; called by all kRowThreads threads
+// One row k: T[k][q] = s_a (Down_a x_k)[q]; called by all 64 * NW threads
 // of a workgroup (uniform control flow, block barriers inside).
-template <bool VEC>
+template <bool VEC, int NW = kRowWaves>
 __device__ __forceinline__ void shrink_row_body(const PoolView& pv, int proj, const uint16_t* __restrict__ X,
                                                 const int32_t* __restrict__ row_key, int k, float* __restrict__ T) {
   const int key = row_key[k];
   if (key < 0) return;  // base-only or invalid: no low-rank term
-  shrink_row_to<VEC>(pv, pv.down_page + ((size_t)key * pv.n_proj + proj) * pv.max_rank, pv.rank[key], pv.scale[key],
-                     X + (size_t)k * pv.din, T + (size_t)k * pv.max_rank);
+  shrink_row_to<VEC, NW>(pv, pv.down_page + ((size_t)key * pv.n_proj + proj) * pv.max_rank, pv.rank[key],
+                         pv.scale[key], X + (size_t)k * pv.din, T + (size_t)k * pv.max_rank);
 }
 
 }  // namespace
