@@ -633,6 +633,106 @@ __device__ __forceinline__ void ring_mainloop4(const RingCtx& c, uint16_t* __res
   __builtin_amdgcn_s_waitcnt(0);  // drain the trailing re-fetches before the workgroup ends
 }
 
+// Fragments of one 32-deep stage, per wave: A rows (MI blocks of 32) and B
+// columns (NJ blocks of 32), for the two 16-deep halves of the stage.
+template <int TM, int TN>
+struct RingFrags {
+  uint4 a[2][TM / 64], b[2][TN / 64];
+};
+
+template <int TM, int TN>
+__device__ __forceinline__ void ring_read(const RingCtx& c, const uint16_t* __restrict__ ra,
+                                          const uint16_t* __restrict__ rb, RingFrags<TM, TN>& f) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int i = 0; i < TM / 64; ++i)
+      f.a[h][i] = *reinterpret_cast<const uint4*>(ra + swz4(c.wm * (TM / 2) + i * 32 + c.fr, 2 * h + c.fk));
+#pragma unroll
+    for (int j = 0; j < TN / 64; ++j)
+      f.b[h][j] = *reinterpret_cast<const uint4*>(rb + swz4(c.wn * (TN / 2) + j * 32 + c.fr, 2 * h + c.fk));
+  }
+}
+
+// Pipelined step k: the MFMAs of stage k run on fragments read during the
+// previous step (cf) while this step reads stage k+1 (ra, rb) into nf and
+// sends the DMA of stage k+4 into the buffer stage k came from (da, db: its
+// data is already in registers).  Then it waits until stage k+2 has landed
+// (stages k+3 and k+4 may still be in flight) and until its own reads of
+// stage k+1 are done (that buffer is overwritten next step), and syncs the
+// workgroup.  The reads are spread over the first MFMAs, so a wave never
+// stalls on a full LDS queue while it could issue matrix work, and the
+// matrix pipe never waits for LDS at the start of a step.
+template <int TM, int TN>
+__device__ __forceinline__ void ring_step_p(const RingCtx& c, const uint16_t* __restrict__ ra,
+                                            const uint16_t* __restrict__ rb, uint16_t* __restrict__ da,
+                                            uint16_t* __restrict__ db, int kt, int kend, const RingFrags<TM, TN>& cf,
+                                            RingFrags<TM, TN>& nf, floatx16 (&acc)[TM / 64][TN / 64]) {
+  constexpr int MI = TM / 64, NJ = TN / 64;
+  constexpr int kReads = 2 * (MI + NJ), kMfma = 2 * MI * NJ, kPer = kMfma / kReads;
+  ring_issue<TM, TN>(c, da, db, min(kt + 4, kend - 1));
+  ring_read<TM, TN>(c, ra, rb, nf);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cf.a[h][i]), as_bf16x8(cf.b[h][j]), acc[i][j], 0,
+                                                            0, 0);
+  // one DMA per group, spread over the first groups: the memory pipe's
+  // queue drains between issues, so a full queue never holds the wave (and
+  // its matrix work) at an issue
+#pragma unroll
+  for (int r = 0; r < kReads; ++r) {
+    if (r < MI + NJ) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one DMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                   // one fragment read
+    __builtin_amdgcn_sched_group_barrier(0x008, kPer, 0);                // kPer MFMAs
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (MI + NJ)) & ~(15 << 8));  // + lgkmcnt(0)
+  ring_barrier();
+}
+
+// K tiles [kt0, kend) in groups of 4 ((kend - kt0) % 4 == 0), pipelined
+// form: four stages in flight at the start, fragments double-buffered in
+// registers
+template <int TM, int TN>
+__device__ __forceinline__ void ring_mainloop_p(const RingCtx& c, uint16_t* __restrict__ a0, uint16_t* __restrict__ a1,
+                                                uint16_t* __restrict__ a2, uint16_t* __restrict__ a3,
+                                                uint16_t* __restrict__ b0, uint16_t* __restrict__ b1,
+                                                uint16_t* __restrict__ b2, uint16_t* __restrict__ b3, int kt0,
+                                                int kend, floatx16 (&acc)[TM / 64][TN / 64]) {
+  constexpr int n = TM / 64 + TN / 64;  // DMA instructions per stage and wave
+  ring_issue<TM, TN>(c, a0, b0, kt0);
+  ring_issue<TM, TN>(c, a1, b1, min(kt0 + 1, kend - 1));
+  ring_issue<TM, TN>(c, a2, b2, min(kt0 + 2, kend - 1));
+  ring_issue<TM, TN>(c, a3, b3, min(kt0 + 3, kend - 1));
+  RingFrags<TM, TN> f0, f1;
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * n));  // stage kt0 has landed
+  ring_barrier();
+  ring_read<TM, TN>(c, a0, b0, f0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * n) & ~(15 << 8));  // stage kt0+1 landed, own reads done
+  ring_barrier();
+  for (int kt = kt0; kt < kend; kt += 4) {
+    ring_step_p<TM, TN>(c, a1, b1, a0, b0, kt, kend, f0, f1, acc);
+    ring_step_p<TM, TN>(c, a2, b2, a1, b1, kt + 1, kend, f1, f0, acc);
+    ring_step_p<TM, TN>(c, a3, b3, a2, b2, kt + 2, kend, f0, f1, acc);
+    ring_step_p<TM, TN>(c, a0, b0, a3, b3, kt + 3, kend, f1, f0, acc);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // drain the trailing re-fetches before the workgroup ends
+}
+
+// MLORA_RING_PIPE=0 keeps the ring on the unpipelined step (A/B timing)
+int ring_pipe_enabled() {
+  static int on = -1;
+  if (on < 0) {
+    const char* e = getenv("MLORA_RING_PIPE");
+    on = (e && e[0] == '0') ? 0 : 1;
+  }
+  return on;
+}
+
 // The low-rank term added in the GEMM's registers (prefill): for every row
 // of the tile on a resident adapter a, acc[row][col] += sum_q t[row][q] *
 // Up_a[col][q].  Rows of one tile carry different adapters, so each wave
@@ -768,7 +868,8 @@ template <int TM, int TN, bool PART, bool LORA>
 __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_ring(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y,
     float* __restrict__ part, int M, int K, int N, int tiles_n, int n_tiles, int per_xcd, int kt_per, PoolView pv,
-    const int32_t* __restrict__ row_key, LoraOperands lo, int proj, float* __restrict__ Trows, int n_shrink) {
+    const int32_t* __restrict__ row_key, LoraOperands lo, int proj, float* __restrict__ Trows, int n_shrink,
+    int pipe) {
   static_assert(!(PART && LORA), "the low-rank epilogue needs the whole K range");
   constexpr int MI = TM / 64, NJ = TN / 64;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -825,10 +926,17 @@ __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(1,
 
   const int kt0 = PART ? blockIdx.y * kt_per : 0;
   const int kend = PART ? kt0 + kt_per : K / GBK;
-  if constexpr (TM == 256)
-    ring_mainloop4<TM, TN>(c, big_a0, big_a1, big_a2, big_a3, big_b0, big_b1, big_b2, big_b3, kt0, kend, acc);
-  else
-    ring_mainloop4<TM, TN>(c, mid_a0, mid_a1, mid_a2, mid_a3, mid_b0, mid_b1, mid_b2, mid_b3, kt0, kend, acc);
+  if constexpr (TM == 256) {
+    if (pipe)
+      ring_mainloop_p<TM, TN>(c, big_a0, big_a1, big_a2, big_a3, big_b0, big_b1, big_b2, big_b3, kt0, kend, acc);
+    else
+      ring_mainloop4<TM, TN>(c, big_a0, big_a1, big_a2, big_a3, big_b0, big_b1, big_b2, big_b3, kt0, kend, acc);
+  } else {
+    if (pipe)
+      ring_mainloop_p<TM, TN>(c, mid_a0, mid_a1, mid_a2, mid_a3, mid_b0, mid_b1, mid_b2, mid_b3, kt0, kend, acc);
+    else
+      ring_mainloop4<TM, TN>(c, mid_a0, mid_a1, mid_a2, mid_a3, mid_b0, mid_b1, mid_b2, mid_b3, kt0, kend, acc);
+  }
 
   int key[MI];  // low-rank epilogue: the keys of the lane's A-fragment rows
   if constexpr (LORA) {
@@ -901,7 +1009,7 @@ hipError_t launch_big(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, 
   const int per_xcd = (n_tiles + 7) / 8;
   MLORA_LAUNCH("gemm_big", (gemm_ring<256, 256, false, false>), dim3(per_xcd * 8), dim3(kRingThreads), 0, st, X, W,
                Y, (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, PoolView{}, (const int32_t*)nullptr,
-               LoraOperands{}, 0, (float*)nullptr, 0);
+               LoraOperands{}, 0, (float*)nullptr, 0, ring_pipe_enabled());
   return launched();
 }
 
@@ -971,9 +1079,22 @@ __global__ __launch_bounds__(64 * kDecWaves) void gemm_decode(const uint16_t* __
   const int cg = wave & 3, kh = wave >> 2;
   const int nseg = Kq / 128;  // 64-element K segments in a wave's half of the quarter (<= 8)
 
-  // W0 first, all 16 loads of the wave at once.  Instruction 2s+h reads rows
+  // X slice -> LDS first (an L2 hit for all but the first workgroups of a
+  // quarter): instruction (row r, 1 KiB block b); lane l fetches logical
+  // chunk l ^ (r & 15) of the block into physical chunk l
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X), (short)0, M * K * 2, 0x00020000);
+  const int blocks = Kq / 512;
+  for (int i = wave; i < M * blocks; i += kDecWaves) {
+    const int r = i / blocks, bl = i % blocks;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, xs + (size_t)r * Kq + bl * 512, 16, (lane ^ (r & 15)) * 16,
+                                             (r * K + kq * Kq + bl * 512) * 2, 0, 0);
+  }
+  // then W0, all 16 loads of the wave at once.  Instruction 2s+h reads rows
   // 8h + (l & 7) of the column group, 16-byte chunk l >> 3 of K segment s:
   // 128 contiguous bytes per row (64-byte row pieces cost 30 % more HBM time).
+  // Segments are consumed as they land (the compiler's waits count the
+  // loads in issue order).
   const size_t kbase = (size_t)kq * Kq + kh * (Kq / 2) + (lane >> 3) * 8;
   const uint16_t* w0p = W + (size_t)min(n0 + 16 * cg + (lane & 7), N - 1) * K + kbase;
   const uint16_t* w1p = W + (size_t)min(n0 + 16 * cg + 8 + (lane & 7), N - 1) * K + kbase;
@@ -982,16 +1103,6 @@ __global__ __launch_bounds__(64 * kDecWaves) void gemm_decode(const uint16_t* __
   for (int sg = 0; sg < 8; ++sg) {
     wv[2 * sg] = *reinterpret_cast<const uint4*>(w0p + min(sg, nseg - 1) * 64);
     wv[2 * sg + 1] = *reinterpret_cast<const uint4*>(w1p + min(sg, nseg - 1) * 64);
-  }
-  // X slice -> LDS: instruction (row r, 1 KiB block b); lane l fetches
-  // logical chunk l ^ (r & 15) of the block into physical chunk l
-  const __amdgpu_buffer_rsrc_t rx =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X), (short)0, M * K * 2, 0x00020000);
-  const int blocks = Kq / 512;
-  for (int i = wave; i < M * blocks; i += kDecWaves) {
-    const int r = i / blocks, bl = i % blocks;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, xs + (size_t)r * Kq + bl * 512, 16, (lane ^ (r & 15)) * 16,
-                                             (r * K + kq * Kq + bl * 512) * 2, 0, 0);
   }
   // The per-row shrink rides along: this workgroup computes the quarter-kq
   // partial of T for rows cb, cb + ncb, ... from the X slice it already
@@ -1017,8 +1128,11 @@ __global__ __launch_bounds__(64 * kDecWaves) void gemm_decode(const uint16_t* __
       }
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();  // X slice in LDS
+  // the X slice has landed once at most the 16 W0 loads and the 4 Down
+  // loads issued after it are in flight (the barrier carries no fence, so
+  // it does not wait for the W0 loads too)
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));
+  ring_barrier();
 
   floatx4 acc[MB];
 #pragma unroll
@@ -1233,7 +1347,7 @@ hipError_t launch_mid_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, in
   const int ns = shrink ? (M + 7) / 8 * 8 : 0;
   MLORA_LAUNCH(shrink ? "gemm_mid+shrink_rows" : "gemm_mid", (gemm_ring<128, 128, true, false>),
                dim3(ns + per_xcd * 8, S), dim3(kRingThreads), 0, st, X, W, Y, part, M, K, N, tiles_n, n_tiles,
-               per_xcd, K / GBK / S, pv, row_key, LoraOperands{}, proj, T, ns);
+               per_xcd, K / GBK / S, pv, row_key, LoraOperands{}, proj, T, ns, ring_pipe_enabled());
   hipError_t e = launched();
   if (e != hipSuccess) return e;
   const int threads = M * (N / 8);
@@ -1325,7 +1439,7 @@ hipError_t launch_big_lora(const PoolView& pv, const uint16_t* X, const uint16_t
   const int per_xcd = (n_tiles + 7) / 8;
   MLORA_LAUNCH("gemm_big_lora", (gemm_ring<256, 256, false, true>), dim3(per_xcd * 8), dim3(kRingThreads), 0, st, X,
                W, Y, (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, pv, ws + MLORA_SEG_ROWKEY(M), lo, 0,
-               (float*)nullptr, 0);
+               (float*)nullptr, 0, ring_pipe_enabled());
   return launched();
 }
 
