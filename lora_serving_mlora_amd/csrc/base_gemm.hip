@@ -546,7 +546,7 @@ constexpr int vmcnt_imm(int v) { return (v & 15) | ((v >> 4) << 14) | (7 << 4) |
 
 struct RingCtx {
   __amdgpu_buffer_rsrc_t rsa, rsb;
-  int voff, row_bytes, wave, wm, wn, fr, fk;
+  int voff, voff64, row_bytes, wave, wm, wn, fr, fk;
 };
 
 // DMA of K tile kt (32 deep) into (da, db): instruction j of this wave
@@ -723,6 +723,193 @@ __device__ __forceinline__ void ring_mainloop_p(const RingCtx& c, uint16_t* __re
   __builtin_amdgcn_s_waitcnt(0);  // drain the trailing re-fetches before the workgroup ends
 }
 
+// ---------------------------------------------------------------------------
+// ring64: the same pipelined ring with 64-deep stages.  A DMA instruction then
+// covers 8 tile rows x 128 contiguous bytes (8 whole cache lines) instead of
+// 16 rows x 64 bytes (16 half lines): the per-CU memory pipe handles cache
+// lines at a fixed rate, so the same bytes reach LDS in about half the time.
+// LDS rows are 128 bytes; 16-byte chunks are XOR-swizzled by (row >> 1) & 7,
+// so the 16 lanes of a fragment read (16 consecutive rows, one logical
+// chunk) cover all 16 slots of a 256-byte window.  Large products use
+// 256 x 128 tiles with 3 stages (48 KiB each), medium split-K ones 128 x 128
+// tiles with 4 stages (32 KiB each).
+// ---------------------------------------------------------------------------
+constexpr int GBK64 = 64;
+__shared__ __attribute__((aligned(16))) uint16_t l64_a0[256 * GBK64];
+__shared__ __attribute__((aligned(16))) uint16_t l64_a1[256 * GBK64];
+__shared__ __attribute__((aligned(16))) uint16_t l64_a2[256 * GBK64];
+__shared__ __attribute__((aligned(16))) uint16_t l64_b0[128 * GBK64];
+__shared__ __attribute__((aligned(16))) uint16_t l64_b1[128 * GBK64];
+__shared__ __attribute__((aligned(16))) uint16_t l64_b2[128 * GBK64];
+__shared__ __attribute__((aligned(16))) uint16_t m64_a0[128 * GBK64];
+__shared__ __attribute__((aligned(16))) uint16_t m64_a1[128 * GBK64];
+__shared__ __attribute__((aligned(16))) uint16_t m64_a2[128 * GBK64];
+__shared__ __attribute__((aligned(16))) uint16_t m64_a3[128 * GBK64];
+__shared__ __attribute__((aligned(16))) uint16_t m64_b0[128 * GBK64];
+__shared__ __attribute__((aligned(16))) uint16_t m64_b1[128 * GBK64];
+__shared__ __attribute__((aligned(16))) uint16_t m64_b2[128 * GBK64];
+__shared__ __attribute__((aligned(16))) uint16_t m64_b3[128 * GBK64];
+
+// LDS element offset of 16-byte chunk `chunk` (0..7) of 128-byte row `row`
+__device__ __forceinline__ int swz8(int row, int chunk) { return row * GBK64 + ((chunk ^ ((row >> 1) & 7)) << 3); }
+
+// DMA of 64-deep K tile kt into (da, db): instruction j of this wave covers
+// tile rows 8i..8i+7, i = wave + 4j; lane L fills row L >> 3 of the group,
+// physical chunk L & 7 (voff64: the logical chunk that slot holds, which
+// depends on the row's parity group, the same for all i of a wave)
+template <int TM, int TN>
+__device__ __forceinline__ void ring64_issue(const RingCtx& c, uint16_t* __restrict__ da, uint16_t* __restrict__ db,
+                                             int kt) {
+#pragma unroll
+  for (int j = 0; j < TM / 32; ++j) {
+    const int i = c.wave + 4 * j;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsa, da + i * 8 * GBK64, 16, c.voff64,
+                                             i * 8 * c.row_bytes + kt * GBK64 * 2, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < TN / 32; ++j) {
+    const int i = c.wave + 4 * j;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsb, db + i * 8 * GBK64, 16, c.voff64,
+                                             i * 8 * c.row_bytes + kt * GBK64 * 2, 0, 0);
+  }
+}
+
+// fragments of one 64-deep stage: four 16-deep quarters
+template <int TM, int TN>
+struct Ring64Frags {
+  uint4 a[4][TM / 64], b[4][TN / 64];
+};
+
+template <int TM, int TN>
+__device__ __forceinline__ void ring64_read(const RingCtx& c, const uint16_t* __restrict__ ra,
+                                            const uint16_t* __restrict__ rb, Ring64Frags<TM, TN>& f) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int i = 0; i < TM / 64; ++i)
+      f.a[q][i] = *reinterpret_cast<const uint4*>(ra + swz8(c.wm * (TM / 2) + i * 32 + c.fr, 2 * q + c.fk));
+#pragma unroll
+    for (int j = 0; j < TN / 64; ++j)
+      f.b[q][j] = *reinterpret_cast<const uint4*>(rb + swz8(c.wn * (TN / 2) + j * 32 + c.fr, 2 * q + c.fk));
+  }
+}
+
+// Step k of an NS-stage ring: MFMAs of stage k on cf, reads of stage k+1
+// (ra, rb) into nf, DMA of stage k+NS into the buffer of stage k (da, db);
+// then wait until stage k+2 has landed and the own reads are done, and sync
+template <int TM, int TN, int NS>
+__device__ __forceinline__ void ring64_step(const RingCtx& c, const uint16_t* __restrict__ ra,
+                                            const uint16_t* __restrict__ rb, uint16_t* __restrict__ da,
+                                            uint16_t* __restrict__ db, int kt, int kend,
+                                            const Ring64Frags<TM, TN>& cf, Ring64Frags<TM, TN>& nf,
+                                            floatx16 (&acc)[TM / 64][TN / 64]) {
+  constexpr int MI = TM / 64, NJ = TN / 64;
+  constexpr int kDma = (TM + TN) / 32, kReads = 4 * (MI + NJ), kMfma = 4 * MI * NJ;
+  static_assert(kDma <= kReads && kMfma >= kReads, "one DMA per read group, at least one MFMA per group");
+  ring64_issue<TM, TN>(c, da, db, min(kt + NS, kend - 1));
+  ring64_read<TM, TN>(c, ra, rb, nf);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cf.a[q][i]), as_bf16x8(cf.b[q][j]), acc[i][j], 0,
+                                                            0, 0);
+#pragma unroll
+  for (int r = 0; r < kReads; ++r) {
+    if (r < kDma) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one DMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                // one fragment read
+    if (r < kMfma % kReads)
+      __builtin_amdgcn_sched_group_barrier(0x008, kMfma / kReads + 1, 0);  // MFMAs
+    else
+      __builtin_amdgcn_sched_group_barrier(0x008, kMfma / kReads, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * kDma) & ~(15 << 8));  // + lgkmcnt(0)
+  ring_barrier();
+}
+
+// K tiles [kt0, kend) through 3 stages (any count >= 1): six steps per
+// round (three buffers x two fragment sets), later steps of the last round
+// skipped by uniform branches
+template <int TM, int TN>
+__device__ __forceinline__ void ring64_loop3(const RingCtx& c, uint16_t* __restrict__ a0, uint16_t* __restrict__ a1,
+                                             uint16_t* __restrict__ a2, uint16_t* __restrict__ b0,
+                                             uint16_t* __restrict__ b1, uint16_t* __restrict__ b2, int kt0, int kend,
+                                             floatx16 (&acc)[TM / 64][TN / 64]) {
+  constexpr int n = (TM + TN) / 32;
+  ring64_issue<TM, TN>(c, a0, b0, kt0);
+  ring64_issue<TM, TN>(c, a1, b1, min(kt0 + 1, kend - 1));
+  ring64_issue<TM, TN>(c, a2, b2, min(kt0 + 2, kend - 1));
+  Ring64Frags<TM, TN> f0, f1;
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * n));  // stage kt0 has landed
+  ring_barrier();
+  ring64_read<TM, TN>(c, a0, b0, f0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(n) & ~(15 << 8));  // stage kt0+1 landed, own reads done
+  ring_barrier();
+  // (nested, so that every path into a step passes the previous step's wait)
+  for (int kt = kt0; kt < kend; kt += 6) {
+    ring64_step<TM, TN, 3>(c, a1, b1, a0, b0, kt, kend, f0, f1, acc);
+    if (kt + 1 < kend) {
+      ring64_step<TM, TN, 3>(c, a2, b2, a1, b1, kt + 1, kend, f1, f0, acc);
+      if (kt + 2 < kend) {
+        ring64_step<TM, TN, 3>(c, a0, b0, a2, b2, kt + 2, kend, f0, f1, acc);
+        if (kt + 3 < kend) {
+          ring64_step<TM, TN, 3>(c, a1, b1, a0, b0, kt + 3, kend, f1, f0, acc);
+          if (kt + 4 < kend) {
+            ring64_step<TM, TN, 3>(c, a2, b2, a1, b1, kt + 4, kend, f0, f1, acc);
+            if (kt + 5 < kend) ring64_step<TM, TN, 3>(c, a0, b0, a2, b2, kt + 5, kend, f1, f0, acc);
+          }
+        }
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // drain the trailing re-fetches before the workgroup ends
+}
+
+// K tiles [kt0, kend) through 4 stages (any count >= 1; later steps of the
+// last round skipped by nested uniform branches)
+template <int TM, int TN>
+__device__ __forceinline__ void ring64_loop4(const RingCtx& c, uint16_t* __restrict__ a0, uint16_t* __restrict__ a1,
+                                             uint16_t* __restrict__ a2, uint16_t* __restrict__ a3,
+                                             uint16_t* __restrict__ b0, uint16_t* __restrict__ b1,
+                                             uint16_t* __restrict__ b2, uint16_t* __restrict__ b3, int kt0, int kend,
+                                             floatx16 (&acc)[TM / 64][TN / 64]) {
+  constexpr int n = (TM + TN) / 32;
+  ring64_issue<TM, TN>(c, a0, b0, kt0);
+  ring64_issue<TM, TN>(c, a1, b1, min(kt0 + 1, kend - 1));
+  ring64_issue<TM, TN>(c, a2, b2, min(kt0 + 2, kend - 1));
+  ring64_issue<TM, TN>(c, a3, b3, min(kt0 + 3, kend - 1));
+  Ring64Frags<TM, TN> f0, f1;
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * n));  // stage kt0 has landed
+  ring_barrier();
+  ring64_read<TM, TN>(c, a0, b0, f0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * n) & ~(15 << 8));  // stage kt0+1 landed, own reads done
+  ring_barrier();
+  for (int kt = kt0; kt < kend; kt += 4) {
+    ring64_step<TM, TN, 4>(c, a1, b1, a0, b0, kt, kend, f0, f1, acc);
+    if (kt + 1 < kend) {
+      ring64_step<TM, TN, 4>(c, a2, b2, a1, b1, kt + 1, kend, f1, f0, acc);
+      if (kt + 2 < kend) {
+        ring64_step<TM, TN, 4>(c, a3, b3, a2, b2, kt + 2, kend, f0, f1, acc);
+        if (kt + 3 < kend) ring64_step<TM, TN, 4>(c, a0, b0, a3, b3, kt + 3, kend, f1, f0, acc);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+// MLORA_RING64=0 keeps the GEMMs on 32-deep stages (A/B timing)
+bool ring64_enabled() {
+  static int on = -1;
+  if (on < 0) {
+    const char* e = getenv("MLORA_RING64");
+    on = (e && e[0] == '0') ? 0 : 1;
+  }
+  return on == 1;
+}
+
 // MLORA_RING_PIPE=0 keeps the ring on the unpipelined step (A/B timing)
 int ring_pipe_enabled() {
   static int on = -1;
@@ -864,7 +1051,7 @@ __device__ __forceinline__ void ring_lora_epilogue(const RingCtx& c, int m0, int
 // n_shrink > 0 (split-K form): the first n_shrink workgroups of the launch
 // (blockIdx.y == 0) compute the per-row shrink T[k] = s_a Down_a x_k for
 // rows k < M instead (independent work that shares the launch).
-template <int TM, int TN, bool PART, bool LORA>
+template <int TM, int TN, int KD, bool PART, bool LORA>
 __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_ring(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y,
     float* __restrict__ part, int M, int K, int N, int tiles_n, int n_tiles, int per_xcd, int kt_per, PoolView pv,
@@ -915,6 +1102,10 @@ __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(1,
   // lane L fills LDS slot (row L >> 2 of its 16-row group, physical chunk
   // L & 3), which holds logical chunk (L & 3) ^ ((row >> 2) & 3)
   c.voff = (lane >> 2) * c.row_bytes + (((lane & 3) ^ ((lane >> 4) & 3)) << 4);
+  // 64-deep stages: lane L fills LDS slot (row L >> 3 of its 8-row group,
+  // physical chunk L & 7); the group's rows 8i + (L >> 3) have (row >> 1) & 7
+  // = (4 (i & 1) + (L >> 4)) & 7, and i & 1 = wave & 1 for every group of a wave
+  c.voff64 = (lane >> 3) * c.row_bytes + (((lane & 7) ^ ((4 * (c.wave & 1) + (lane >> 4)) & 7)) << 4);
 
   floatx16 acc[MI][NJ];
 #pragma unroll
@@ -925,8 +1116,12 @@ __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(1,
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   const int kt0 = PART ? blockIdx.y * kt_per : 0;
-  const int kend = PART ? kt0 + kt_per : K / GBK;
-  if constexpr (TM == 256) {
+  const int kend = PART ? kt0 + kt_per : K / KD;
+  if constexpr (KD == 64 && TM == 256) {
+    ring64_loop3<TM, TN>(c, l64_a0, l64_a1, l64_a2, l64_b0, l64_b1, l64_b2, kt0, kend, acc);
+  } else if constexpr (KD == 64) {
+    ring64_loop4<TM, TN>(c, m64_a0, m64_a1, m64_a2, m64_a3, m64_b0, m64_b1, m64_b2, m64_b3, kt0, kend, acc);
+  } else if constexpr (TM == 256) {
     if (pipe)
       ring_mainloop_p<TM, TN>(c, big_a0, big_a1, big_a2, big_a3, big_b0, big_b1, big_b2, big_b3, kt0, kend, acc);
     else
@@ -1004,12 +1199,19 @@ bool big_gemm_enabled() {
 }
 
 hipError_t launch_big(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N, hipStream_t st) {
-  const int tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
+  const bool r64 = ring64_enabled();
+  const int TN = r64 ? 128 : 256;
+  const int tiles_m = (M + 255) / 256, tiles_n = (N + TN - 1) / TN;
   const int n_tiles = tiles_m * tiles_n;
   const int per_xcd = (n_tiles + 7) / 8;
-  MLORA_LAUNCH("gemm_big", (gemm_ring<256, 256, false, false>), dim3(per_xcd * 8), dim3(kRingThreads), 0, st, X, W,
-               Y, (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, PoolView{}, (const int32_t*)nullptr,
-               LoraOperands{}, 0, (float*)nullptr, 0, ring_pipe_enabled());
+  if (r64)
+    MLORA_LAUNCH("gemm_big", (gemm_ring<256, 128, 64, false, false>), dim3(per_xcd * 8), dim3(kRingThreads), 0, st,
+                 X, W, Y, (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, PoolView{}, (const int32_t*)nullptr,
+                 LoraOperands{}, 0, (float*)nullptr, 0, 1);
+  else
+    MLORA_LAUNCH("gemm_big", (gemm_ring<256, 256, 32, false, false>), dim3(per_xcd * 8), dim3(kRingThreads), 0, st,
+                 X, W, Y, (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, PoolView{}, (const int32_t*)nullptr,
+                 LoraOperands{}, 0, (float*)nullptr, 0, ring_pipe_enabled());
   return launched();
 }
 
@@ -1345,9 +1547,14 @@ hipError_t launch_mid_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, in
   // shrink workgroups: one per row, a multiple of 8 so the GEMM blocks keep
   // their XCD mapping
   const int ns = shrink ? (M + 7) / 8 * 8 : 0;
-  MLORA_LAUNCH(shrink ? "gemm_mid+shrink_rows" : "gemm_mid", (gemm_ring<128, 128, true, false>),
-               dim3(ns + per_xcd * 8, S), dim3(kRingThreads), 0, st, X, W, Y, part, M, K, N, tiles_n, n_tiles,
-               per_xcd, K / GBK / S, pv, row_key, LoraOperands{}, proj, T, ns, ring_pipe_enabled());
+  if (ring64_enabled())
+    MLORA_LAUNCH(shrink ? "gemm_mid+shrink_rows" : "gemm_mid", (gemm_ring<128, 128, 64, true, false>),
+                 dim3(ns + per_xcd * 8, S), dim3(kRingThreads), 0, st, X, W, Y, part, M, K, N, tiles_n, n_tiles,
+                 per_xcd, K / GBK64 / S, pv, row_key, LoraOperands{}, proj, T, ns, 1);
+  else
+    MLORA_LAUNCH(shrink ? "gemm_mid+shrink_rows" : "gemm_mid", (gemm_ring<128, 128, 32, true, false>),
+                 dim3(ns + per_xcd * 8, S), dim3(kRingThreads), 0, st, X, W, Y, part, M, K, N, tiles_n, n_tiles,
+                 per_xcd, K / GBK / S, pv, row_key, LoraOperands{}, proj, T, ns, ring_pipe_enabled());
   hipError_t e = launched();
   if (e != hipSuccess) return e;
   const int threads = M * (N / 8);
@@ -1434,12 +1641,19 @@ bool big_lora_ok(const PoolView& pv, const uint16_t* X, const uint16_t* W, int M
 hipError_t launch_big_lora(const PoolView& pv, const uint16_t* X, const uint16_t* W, const int32_t* ws,
                            const LoraOperands& lo, uint16_t* Y, int M, hipStream_t st) {
   const int K = pv.din, N = pv.dout;
-  const int tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
+  const bool r64 = ring64_enabled();
+  const int TN = r64 ? 128 : 256;
+  const int tiles_m = (M + 255) / 256, tiles_n = (N + TN - 1) / TN;
   const int n_tiles = tiles_m * tiles_n;
   const int per_xcd = (n_tiles + 7) / 8;
-  MLORA_LAUNCH("gemm_big_lora", (gemm_ring<256, 256, false, true>), dim3(per_xcd * 8), dim3(kRingThreads), 0, st, X,
-               W, Y, (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, pv, ws + MLORA_SEG_ROWKEY(M), lo, 0,
-               (float*)nullptr, 0, ring_pipe_enabled());
+  if (r64)
+    MLORA_LAUNCH("gemm_big_lora", (gemm_ring<256, 128, 64, false, true>), dim3(per_xcd * 8), dim3(kRingThreads), 0,
+                 st, X, W, Y, (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, pv, ws + MLORA_SEG_ROWKEY(M), lo,
+                 0, (float*)nullptr, 0, 1);
+  else
+    MLORA_LAUNCH("gemm_big_lora", (gemm_ring<256, 256, 32, false, true>), dim3(per_xcd * 8), dim3(kRingThreads), 0,
+                 st, X, W, Y, (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, pv, ws + MLORA_SEG_ROWKEY(M), lo,
+                 0, (float*)nullptr, 0, ring_pipe_enabled());
   return launched();
 }
 
