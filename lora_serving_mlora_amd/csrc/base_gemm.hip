@@ -900,6 +900,113 @@ __device__ __forceinline__ void ring64_loop4(const RingCtx& c, uint16_t* __restr
   __builtin_amdgcn_s_waitcnt(0);
 }
 
+// 256 x 256 tiles with 64-deep stages: two 64 KiB stages fill the LDS, so the
+// ring is double-buffered and pipelined at half-stage granularity (two
+// 16-deep quarters per register set): the MFMAs of one half run while the
+// other half, or the first half of the next stage, is read.  One barrier
+// per stage, after the second half has been read: every wave is then done
+// with the stage's buffer, which receives the DMA of stage k+2, and stage
+// k+1 has landed (the only DMA in flight was waited for).
+__shared__ __attribute__((aligned(16))) uint16_t h64_a0[256 * GBK64];
+__shared__ __attribute__((aligned(16))) uint16_t h64_a1[256 * GBK64];
+__shared__ __attribute__((aligned(16))) uint16_t h64_b0[256 * GBK64];
+__shared__ __attribute__((aligned(16))) uint16_t h64_b1[256 * GBK64];
+
+template <int TM, int TN>
+struct RingHalf {
+  uint4 a[2][TM / 64], b[2][TN / 64];
+};
+
+template <int TM, int TN>
+__device__ __forceinline__ void ring64_read_half(const RingCtx& c, const uint16_t* __restrict__ ra,
+                                                 const uint16_t* __restrict__ rb, int h, RingHalf<TM, TN>& f) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+#pragma unroll
+    for (int i = 0; i < TM / 64; ++i)
+      f.a[q][i] = *reinterpret_cast<const uint4*>(ra + swz8(c.wm * (TM / 2) + i * 32 + c.fr, 4 * h + 2 * q + c.fk));
+#pragma unroll
+    for (int j = 0; j < TN / 64; ++j)
+      f.b[q][j] = *reinterpret_cast<const uint4*>(rb + swz8(c.wn * (TN / 2) + j * 32 + c.fr, 4 * h + 2 * q + c.fk));
+  }
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void ring64_mfma_half(const RingHalf<TM, TN>& f, floatx16 (&acc)[TM / 64][TN / 64]) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int i = 0; i < TM / 64; ++i)
+#pragma unroll
+      for (int j = 0; j < TN / 64; ++j)
+        acc[i][j] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(f.a[q][i]), as_bf16x8(f.b[q][j]), acc[i][j], 0, 0, 0);
+}
+
+// stage k in (ca, cb), the other buffer (oa, ob) holds stage k+1 (landed
+// before this call); h0 holds the first half of stage k
+template <int TM, int TN>
+__device__ __forceinline__ void ring64x2_stage(const RingCtx& c, uint16_t* __restrict__ ca, uint16_t* __restrict__ cb,
+                                               const uint16_t* __restrict__ oa, const uint16_t* __restrict__ ob,
+                                               int kt, int kend, RingHalf<TM, TN>& h0, RingHalf<TM, TN>& h1,
+                                               floatx16 (&acc)[TM / 64][TN / 64]) {
+  constexpr int MI = TM / 64, NJ = TN / 64;
+  constexpr int kReads = 2 * (MI + NJ), kMfma = 2 * MI * NJ, kDma = (TM + TN) / 32;
+  static_assert(kDma <= kReads && kMfma % kReads == 0, "schedule pattern");
+  // first half: MFMAs on h0, reads of the second half into h1
+  ring64_read_half<TM, TN>(c, ca, cb, 1, h1);
+  ring64_mfma_half<TM, TN>(h0, acc);
+#pragma unroll
+  for (int r = 0; r < kReads; ++r) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfma / kReads, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // every wave is done with this buffer; stage k+1 (the one DMA in flight) has landed
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & ~(15 << 8));
+  ring_barrier();
+  // second half: DMA of stage k+2 into this buffer, MFMAs on h1, reads of
+  // the next stage's first half into h0
+  ring64_issue<TM, TN>(c, ca, cb, min(kt + 2, kend - 1));
+  ring64_read_half<TM, TN>(c, oa, ob, 0, h0);
+  ring64_mfma_half<TM, TN>(h1, acc);
+#pragma unroll
+  for (int r = 0; r < kReads; ++r) {
+    if (r < kDma) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfma / kReads, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void ring64x2_loop(const RingCtx& c, uint16_t* __restrict__ a0, uint16_t* __restrict__ a1,
+                                              uint16_t* __restrict__ b0, uint16_t* __restrict__ b1, int kt0, int kend,
+                                              floatx16 (&acc)[TM / 64][TN / 64]) {
+  constexpr int n = (TM + TN) / 32;
+  ring64_issue<TM, TN>(c, a0, b0, kt0);
+  ring64_issue<TM, TN>(c, a1, b1, min(kt0 + 1, kend - 1));
+  RingHalf<TM, TN> h0, h1;
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(n));  // stage kt0 has landed
+  ring_barrier();
+  ring64_read_half<TM, TN>(c, a0, b0, 0, h0);
+  for (int kt = kt0; kt < kend; kt += 2) {  // (kend - kt0) even: K is a multiple of 128
+    ring64x2_stage<TM, TN>(c, a0, b0, a1, b1, kt, kend, h0, h1, acc);
+    ring64x2_stage<TM, TN>(c, a1, b1, a0, b0, kt + 1, kend, h0, h1, acc);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+// MLORA_RING64X2=0 keeps large products on the 3-stage 256 x 128 ring (A/B timing)
+bool ring64x2_enabled() {
+  static int on = -1;
+  if (on < 0) {
+    const char* e = getenv("MLORA_RING64X2");
+    on = (e && e[0] == '0') ? 0 : 1;
+  }
+  return on == 1;
+}
+
 // MLORA_RING64=0 keeps the GEMMs on 32-deep stages (A/B timing)
 bool ring64_enabled() {
   static int on = -1;
@@ -1117,7 +1224,9 @@ __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(1,
 
   const int kt0 = PART ? blockIdx.y * kt_per : 0;
   const int kend = PART ? kt0 + kt_per : K / KD;
-  if constexpr (KD == 64 && TM == 256) {
+  if constexpr (KD == 64 && TM == 256 && TN == 256) {
+    ring64x2_loop<TM, TN>(c, h64_a0, h64_a1, h64_b0, h64_b1, kt0, kend, acc);
+  } else if constexpr (KD == 64 && TM == 256) {
     ring64_loop3<TM, TN>(c, l64_a0, l64_a1, l64_a2, l64_b0, l64_b1, l64_b2, kt0, kend, acc);
   } else if constexpr (KD == 64) {
     ring64_loop4<TM, TN>(c, m64_a0, m64_a1, m64_a2, m64_a3, m64_b0, m64_b1, m64_b2, m64_b3, kt0, kend, acc);
@@ -1139,15 +1248,20 @@ __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(1,
     ring_lora_epilogue<TM, TN>(c, m0, n0, M, N, pv, row_key, lo, acc, key);
   }
 
-  // C layout of a 32x32 tile: lane l holds column l%32, rows 8*(v/4) + 4*(l/32) + v%4
+  // C layout of a 32x32 tile: lane l holds column l%32, rows 8*(v/4) + 4*(l/32) + v%4.
+  // The lane index passes through an empty asm statement, so the stores'
+  // addresses are computed here and not hoisted above the main loop, where
+  // they would hold registers the fragments need.
+  int sl = lane;
+  asm volatile("" : "+v"(sl));
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int col = n0 + c.wn * (TN / 2) + j * 32 + (lane & 31);
+      const int col = n0 + c.wn * (TN / 2) + j * 32 + (sl & 31);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int r = m0 + c.wm * (TM / 2) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int r = m0 + c.wm * (TM / 2) + i * 32 + 8 * (v >> 2) + 4 * (sl >> 5) + (v & 3);
         if (r < M && col < N) {
           if (PART)
             part[((size_t)blockIdx.y * M + r) * N + col] = acc[i][j][v];
@@ -1199,12 +1313,16 @@ bool big_gemm_enabled() {
 }
 
 hipError_t launch_big(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N, hipStream_t st) {
-  const bool r64 = ring64_enabled();
-  const int TN = r64 ? 128 : 256;
+  const bool r64 = ring64_enabled(), x2 = r64 && ring64x2_enabled();
+  const int TN = (r64 && !x2) ? 128 : 256;
   const int tiles_m = (M + 255) / 256, tiles_n = (N + TN - 1) / TN;
   const int n_tiles = tiles_m * tiles_n;
   const int per_xcd = (n_tiles + 7) / 8;
-  if (r64)
+  if (x2)
+    MLORA_LAUNCH("gemm_big", (gemm_ring<256, 256, 64, false, false>), dim3(per_xcd * 8), dim3(kRingThreads), 0, st,
+                 X, W, Y, (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, PoolView{}, (const int32_t*)nullptr,
+                 LoraOperands{}, 0, (float*)nullptr, 0, 1);
+  else if (r64)
     MLORA_LAUNCH("gemm_big", (gemm_ring<256, 128, 64, false, false>), dim3(per_xcd * 8), dim3(kRingThreads), 0, st,
                  X, W, Y, (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, PoolView{}, (const int32_t*)nullptr,
                  LoraOperands{}, 0, (float*)nullptr, 0, 1);
@@ -1641,12 +1759,16 @@ bool big_lora_ok(const PoolView& pv, const uint16_t* X, const uint16_t* W, int M
 hipError_t launch_big_lora(const PoolView& pv, const uint16_t* X, const uint16_t* W, const int32_t* ws,
                            const LoraOperands& lo, uint16_t* Y, int M, hipStream_t st) {
   const int K = pv.din, N = pv.dout;
-  const bool r64 = ring64_enabled();
-  const int TN = r64 ? 128 : 256;
+  const bool r64 = ring64_enabled(), x2 = r64 && ring64x2_enabled();
+  const int TN = (r64 && !x2) ? 128 : 256;
   const int tiles_m = (M + 255) / 256, tiles_n = (N + TN - 1) / TN;
   const int n_tiles = tiles_m * tiles_n;
   const int per_xcd = (n_tiles + 7) / 8;
-  if (r64)
+  if (x2)
+    MLORA_LAUNCH("gemm_big_lora", (gemm_ring<256, 256, 64, false, true>), dim3(per_xcd * 8), dim3(kRingThreads), 0,
+                 st, X, W, Y, (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, pv, ws + MLORA_SEG_ROWKEY(M), lo,
+                 0, (float*)nullptr, 0, 1);
+  else if (r64)
     MLORA_LAUNCH("gemm_big_lora", (gemm_ring<256, 128, 64, false, true>), dim3(per_xcd * 8), dim3(kRingThreads), 0,
                  st, X, W, Y, (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, pv, ws + MLORA_SEG_ROWKEY(M), lo,
                  0, (float*)nullptr, 0, 1);
