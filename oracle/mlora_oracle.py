@@ -45,7 +45,12 @@ Pages cited (by address and section):
    path splits the branch into (wiblog article, Punica section: each group
    computes its BAx and writes back in original order).
 
-4. Accounting: `branch_flops` / `padded_flops` (M031 card section 03:
+4. `merge` - the merged alternative: W0 + sign * s_a * Up_a Down_a, the
+   weight that serves adapter a's rows with the base product alone (M031
+   card section 04; airsota card section three, derivation 2); sign = -1
+   takes the term out again.
+
+5. Accounting: `branch_flops` / `padded_flops` (M031 card section 03:
    2 * rows * r * (din + dout) per group, and the same with every row padded
    to the largest rank) and `adapter_bytes` (M031 card section 06: rank-r
    factors of one din x dout projection at 2 bytes per parameter).
@@ -68,7 +73,7 @@ import numpy as np
 
 __all__ = [
     "NONE", "STATUS_BAD_ID", "STATUS_NOT_RESIDENT", "Adapter",
-    "widen_bf16", "row_keys", "segments", "linear", "shrink_rows", "expand_rows",
+    "widen_bf16", "row_keys", "segments", "linear", "shrink_rows", "expand_rows", "merge",
     "branch_flops", "padded_flops", "base_flops", "adapter_bytes", "within_tolerance",
     "max_scaled_error",
 ]
@@ -214,6 +219,15 @@ def linear(X: np.ndarray, W0: np.ndarray, row_adapter: Sequence[int],
             y[:] = np.nan
         Y[i] = y
     return Y
+
+
+def merge(W0: np.ndarray, adapter: Adapter, sign: float = 1.0, dtype=np.float64) -> np.ndarray:
+    """W0 + sign * s * (Up @ Down) for one adapter's (s, Down, Up), the
+    merged weight of the M031 card's section 04 (a new array; W0 is not
+    changed)."""
+    s, down, up = adapter
+    W0 = np.asarray(W0, dtype=dtype)
+    return W0 + dtype(sign) * dtype(s) * (np.asarray(up, dtype=dtype) @ np.asarray(down, dtype=dtype))
 
 
 def branch_flops(active_ranks: Iterable[int], din: int, dout: int) -> int:

@@ -126,6 +126,41 @@ def test_merge_identity(seed, din, dout, ranks):
         np.testing.assert_allclose(Y[k], ref, rtol=1e-10, atol=1e-10 * np.abs(ref).max())
 
 
+@pytest.mark.parametrize("seed,din,dout,rank", [(31, 16, 24, 3), (32, 40, 8, 8), (33, 8, 64, 16)])
+def test_merge_serves_its_adapter(seed, din, dout, rank):
+    """O.merge: the merged weight's plain product equals the layer's output
+    for every row of that adapter (M031 card section 04), and differs for a
+    row of another adapter; merging with -1 restores W0."""
+    ranks = {0: rank, 1: rank + 1}
+    ids = np.array([0, 1, 0, -1, 0, 1], dtype=np.int32)
+    w = synth.custom("mrg", seed, din, dout, ids, ranks, scales={0: 1.5, 1: 0.75})
+    X, W0 = O.widen_bf16(w.x_bits()), O.widen_bf16(w.w0_bits())
+    ad = _adapters_f64(w)
+    Y = O.linear(X, W0, ids, ad, w.max_adapters)
+    Wm = O.merge(W0, ad[0])
+    for k in (0, 2, 4):
+        np.testing.assert_allclose(Wm @ X[k], Y[k], rtol=1e-10, atol=1e-12)
+    assert not O.within_tolerance(Wm @ X[1], Y[1])
+    np.testing.assert_allclose(O.merge(Wm, ad[0], sign=-1.0), W0, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(O.merge(W0, (0.0, ad[0][1], ad[0][2])), W0)  # scale 0: no change
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_merge_exact_rational(seed):
+    """O.merge against an exact rational evaluation on tiny integer factors."""
+    g = np.random.default_rng(700 + seed)
+    din, dout, r = int(g.integers(1, 7)), int(g.integers(1, 7)), int(g.integers(1, 5))
+    s = float(g.choice([1.0, 2.0, 0.5]))
+    sign = float(g.choice([1.0, -1.0]))
+    W0 = g.integers(-3, 4, size=(dout, din)).astype(np.float64)
+    D = g.integers(-2, 3, size=(r, din)).astype(np.float64)
+    U = g.integers(-2, 3, size=(dout, r)).astype(np.float64)
+    got = O.merge(W0, (s, D, U), sign=sign)
+    want = [[Fraction(int(W0[c][i])) + Fraction(sign) * Fraction(s) *
+             sum(Fraction(int(U[c][q])) * int(D[q][i]) for q in range(r)) for i in range(din)] for c in range(dout)]
+    assert [[Fraction(v) for v in row] for row in got.tolist()] == want
+
+
 def test_all_rows_one_adapter_is_one_matmul():
     ranks = {0: 5}
     ids = np.zeros(29, dtype=np.int32)
