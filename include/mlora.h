@@ -296,6 +296,24 @@ mlora_status mlora_apply(const mlora_pool* pool, int32_t proj, const uint16_t* X
                          int32_t variant, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * The merged alternative (M031 card, section 04: W_merged = W_base + scale *
+ * Up Down serves that one adapter with a plain GEMM; airsota card, section
+ * three, derivation 2): adds, or with sign = -1 takes out, one resident
+ * adapter's low-rank term into a base weight IN PLACE:
+ *   W0[c][i] <- bf16_rne( W0[c][i] + sign * s_a * sum_q Up_a[c][q] Down_a[q][i] )
+ * with the sum over q < rank(a) in fp32, in rank order.
+ *   W0: device bf16 [dout][din] of projection `proj` (read and written);
+ *   sign: +1 merges, -1 unmerges (any finite factor is accepted; an unmerge
+ *   restores W0 only up to the bf16 rounding of the two stores).
+ * Returns MLORA_ENOENT if the adapter is not resident, MLORA_EINVAL for a bad
+ * id, projection, NULL W0 or non-finite sign.  Rows of a merged weight give
+ * the adapter's output through mlora_base_gemm (or mlora_apply with id -1);
+ * rows of other adapters must not be served from it.
+ * ------------------------------------------------------------------------- */
+mlora_status mlora_merge(const mlora_pool* pool, int32_t adapter_id, int32_t proj, uint16_t* W0, float sign,
+                         void* stream);
+
+/* ---------------------------------------------------------------------------
  * Measurement helper: a plain streaming copy (dst = src, `bytes` a multiple
  * of 16, both 16-byte aligned), used to calibrate achievable HBM bandwidth
  * and hardware byte counters against a kernel of known traffic.

@@ -23,7 +23,7 @@ import numpy as np
 __all__ = [
     "MloraError", "lib", "Pool", "build_segments", "segments_header", "read_segments",
     "base_gemm", "shrink", "shrink_max_chunks", "expand", "fused", "shrink_rows", "gemm_lora", "new_work", "rows_t", "apply", "plan", "work_bytes",
-    "hbm_copy", "timing_arm", "timing_read", "VARIANTS", "ITEM_ROWS", "TILE_ROWS", "MAX_ROWS", "MAX_RANK", "SEG", "EXPORTS", "LIB_PATH",
+    "merge", "hbm_copy", "timing_arm", "timing_read", "VARIANTS", "ITEM_ROWS", "TILE_ROWS", "MAX_ROWS", "MAX_RANK", "SEG", "EXPORTS", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmlora.so")
@@ -74,6 +74,7 @@ EXPORTS = {
     "mlora_plan": (ctypes.c_int, [_c_void_p, _i32, _i32, _pi32, _pi32]),
     "mlora_apply": (ctypes.c_int, [_c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p,
                                    _sz, _i32, _c_void_p]),
+    "mlora_merge": (ctypes.c_int, [_c_void_p, _i32, _i32, _c_void_p, _f32, _c_void_p]),
     "mlora_hbm_copy": (ctypes.c_int, [_c_void_p, _c_void_p, _sz, _c_void_p]),
     "mlora_timing_arm": (ctypes.c_int, [ctypes.c_int32]),
     "mlora_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float), ctypes.c_int32,
@@ -386,6 +387,18 @@ def apply(pool: Pool, proj: int, X, W0, seg_ws, Y=None, work=None, variant: str 
     _check(lib().mlora_apply(pool.handle, proj, _ptr(X), _ptr(W0), _ptr(seg_ws), _ptr(Y), n, _ptr(work),
                              work.numel() * work.element_size(), VARIANTS[variant], _stream()), "mlora_apply")
     return Y
+
+
+def merge(pool: Pool, adapter_id: int, proj: int, W0, sign: float = 1.0):
+    """W0 (device bf16 [dout][din], in place) += sign * s_a * Up_a Down_a."""
+    torch = _torch()
+    if W0.dtype != torch.bfloat16 or not W0.is_cuda or not W0.is_contiguous() or W0.dim() != 2:
+        raise ValueError("W0 must be a contiguous CUDA bfloat16 matrix")
+    if tuple(W0.shape) != (pool.dout, pool.din):
+        raise ValueError(f"W0 must be [{pool.dout}][{pool.din}], got {tuple(W0.shape)}")
+    _check(lib().mlora_merge(pool.handle, adapter_id, proj, _ptr(W0), ctypes.c_float(sign), _stream()),
+           f"mlora_merge({adapter_id})")
+    return W0
 
 
 def hbm_copy(dst, src, nbytes: Optional[int] = None):

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <cmath>
 #include <mutex>
 #include <string>
 #include <utility>
@@ -775,6 +776,25 @@ mlora_status mlora_timing_read(float* ms, int32_t capacity, int32_t* out_n) {
 const char* mlora_timing_name(int32_t i) {
   std::lock_guard<std::mutex> lk(g_timing.mu);
   return (i >= 0 && i < g_timing.used) ? g_timing.name[i] : nullptr;
+}
+
+mlora_status mlora_merge(const mlora_pool* p, int32_t id, int32_t proj, uint16_t* W0, float sign, void* stream) {
+  g_err.clear();
+  if (!p) return fail(MLORA_EINVAL, "pool is NULL");
+  if (!W0) return fail(MLORA_EINVAL, "W0 must not be NULL");
+  if (!std::isfinite(sign)) return fail(MLORA_EINVAL, "sign must be finite");
+  if (id < 0 || id >= p->d.max_adapters) return fail(MLORA_EINVAL, "adapter id %d outside [0, %d)", id, p->d.max_adapters);
+  if (proj < 0 || proj >= p->d.n_proj) return fail(MLORA_EINVAL, "projection %d outside [0, %d)", proj, p->d.n_proj);
+  int32_t rank;
+  float scale;
+  {
+    std::lock_guard<std::mutex> lock(const_cast<mlora_pool*>(p)->mu);
+    rank = p->rank[id];
+    scale = p->scale[id];
+  }
+  if (rank <= 0) return fail(MLORA_ENOENT, "adapter %d is not resident", id);
+  return hip_check(mlora::launch_merge(p->view(), id, proj, rank, sign * scale, W0, as_stream(stream)),
+                   "merge launch");
 }
 
 mlora_status mlora_hbm_copy(void* dst, const void* src, size_t bytes, void* stream) {
