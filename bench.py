@@ -63,6 +63,9 @@ def parse_args():
     ap.add_argument("--copy-only", action="store_true", help="only run the HBM copy calibration kernel")
     ap.add_argument("--yardstick", action="store_true",
                     help="also time the vendor GEMM (torch linear) on the same rotated operands, for context")
+    ap.add_argument("--compare-merged", action="store_true",
+                    help="also time the merged alternative: merge/unmerge of one adapter into W0, the plain GEMM "
+                         "on merged weights, and serving the batch adapter by adapter from merged weights")
     return ap.parse_args()
 
 
@@ -140,6 +143,78 @@ def measured_traffic(kernel, workload):
     if not rec or rec.get("source_sha256_16") != source_hash(kernel):
         return None
     return rec.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# the merged alternative (M031 card section 04; airsota card section three)
+# ---------------------------------------------------------------------------
+
+def compare_merged(M, torch, w, pool, X, W0s, R, seg_ws, Y, work, variant, iters=50):
+    """Times, with events on the launch stream and the same W0 rotation:
+    the grouped layer on a batch whose rows all use one adapter against the
+    plain GEMM on that adapter's merged weight (the overhead the pages put
+    at 10-25 %); one merge and one unmerge; and the mixed batch served
+    adapter by adapter from merged weights (merge, GEMM over its rows,
+    unmerge) against the grouped layer."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn):
+        for i in range(min(iters, 2 * R)):
+            fn(i)
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i in range(iters):
+            fn(i)
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / iters * 1e3
+
+    n = w.n
+    a0 = w.adapter_ids()[0]
+    ids1 = torch.full((n,), a0, dtype=torch.int32, device="cuda")
+    seg1 = M.build_segments(pool, ids1)
+    grouped_one = timed(lambda i: M.apply(pool, i % R, X, W0s[i % R], seg1, Y=Y, work=work, variant=variant))
+    Wm = [W.clone() for W in W0s]
+    for p in range(R):
+        M.merge(pool, a0, p, Wm[p], 1.0)
+    merged_gemm = timed(lambda i: M.base_gemm(X, Wm[i % R], Y))
+    merge_us = timed(lambda i: M.merge(pool, a0, i % R, Wm[i % R], 1.0 if i % 2 == 0 else -1.0))
+    del Wm
+    ids = w.row_adapter
+    groups = [(a, torch.from_numpy(np.flatnonzero(ids == a)).cuda()) for a in w.adapter_ids() if (ids == a).any()]
+    base_rows = torch.from_numpy(np.flatnonzero(ids < 0)).cuda()
+    Xa = [(a, X.index_select(0, r).contiguous(), r) for a, r in groups]
+    Xb = X.index_select(0, base_rows).contiguous() if len(base_rows) else None
+    Ya = [torch.empty((len(r), w.dout), dtype=torch.bfloat16, device="cuda") for _, r in groups]
+    Yb = torch.empty((len(base_rows), w.dout), dtype=torch.bfloat16, device="cuda") if len(base_rows) else None
+
+    Wc = [W.clone() for W in W0s]  # merged in place: keep W0s untouched
+
+    def merged_serving(i):
+        p = i % R
+        if Xb is not None:
+            M.base_gemm(Xb, Wc[p], Yb)
+        for (a, xa, _), ya in zip(Xa, Ya):
+            M.merge(pool, a, p, Wc[p], 1.0)
+            M.base_gemm(xa, Wc[p], ya)
+            M.merge(pool, a, p, Wc[p], -1.0)
+
+    ids_dev = torch.from_numpy(ids.astype(np.int32)).cuda()
+
+    def grouped(i):
+        M.build_segments(pool, ids_dev, seg_ws)
+        M.apply(pool, i % R, X, W0s[i % R], seg_ws, Y=Y, work=work, variant=variant)
+
+    grouped_mixed = timed(grouped)
+    merged_mixed = timed(merged_serving)
+    return {"adapter": int(a0), "rows": int(n),
+            "one_adapter": {"grouped_apply_us": round(grouped_one, 3), "merged_gemm_us": round(merged_gemm, 3),
+                            "grouped_over_merged_pct": round(100.0 * (grouped_one / merged_gemm - 1.0), 1)},
+            "merge_or_unmerge_us": round(merge_us, 3),
+            "mixed_batch": {"adapters": len(groups), "grouped_step_us": round(grouped_mixed, 3),
+                            "merged_serving_us": round(merged_mixed, 3)},
+            "timing": f"torch events on the launch stream around {iters} eager iterations, same W0 rotation; "
+                      "merged serving = per adapter merge + GEMM over its rows + unmerge (base-only rows on W0)"}
 
 
 # ---------------------------------------------------------------------------
@@ -379,6 +454,8 @@ def main():
     }
     if yardstick is not None:
         result["vendor_gemm_us"] = yardstick
+    if args.compare_merged:
+        result["merged_comparison"] = compare_merged(M, torch, w, pool, X, W0s, R, seg_ws, Y, work, variant)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result))

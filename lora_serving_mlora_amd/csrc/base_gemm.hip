@@ -1155,9 +1155,11 @@ __device__ __forceinline__ void ring_lora_epilogue(const RingCtx& c, int m0, int
 
 // LORA (whole-K form only): the low-rank term of every row is added in the
 // epilogue (ring_lora_epilogue) and rows with an invalid id become NaN.
-// n_shrink > 0 (split-K form): the first n_shrink workgroups of the launch
-// (blockIdx.y == 0) compute the per-row shrink T[k] = s_a Down_a x_k for
-// rows k < M instead (independent work that shares the launch).
+// n_shrink > 0 (split-K form): after its tile, every workgroup also computes
+// the per-row shrink T[k] = s_a Down_a x_k for rows k = g, g + G, ... (g its
+// index among the G = n_tiles * S tile workgroups): independent work that
+// shares the launch.  (As workgroups of their own, ahead of the tiles, the
+// rows held whole CUs: a workgroup of this kernel reserves the ring's LDS.)
 template <int TM, int TN, int KD, bool PART, bool LORA>
 __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_ring(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y,
@@ -1167,15 +1169,7 @@ __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(1,
   static_assert(!(PART && LORA), "the low-rank epilogue needs the whole K range");
   constexpr int MI = TM / 64, NJ = TN / 64;
   const int tid = threadIdx.x, lane = tid & 63;
-  if constexpr (PART) {
-    if ((int)blockIdx.x < n_shrink) {
-      if (blockIdx.y == 0)
-        for (int k = blockIdx.x; k < M; k += n_shrink)
-          shrink_row_body<true, kRingThreads / 64>(pv, proj, X, row_key, k, Trows);
-      return;
-    }
-  }
-  const int bx = (int)blockIdx.x - n_shrink;
+  const int bx = (int)blockIdx.x;
   const int t = (bx & 7) * per_xcd + (bx >> 3);
   if (t >= n_tiles) return;
   // large: groups of kGroupM row bands walked column by column, so the
@@ -1270,6 +1264,13 @@ __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(1,
         }
       }
     }
+  if constexpr (PART) {
+    if (n_shrink) {
+      const int G = n_tiles * (int)gridDim.y;
+      for (int k = t + n_tiles * (int)blockIdx.y; k < M; k += G)
+        shrink_row_body<true, kRingThreads / 64>(pv, proj, X, row_key, k, Trows);
+    }
+  }
 }
 
 // MLORA_DECODE_SPLITK=0 keeps decode batches on the one-pass skinny kernel (A/B timing)
@@ -1312,6 +1313,16 @@ bool big_gemm_enabled() {
   return on == 1;
 }
 
+// MLORA_MID_BASE=0 keeps the plain medium GEMM on the K-split kernel (A/B timing)
+bool mid_base_enabled() {
+  static int on = -1;
+  if (on < 0) {
+    const char* e = getenv("MLORA_MID_BASE");
+    on = (e && e[0] == '0') ? 0 : 1;
+  }
+  return on == 1;
+}
+
 hipError_t launch_big(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N, hipStream_t st) {
   const bool r64 = ring64_enabled(), x2 = r64 && ring64x2_enabled();
   const int TN = (r64 && !x2) ? 128 : 256;
@@ -1341,6 +1352,16 @@ hipError_t launch_gemm(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M,
     else if (M <= 32) MLORA_LAUNCH("gemm_skinny", (gemm_skinny<2, VEC>), grid, block, 0, st, X, W, Y, M, K, N);
     else if (M <= 48) MLORA_LAUNCH("gemm_skinny", (gemm_skinny<3, VEC>), grid, block, 0, st, X, W, Y, M, K, N);
     else MLORA_LAUNCH("gemm_skinny", (gemm_skinny<4, VEC>), grid, block, 0, st, X, W, Y, M, K, N);
+  } else if (VEC && M <= 1024 && K % (GBK64 * 4) == 0 && (long)M * K * 2 < (1L << 31) &&
+             (long)N * K * 2 < (1L << 31) && ring64_enabled() && mid_base_enabled()) {
+    // medium batches without scratch for split-K partials: 128x128 ring
+    // tiles over the whole K, Y written once in bf16
+    const int tiles_n = (N + 127) / 128, n_tiles = ((M + 127) / 128) * tiles_n;
+    const int per_xcd = (n_tiles + 7) / 8;
+    MLORA_LAUNCH("gemm_mid", (gemm_ring<128, 128, 64, false, false>), dim3(per_xcd * 8), dim3(kRingThreads), 0, st,
+                 X, W, Y, (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, PoolView{}, (const int32_t*)nullptr,
+                 LoraOperands{}, 0, (float*)nullptr, 0, 1);
+    return launched();
   } else if (M <= 1024 && (long)((M + 127) / 128) * ((N + 31) / 32) >= 128 && ksplit_enabled()) {
     const dim3 grid((N + 31) / 32, (M + 32 * KS_MB - 1) / (32 * KS_MB)), block(64 * kKsWaves);
     MLORA_LAUNCH("gemm_ksplit", (gemm_ksplit<VEC, false>), grid, block, 0, st, X, W, Y, M, K, N, PoolView{}, 0, nullptr,
@@ -1655,23 +1676,21 @@ int mid_split(int M, int N, int K) {
 
 bool mid_ring_ok(int M, int K) { return K % (GBK * kRingStages) == 0 && (long)M * K * 2 < (1L << 31); }
 
-// shrink: the per-row shrink (T, one slice) runs as extra workgroups of the
-// GEMM launch
+// shrink: the per-row shrink (T, one slice) runs in the tile workgroups
+// after their tiles
 hipError_t launch_mid_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N, const PoolView& pv,
                            int proj, const int32_t* row_key, float* T, float* part, bool shrink, hipStream_t st) {
   const int S = mid_split(M, N, K);
   const int tiles_n = (N + 127) / 128, n_tiles = ((M + 127) / 128) * tiles_n;
   const int per_xcd = (n_tiles + 7) / 8;
-  // shrink workgroups: one per row, a multiple of 8 so the GEMM blocks keep
-  // their XCD mapping
-  const int ns = shrink ? (M + 7) / 8 * 8 : 0;
+  const int ns = shrink ? 1 : 0;  // the tile workgroups compute the per-row shrink after their tiles
   if (ring64_enabled())
     MLORA_LAUNCH(shrink ? "gemm_mid+shrink_rows" : "gemm_mid", (gemm_ring<128, 128, 64, true, false>),
-                 dim3(ns + per_xcd * 8, S), dim3(kRingThreads), 0, st, X, W, Y, part, M, K, N, tiles_n, n_tiles,
+                 dim3(per_xcd * 8, S), dim3(kRingThreads), 0, st, X, W, Y, part, M, K, N, tiles_n, n_tiles,
                  per_xcd, K / GBK64 / S, pv, row_key, LoraOperands{}, proj, T, ns, 1);
   else
     MLORA_LAUNCH(shrink ? "gemm_mid+shrink_rows" : "gemm_mid", (gemm_ring<128, 128, 32, true, false>),
-                 dim3(ns + per_xcd * 8, S), dim3(kRingThreads), 0, st, X, W, Y, part, M, K, N, tiles_n, n_tiles,
+                 dim3(per_xcd * 8, S), dim3(kRingThreads), 0, st, X, W, Y, part, M, K, N, tiles_n, n_tiles,
                  per_xcd, K / GBK / S, pv, row_key, LoraOperands{}, proj, T, ns, ring_pipe_enabled());
   hipError_t e = launched();
   if (e != hipSuccess) return e;
