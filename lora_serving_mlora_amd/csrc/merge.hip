@@ -11,28 +11,35 @@
 // The update reads and writes every element of W0 once and does rank
 // multiply-adds per element, so it is bound by HBM traffic (4 bytes per
 // element against 2 * rank flops: 8 flop/B at rank 16), not by arithmetic:
-// plain vector FMAs, no matrix cores.  A workgroup owns 16 rows of W0 and
-// 2048 columns (8 per thread).  It stages its rows' Up entries (16 x rank,
-// gathered from the rank-major Up pages) in LDS; each thread loads its 16 W0
-// pieces first (the HBM stream), then walks the ranks: one 16-byte Down
-// piece (an L2 hit after the first workgroups: Down is rank x din) and 16
-// LDS broadcasts per rank, 128 fp32 accumulators, summed in rank order.
+// plain vector FMAs, no matrix cores.  A workgroup owns 4 rows of W0 and
+// 2048 columns (8 per thread): small, so the ~8 workgroups a CU holds are in
+// different phases (loading, summing, storing) and the HBM stream does not
+// stall while they all sum at once.  It stages its rows' Up entries (4 x rank,
+// gathered from the rank-major Up pages) and the Down page ids in LDS; each
+// thread loads its 4 W0 pieces first (the HBM stream), then walks the ranks
+// eight at a time: eight 16-byte Down pieces in flight together (L2 hits
+// after the first workgroups: Down is rank x din), 4 LDS broadcasts per
+// rank, 32 fp32 accumulators, summed in rank order.
 #include "internal.h"
 
 namespace mlora {
 namespace {
 
-constexpr int kMergeRows = 16;      // W0 rows per workgroup
+constexpr int kMergeRows = 4;       // W0 rows per workgroup
 constexpr int kMergeThreads = 256;  // 8 columns each: 2048 columns per workgroup
 
 template <bool VEC>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(PoolView pv, int adapter, int proj, int rank, float f,
                                                               uint16_t* __restrict__ W) {
+  // Up entries of the workgroup's rows, ranks padded to a multiple of 8 with
+  // zeros; Down page ids, the padding pointing at the last rank's page
   __shared__ float up_s[kMergeRows][MLORA_MAX_RANK];
+  __shared__ int32_t dp_s[MLORA_MAX_RANK];
   const int din = pv.din, dout = pv.dout;
   const int tid = threadIdx.x;
   const int c0 = blockIdx.y * kMergeRows;
   const int i0 = blockIdx.x * (kMergeThreads * 8) + tid * 8;
+  const int rpad = (rank + 7) & ~7;
   const size_t pt = ((size_t)adapter * pv.n_proj + proj) * pv.max_rank;
   const int32_t* dpage = pv.down_page + pt;
   const int32_t* upage = pv.up_page + pt;
@@ -45,10 +52,10 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(PoolView pv, int a
     for (int c = 0; c < kMergeRows; ++c)
       if (c0 + c < dout) w[c] = *reinterpret_cast<const uint4*>(W + (size_t)(c0 + c) * din + i0);
   }
-  // Up[c0 + c][q] for the workgroup's rows, from page q at offset c0 + c
-  for (int e = tid; e < kMergeRows * rank; e += kMergeThreads) {
+  if (tid < rpad) dp_s[tid] = dpage[min(tid, rank - 1)];
+  for (int e = tid; e < kMergeRows * rpad; e += kMergeThreads) {
     const int c = e % kMergeRows, q = e / kMergeRows;
-    up_s[c][q] = (c0 + c < dout) ? bf2f(pv.up[(size_t)upage[q] * dout + c0 + c]) : 0.f;
+    up_s[c][q] = (q < rank && c0 + c < dout) ? bf2f(pv.up[(size_t)upage[q] * dout + c0 + c]) : 0.f;
   }
   __syncthreads();
   if (!live) return;
@@ -58,15 +65,19 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(PoolView pv, int a
   for (int c = 0; c < kMergeRows; ++c)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[c][e] = 0.f;
-  for (int q = 0; q < rank; ++q) {
-    float d[8];
-    load8<VEC>(pv.down + (size_t)dpage[q] * din, i0, din, d);
+  // eight ranks per round: their Down pieces are in flight together
+  for (int q0 = 0; q0 < rpad; q0 += 8) {
+    float d[8][8];
 #pragma unroll
-    for (int c = 0; c < kMergeRows; ++c) {
-      const float u = up_s[c][q];
+    for (int j = 0; j < 8; ++j) load8<VEC>(pv.down + (size_t)dp_s[q0 + j] * din, i0, din, d[j]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[c][e] = fmaf(u, d[e], acc[c][e]);
-    }
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int c = 0; c < kMergeRows; ++c) {
+        const float u = up_s[c][q0 + j];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[c][e] = fmaf(u, d[j][e], acc[c][e]);
+      }
   }
 
 #pragma unroll
