@@ -63,6 +63,9 @@ def parse_args():
     ap.add_argument("--copy-only", action="store_true", help="only run the HBM copy calibration kernel")
     ap.add_argument("--yardstick", action="store_true",
                     help="also time the vendor GEMM (torch linear) on the same rotated operands, for context")
+    ap.add_argument("--compare-baselines", action="store_true",
+                    help="also time the pages' naive baselines on the device: each adapter group served by its own "
+                         "launches, and the branch with every adapter padded to the largest rank")
     ap.add_argument("--compare-merged", action="store_true",
                     help="also time the merged alternative: merge/unmerge of one adapter into W0, the plain GEMM "
                          "on merged weights, and serving the batch adapter by adapter from merged weights")
@@ -215,6 +218,92 @@ def compare_merged(M, torch, w, pool, X, W0s, R, seg_ws, Y, work, variant, iters
                             "merged_serving_us": round(merged_mixed, 3)},
             "timing": f"torch events on the launch stream around {iters} eager iterations, same W0 rotation; "
                       "merged serving = per adapter merge + GEMM over its rows + unmerge (base-only rows on W0)"}
+
+
+# ---------------------------------------------------------------------------
+# the pages' naive baselines on the device (wiblog article, baseline methods;
+# M031 card section 03, padded FLOPs)
+# ---------------------------------------------------------------------------
+
+def compare_baselines(M, torch, w, pool, X, W0s, R, seg_ws, Y, work, variant, iters=30):
+    """Times, with events on the launch stream and the same W0 rotation:
+    the grouped layer (segments + apply); the batch served group by group,
+    each adapter's rows through their own segment build and apply and the
+    base-only rows through the plain GEMM (per-request application: many
+    small launches); and the grouped layer on a pool where every adapter is
+    zero-padded to the largest rank (what a padded dense branch computes:
+    the same outputs, max_rank work per row)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn):
+        for i in range(min(iters, 2 * R)):
+            fn(i)
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i in range(iters):
+            fn(i)
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / iters * 1e3
+
+    ids = w.row_adapter
+    ids_dev = torch.from_numpy(ids.astype(np.int32)).cuda()
+
+    def grouped(i):
+        M.build_segments(pool, ids_dev, seg_ws)
+        M.apply(pool, i % R, X, W0s[i % R], seg_ws, Y=Y, work=work, variant=variant)
+
+    t_grouped = timed(grouped)
+
+    groups = []
+    for a in w.adapter_ids():
+        rows = np.flatnonzero(ids == a)
+        if len(rows):
+            r = torch.from_numpy(rows).cuda()
+            xa = X.index_select(0, r).contiguous()
+            ia = torch.full((len(rows),), a, dtype=torch.int32, device="cuda")
+            groups.append((xa, ia, M.build_segments(pool, ia), torch.empty((len(rows), w.dout),
+                          dtype=torch.bfloat16, device="cuda"), M.new_work(pool, len(rows))))
+    base_rows = np.flatnonzero(ids < 0)
+    xb = X.index_select(0, torch.from_numpy(base_rows).cuda()).contiguous() if len(base_rows) else None
+    yb = torch.empty((len(base_rows), w.dout), dtype=torch.bfloat16, device="cuda") if len(base_rows) else None
+
+    def per_group(i):
+        p = i % R
+        if xb is not None:
+            M.base_gemm(xb, W0s[p], yb)
+        for xa, ia, sa, ya, wa in groups:
+            M.build_segments(pool, ia, sa)
+            M.apply(pool, p, xa, W0s[p], sa, Y=ya, work=wa)
+
+    t_serial = timed(per_group)
+
+    # every adapter padded to the largest rank with zero factors
+    rmax = max(w.ranks.values())
+    n_pages = len(w.ranks) * rmax * R
+    padded = M.Pool(w.din, w.dout, R, w.max_adapters, w.max_rank, n_pages)
+    for a in w.adapter_ids():
+        r = w.ranks[a]
+        d = np.zeros((R, rmax, w.din), dtype=np.uint16)
+        u = np.zeros((R, w.dout, rmax), dtype=np.uint16)
+        for p in range(R):
+            d[p, :r] = w.down_bits(a, p if w.n_proj > 1 else 0)
+            u[p, :, :r] = w.up_bits(a, p if w.n_proj > 1 else 0)
+        padded.load(a, rmax, w.scales[a], d, u)
+    seg_p = M.build_segments(padded, ids_dev)
+    work_p = M.new_work(padded, w.n)
+    Yp = torch.empty_like(Y)
+
+    def padded_step(i):
+        M.build_segments(padded, ids_dev, seg_p)
+        M.apply(padded, i % R, X, W0s[i % R], seg_p, Y=Yp, work=work_p, variant=variant)
+
+    t_padded = timed(padded_step)
+    del padded
+    return {"grouped_step_us": round(t_grouped, 3),
+            "per_group_launches_us": round(t_serial, 3), "groups": len(groups),
+            "padded_to_max_rank_us": round(t_padded, 3), "max_rank": rmax,
+            "timing": f"torch events on the launch stream around {iters} eager iterations, same W0 rotation"}
 
 
 # ---------------------------------------------------------------------------
@@ -454,6 +543,8 @@ def main():
     }
     if yardstick is not None:
         result["vendor_gemm_us"] = yardstick
+    if args.compare_baselines:
+        result["baseline_comparison"] = compare_baselines(M, torch, w, pool, X, W0s, R, seg_ws, Y, work, variant)
     if args.compare_merged:
         result["merged_comparison"] = compare_merged(M, torch, w, pool, X, W0s, R, seg_ws, Y, work, variant)
     if not args.no_cpu_baseline:
