@@ -1160,16 +1160,30 @@ __device__ __forceinline__ void ring_lora_epilogue(const RingCtx& c, int m0, int
 // index among the G = n_tiles * S tile workgroups): independent work that
 // shares the launch.  (As workgroups of their own, ahead of the tiles, the
 // rows held whole CUs: a workgroup of this kernel reserves the ring's LDS.)
-template <int TM, int TN, int KD, bool PART, bool LORA>
-__global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_ring(
+// CO (medium split-K tiles only): the per-row shrink runs in n_shrink
+// workgroups of its own ahead of the tiles, and the tiles take the ring with
+// two 32 KiB stages, so a shrink workgroup and a tile workgroup fit on one CU
+// together (64 KiB of LDS each, at most 256 registers per lane) and the
+// shrink's Down reads overlap the tiles' work instead of following it.
+template <int TM, int TN, int KD, bool PART, bool LORA, bool CO>
+__device__ __forceinline__ void gemm_ring_body(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y,
     float* __restrict__ part, int M, int K, int N, int tiles_n, int n_tiles, int per_xcd, int kt_per, PoolView pv,
     const int32_t* __restrict__ row_key, LoraOperands lo, int proj, float* __restrict__ Trows, int n_shrink,
     int pipe) {
   static_assert(!(PART && LORA), "the low-rank epilogue needs the whole K range");
+  static_assert(!CO || (PART && KD == 64 && TM == 128 && TN == 128), "co-resident form: medium split-K tiles");
   constexpr int MI = TM / 64, NJ = TN / 64;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int bx = (int)blockIdx.x;
+  if constexpr (CO) {
+    if ((int)blockIdx.x < n_shrink) {
+      if (blockIdx.y == 0)
+        for (int k = blockIdx.x; k < M; k += n_shrink)
+          shrink_row_body<true, kRingThreads / 64>(pv, proj, X, row_key, k, Trows);
+      return;
+    }
+  }
+  const int bx = (int)blockIdx.x - (CO ? n_shrink : 0);
   const int t = (bx & 7) * per_xcd + (bx >> 3);
   if (t >= n_tiles) return;
   // large: groups of kGroupM row bands walked column by column, so the
@@ -1218,7 +1232,9 @@ __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(1,
 
   const int kt0 = PART ? blockIdx.y * kt_per : 0;
   const int kend = PART ? kt0 + kt_per : K / KD;
-  if constexpr (KD == 64 && TM == 256 && TN == 256) {
+  if constexpr (CO) {
+    ring64x2_loop<TM, TN>(c, m64_a0, m64_a1, m64_b0, m64_b1, kt0, kend, acc);
+  } else if constexpr (KD == 64 && TM == 256 && TN == 256) {
     ring64x2_loop<TM, TN>(c, h64_a0, h64_a1, h64_b0, h64_b1, kt0, kend, acc);
   } else if constexpr (KD == 64 && TM == 256) {
     ring64_loop3<TM, TN>(c, l64_a0, l64_a1, l64_a2, l64_b0, l64_b1, l64_b2, kt0, kend, acc);
@@ -1264,13 +1280,31 @@ __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(1,
         }
       }
     }
-  if constexpr (PART) {
+  if constexpr (PART && !CO) {
     if (n_shrink) {
       const int G = n_tiles * (int)gridDim.y;
       for (int k = t + n_tiles * (int)blockIdx.y; k < M; k += G)
         shrink_row_body<true, kRingThreads / 64>(pv, proj, X, row_key, k, Trows);
     }
   }
+}
+
+template <int TM, int TN, int KD, bool PART, bool LORA>
+__global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_ring(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y,
+    float* __restrict__ part, int M, int K, int N, int tiles_n, int n_tiles, int per_xcd, int kt_per, PoolView pv,
+    const int32_t* __restrict__ row_key, LoraOperands lo, int proj, float* __restrict__ Trows, int n_shrink,
+    int pipe) {
+  gemm_ring_body<TM, TN, KD, PART, LORA, false>(X, W, Y, part, M, K, N, tiles_n, n_tiles, per_xcd, kt_per, pv,
+                                                row_key, lo, proj, Trows, n_shrink, pipe);
+}
+
+__global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_ring_co(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y,
+    float* __restrict__ part, int M, int K, int N, int tiles_n, int n_tiles, int per_xcd, int kt_per, PoolView pv,
+    const int32_t* __restrict__ row_key, int proj, float* __restrict__ Trows, int n_shrink) {
+  gemm_ring_body<128, 128, 64, true, false, true>(X, W, Y, part, M, K, N, tiles_n, n_tiles, per_xcd, kt_per, pv,
+                                                  row_key, LoraOperands{}, proj, Trows, n_shrink, 1);
 }
 
 // MLORA_DECODE_SPLITK=0 keeps decode batches on the one-pass skinny kernel (A/B timing)
@@ -1308,6 +1342,17 @@ bool big_gemm_enabled() {
   static int on = -1;
   if (on < 0) {
     const char* e = getenv("MLORA_GEMM_BIG");
+    on = (e && e[0] == '0') ? 0 : 1;
+  }
+  return on == 1;
+}
+
+// MLORA_MID_CO=0 keeps medium split-K tiles on the 4-stage ring with the
+// shrink after the tiles (A/B timing)
+bool mid_co_enabled() {
+  static int on = -1;
+  if (on < 0) {
+    const char* e = getenv("MLORA_MID_CO");
     on = (e && e[0] == '0') ? 0 : 1;
   }
   return on == 1;
@@ -1684,7 +1729,15 @@ hipError_t launch_mid_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, in
   const int tiles_n = (N + 127) / 128, n_tiles = ((M + 127) / 128) * tiles_n;
   const int per_xcd = (n_tiles + 7) / 8;
   const int ns = shrink ? 1 : 0;  // the tile workgroups compute the per-row shrink after their tiles
-  if (ring64_enabled())
+  if (ring64_enabled() && mid_co_enabled()) {
+    // shrink workgroups ahead of the tiles: one per row up to one per CU
+    // (each then loops over rows, so the tiles still find a free slot on
+    // every CU), a multiple of 8 so the tile workgroups keep their XCD mapping
+    const int nsw = shrink ? min((M + 7) / 8 * 8, 256) : 0;
+    MLORA_LAUNCH(shrink ? "gemm_mid+shrink_rows" : "gemm_mid", gemm_ring_co, dim3(nsw + per_xcd * 8, S),
+                 dim3(kRingThreads), 0, st, X, W, Y, part, M, K, N, tiles_n, n_tiles, per_xcd, K / GBK64 / S, pv,
+                 row_key, proj, T, nsw);
+  } else if (ring64_enabled())
     MLORA_LAUNCH(shrink ? "gemm_mid+shrink_rows" : "gemm_mid", (gemm_ring<128, 128, 64, true, false>),
                  dim3(per_xcd * 8, S), dim3(kRingThreads), 0, st, X, W, Y, part, M, K, N, tiles_n, n_tiles,
                  per_xcd, K / GBK64 / S, pv, row_key, LoraOperands{}, proj, T, ns, 1);
