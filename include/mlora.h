@@ -255,9 +255,11 @@ mlora_status mlora_fused(const mlora_pool* pool, int32_t proj, const uint16_t* X
  * (Down_a x_k)[q] for every row k on a resident adapter a, q < rank(a), in
  * ORIGINAL row order (rows read directly by index, as the M031 card's
  * section 02 allows instead of regrouping); other entries are not written.
- * The rest of `work` is the GEMM's scratch (split-K partials), so the two
- * calls go in this order on one stream, and calls that share a `work` buffer
- * must not overlap.  mlora_apply with ROWS computes the same T and Y; for
+ * After the T slices, T's region holds a descriptor per row (its adapter,
+ * rank, scale and Up pages) that mlora_shrink_rows writes and
+ * mlora_gemm_lora reads.  The rest of `work` is the GEMM's scratch (split-K
+ * partials), so the two calls go in this order on one stream, and calls
+ * that share a `work` buffer must not overlap.  mlora_apply with ROWS computes the same T and Y; for
  * decode shapes it runs the per-row shrink as extra workgroups of the GEMM
  * launch (two kernels in all: GEMM + shrink, then partial sums + expand). */
 mlora_status mlora_shrink_rows(const mlora_pool* pool, int32_t proj, const uint16_t* X, const void* seg_ws,

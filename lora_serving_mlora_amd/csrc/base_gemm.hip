@@ -1179,7 +1179,7 @@ __device__ __forceinline__ void gemm_ring_body(
     if ((int)blockIdx.x < n_shrink) {
       if (blockIdx.y == 0)
         for (int k = blockIdx.x; k < M; k += n_shrink)
-          shrink_row_body<true, kRingThreads / 64>(pv, proj, X, row_key, k, Trows);
+          shrink_row_body<true, kRingThreads / 64>(pv, proj, X, row_key, k, Trows, row_desc(Trows, M, pv.max_rank));
       return;
     }
   }
@@ -1284,7 +1284,7 @@ __device__ __forceinline__ void gemm_ring_body(
     if (n_shrink) {
       const int G = n_tiles * (int)gridDim.y;
       for (int k = t + n_tiles * (int)blockIdx.y; k < M; k += G)
-        shrink_row_body<true, kRingThreads / 64>(pv, proj, X, row_key, k, Trows);
+        shrink_row_body<true, kRingThreads / 64>(pv, proj, X, row_key, k, Trows, row_desc(Trows, M, pv.max_rank));
     }
   }
 }
@@ -1558,6 +1558,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void gemm_decode(const uint16_t* __
     for (int r = cb; r < M; r += ncb) {
       const bool first = r == cb;
       const int key = first ? key0 : __builtin_amdgcn_readfirstlane(row_key[r]);
+      if (kq == 0) write_row_desc(pv, proj, key, r, row_desc(Tp, M, pv.max_rank));
       if (key < 0) continue;
       const int rank = first ? rank0 : __builtin_amdgcn_readfirstlane(pv.rank[key]);
       const int32_t* dpage = pv.down_page + ((size_t)key * pv.n_proj + proj) * pv.max_rank;
@@ -1665,7 +1666,7 @@ __global__ __launch_bounds__(kFinishThreads) void finish_part(const float* __res
   }
   float y[8];
   if (LORA) {
-    lora_delta8<true, TP>(pv, proj, row_key, T, r, M, c0, N, y);
+    lora_delta8_desc<true, TP>(pv, row_desc(const_cast<float*>(T), M, pv.max_rank), T, r, M, c0, N, y);
   } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = 0.f;

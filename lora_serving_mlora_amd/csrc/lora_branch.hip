@@ -361,7 +361,8 @@ template <bool VEC>
 __global__ __launch_bounds__(kRowThreads) void shrink_rows_kernel(PoolView pv, int proj, const uint16_t* __restrict__ X,
                                                                   const int32_t* __restrict__ row_key, int n,
                                                                   float* __restrict__ T) {
-  for (int k = blockIdx.x; k < n; k += gridDim.x) shrink_row_body<VEC>(pv, proj, X, row_key, k, T);
+  for (int k = blockIdx.x; k < n; k += gridDim.x)
+    shrink_row_body<VEC>(pv, proj, X, row_key, k, T, row_desc(T, n, pv.max_rank));
 }
 
 // ---------------------------------------------------------------------------

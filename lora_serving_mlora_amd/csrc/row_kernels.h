@@ -76,6 +76,64 @@ __device__ __forceinline__ void lora_delta8(const PoolView& pv, int proj, const 
   }
 }
 
+// The low-rank term of row r at columns [c0, c0+8) as lora_delta8, with the
+// key, rank, scale and Up page ids taken from the row's descriptor: they
+// are loaded together, so the Up loads wait for one dependent load.
+template <bool VEC, int TP = 1>
+__device__ __forceinline__ void lora_delta8_desc(const PoolView& pv, const int32_t* __restrict__ desc,
+                                                 const float* __restrict__ T, int r, int M, int c0, int N,
+                                                 float (&acc8)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc8[e] = 0.f;
+  if (r >= M || c0 >= N) return;
+  const int words = row_desc_words(pv.max_rank);
+  const int32_t* d = desc + (size_t)r * words;
+  const int key = d[0];
+  const int rank = d[1];
+  const float tscale = TP > 1 ? __int_as_float(d[2]) : 1.f;
+  if (key >= 0) {
+    const float* tr = T + (size_t)r * pv.max_rank;
+    const size_t tstride = (size_t)M * pv.max_rank;
+    const bool tvec = (pv.max_rank & 7) == 0;
+    int q0 = 0;
+    do {
+      float u8[8][8], tv[8], tq[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) load8<VEC>(pv.up + (size_t)d[4 + min(q0 + q, pv.max_rank - 1)] * pv.dout, c0, N,
+                                             u8[q]);
+      if (tvec) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) tv[q] = 0.f;
+#pragma unroll
+        for (int p = 0; p < TP; ++p) {
+          const float4 a = *reinterpret_cast<const float4*>(tr + p * tstride + q0);
+          const float4 b = *reinterpret_cast<const float4*>(tr + p * tstride + q0 + 4);
+          tv[0] += a.x; tv[1] += a.y; tv[2] += a.z; tv[3] += a.w;
+          tv[4] += b.x; tv[5] += b.y; tv[6] += b.z; tv[7] += b.w;
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int qq = min(q0 + q, pv.max_rank - 1);
+          tv[q] = tr[qq];
+#pragma unroll
+          for (int p = 1; p < TP; ++p) tv[q] += tr[p * tstride + qq];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) tq[q] = (q0 + q < rank) ? tscale * tv[q] : 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc8[e] = fmaf(tq[q], u8[q][e], acc8[e]);
+      q0 += 8;
+    } while (q0 < rank);
+  } else if (key == -2) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc8[e] = __uint_as_float(0x7fc00000u);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // shrink_rows (decode): one 8-wave workgroup per row, rows read by index in
 // original order; T[k][q] = s_a * (Down_a x_k)[q].  Each lane holds the
@@ -147,12 +205,41 @@ __device__ __forceinline__ void shrink_row_to(const PoolView& pv, const int32_t*
   } while (g0 < rank);
 }
 
-// One row k: T[k][q] = s_a (Down_a x_k)[q]; called by all 64 * NW threads
-// of a workgroup (uniform control flow, block barriers inside).
+// Row k's descriptor (row_desc_words(max_rank) words at desc + k * words),
+// one word per thread of the calling workgroup (which has at least that many
+// threads); key is the row's key, uniform.
+__device__ __forceinline__ void write_row_desc(const PoolView& pv, int proj, int key, int k,
+                                               int32_t* __restrict__ desc) {
+  const int tid = threadIdx.x;
+  const int words = row_desc_words(pv.max_rank);
+  if (tid < words) {
+    int32_t v = 0;
+    if (tid == 0) {
+      v = key;
+    } else if (key >= 0) {
+      if (tid == 1) {
+        v = pv.rank[key];
+      } else if (tid == 2) {
+        v = __float_as_int(pv.scale[key]);
+      } else if (tid >= 4) {
+        const int32_t* upage = pv.up_page + ((size_t)key * pv.n_proj + proj) * pv.max_rank;
+        const int32_t pg = upage[tid - 4];
+        v = pg < 0 ? upage[0] : pg;
+      }
+    }
+    desc[(size_t)k * words + tid] = v;
+  }
+}
+
+// One row k: T[k][q] = s_a (Down_a x_k)[q] and the row's descriptor; called
+// by all 64 * NW threads of a workgroup (uniform control flow, block
+// barriers inside).
 template <bool VEC, int NW = kRowWaves>
 __device__ __forceinline__ void shrink_row_body(const PoolView& pv, int proj, const uint16_t* __restrict__ X,
-                                                const int32_t* __restrict__ row_key, int k, float* __restrict__ T) {
+                                                const int32_t* __restrict__ row_key, int k, float* __restrict__ T,
+                                                int32_t* __restrict__ desc) {
   const int key = row_key[k];
+  write_row_desc(pv, proj, key, k, desc);
   if (key < 0) return;  // base-only or invalid: no low-rank term
   shrink_row_to<VEC, NW>(pv, pv.down_page + ((size_t)key * pv.n_proj + proj) * pv.max_rank, pv.rank[key],
                          pv.scale[key], X + (size_t)k * pv.din, T + (size_t)k * pv.max_rank);

@@ -240,7 +240,9 @@ def test_gemm_lora_with_synthetic_t(M, n, din, dout):
     Tn = synth.draw_t(w.seed, w.n, w.max_rank, 1)[0]
     W0 = w.w0_bits()
     say(f"gemm_lora synthetic T n={n} dout={dout}")
-    work = M.new_work(pool, w.n)
+    # the per-row shrink fills T and the rows' descriptors; T is then
+    # replaced by the synthetic values (the descriptors stay)
+    work = M.shrink_rows(pool, 0, to_dev_bf16(X), seg_ws)
     M.rows_t(pool, work, w.n).copy_(torch.from_numpy(Tn))
     Y = M.gemm_lora(pool, 0, to_dev_bf16(X), to_dev_bf16(W0), seg_ws, work)
     base = O.widen_bf16(X) @ O.widen_bf16(W0).T
