@@ -1172,7 +1172,7 @@ __device__ __forceinline__ void gemm_ring_body(
     const int32_t* __restrict__ row_key, LoraOperands lo, int proj, float* __restrict__ Trows, int n_shrink,
     int pipe) {
   static_assert(!(PART && LORA), "the low-rank epilogue needs the whole K range");
-  static_assert(!CO || (PART && KD == 64 && TM == 128 && TN == 128), "co-resident form: medium split-K tiles");
+  static_assert(!CO || (KD == 64 && TM == 128 && TN == 128), "co-resident form: 128x128 tiles, 64-deep stages");
   constexpr int MI = TM / 64, NJ = TN / 64;
   const int tid = threadIdx.x, lane = tid & 63;
   if constexpr (CO) {
@@ -1299,6 +1299,22 @@ __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(1,
                                                 row_key, lo, proj, Trows, n_shrink, pipe);
 }
 
+// two workgroups per CU on whole-K 128x128 tiles (plain GEMM, Y in bf16)
+__global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_ring_co_whole(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y, int M, int K, int N,
+    int tiles_n, int n_tiles, int per_xcd) {
+  gemm_ring_body<128, 128, 64, false, false, true>(X, W, Y, nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0,
+                                                   PoolView{}, nullptr, LoraOperands{}, 0, nullptr, 0, 1);
+}
+
+// the same with the low-rank epilogue
+__global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_ring_co_lora(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y, int M, int K, int N,
+    int tiles_n, int n_tiles, int per_xcd, PoolView pv, const int32_t* __restrict__ row_key, LoraOperands lo) {
+  gemm_ring_body<128, 128, 64, false, true, true>(X, W, Y, nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, pv,
+                                                  row_key, lo, 0, nullptr, 0, 1);
+}
+
 __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_ring_co(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y,
     float* __restrict__ part, int M, int K, int N, int tiles_n, int n_tiles, int per_xcd, int kt_per, PoolView pv,
@@ -1368,7 +1384,27 @@ bool mid_base_enabled() {
   return on == 1;
 }
 
+// Large products: 256x256 tiles, one workgroup per CU, unless too few tiles
+// fill the chip's 256 slots; then 128x128 tiles two workgroups per CU
+// (measured ~8 % slower per tile-flop at full occupancy, so they win when
+// they fill the machine clearly better: 2048x4096x4096 in 64 us against 91).
+bool big_prefers_co(int M, int N) {
+  if (!ring64_enabled() || !mid_co_enabled()) return false;
+  const long t256 = (long)((M + 255) / 256) * ((N + 255) / 256);
+  const long t128 = (long)((M + 127) / 128) * ((N + 127) / 128);
+  const double e256 = (double)t256 / (((t256 + 255) / 256) * 256);
+  const double e128 = (double)t128 / (((t128 + 511) / 512) * 512);
+  return e128 > 1.08 * e256;
+}
+
 hipError_t launch_big(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N, hipStream_t st) {
+  if (big_prefers_co(M, N)) {
+    const int tiles_n = (N + 127) / 128, n_tiles = ((M + 127) / 128) * tiles_n;
+    const int per_xcd = (n_tiles + 7) / 8;
+    MLORA_LAUNCH("gemm_big", gemm_ring_co_whole, dim3(per_xcd * 8), dim3(kRingThreads), 0, st, X, W, Y, M, K, N,
+                 tiles_n, n_tiles, per_xcd);
+    return launched();
+  }
   const bool r64 = ring64_enabled(), x2 = r64 && ring64x2_enabled();
   const int TN = (r64 && !x2) ? 128 : 256;
   const int tiles_m = (M + 255) / 256, tiles_n = (N + TN - 1) / TN;
@@ -1832,6 +1868,13 @@ bool big_lora_ok(const PoolView& pv, const uint16_t* X, const uint16_t* W, int M
 hipError_t launch_big_lora(const PoolView& pv, const uint16_t* X, const uint16_t* W, const int32_t* ws,
                            const LoraOperands& lo, uint16_t* Y, int M, hipStream_t st) {
   const int K = pv.din, N = pv.dout;
+  if (big_prefers_co(M, N)) {
+    const int tiles_n = (N + 127) / 128, n_tiles = ((M + 127) / 128) * tiles_n;
+    const int per_xcd = (n_tiles + 7) / 8;
+    MLORA_LAUNCH("gemm_big_lora", gemm_ring_co_lora, dim3(per_xcd * 8), dim3(kRingThreads), 0, st, X, W, Y, M, K,
+                 N, tiles_n, n_tiles, per_xcd, pv, ws + MLORA_SEG_ROWKEY(M), lo);
+    return launched();
+  }
   const bool r64 = ring64_enabled(), x2 = r64 && ring64x2_enabled();
   const int TN = (r64 && !x2) ? 128 : 256;
   const int tiles_m = (M + 255) / 256, tiles_n = (N + TN - 1) / TN;

@@ -315,14 +315,16 @@ def test_base_only_rows_bitwise_and_deterministic(M, variant):
         assert_close(dev_to_f64(Yb), dev_to_f64(M.base_gemm(Xd, W0d)), "rows all-none", tol=1e-2)
 
 
-def test_apply_large_batch_epilogue(M):
-    """Batches large enough for the 256x256 GEMM take the split variant with
+@pytest.mark.parametrize("n,dout", [(2100, 2200),   # few 256x256 tiles: 128x128 tiles, two per CU
+                                    (4090, 4090)])  # 16 x 16 tiles of 256x256
+def test_apply_large_batch_epilogue(M, n, dout):
+    """Batches large enough for the large GEMM take the split variant with
     the low-rank term added in the GEMM's epilogue: ragged M and N, ranks 1
     to 128 (up to 8 groups of 16), base-only rows and invalid ids (NaN), all
-    rows checked."""
-    w = small_workload(91, 640, 2200, 2100, {0: 1, 1: 8, 2: 17, 3: 64, 4: 128, 6: 16}, p_none=0.1)
+    rows checked, on both tile shapes of the large GEMM."""
+    w = small_workload(91, 640, dout, n, {0: 1, 1: 8, 2: 17, 3: 64, 4: 128, 6: 16}, p_none=0.1)
     ids = w.row_adapter.copy()
-    ids[[5, 700, 2099]] = [5, 99, -3]       # 5 not resident, 99 out of range, -3 invalid
+    ids[[5, 700, n - 1]] = [5, 99, -3]      # 5 not resident, 99 out of range, -3 invalid
     w = synth.custom("large_epi", w.seed, w.din, w.dout, ids, w.ranks, scales=w.scales, max_adapters=7,
                      max_rank=128)
     check_apply(M, w, variants=("split",))
