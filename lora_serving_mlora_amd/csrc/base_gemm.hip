@@ -1680,7 +1680,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void gemm_decode(const uint16_t* __
 // coalesced 16-byte pieces.
 constexpr int kFinishThreads = 64;  // one wave per workgroup: the decode grid spreads over every CU
 
-template <bool LORA, int TP>
+template <bool LORA, int TP, int QG = 8>
 __global__ __launch_bounds__(kFinishThreads) void finish_part(const float* __restrict__ part, int S,
                                                               uint16_t* __restrict__ Y, int M, int N, PoolView pv,
                                                               int proj, const int32_t* __restrict__ row_key,
@@ -1702,7 +1702,7 @@ __global__ __launch_bounds__(kFinishThreads) void finish_part(const float* __res
   }
   float y[8];
   if (LORA) {
-    lora_delta8_desc<true, TP>(pv, row_desc(const_cast<float*>(T), M, pv.max_rank), T, r, M, c0, N, y);
+    lora_delta8_desc<true, TP, QG>(pv, row_desc(const_cast<float*>(T), M, pv.max_rank), T, r, M, c0, N, y);
   } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = 0.f;
@@ -1738,11 +1738,13 @@ hipError_t launch_decode(const uint16_t* X, const uint16_t* W, uint16_t* Y, int 
   hipError_t e = launched();
   if (e != hipSuccess) return e;
   const int threads = M * (N / 8);
+  // a decode batch's finish has few waves per SIMD: ranks in rounds of 16
   if (shrink)
-    MLORA_LAUNCH("finish_part", (finish_part<true, kRowsTParts>), dim3((threads + kFinishThreads - 1) / kFinishThreads),
-                 dim3(kFinishThreads), 0, st, part, kDecSplit, Y, M, N, pv, proj, row_key, T);
+    MLORA_LAUNCH("finish_part", (finish_part<true, kRowsTParts, 16>),
+                 dim3((threads + kFinishThreads - 1) / kFinishThreads), dim3(kFinishThreads), 0, st, part, kDecSplit,
+                 Y, M, N, pv, proj, row_key, T);
   else
-    MLORA_LAUNCH("finish_part", (finish_part<true, 1>), dim3((threads + kFinishThreads - 1) / kFinishThreads),
+    MLORA_LAUNCH("finish_part", (finish_part<true, 1, 16>), dim3((threads + kFinishThreads - 1) / kFinishThreads),
                  dim3(kFinishThreads), 0, st, part, kDecSplit, Y, M, N, pv, proj, row_key, T);
   return launched();
 }

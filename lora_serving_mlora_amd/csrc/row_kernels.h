@@ -78,11 +78,16 @@ __device__ __forceinline__ void lora_delta8(const PoolView& pv, int proj, const 
 
 // The low-rank term of row r at columns [c0, c0+8) as lora_delta8, with the
 // key, rank, scale and Up page ids taken from the row's descriptor: they
-// are loaded together, so the Up loads wait for one dependent load.
-template <bool VEC, int TP = 1>
+// are loaded together, so the Up loads wait for one dependent load.  Ranks
+// go in rounds of QG (8 or 16): each round's QG page loads go out at once,
+// so a rank-16 row takes one round with QG = 16; QG = 8 keeps the register
+// count low where many waves must share each SIMD.  The sum over ranks runs
+// in rank order either way.
+template <bool VEC, int TP = 1, int QG = 8>
 __device__ __forceinline__ void lora_delta8_desc(const PoolView& pv, const int32_t* __restrict__ desc,
                                                  const float* __restrict__ T, int r, int M, int c0, int N,
                                                  float (&acc8)[8]) {
+  static_assert(QG == 8 || QG == 16, "rank rounds of 8 or 16");
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc8[e] = 0.f;
   if (r >= M || c0 >= N) return;
@@ -94,26 +99,27 @@ __device__ __forceinline__ void lora_delta8_desc(const PoolView& pv, const int32
   if (key >= 0) {
     const float* tr = T + (size_t)r * pv.max_rank;
     const size_t tstride = (size_t)M * pv.max_rank;
-    const bool tvec = (pv.max_rank & 7) == 0;
+    const bool tvec = (pv.max_rank & 7) == 0;  // rows of T 16-byte aligned
     int q0 = 0;
     do {
-      float u8[8][8], tv[8], tq[8];
+      float u8[QG][8], tv[QG], tq[QG];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) load8<VEC>(pv.up + (size_t)d[4 + min(q0 + q, pv.max_rank - 1)] * pv.dout, c0, N,
-                                             u8[q]);
-      if (tvec) {
+      for (int q = 0; q < QG; ++q) load8<VEC>(pv.up + (size_t)d[4 + min(q0 + q, pv.max_rank - 1)] * pv.dout, c0, N,
+                                              u8[q]);
+      if (tvec && q0 + QG <= pv.max_rank) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) tv[q] = 0.f;
+        for (int q = 0; q < QG; ++q) tv[q] = 0.f;
 #pragma unroll
         for (int p = 0; p < TP; ++p) {
-          const float4 a = *reinterpret_cast<const float4*>(tr + p * tstride + q0);
-          const float4 b = *reinterpret_cast<const float4*>(tr + p * tstride + q0 + 4);
-          tv[0] += a.x; tv[1] += a.y; tv[2] += a.z; tv[3] += a.w;
-          tv[4] += b.x; tv[5] += b.y; tv[6] += b.z; tv[7] += b.w;
+#pragma unroll
+          for (int h = 0; h < QG / 4; ++h) {
+            const float4 a = *reinterpret_cast<const float4*>(tr + p * tstride + q0 + 4 * h);
+            tv[4 * h] += a.x; tv[4 * h + 1] += a.y; tv[4 * h + 2] += a.z; tv[4 * h + 3] += a.w;
+          }
         }
       } else {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < QG; ++q) {
           const int qq = min(q0 + q, pv.max_rank - 1);
           tv[q] = tr[qq];
 #pragma unroll
@@ -121,12 +127,12 @@ __device__ __forceinline__ void lora_delta8_desc(const PoolView& pv, const int32
         }
       }
 #pragma unroll
-      for (int q = 0; q < 8; ++q) tq[q] = (q0 + q < rank) ? tscale * tv[q] : 0.f;
+      for (int q = 0; q < QG; ++q) tq[q] = (q0 + q < rank) ? tscale * tv[q] : 0.f;
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
+      for (int q = 0; q < QG; ++q)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc8[e] = fmaf(tq[q], u8[q][e], acc8[e]);
-      q0 += 8;
+      q0 += QG;
     } while (q0 < rank);
   } else if (key == -2) {
 #pragma unroll
