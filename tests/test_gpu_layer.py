@@ -355,3 +355,15 @@ def test_zero_rows_is_a_noop(M):
 def test_one_row(M):
     check_apply(M, synth.custom("one", 51, 4096, 4096, [0], {0: 16}, max_rank=16))
     check_apply(M, synth.custom("one_none", 52, 4096, 4096, [-1], {0: 16}, max_rank=16))
+
+
+def test_apply_max_rows(M):
+    """A batch at the row limit (MLORA_MAX_ROWS = 16384) through both grouped
+    variants: the segment builder's largest form, tile and item lists of
+    every length, the large-batch GEMM with the low-rank epilogue (split)
+    and the fused branch; mixed ranks, base-only rows; every 7th row and the
+    first and last rows checked."""
+    n = 16384
+    w = small_workload(97, 136, 264, n, {0: 1, 1: 8, 2: 17, 3: 64, 4: 16}, p_none=0.1)
+    assert w.n == n
+    check_apply(M, w, rows=lambda seg: np.unique(np.concatenate([np.arange(0, n, 7), [0, n - 1]])))
