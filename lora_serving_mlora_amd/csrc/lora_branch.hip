@@ -303,6 +303,155 @@ __device__ __forceinline__ void expand_cols_pre(const PoolView& pv, const int32_
   }
 }
 
+// One step of the reduce-scatter of G partial sums over a wave (as in
+// shrink_row_to): lanes with bit MSK set keep the upper LEN values, the
+// others the lower LEN, each adding its partner's copy.
+template <int MSK, int LEN>
+__device__ __forceinline__ void reduce_scatter_step(float (&v)[G], int lane) {
+  const bool upper = (lane & MSK) != 0;
+#pragma unroll
+  for (int j = 0; j < LEN; ++j) {
+    const float send = upper ? v[j] : v[j + LEN];
+    const float keep = upper ? v[j + LEN] : v[j];
+    v[j] = keep + __shfl_xor(send, MSK, 64);
+  }
+}
+
+// Fast form of one item (rank <= G, din and dout <= 8 * kFusedThreads, 16-byte
+// aligned rows): each thread owns 8 elements of din for the shrink and 8
+// columns of dout for the expand, and every load of the item goes out before
+// any arithmetic waits for one: the X rows and the Down rows first, then the
+// Up pieces and the Y pieces of the read-modify-write.  Loads return in
+// issue order, so the Down stream is not queued behind the Up stream, and
+// the Y read is not a round trip of its own at the end.  The arithmetic is
+// that of shrink_row_to and expand_cols_pre.
+__device__ __forceinline__ void fused_item_fast(const PoolView& pv, const Item& m, const int32_t* __restrict__ dpage,
+                                                const int32_t* __restrict__ upage, const uint16_t* __restrict__ X,
+                                                const int32_t* __restrict__ perm, uint16_t* __restrict__ Y,
+                                                float (*ts)[MLORA_MAX_RANK], float (*red)[G]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k0 = tid * 8;  // this thread's din elements and dout columns
+  const bool kin = k0 < pv.din, cin = k0 < pv.dout;
+  // page ids and rows are uniform over the workgroup (scalar registers)
+  int dp[G], up[G], row[R];
+#pragma unroll
+  for (int q = 0; q < G; ++q) {
+    dp[q] = __builtin_amdgcn_readfirstlane(dpage[min(q, pv.max_rank - 1)]);
+    up[q] = __builtin_amdgcn_readfirstlane(upage[min(q, pv.max_rank - 1)]);
+  }
+#pragma unroll
+  for (int q = 1; q < G; ++q) {  // pages past the rank: the first page, weighed 0
+    dp[q] = dp[q] < 0 ? dp[0] : dp[q];
+    up[q] = up[q] < 0 ? up[0] : up[q];
+  }
+#pragma unroll
+  for (int i = 0; i < R; ++i) row[i] = __builtin_amdgcn_readfirstlane(perm[m.j0 + min(i, m.nr - 1)]);
+  // the first row's X and Y pieces go out with the weights; an item's
+  // further rows (same adapter) load theirs when they come up
+  // loads are unconditional (threads past din or dout read the last piece;
+  // their X piece is zeroed, their expand is never stored), so every load
+  // is a plain global load from a uniform base
+  const int kc = min(k0, pv.din - 8), cc = min(k0, pv.dout - 8);
+  uint4 d[G], u[G];
+  uint4 x0 = *reinterpret_cast<const uint4*>(X + (size_t)row[0] * pv.din + kc);
+#pragma unroll
+  for (int q = 0; q < G; ++q) d[q] = *reinterpret_cast<const uint4*>(pv.down + (size_t)dp[q] * pv.din + kc);
+#pragma unroll
+  for (int q = 0; q < G; ++q) u[q] = *reinterpret_cast<const uint4*>(pv.up + (size_t)up[q] * pv.dout + cc);
+  const uint4 y0 = *reinterpret_cast<const uint4*>(Y + (size_t)row[0] * pv.dout + cc);
+  if (!kin) x0 = make_uint4(0u, 0u, 0u, 0u);
+  // shrink, row by row: partial dot products of 8 din elements, the
+  // reduce-scatter of shrink_row_to, then the 8 waves summed in order
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    if (i >= m.nr) break;
+    uint4 xi = x0;
+    if (i > 0) {
+      xi = *reinterpret_cast<const uint4*>(X + (size_t)row[i] * pv.din + kc);
+      if (!kin) xi = make_uint4(0u, 0u, 0u, 0u);
+    }
+    const uint32_t xw[4] = {xi.x, xi.y, xi.z, xi.w};
+    float v[G];
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+      const uint32_t dw[4] = {d[q].x, d[q].y, d[q].z, d[q].w};
+      float s = 0.f;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        s = fmaf(lo_bf(dw[h]), lo_bf(xw[h]), s);
+        s = fmaf(hi_bf(dw[h]), hi_bf(xw[h]), s);
+      }
+      v[q] = s;
+    }
+    reduce_scatter_step<32, 8>(v, lane);
+    reduce_scatter_step<16, 4>(v, lane);
+    reduce_scatter_step<8, 2>(v, lane);
+    reduce_scatter_step<4, 1>(v, lane);
+    float tot = v[0];
+    tot += __shfl_xor(tot, 2, 64);
+    tot += __shfl_xor(tot, 1, 64);
+    if ((lane & 3) == 0) red[wave][lane >> 2] = tot;
+    __syncthreads();
+    if (tid < G) {
+      float sum = red[0][tid];
+#pragma unroll
+      for (int w = 1; w < kFusedThreads / 64; ++w) sum += red[w][tid];
+      ts[i][tid] = tid < m.rank ? m.scale * sum : 0.f;  // zeros past the rank
+    }
+    __syncthreads();
+  }
+  if (!cin) return;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    if (i >= m.nr) break;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+      const uint32_t w[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
+      const float t = ts[i][q];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        acc[2 * h] = fmaf(t, lo_bf(w[h]), acc[2 * h]);
+        acc[2 * h + 1] = fmaf(t, hi_bf(w[h]), acc[2 * h + 1]);
+      }
+    }
+    const uint4 o = i == 0 ? y0 : *reinterpret_cast<const uint4*>(Y + (size_t)row[i] * pv.dout + cc);
+    uint4 w;
+    w.x = pack_bf2(lo_bf(o.x) + acc[0], hi_bf(o.x) + acc[1]);
+    w.y = pack_bf2(lo_bf(o.y) + acc[2], hi_bf(o.y) + acc[3]);
+    w.z = pack_bf2(lo_bf(o.z) + acc[4], hi_bf(o.z) + acc[5]);
+    w.w = pack_bf2(lo_bf(o.w) + acc[6], hi_bf(o.w) + acc[7]);
+    *reinterpret_cast<uint4*>(Y + (size_t)row[i] * pv.dout + k0) = w;
+  }
+}
+
+// Batches whose every item takes the fast form (the pool's largest rank at
+// most G; din, dout <= 8 * kFusedThreads; 16-byte aligned rows): the fused
+// kernel without the general form's registers.
+__global__ __launch_bounds__(kFusedThreads) void fused_fast_kernel(PoolView pv, int proj,
+                                                                   const uint16_t* __restrict__ X,
+                                                                   const int32_t* __restrict__ ws,
+                                                                   uint16_t* __restrict__ Y, int n) {
+  __shared__ float ts[R][MLORA_MAX_RANK];
+  __shared__ float red[kFusedThreads / 64][G];
+  const int n_items = ws[MLORA_SEG_NITEMS];
+  const int n_bad = ws[MLORA_SEG_NBAD];
+  const int32_t* perm = ws + MLORA_SEG_PERM(n);
+  for (int it = blockIdx.x; it < n_items + n_bad; it += gridDim.x) {
+    if (it < n_items) {
+      const Item m = load_item(pv, ws, n, it);
+      const size_t pt = ((size_t)m.adapter * pv.n_proj + proj) * pv.max_rank;
+      fused_item_fast(pv, m, pv.down_page + pt, pv.up_page + pt, X, perm, Y, ts, red);
+      __syncthreads();
+    } else {
+      uint16_t* y = Y + (size_t)perm[n - n_bad + (it - n_items)] * pv.dout;
+      for (int c = threadIdx.x * 8; c < pv.dout; c += kFusedThreads * 8) nan_cols<true>(y, c, pv.dout);
+    }
+  }
+}
+
 template <bool VEC>
 __global__ __launch_bounds__(kFusedThreads) void fused_kernel(PoolView pv, int proj, const uint16_t* __restrict__ X,
                                                               const int32_t* __restrict__ ws,
@@ -680,7 +829,9 @@ hipError_t launch_expand(const PoolView& pv, int proj, const float* T, int n_chu
 hipError_t launch_fused(const PoolView& pv, int proj, const uint16_t* X, const int32_t* ws, uint16_t* Y, int n,
                         hipStream_t stream) {
   const dim3 grid(item_grid(n)), block(kFusedThreads);
-  if (vec_ok(pv, X, Y))
+  if (vec_ok(pv, X, Y) && pv.max_rank <= G && pv.din <= 8 * kFusedThreads && pv.dout <= 8 * kFusedThreads)
+    MLORA_LAUNCH("fused", fused_fast_kernel, grid, block, 0, stream, pv, proj, X, ws, Y, n);
+  else if (vec_ok(pv, X, Y))
     MLORA_LAUNCH("fused", (fused_kernel<true>), grid, block, 0, stream, pv, proj, X, ws, Y, n);
   else
     MLORA_LAUNCH("fused", (fused_kernel<false>), grid, block, 0, stream, pv, proj, X, ws, Y, n);
