@@ -138,17 +138,31 @@ mlora_status mlora_pool_destroy(mlora_pool* pool); /* waits for its own pending 
  * on the host, and the pages plus metadata are copied on `stream` from
  * pinned staging.  The caller's buffers may be reused when this returns.
  * The weights are ready for any later call on the same stream (the card's
- * lifecycle: weights must be resident before the branch runs).
+ * lifecycle: weights must be resident before the branch runs); a call on
+ * another stream first makes that stream wait with mlora_pool_ready, so a
+ * load on a copy stream can overlap the layer running on a compute stream.
+ * Pages an unload parked (below) are reused only after `stream` waits, on
+ * the device, for their last readers; the host does not block on readers.
  * Errors: EINVAL (id, rank, pointers), EEXIST (already resident: no silent
  * overwrite of a live id), ENOSPC (not enough free pages; nothing changed). */
 mlora_status mlora_pool_load(mlora_pool* pool, int32_t adapter_id, int32_t rank, float scale,
                              const uint16_t* down, const uint16_t* up, void* stream);
 
-/* Marks the adapter not resident (rank 0, on `stream`) and returns its pages
- * to the free lists.  Work enqueued earlier on the same stream still reads
- * the old pages before any later load can overwrite them (evict only after
- * the last reader).  Errors: EINVAL (id range), ENOENT (not resident). */
+/* Marks the adapter not resident (rank 0, on `stream`) and parks its pages
+ * behind an event recorded on `stream`: every reader enqueued on `stream`
+ * before the unload finishes before a later load, on ANY stream, writes
+ * those pages (the M031 card, sections 06-07: evict only after the last
+ * reader).  Readers on other streams must be ordered before the unload by
+ * the caller (an event, as for any buffer).  Parked pages count as free in
+ * mlora_pool_free_pages.  Errors: EINVAL (id range), ENOENT (not resident). */
 mlora_status mlora_pool_unload(mlora_pool* pool, int32_t adapter_id, void* stream);
+
+/* Makes `stream` wait, on the device, until the copies of the adapter's
+ * latest load (possibly issued on another stream) have completed: the
+ * adapter's weights and metadata are then visible to work enqueued on
+ * `stream` afterwards.  The host does not block.
+ * Errors: EINVAL (id range), ENOENT (not resident). */
+mlora_status mlora_pool_ready(mlora_pool* pool, int32_t adapter_id, void* stream);
 
 /* Host-side view of the pool (no device access). */
 mlora_status mlora_pool_query(const mlora_pool* pool, int32_t adapter_id, int32_t* rank, float* scale);

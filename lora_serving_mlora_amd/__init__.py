@@ -57,6 +57,7 @@ EXPORTS = {
     "mlora_pool_destroy": (ctypes.c_int, [_c_void_p]),
     "mlora_pool_load": (ctypes.c_int, [_c_void_p, _i32, _i32, _f32, _c_void_p, _c_void_p, _c_void_p]),
     "mlora_pool_unload": (ctypes.c_int, [_c_void_p, _i32, _c_void_p]),
+    "mlora_pool_ready": (ctypes.c_int, [_c_void_p, _i32, _c_void_p]),
     "mlora_pool_query": (ctypes.c_int, [_c_void_p, _i32, _pi32, _pf32]),
     "mlora_pool_free_pages": (ctypes.c_int, [_c_void_p, _pi64, _pi64, _pi32]),
     "mlora_segments_bytes": (_sz, [_i32]),
@@ -191,6 +192,11 @@ class Pool:
 
     def unload(self, adapter_id: int) -> None:
         _check(lib().mlora_pool_unload(self.handle, adapter_id, _stream()), f"mlora_pool_unload({adapter_id})")
+
+    def ready(self, adapter_id: int) -> None:
+        """Makes the current stream wait (on the device) for the adapter's
+        latest load, which may have been issued on another stream."""
+        _check(lib().mlora_pool_ready(self.handle, adapter_id, _stream()), f"mlora_pool_ready({adapter_id})")
 
     def query(self, adapter_id: int):
         r, s = ctypes.c_int32(), ctypes.c_float()

@@ -165,6 +165,22 @@ struct mlora_pool {
   hipEvent_t ev[2] = {nullptr, nullptr};
   bool pending[2] = {false, false};
   int cur = 0;
+  // Cross-stream lifecycle.  An unloaded adapter's pages are parked with an
+  // event recorded on the unload's stream behind every earlier reader there;
+  // a load (on any stream) that takes them first makes its stream wait for
+  // that event on the device.  Pages a load released but did not use stay
+  // behind `guard`, which every later load waits for.  ready[id] is recorded
+  // on the load's stream after the adapter's copies (mlora_pool_ready).
+  struct Parked {
+    RangeAlloc::Runs d, u;
+    int64_t pages;
+    hipEvent_t last_reader;
+  };
+  std::vector<Parked> parked;
+  hipEvent_t guard = nullptr;
+  bool guarded = false;
+  std::vector<hipEvent_t> ready;
+  std::vector<hipEvent_t> spare;  // recorded events no longer referenced
   std::mutex mu;
 
   PoolView view() const {
@@ -251,6 +267,51 @@ class Stager {
   std::vector<Copy> copies_;
 };
 
+mlora_status take_event(mlora_pool* p, hipEvent_t* e) {
+  if (!p->spare.empty()) {
+    *e = p->spare.back();
+    p->spare.pop_back();
+    return MLORA_OK;
+  }
+  return hip_check(hipEventCreateWithFlags(e, hipEventDisableTiming), "hipEventCreate(pool)");
+}
+
+// Makes `s` wait on the device for the last readers of every parked page
+// run, then returns those runs to the free lists behind the guard event
+// (recorded on `s` after the waits, so any later load waits for it too).
+// Runs whose readers are known to have finished need no wait.
+mlora_status unpark(mlora_pool* p, hipStream_t s) {
+  bool waited = false;
+  for (auto& k : p->parked) {
+    const hipError_t q = hipEventQuery(k.last_reader);
+    if (q == hipErrorNotReady) {
+      HIP_TRY(hipStreamWaitEvent(s, k.last_reader, 0));
+      waited = true;
+    } else if (q != hipSuccess) {
+      return hip_check(q, "hipEventQuery(last reader)");
+    }
+    p->dfree.release(k.d);
+    p->ufree.release(k.u);
+    p->spare.push_back(k.last_reader);  // the wait above holds the record it saw
+  }
+  p->parked.clear();
+  if (waited) {
+    if (!p->guard) {
+      mlora_status st = take_event(p, &p->guard);
+      if (st != MLORA_OK) return st;
+    }
+    HIP_TRY(hipEventRecord(p->guard, s));
+    p->guarded = true;
+  }
+  return MLORA_OK;
+}
+
+int64_t parked_pages(const mlora_pool* p) {
+  int64_t n = 0;
+  for (const auto& k : p->parked) n += k.pages;
+  return n;
+}
+
 mlora_status check_pool(const mlora_pool* p) {
   if (!p) return fail(MLORA_EINVAL, "pool is NULL");
   int dev = -1;
@@ -320,6 +381,7 @@ mlora_status mlora_pool_create(const mlora_pool_desc* desc, void* stream, mlora_
   p->scale.assign(d.max_adapters, 0.f);
   p->druns.resize(d.max_adapters);
   p->uruns.resize(d.max_adapters);
+  p->ready.assign(d.max_adapters, nullptr);
   auto cleanup = [&](mlora_status st) {
     for (int b = 0; b < 2; ++b) {
       if (p->stage[b]) (void)hipHostFree(p->stage[b]);
@@ -351,6 +413,11 @@ mlora_status mlora_pool_destroy(mlora_pool* p) {
     if (p->stage[b]) (void)hipHostFree(p->stage[b]);
     if (p->ev[b]) (void)hipEventDestroy(p->ev[b]);
   }
+  for (auto& k : p->parked) (void)hipEventDestroy(k.last_reader);
+  for (hipEvent_t e : p->ready)
+    if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : p->spare) (void)hipEventDestroy(e);
+  if (p->guard) (void)hipEventDestroy(p->guard);
   delete p;
   return st;
 }
@@ -367,6 +434,22 @@ mlora_status mlora_pool_load(mlora_pool* p, int32_t id, int32_t rank, float scal
   if (!down || !up) return fail(MLORA_EINVAL, "down and up must not be NULL");
   if (p->rank[id] != 0) return fail(MLORA_EEXIST, "adapter %d is already resident (unload it first)", id);
   const int64_t npages = (int64_t)d.n_proj * rank;
+  hipStream_t s = as_stream(stream);
+  // parked pages join the free lists once this stream waits for their
+  // last readers; free pages released that way are written only after
+  // the guard
+  if ((p->dfree.nfree() < npages || p->ufree.nfree() < npages) && !p->parked.empty()) {
+    if ((st = unpark(p, s)) != MLORA_OK) return st;
+  }
+  if (p->guarded) {
+    const hipError_t q = hipEventQuery(p->guard);
+    if (q == hipSuccess)
+      p->guarded = false;
+    else if (q == hipErrorNotReady)
+      HIP_TRY(hipStreamWaitEvent(s, p->guard, 0));
+    else
+      return hip_check(q, "hipEventQuery(guard)");
+  }
   RangeAlloc::Runs dr, ur;
   if (!p->dfree.alloc(npages, dr))
     return fail(MLORA_ENOSPC, "Down arena: %lld pages needed, %lld free", (long long)npages, (long long)p->dfree.nfree());
@@ -380,7 +463,6 @@ mlora_status mlora_pool_load(mlora_pool* p, int32_t id, int32_t rank, float scal
     return s;
   };
 
-  hipStream_t s = as_stream(stream);
   Stager sg(p, s);
   const size_t drow = (size_t)d.din * 2, urow = (size_t)d.dout * 2;
   char* dbase = static_cast<char*>(d.down_pages);
@@ -419,6 +501,8 @@ mlora_status mlora_pool_load(mlora_pool* p, int32_t id, int32_t rank, float scal
   if ((st = sg.reserve(meta + p->ml.rank + (size_t)id * 4, 4, &h)) != MLORA_OK) return undo(st);
   std::memcpy(h, &rank, 4);
   if ((st = sg.flush()) != MLORA_OK) return undo(st);
+  if (!p->ready[id] && (st = take_event(p, &p->ready[id])) != MLORA_OK) return undo(st);
+  if ((st = hip_check(hipEventRecord(p->ready[id], s), "hipEventRecord(ready)")) != MLORA_OK) return undo(st);
 
   p->rank[id] = rank;
   p->scale[id] = scale;
@@ -436,15 +520,30 @@ mlora_status mlora_pool_unload(mlora_pool* p, int32_t id, void* stream) {
   if (id < 0 || id >= p->d.max_adapters) return fail(MLORA_EINVAL, "adapter id %d outside [0, %d)", id, p->d.max_adapters);
   if (p->rank[id] == 0) return fail(MLORA_ENOENT, "adapter %d is not resident", id);
   char* meta = static_cast<char*>(p->d.meta);
-  HIP_TRY(hipMemsetAsync(meta + p->ml.rank + (size_t)id * 4, 0, 4, as_stream(stream)));
-  p->dfree.release(p->druns[id]);
-  p->ufree.release(p->uruns[id]);
+  hipStream_t s = as_stream(stream);
+  HIP_TRY(hipMemsetAsync(meta + p->ml.rank + (size_t)id * 4, 0, 4, s));
+  // the pages are parked behind every reader enqueued so far on `stream`
+  hipEvent_t e = nullptr;
+  mlora_status est = take_event(p, &e);
+  if (est != MLORA_OK) return est;
+  HIP_TRY(hipEventRecord(e, s));
+  p->parked.push_back({p->druns[id], p->uruns[id], (int64_t)p->d.n_proj * p->rank[id], e});
   p->druns[id].clear();
   p->uruns[id].clear();
   p->rank[id] = 0;
   p->scale[id] = 0.f;
   --p->n_resident;
   return MLORA_OK;
+}
+
+mlora_status mlora_pool_ready(mlora_pool* p, int32_t id, void* stream) {
+  g_err.clear();
+  mlora_status st = check_pool(p);
+  if (st != MLORA_OK) return st;
+  std::lock_guard<std::mutex> lock(p->mu);
+  if (id < 0 || id >= p->d.max_adapters) return fail(MLORA_EINVAL, "adapter id %d outside [0, %d)", id, p->d.max_adapters);
+  if (p->rank[id] == 0) return fail(MLORA_ENOENT, "adapter %d is not resident", id);
+  return hip_check(hipStreamWaitEvent(as_stream(stream), p->ready[id], 0), "hipStreamWaitEvent(ready)");
 }
 
 mlora_status mlora_pool_query(const mlora_pool* p, int32_t id, int32_t* rank, float* scale) {
@@ -461,8 +560,9 @@ mlora_status mlora_pool_free_pages(const mlora_pool* p, int64_t* free_down, int6
   g_err.clear();
   if (!p) return fail(MLORA_EINVAL, "pool is NULL");
   std::lock_guard<std::mutex> lock(const_cast<mlora_pool*>(p)->mu);
-  if (free_down) *free_down = p->dfree.nfree();
-  if (free_up) *free_up = p->ufree.nfree();
+  const int64_t pk = parked_pages(p);  // usable by the next load (which waits for their readers)
+  if (free_down) *free_down = p->dfree.nfree() + pk;
+  if (free_up) *free_up = p->ufree.nfree() + pk;
   if (n_resident) *n_resident = p->n_resident;
   return MLORA_OK;
 }

@@ -138,3 +138,60 @@ def test_layer_stack_pool_is_1600_mib_and_full(M):
         pool.load(0, 16, 2.0, d, u)
     assert e.value.status == M.EEXIST
     torch.cuda.synchronize()
+
+
+def _spin_cycles(torch, ms):
+    """Cycles of torch's spin kernel that take about `ms` milliseconds."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    torch.cuda._sleep(1_000_000)
+    b.record()
+    torch.cuda.synchronize()
+    return int(ms / max(a.elapsed_time(b), 1e-3) * 1_000_000)
+
+
+def test_cross_stream_reuse_waits_for_last_reader(M):
+    """Evict only after the last reader, across streams: the layer runs on
+    stream A behind a ~50 ms spin, adapter 0 is unloaded on A, and a new
+    adapter is loaded on stream B into the only free pages (adapter 0's).
+    B's copies must wait on the device for A's layer: the layer still sees
+    the old weights.  Then A waits for the new adapter (pool.ready) and
+    serves a batch with it."""
+    torch = torch_cuda()
+    ranks = {0: 16, 1: 16, 2: 16}
+    w = _w(ranks, n=24, seed=81, din=512, dout=520, n_proj=1, max_adapters=4, max_rank=16)
+    ids_a = np.where(w.row_adapter == 2, 0, w.row_adapter).astype(np.int32)  # batch on adapters 0 and 1
+    ids_b = np.where(ids_a == 0, 2, ids_a).astype(np.int32)                 # adapter 0's rows on adapter 2
+    pool = M.Pool(w.din, w.dout, 1, 4, 16, 32)  # room for two rank-16 adapters
+    for a in (0, 1):
+        pool.load(a, 16, w.scales[a], w.down_all_bits(a), w.up_all_bits(a))
+    X, W0 = w.x_bits(), w.w0_bits(0)
+    Xd, W0d = to_dev_bf16(X), to_dev_bf16(W0)
+    seg_a = M.build_segments(pool, ids_dev(ids_a))
+    spin = _spin_cycles(torch, 50.0)
+    torch.cuda.synchronize()
+    say("pool cross-stream reuse")
+    s_b = torch.cuda.Stream()
+    torch.cuda._sleep(spin)                       # stream A: the layer starts ~50 ms from now
+    Y_a = M.apply(pool, 0, Xd, W0d, seg_a, variant="split")
+    pool.unload(0)                                # parked behind the layer
+    assert pool.free_pages()[0] == 16
+    with torch.cuda.stream(s_b):
+        pool.load(2, 16, w.scales[2], w.down_all_bits(2), w.up_all_bits(2))   # reuses adapter 0's pages
+    assert pool.free_pages()[0] == 0
+    torch.cuda.synchronize()
+    ref_a = O.linear(O.widen_bf16(X), O.widen_bf16(W0), ids_a, oracle_adapters(w, 0, [0, 1]), w.max_adapters)
+    assert_close(dev_to_f64(Y_a), ref_a, "layer read its adapter after the unload, before the reload on B")
+
+    # a load on B, used on A after A waits for it
+    with torch.cuda.stream(s_b):
+        pool.unload(2)
+        pool.load(2, 16, w.scales[2], w.down_all_bits(2), w.up_all_bits(2))
+    pool.ready(2)
+    seg_b = M.build_segments(pool, ids_dev(ids_b))
+    Y_b = M.apply(pool, 0, Xd, W0d, seg_b, variant="split")
+    torch.cuda.synchronize()
+    ref_b = O.linear(O.widen_bf16(X), O.widen_bf16(W0), ids_b, oracle_adapters(w, 0, [1, 2]), w.max_adapters)
+    assert_close(dev_to_f64(Y_b), ref_b, "layer on the adapter loaded on another stream")
+    with pytest.raises(M.MloraError):
+        pool.ready(0)                             # not resident
