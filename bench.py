@@ -66,6 +66,10 @@ def parse_args():
     ap.add_argument("--compare-baselines", action="store_true",
                     help="also time the pages' naive baselines on the device: each adapter group served by its own "
                          "launches, and the branch with every adapter padded to the largest rank")
+    ap.add_argument("--compare-paging", action="store_true",
+                    help="also time the adapter paging lifecycle: one adapter's load from host memory, a step whose "
+                         "adapter must be loaded first (miss) against one whose adapters are resident (hit), and "
+                         "the step while a second stream reloads a spare adapter into the same pool")
     ap.add_argument("--compare-merged", action="store_true",
                     help="also time the merged alternative: merge/unmerge of one adapter into W0, the plain GEMM "
                          "on merged weights, and serving the batch adapter by adapter from merged weights")
@@ -310,6 +314,70 @@ def compare_baselines(M, torch, w, pool, X, W0s, R, seg_ws, Y, work, variant, it
 # CPU oracle baseline
 # ---------------------------------------------------------------------------
 
+def compare_paging(M, torch, w, pool, step_fn, spare_id, R, iters=20):
+    """The host<->HBM paging lifecycle (M031 card sections 06-07; wiblog
+    memory-cost section): the adapter of the batch's largest group is
+    unloaded and loaded again from host memory (pinned staging; its R
+    projections), and the same step is timed with and without a reload of
+    a spare adapter (an id no row uses) on a second stream into the same
+    pool."""
+    import collections
+    a = collections.Counter(int(x) for x in w.row_adapter if x >= 0).most_common(1)[0][0]
+    rank = w.ranks[a]
+    d = np.ascontiguousarray(np.repeat(w.down_bits(a, 0)[None], R, axis=0))
+    u = np.ascontiguousarray(np.repeat(w.up_bits(a, 0)[None], R, axis=0))
+    nbytes = 2 * R * rank * (w.din + w.dout)
+    torch.cuda.synchronize()
+    loads = []
+    for _ in range(5):
+        pool.unload(a)
+        t0 = time.perf_counter()
+        pool.load(a, rank, w.scales[a], d, u)
+        torch.cuda.synchronize()
+        loads.append(time.perf_counter() - t0)
+    load_ms = float(np.median(loads)) * 1e3
+
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n
+
+    for i in range(3):
+        step_fn(i)
+    hit_ms = timed(step_fn, iters)
+
+    def miss(i):
+        pool.unload(a)
+        pool.load(a, rank, w.scales[a], d, u)
+        step_fn(i)
+    miss_ms = timed(miss, 5)
+
+    copy = torch.cuda.Stream()
+    pool.load(spare_id, rank, w.scales[a], d, u)
+
+    def reload_spare(i):
+        with torch.cuda.stream(copy):
+            pool.unload(spare_id)
+            pool.load(spare_id, rank, w.scales[a], d, u)
+
+    def overlapped(i):
+        reload_spare(i)
+        step_fn(i)
+    for i in range(2):
+        overlapped(i)
+    ov_ms = timed(overlapped, iters)
+    spare_ms = timed(reload_spare, 5)
+    return {"adapter": a, "adapter_bytes": nbytes, "projections": R,
+            "load_ms": round(load_ms, 3), "load_gbps": round(nbytes / (load_ms * 1e-3) / 1e9, 2),
+            "step_hit_us": round(hit_ms * 1e3, 2), "step_miss_us": round(miss_ms * 1e3, 2),
+            "spare_reload_alone_us": round(spare_ms * 1e3, 2),
+            "step_with_spare_reload_on_copy_stream_us": round(ov_ms * 1e3, 2),
+            "timing": "host clock around synchronised loops of eager launches"}
+
+
 def cpu_baseline(w, seconds):
     """The oracle as it stands, in fp32, on this host: per-row loop over the
     workload's rows (projection 0), repeated until `seconds` have passed."""
@@ -391,7 +459,12 @@ def main():
           f"rotation={R} projections", file=sys.stderr, flush=True)
 
     n_pages = sum(w.ranks.values()) * R
-    pool = M.Pool(w.din, w.dout, R, w.max_adapters, w.max_rank, n_pages)
+    max_adapters = w.max_adapters
+    if args.compare_paging:
+        # one more id (no row uses it) and pages for a spare adapter
+        max_adapters += 1
+        n_pages += max(w.ranks.values()) * R
+    pool = M.Pool(w.din, w.dout, R, max_adapters, w.max_rank, n_pages)
     for a in w.adapter_ids():
         if w.n_proj > 1:
             d, u = w.down_all_bits(a), w.up_all_bits(a)
@@ -547,6 +620,9 @@ def main():
         result["baseline_comparison"] = compare_baselines(M, torch, w, pool, X, W0s, R, seg_ws, Y, work, variant)
     if args.compare_merged:
         result["merged_comparison"] = compare_merged(M, torch, w, pool, X, W0s, R, seg_ws, Y, work, variant)
+    if args.compare_paging:
+        result["paging_comparison"] = (None if w.n_proj > 1 else
+                                       compare_paging(M, torch, w, pool, step, max_adapters - 1, R))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result))
