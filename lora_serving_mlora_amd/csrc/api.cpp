@@ -8,10 +8,12 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <functional>
 #include <map>
 #include <cmath>
 #include <mutex>
 #include <string>
+#include <thread>
 #include <utility>
 #include <vector>
 
@@ -240,8 +242,12 @@ class Stager {
     return MLORA_OK;
   }
 
+  // work that fills the reserved staging slots; run before their copies go out
+  void on_flush(std::function<void()> f) { fill_ = std::move(f); }
+
   mlora_status flush() {
     if (!open_) return MLORA_OK;
+    if (fill_) fill_();
     const int b = p_->cur;
     char* base = static_cast<char*>(p_->stage[b]);
     for (const auto& c : copies_) HIP_TRY(hipMemcpyAsync(c.dst, base + c.src, c.bytes, hipMemcpyHostToDevice, s_));
@@ -262,6 +268,7 @@ class Stager {
   };
   mlora_pool* p_;
   hipStream_t s_;
+  std::function<void()> fill_;
   bool open_ = false;
   size_t used_ = 0;
   std::vector<Copy> copies_;
@@ -468,24 +475,62 @@ mlora_status mlora_pool_load(mlora_pool* p, int32_t id, int32_t rank, float scal
   char* dbase = static_cast<char*>(d.down_pages);
   char* ubase = static_cast<char*>(d.up_pages);
   std::vector<int32_t> dpt((size_t)d.n_proj * d.max_rank, -1), upt((size_t)d.n_proj * d.max_rank, -1);
+  // Page rows are packed into the reserved staging slots just before each
+  // flush, by several host threads when the chunk is large: Down rows are
+  // copies, Up rows a transpose (the host work bounds a load's rate).
+  struct Fill {
+    char* h;
+    int64_t i;  // page row of the adapter: i = p*rank + q
+    bool upr;   // Up row (column q of Up for projection p), else Down row
+  };
+  std::vector<Fill> fills;
+  auto fill_range = [&](size_t b, size_t e) {
+    for (size_t k = b; k < e; ++k) {
+      const Fill& f = fills[k];
+      if (!f.upr) {
+        std::memcpy(f.h, down + (size_t)f.i * d.din, drow);
+      } else {
+        uint16_t* row = reinterpret_cast<uint16_t*>(f.h);
+        const uint16_t* src = up + (size_t)(f.i / rank) * d.dout * rank + f.i % rank;
+        for (int32_t c = 0; c < d.dout; ++c) row[c] = src[(size_t)c * rank];
+      }
+    }
+  };
+  sg.on_flush([&]() {
+    const size_t n = fills.size();
+    const size_t bytes = n * std::max(drow, urow);
+    const unsigned hw = std::max(1u, std::thread::hardware_concurrency());
+    const size_t nt = bytes < ((size_t)4 << 20) ? 1 : std::min<size_t>(std::min(hw, 8u), n);
+    if (nt <= 1) {
+      fill_range(0, n);
+    } else {
+      std::vector<std::thread> ts;
+      size_t t = 1;
+      try {
+        for (; t < nt; ++t) ts.emplace_back(fill_range, n * t / nt, n * (t + 1) / nt);
+      } catch (...) {  // no thread to spare: this thread packs the rest
+      }
+      fill_range(0, n / nt);
+      fill_range(n * t / nt, n);
+      for (auto& th : ts) th.join();
+    }
+    fills.clear();
+  });
   // Down rows: page i of the run list holds row (p, q), i = p*rank + q
   for (int64_t i = 0; i < npages; ++i) {
     const int64_t pg = page_at(dr, i);
     char* h = nullptr;
     if ((st = sg.reserve(dbase + pg * drow, drow, &h)) != MLORA_OK) return undo(st);
-    std::memcpy(h, down + (size_t)i * d.din, drow);
+    fills.push_back({h, i, false});
     dpt[(size_t)(i / rank) * d.max_rank + (i % rank)] = (int32_t)pg;
   }
   // Up^T rows: page i holds column q of Up for projection p
   for (int64_t i = 0; i < npages; ++i) {
     const int64_t pg = page_at(ur, i);
-    const int64_t pj = i / rank, q = i % rank;
     char* h = nullptr;
     if ((st = sg.reserve(ubase + pg * urow, urow, &h)) != MLORA_OK) return undo(st);
-    uint16_t* row = reinterpret_cast<uint16_t*>(h);
-    const uint16_t* src = up + (size_t)pj * d.dout * rank + q;
-    for (int32_t c = 0; c < d.dout; ++c) row[c] = src[(size_t)c * rank];
-    upt[(size_t)pj * d.max_rank + q] = (int32_t)pg;
+    fills.push_back({h, i, true});
+    upt[(size_t)(i / rank) * d.max_rank + (i % rank)] = (int32_t)pg;
   }
   // metadata: page tables, scale, then rank (all ordered on the stream)
   char* meta = static_cast<char*>(d.meta);
