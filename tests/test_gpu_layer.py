@@ -75,6 +75,7 @@ SMALL = [
     (7, 4128, 264, 300, {0: 1, 1: 8, 2: 17, 3: 64, 4: 128}),   # din = 32 * 129: K tail, empty slices
     (8, 512, 1000, 700, {i: (16 if i % 3 else 64) for i in range(40)}),
     (9, 1000, 520, 260, {0: 16, 1: 3, 2: 64}),        # din not a multiple of 32: vector-ALU shrink
+    (10, 520, 1000, 13, {0: 16, 1: 5, 2: 9}),          # ranks <= 16, din and dout <= 4096: fused fast form
 ]
 
 
