@@ -289,28 +289,37 @@ mlora_status take_event(mlora_pool* p, hipEvent_t* e) {
 // Runs whose readers are known to have finished need no wait.
 mlora_status unpark(mlora_pool* p, hipStream_t s) {
   bool waited = false;
-  for (auto& k : p->parked) {
+  size_t done = 0;  // entries released so far (dropped from the list even on an error)
+  mlora_status st = MLORA_OK;
+  for (; done < p->parked.size(); ++done) {
+    auto& k = p->parked[done];
     const hipError_t q = hipEventQuery(k.last_reader);
     if (q == hipErrorNotReady) {
-      HIP_TRY(hipStreamWaitEvent(s, k.last_reader, 0));
+      st = hip_check(hipStreamWaitEvent(s, k.last_reader, 0), "hipStreamWaitEvent(last reader)");
+      if (st != MLORA_OK) break;
       waited = true;
     } else if (q != hipSuccess) {
-      return hip_check(q, "hipEventQuery(last reader)");
+      st = hip_check(q, "hipEventQuery(last reader)");
+      break;
     }
     p->dfree.release(k.d);
     p->ufree.release(k.u);
     p->spare.push_back(k.last_reader);  // the wait above holds the record it saw
   }
-  p->parked.clear();
+  p->parked.erase(p->parked.begin(), p->parked.begin() + done);
   if (waited) {
-    if (!p->guard) {
-      mlora_status st = take_event(p, &p->guard);
-      if (st != MLORA_OK) return st;
+    // the guard covers the waits enqueued above (even when a later entry
+    // failed); without a guard, the host waits for them instead, so the
+    // released pages are never reused ahead of their readers
+    mlora_status gs = p->guard ? MLORA_OK : take_event(p, &p->guard);
+    if (gs == MLORA_OK) gs = hip_check(hipEventRecord(p->guard, s), "hipEventRecord(guard)");
+    if (gs != MLORA_OK) {
+      (void)hipStreamSynchronize(s);
+      return gs;
     }
-    HIP_TRY(hipEventRecord(p->guard, s));
     p->guarded = true;
   }
-  return MLORA_OK;
+  return st;
 }
 
 int64_t parked_pages(const mlora_pool* p) {
@@ -566,12 +575,16 @@ mlora_status mlora_pool_unload(mlora_pool* p, int32_t id, void* stream) {
   if (p->rank[id] == 0) return fail(MLORA_ENOENT, "adapter %d is not resident", id);
   char* meta = static_cast<char*>(p->d.meta);
   hipStream_t s = as_stream(stream);
-  HIP_TRY(hipMemsetAsync(meta + p->ml.rank + (size_t)id * 4, 0, 4, s));
   // the pages are parked behind every reader enqueued so far on `stream`
   hipEvent_t e = nullptr;
   mlora_status est = take_event(p, &e);
   if (est != MLORA_OK) return est;
-  HIP_TRY(hipEventRecord(e, s));
+  est = hip_check(hipMemsetAsync(meta + p->ml.rank + (size_t)id * 4, 0, 4, s), "hipMemsetAsync(rank)");
+  if (est == MLORA_OK) est = hip_check(hipEventRecord(e, s), "hipEventRecord(last reader)");
+  if (est != MLORA_OK) {
+    p->spare.push_back(e);
+    return est;
+  }
   p->parked.push_back({p->druns[id], p->uruns[id], (int64_t)p->d.n_proj * p->rank[id], e});
   p->druns[id].clear();
   p->uruns[id].clear();
