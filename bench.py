@@ -111,6 +111,7 @@ def algorithmic(w, chunks):
         "gemm_decode+shrink_rows": (split_dense[0] + shrink_rows[0], split_dense[1] + shrink_rows[1]),
         "gemm_mid+shrink_rows": (split_dense[0] + shrink_rows[0], split_dense[1] + shrink_rows[1]),
         "finish_part": finish,
+        "finish_base": (2 * n * dout, 0),   # the base GEMM's partials summed (scratch) into Y
         "gemm_skinny_lora": gemm_lora, "gemm_ksplit_lora": gemm_lora, "gemm_big_lora": gemm_lora,
         # the epilogue's operands: chunk partials in, bf16 t per row out; Up
         # pages in, the same Up with ranks contiguous out

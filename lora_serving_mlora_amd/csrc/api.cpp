@@ -890,7 +890,14 @@ mlora_status mlora_apply(const mlora_pool* p, int32_t proj, const uint16_t* X, c
     const mlora::LoraOperands lo{tb, koff, upt, wt};
     return hip_check(mlora::launch_big_lora(v, X, W0, ws, lo, Y, n, s), "GEMM + low-rank epilogue launch");
   }
-  st = hip_check(mlora::launch_base_gemm(X, W0, Y, n, d.din, d.dout, s), "base GEMM launch");
+  // the base GEMM: split over K with its partials in `work` (per-row
+  // layout) when the batch and the buffer allow, else the plain form
+  hipError_t ge = hipErrorNotSupported;
+  if (n <= kRowsMax && work && work_bytes >= rows_work_bytes(p, n) &&
+      (reinterpret_cast<uintptr_t>(work) & 255u) == 0)
+    ge = mlora::launch_base_split(X, W0, Y, n, d.din, d.dout, rows_work(p, n, work).part, s);
+  if (ge == hipErrorNotSupported) ge = mlora::launch_base_gemm(X, W0, Y, n, d.din, d.dout, s);
+  st = hip_check(ge, "base GEMM launch");
   if (st != MLORA_OK) return st;
   if (variant == MLORA_VARIANT_FUSED)
     return hip_check(mlora::launch_fused(v, proj, X, ws, Y, n, s), "fused launch");

@@ -1722,7 +1722,8 @@ size_t decode_lds_bytes(int M, int K, int MB) { return (size_t)M * (K / kDecSpli
 // otherwise T holds the finished t (scale folded).
 template <int MB>
 hipError_t launch_decode(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N, const PoolView& pv,
-                         int proj, const int32_t* row_key, float* T, float* part, bool shrink, hipStream_t st) {
+                         int proj, const int32_t* row_key, float* T, float* part, bool shrink, hipStream_t st,
+                         bool lora = true) {
   static_assert(kDecSplit == kRowsTParts, "T partial slices are the K quarters");
   const size_t lds = decode_lds_bytes(M, K, MB);
   static size_t attr = 0;
@@ -1739,7 +1740,10 @@ hipError_t launch_decode(const uint16_t* X, const uint16_t* W, uint16_t* Y, int 
   if (e != hipSuccess) return e;
   const int threads = M * (N / 8);
   // a decode batch's finish has few waves per SIMD: ranks in rounds of 16
-  if (shrink)
+  if (!lora)
+    MLORA_LAUNCH("finish_base", (finish_part<false, 1>), dim3((threads + kFinishThreads - 1) / kFinishThreads),
+                 dim3(kFinishThreads), 0, st, part, kDecSplit, Y, M, N, pv, proj, row_key, T);
+  else if (shrink)
     MLORA_LAUNCH("finish_part", (finish_part<true, kRowsTParts, 16>),
                  dim3((threads + kFinishThreads - 1) / kFinishThreads), dim3(kFinishThreads), 0, st, part, kDecSplit,
                  Y, M, N, pv, proj, row_key, T);
@@ -1763,7 +1767,8 @@ bool mid_ring_ok(int M, int K) { return K % (GBK * kRingStages) == 0 && (long)M 
 // shrink: the per-row shrink (T, one slice) runs in the tile workgroups
 // after their tiles
 hipError_t launch_mid_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N, const PoolView& pv,
-                           int proj, const int32_t* row_key, float* T, float* part, bool shrink, hipStream_t st) {
+                           int proj, const int32_t* row_key, float* T, float* part, bool shrink, hipStream_t st,
+                           bool lora = true) {
   const int S = mid_split(M, N, K);
   const int tiles_n = (N + 127) / 128, n_tiles = ((M + 127) / 128) * tiles_n;
   const int per_xcd = (n_tiles + 7) / 8;
@@ -1787,8 +1792,12 @@ hipError_t launch_mid_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, in
   hipError_t e = launched();
   if (e != hipSuccess) return e;
   const int threads = M * (N / 8);
-  MLORA_LAUNCH("finish_part", (finish_part<true, 1>), dim3((threads + kFinishThreads - 1) / kFinishThreads),
-               dim3(kFinishThreads), 0, st, part, S, Y, M, N, pv, proj, row_key, T);
+  if (!lora)
+    MLORA_LAUNCH("finish_base", (finish_part<false, 1>), dim3((threads + kFinishThreads - 1) / kFinishThreads),
+                 dim3(kFinishThreads), 0, st, part, S, Y, M, N, pv, proj, row_key, T);
+  else
+    MLORA_LAUNCH("finish_part", (finish_part<true, 1>), dim3((threads + kFinishThreads - 1) / kFinishThreads),
+                 dim3(kFinishThreads), 0, st, part, S, Y, M, N, pv, proj, row_key, T);
   return launched();
 }
 
@@ -1847,6 +1856,23 @@ hipError_t launch_gemm_lora(const PoolView& pv, int proj, const uint16_t* X, con
 
 size_t gemm_lora_part_floats(int M, int N, int K) {
   return (size_t)(M > 64 ? mid_split(M, N, K) : kDecSplit) * M * N;
+}
+
+hipError_t launch_base_split(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N, float* part,
+                             hipStream_t stream) {
+  if (M <= 0) return hipSuccess;
+  const uintptr_t al = reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(W) | reinterpret_cast<uintptr_t>(Y);
+  const bool vec = (K % 8 == 0) && (N % 8 == 0) && (al % 16 == 0);
+  const PoolView none{};
+  if (decode_splitk_ok(M, K, N, vec) && decode_splitk_enabled()) {
+    if (M <= 16) return launch_decode<1>(X, W, Y, M, K, N, none, 0, nullptr, nullptr, part, false, stream, false);
+    if (M <= 32) return launch_decode<2>(X, W, Y, M, K, N, none, 0, nullptr, nullptr, part, false, stream, false);
+    if (M <= 48) return launch_decode<3>(X, W, Y, M, K, N, none, 0, nullptr, nullptr, part, false, stream, false);
+    return launch_decode<4>(X, W, Y, M, K, N, none, 0, nullptr, nullptr, part, false, stream, false);
+  }
+  if (M > 64 && vec && mid_ring_ok(M, K) && (long)N * K * 2 < (1L << 31) && mid_enabled())
+    return launch_mid_lora(X, W, Y, M, K, N, none, 0, nullptr, nullptr, part, false, stream, false);
+  return hipErrorNotSupported;
 }
 
 // MLORA_BIG_EPILOGUE=0 keeps large batches on base GEMM + separate expand (A/B timing)

@@ -97,6 +97,11 @@ __host__ __device__ inline int32_t* row_desc(float* T, int M, int max_rank) {
   return reinterpret_cast<int32_t*>(T + (size_t)kRowsTParts * M * max_rank);
 }
 size_t gemm_lora_part_floats(int M, int N, int K);
+// Y = X W^T alone on the split-K decode / medium forms, with fp32 scratch
+// `part` of gemm_lora_part_floats(M, N, K) floats (a finish pass sums the
+// partials); hipErrorNotSupported where those forms do not apply.
+hipError_t launch_base_split(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N, float* part,
+                             hipStream_t stream);
 
 hipError_t launch_shrink_rows(const PoolView& pv, int proj, const uint16_t* X, const int32_t* ws, int n, float* T,
                               hipStream_t stream);

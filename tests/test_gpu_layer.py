@@ -308,12 +308,10 @@ def test_base_only_rows_bitwise_and_deterministic(M, variant):
     Yb = M.apply(pool, 0, Xd, W0d, none, variant=variant)
     rows = torch.from_numpy(np.nonzero(ids < 0)[0]).cuda()
     assert torch.equal(Y1[rows].view(torch.int16), Yb[rows].view(torch.int16))
-    # and the all-none run is exactly the base GEMM (the per-row variant adds
-    # a zero delta inside its own kernel, so it is compared within tolerance)
-    if variant != "rows":
-        assert torch.equal(Yb.view(torch.int16), M.base_gemm(Xd, W0d).view(torch.int16))
-    else:
-        assert_close(dev_to_f64(Yb), dev_to_f64(M.base_gemm(Xd, W0d)), "rows all-none", tol=1e-2)
+    # and the all-none run is the base GEMM (the layer sums K in split
+    # partials through its work buffer, the plain entry point in one pass:
+    # the same products in another order, so within rounding)
+    assert_close(dev_to_f64(Yb), dev_to_f64(M.base_gemm(Xd, W0d)), f"{variant} all-none", tol=1e-2)
 
 
 @pytest.mark.parametrize("n,dout", [(2100, 2200),   # few 256x256 tiles: 128x128 tiles, two per CU
