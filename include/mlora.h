@@ -60,14 +60,19 @@ typedef enum mlora_status {
  * implementation of the low-rank branch (all give the same result within
  * the bf16 tolerance, each is bitwise deterministic). */
 typedef enum mlora_variant {
-  MLORA_VARIANT_AUTO = 0,
-  MLORA_VARIANT_SPLIT = 1, /* shrink kernel -> fp32 t in `work` -> expand kernel */
-  MLORA_VARIANT_FUSED = 2, /* one kernel per row tile: t stays on chip           */
-  MLORA_VARIANT_ROWS = 3   /* decode-sized batches (n_rows <= 1024): per-row
-                              shrink, then the base GEMM with the expand in extra
-                              waves of the same kernel, overlapped with its K
-                              loop                                               */
+  MLORA_VARIANT_AUTO = 0,  /* ROWS up to 1024 rows, SPLIT above                  */
+  MLORA_VARIANT_SPLIT = 1, /* base GEMM, then shrink kernel -> fp32 t in `work`
+                              -> expand kernel (large batches: the expand in the
+                              GEMM's epilogue instead)                           */
+  MLORA_VARIANT_FUSED = 2, /* base GEMM, then one kernel per work item of up to
+                              MLORA_ITEM_ROWS rows: t stays on chip              */
+  MLORA_VARIANT_ROWS = 3   /* n_rows <= 1024: the per-row shrink inside the
+                              split-K base GEMM's launch, then a pass that sums
+                              the K partials and adds each row's expand          */
 } mlora_variant;
+/* SPLIT and FUSED split the base GEMM's K over workgroups too (partials in
+ * `work`) when n_rows <= 1024 and `work` holds mlora_work_bytes(); with a
+ * smaller or absent buffer (FUSED needs none) they take the one-pass GEMM. */
 
 /* Limits. */
 #define MLORA_MAX_ROWS 16384        /* rows per batch (segment builder works in one workgroup) */
