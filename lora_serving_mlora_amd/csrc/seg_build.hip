@@ -77,13 +77,21 @@ __global__ __launch_bounds__(NT) void seg_build_kernel(const int32_t* __restrict
   int32_t* items = ws + MLORA_SEG_ITEMS(n);
   int32_t* row_key = ws + MLORA_SEG_ROWKEY(n);
 
+  // The resident table (one rank per adapter id) is read into the free
+  // buffer in the same round trip as the first row ids, so a row's residency
+  // test is an LDS read instead of a second, dependent global load.  Used
+  // when the table takes one load per thread and fits that buffer.
+  const bool table = max_adapters <= kThreads && max_adapters <= cap;
+  int32_t* rank_tab = reinterpret_cast<int32_t*>(bufB);
+  const int a_first = tid < n ? row_adapter[tid] : -1;
+  if (table && tid < max_adapters) rank_tab[tid] = pool_rank[tid];
   if (tid < 3) s_cnt[tid] = 0;
   __syncthreads();
 
   // 1. key of every row, packed with its index: (key << 16) | row
   int my_none = 0, my_bad = 0, my_status = 0;
   for (int k = tid; k < n; k += kThreads) {
-    const int a = row_adapter[k];
+    const int a = k == tid ? a_first : row_adapter[k];
     uint32_t key;
     if (a == -1) {
       key = A;
@@ -92,7 +100,7 @@ __global__ __launch_bounds__(NT) void seg_build_kernel(const int32_t* __restrict
       key = A + 1;
       ++my_bad;
       my_status |= MLORA_SEG_BAD_ID;
-    } else if (pool_rank[a] <= 0) {
+    } else if ((table ? rank_tab[a] : pool_rank[a]) <= 0) {
       key = A + 1;
       ++my_bad;
       my_status |= MLORA_SEG_NOT_RESIDENT;
@@ -284,18 +292,23 @@ __global__ __launch_bounds__(64) void seg_build_small(const int32_t* __restrict_
                                                       const int32_t* __restrict__ pool_rank, int max_adapters,
                                                       int32_t* __restrict__ ws) {
   __shared__ int s_sorted[65];  // sorted keys, then segment offsets
+  __shared__ int s_rank[64];    // the resident table, when it has at most 64 ids
   const int lane = threadIdx.x;
   const bool valid = lane < n;
   const int A = max_adapters;
+  const bool table = A <= 64;
+  // row id and table entry travel in the same round trip
+  const int a = valid ? row_adapter[lane] : -1;
+  if (table && lane < A) s_rank[lane] = pool_rank[lane];
+  __syncthreads();
   int key = A + 2, status = 0;  // lanes past n sort after everything
   if (valid) {
-    const int a = row_adapter[lane];
     if (a == -1) {
       key = A;
     } else if (a < -1 || a >= A) {
       key = A + 1;
       status = MLORA_SEG_BAD_ID;
-    } else if (pool_rank[a] <= 0) {
+    } else if ((table ? s_rank[a] : pool_rank[a]) <= 0) {
       key = A + 1;
       status = MLORA_SEG_NOT_RESIDENT;
     } else {

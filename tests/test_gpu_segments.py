@@ -90,7 +90,11 @@ def test_all_assignments_of_five_rows(M):
 
 @pytest.mark.parametrize("n,A,seed", [(0, 4, 1), (1, 4, 2), (63, 7, 3), (64, 254, 4), (65, 255, 5),
                                       (1000, 256, 6), (4097, 300, 7), (16384, 5000, 8), (16384, 3, 9),
-                                      (777, 1, 10)])
+                                      (777, 1, 10),
+                                      # resident-table edges: read into LDS up to 64 ids (one wave) and up
+                                      # to one id per thread within the free buffer, else per row
+                                      (40, 64, 11), (40, 65, 12), (200, 256, 13), (200, 257, 14),
+                                      (70, 200, 15), (1025, 1024, 16), (1025, 1025, 17)])
 def test_random_batches(M, n, A, seed):
     g = np.random.default_rng(seed)
     resident = sorted(g.choice(A, size=max(1, (2 * A) // 3), replace=False).tolist())
