@@ -2,8 +2,10 @@
 """Throughput of the heterogeneous multi-LoRA linear on one MI355X.
 
 One step = one batch through the whole layer: build the segments (group rows
-by adapter), then mlora_apply (the base GEMM Y = X W0^T and the low-rank
-branch, shrink and expand), for the variant the library's planner picks.
+by adapter) and apply the layer (the base GEMM Y = X W0^T and the low-rank
+branch, shrink and expand), for the variant the library's planner picks, in
+one mlora_forward call (--separate-build: mlora_build_segments, then
+mlora_apply).
 The steps of the timed region are replayed from a captured HIP graph, so the
 number is the GPU's, not the Python launcher's.  Inputs are seeded synthetic
 tensors already resident in HBM.  Consecutive steps rotate over distinct
@@ -41,6 +43,7 @@ RIDGE = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
 KERNEL_SOURCES = {"seg_build": "seg_build.hip", "gemm_skinny": "base_gemm.hip", "gemm_ksplit": "base_gemm.hip",
                   "gemm_tiled": "base_gemm.hip", "gemm_big": "base_gemm.hip", "gemm_decode": "base_gemm.hip",
                   "gemm_decode+shrink_rows": "base_gemm.hip", "finish_part": "base_gemm.hip",
+                  "gemm_decode+seg+shrink_rows": "base_gemm.hip",
                   "gemm_mid+shrink_rows": "base_gemm.hip",
                   "gemm_mid": "base_gemm.hip", "gemm_skinny_lora": "base_gemm.hip",
                   "gemm_ksplit_lora": "base_gemm.hip", "shrink": "lora_branch.hip", "expand": "lora_branch.hip",
@@ -60,6 +63,8 @@ def parse_args():
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of from a HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-build", action="store_true",
+                    help="run each step as two library calls (build_segments, then apply) instead of forward")
     ap.add_argument("--copy-only", action="store_true", help="only run the HBM copy calibration kernel")
     ap.add_argument("--yardstick", action="store_true",
                     help="also time the vendor GEMM (torch linear) on the same rotated operands, for context")
@@ -101,8 +106,9 @@ def algorithmic(w, chunks):
     split_dense = (2 * (dout * din + n * din), 2 * n * din * dout)   # Y comes from the finish pass
     finish = (2 * sum_r * dout + 4 * sum_nr + 2 * n * dout, 2 * sum_nr * dout)
     gemm_lora = (base[0] + 2 * sum_r * dout + 4 * sum_nr, base[1] + 2 * sum_nr * dout)
+    seg = (4 * n + 4 * 4 * n, 0)   # ids in; perm, inv, row keys and segment tables out
     out = {
-        "seg_build": (4 * n + 4 * 4 * n, 0),
+        "seg_build": seg,
         "shrink": (2 * sum_r * din + 2 * n_act * din + 4 * sum_nr * max(chunks, 1), 2 * sum_nr * din),
         "expand": (2 * sum_r * dout + 4 * n_act * dout + 4 * sum_nr * max(chunks, 1), 2 * sum_nr * dout),
         "fused": (2 * sum_r * (din + dout) + 2 * n_act * din + 4 * n_act * dout, 2 * sum_nr * (din + dout)),
@@ -110,6 +116,7 @@ def algorithmic(w, chunks):
         "gemm_decode": split_dense, "gemm_mid": split_dense,
         "gemm_decode+shrink_rows": (split_dense[0] + shrink_rows[0], split_dense[1] + shrink_rows[1]),
         "gemm_mid+shrink_rows": (split_dense[0] + shrink_rows[0], split_dense[1] + shrink_rows[1]),
+        "gemm_decode+seg+shrink_rows": (split_dense[0] + shrink_rows[0] + seg[0], split_dense[1] + shrink_rows[1]),
         "finish_part": finish,
         "finish_base": (2 * n * dout, 0),   # the base GEMM's partials summed (scratch) into Y
         "gemm_skinny_lora": gemm_lora, "gemm_ksplit_lora": gemm_lora, "gemm_big_lora": gemm_lora,
@@ -124,14 +131,17 @@ def algorithmic(w, chunks):
 
 
 DENSE = ("gemm_skinny", "gemm_ksplit", "gemm_tiled", "gemm_big", "gemm_decode", "gemm_mid", "gemm_mid+shrink_rows",
-         "gemm_decode+shrink_rows", "gemm_skinny_lora", "gemm_ksplit_lora", "gemm_big_lora")
+         "gemm_decode+shrink_rows", "gemm_decode+seg+shrink_rows", "gemm_skinny_lora", "gemm_ksplit_lora",
+         "gemm_big_lora")
 
 
 def source_hash(kernel):
     """Hash of the kernel's source file and the headers every kernel shares."""
     h = hashlib.sha256()
     base = os.path.join(ROOT, "lora_serving_mlora_amd", "csrc")
-    for f in (KERNEL_SOURCES[kernel.split("#")[0]], "internal.h", "row_kernels.h"):
+    src = KERNEL_SOURCES[kernel.split("#")[0]]
+    shared = ("internal.h", "row_kernels.h") + (("seg_wave.h",) if src in ("base_gemm.hip", "seg_build.hip") else ())
+    for f in (src,) + shared:
         with open(os.path.join(base, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -489,10 +499,17 @@ def main():
 
     work = M.new_work(pool, n)
 
-    def step(i):
-        p = i % R
-        M.build_segments(pool, ids, seg_ws)
-        M.apply(pool, p, X, W0s[p], seg_ws, Y=Y, work=work, variant=variant)
+    if args.separate_build:
+        def step(i):
+            p = i % R
+            M.build_segments(pool, ids, seg_ws)
+            M.apply(pool, p, X, W0s[p], seg_ws, Y=Y, work=work, variant=variant)
+    else:
+        def step(i):
+            # segment build + layer in one library call (one launch fewer
+            # where the build rides in the GEMM launch)
+            p = i % R
+            M.forward(pool, p, X, W0s[p], ids, seg_ws=seg_ws, Y=Y, work=work, variant=variant)
 
     K, W = args.steps, args.warmup
     for i in range(W):
@@ -608,6 +625,7 @@ def main():
         "config": {"workload": w.name, "n_tokens": n, "din": w.din, "dout": w.dout,
                    "adapters": len(w.ranks), "ranks": sorted(set(w.ranks.values())),
                    "variant": variant, "shrink_chunks": chunks, "rotation_projections": R,
+                   "step": "build_segments+apply" if args.separate_build else "forward",
                    "launch": "hipgraph" if use_graph else "eager", "parallelism": "single-gpu"},
         "roofline": roofline,
         "per_kernel_us": {k: (round(v * 1e3, 3) if v else None) for k, v in per_kernel_ms.items()},

@@ -316,6 +316,26 @@ mlora_status mlora_apply(const mlora_pool* pool, int32_t proj, const uint16_t* X
                          const void* seg_ws, uint16_t* Y, int32_t n_rows, void* work, size_t work_bytes,
                          int32_t variant, void* stream);
 
+/* Segment build and the layer for one projection in a single call: what
+ * mlora_build_segments(pool, row_adapter, n_rows, seg_ws) followed by
+ * mlora_apply(pool, proj, X, W0, seg_ws, Y, n_rows, work, work_bytes,
+ * variant) computes (M031 card, sections 02-03: group the batch's rows by
+ * adapter, one shared base product, each row's low-rank term back at its
+ * original row), with the same results in Y, seg_ws and work.
+ *   row_adapter: device int32 [n_rows], as for mlora_build_segments;
+ *   seg_ws: device, mlora_segments_bytes(n_rows) bytes, 8-byte aligned;
+ *   the other arguments as for mlora_apply.
+ * For the per-row plan at decode sizes (n_rows <= 64, 16-byte aligned
+ * operands, din a multiple of 2048 up to 4096) the segment build runs as one
+ * more workgroup of the base GEMM's launch, whose other workgroups take each
+ * row's key from row_adapter and the resident table directly: one launch
+ * fewer on the stream.  Otherwise the two calls run one after the other.
+ * seg_ws stays valid for mlora_apply on further projections of the batch.
+ * Errors: those of the two calls; nothing is launched on an argument error. */
+mlora_status mlora_forward(const mlora_pool* pool, int32_t proj, const uint16_t* X, const uint16_t* W0,
+                           const int32_t* row_adapter, void* seg_ws, uint16_t* Y, int32_t n_rows, void* work,
+                           size_t work_bytes, int32_t variant, void* stream);
+
 /* ---------------------------------------------------------------------------
  * The merged alternative (M031 card, section 04: W_merged = W_base + scale *
  * Up Down serves that one adapter with a plain GEMM; airsota card, section

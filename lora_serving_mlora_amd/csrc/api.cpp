@@ -909,6 +909,38 @@ mlora_status mlora_apply(const mlora_pool* p, int32_t proj, const uint16_t* X, c
   return hip_check(mlora::launch_expand(v, proj, T, chunks, ws, Y, n, s), "expand launch");
 }
 
+mlora_status mlora_forward(const mlora_pool* p, int32_t proj, const uint16_t* X, const uint16_t* W0,
+                           const int32_t* row_adapter, void* seg_ws, uint16_t* Y, int32_t n, void* work,
+                           size_t work_bytes, int32_t variant, void* stream) {
+  g_err.clear();
+  mlora_status st = check_pool(p);
+  if (st != MLORA_OK) return st;
+  if (n < 0 || n > MLORA_MAX_ROWS) return fail(MLORA_EINVAL, "n_rows %d outside [0, %d]", n, MLORA_MAX_ROWS);
+  if (!seg_ws || (n > 0 && !row_adapter)) return fail(MLORA_EINVAL, "row_adapter and seg_ws must not be NULL");
+  if ((reinterpret_cast<uintptr_t>(seg_ws) & 7u) != 0) return fail(MLORA_EINVAL, "seg_ws must be 8-byte aligned");
+  if ((st = check_branch_args(p, proj, seg_ws, n)) != MLORA_OK) return st;
+  if (variant < MLORA_VARIANT_AUTO || variant > MLORA_VARIANT_ROWS) return fail(MLORA_EINVAL, "unknown variant %d", variant);
+  if (variant == MLORA_VARIANT_ROWS && n > kRowsMax)
+    return fail(MLORA_EINVAL, "the per-row variant takes at most %d rows", kRowsMax);
+  if (n > 0 && (!X || !W0 || !Y)) return fail(MLORA_EINVAL, "X, W0 and Y must not be NULL");
+  const int32_t resolved = variant == MLORA_VARIANT_AUTO ? auto_variant(p, n) : variant;
+  if (n > 0 && (resolved == MLORA_VARIANT_SPLIT || resolved == MLORA_VARIANT_ROWS)) {
+    // the work checks of mlora_apply, before anything is launched
+    const size_t need = mlora_work_bytes(p, n);
+    if (!work || work_bytes < need) return fail(MLORA_EINVAL, "work: %zu bytes given, %zu needed", work_bytes, need);
+    if (!aligned16(work)) return fail(MLORA_EINVAL, "work must be 16-byte aligned");
+    if (resolved == MLORA_VARIANT_ROWS && (st = check_rows_work(p, n, work, work_bytes)) != MLORA_OK) return st;
+  }
+  if (n > 0 && resolved == MLORA_VARIANT_ROWS) {
+    const RowsWork w = rows_work(p, n, work);
+    const hipError_t e = mlora::launch_forward_rows(p->view(), proj, X, W0, row_adapter, static_cast<int32_t*>(seg_ws),
+                                                    w.T, w.part, Y, n, as_stream(stream));
+    if (e != hipErrorNotSupported) return hip_check(e, "segment build + per-row shrink + GEMM + expand launch");
+  }
+  if ((st = mlora_build_segments(p, row_adapter, n, seg_ws, stream)) != MLORA_OK) return st;
+  return mlora_apply(p, proj, X, W0, seg_ws, Y, n, work, work_bytes, variant, stream);
+}
+
 mlora_status mlora_timing_arm(int32_t n_launches) {
   g_err.clear();
   if (n_launches < 1 || n_launches > kTimingMax) return fail(MLORA_EINVAL, "n_launches %d outside [1, %d]", n_launches, kTimingMax);

@@ -22,6 +22,7 @@
 
 #include "internal.h"
 #include "row_kernels.h"
+#include "seg_wave.h"
 
 namespace mlora {
 namespace {
@@ -1481,14 +1482,37 @@ hipError_t launch_gemm(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M,
 constexpr int kDecCols = 64, kDecSplit = 4, kDecWaves = 8;
 constexpr int kMidMaxSplit = 8;
 
-template <int MB>
+// Row r's key and its adapter's rank (0 for a key < 0) from the batch's
+// adapter ids and the resident table; every value is wave-uniform, so the
+// loads are scalar and never wait for the vector loads in flight.
+struct KeyRank {
+  int key, rank;
+};
+__device__ __forceinline__ KeyRank key_rank_from_ids(const int32_t* __restrict__ ids, const PoolView& pv, int r) {
+  const int a = __builtin_amdgcn_readfirstlane(ids[r]);
+  int rk = 0;
+  if (a >= 0 && a < pv.max_adapters) rk = __builtin_amdgcn_readfirstlane(pv.rank[a]);
+  const int key = __builtin_amdgcn_readfirstlane(row_key_of(a, rk, pv.max_adapters));
+  return {key, key >= 0 ? rk : 0};
+}
+
+// IDS: the row keys come from the adapter ids `ids` and the resident table
+// instead of a built workspace, and one workgroup past the GEMM's builds
+// that workspace (seg_ws) beside it.
+template <int MB, bool IDS>
 __global__ __launch_bounds__(64 * kDecWaves) void gemm_decode(const uint16_t* __restrict__ X,
                                                              const uint16_t* __restrict__ W, int M, int K, int N,
                                                              PoolView pv, int proj,
                                                              const int32_t* __restrict__ row_key,
                                                              float* __restrict__ Tp, float* __restrict__ part,
-                                                             int shrink) {
+                                                             int shrink, const int32_t* __restrict__ ids,
+                                                             int32_t* __restrict__ seg_ws) {
   extern __shared__ __attribute__((aligned(16))) uint16_t dec_lds[];
+  if (IDS && (int)blockIdx.x == ((N + kDecCols - 1) / kDecCols) * kDecSplit) {
+    int* scratch_lds = reinterpret_cast<int*>(dec_lds);  // 516 bytes of at least 4 KiB (the reduction area alone)
+    seg_build_wave(ids, M, pv.rank, pv.max_adapters, seg_ws, scratch_lds, scratch_lds + 65);
+    return;
+  }
   const int Kq = K / kDecSplit;
   uint16_t* xs = dec_lds;                                               // [M][Kq]
   floatx4* red = reinterpret_cast<floatx4*>(dec_lds + (size_t)M * Kq);  // [4][MB][64]
@@ -1536,9 +1560,15 @@ __global__ __launch_bounds__(64 * kDecWaves) void gemm_decode(const uint16_t* __
   int key0 = -1, rank0 = 0;
   uint4 dn[2][2];
   if (shrink && cb < M) {
-    key0 = __builtin_amdgcn_readfirstlane(row_key[cb]);
+    if (IDS) {
+      const KeyRank kr = key_rank_from_ids(ids, pv, cb);
+      key0 = kr.key;
+      rank0 = kr.rank;
+    } else {
+      key0 = __builtin_amdgcn_readfirstlane(row_key[cb]);
+    }
     if (key0 >= 0) {
-      rank0 = __builtin_amdgcn_readfirstlane(pv.rank[key0]);
+      if (!IDS) rank0 = __builtin_amdgcn_readfirstlane(pv.rank[key0]);
       const int32_t* dpage = pv.down_page + ((size_t)key0 * pv.n_proj + proj) * pv.max_rank;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
@@ -1593,10 +1623,20 @@ __global__ __launch_bounds__(64 * kDecWaves) void gemm_decode(const uint16_t* __
   if (shrink) {
     for (int r = cb; r < M; r += ncb) {
       const bool first = r == cb;
-      const int key = first ? key0 : __builtin_amdgcn_readfirstlane(row_key[r]);
+      int key, rank;
+      if (first) {
+        key = key0;
+        rank = rank0;
+      } else if (IDS) {
+        const KeyRank kr = key_rank_from_ids(ids, pv, r);
+        key = kr.key;
+        rank = kr.rank;
+      } else {
+        key = __builtin_amdgcn_readfirstlane(row_key[r]);
+      }
       if (kq == 0) write_row_desc(pv, proj, key, r, row_desc(Tp, M, pv.max_rank));
       if (key < 0) continue;
-      const int rank = first ? rank0 : __builtin_amdgcn_readfirstlane(pv.rank[key]);
+      if (!first && !IDS) rank = __builtin_amdgcn_readfirstlane(pv.rank[key]);
       const int32_t* dpage = pv.down_page + ((size_t)key * pv.n_proj + proj) * pv.max_rank;
       uint4 d[2][2];
       // Down chunks of ranks q0 + wave and q0 + wave + 8 (the first group of
@@ -1723,19 +1763,28 @@ size_t decode_lds_bytes(int M, int K, int MB) { return (size_t)M * (K / kDecSpli
 template <int MB>
 hipError_t launch_decode(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N, const PoolView& pv,
                          int proj, const int32_t* row_key, float* T, float* part, bool shrink, hipStream_t st,
-                         bool lora = true) {
+                         bool lora = true, const int32_t* ids = nullptr, int32_t* seg_ws = nullptr) {
   static_assert(kDecSplit == kRowsTParts, "T partial slices are the K quarters");
   const size_t lds = decode_lds_bytes(M, K, MB);
   static size_t attr = 0;
   if (lds > attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_decode<MB>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_decode<MB, false>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)gemm_decode<MB, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
     if (e != hipSuccess) return e;
     attr = lds;
   }
   const int ncb = (N + kDecCols - 1) / kDecCols;
-  MLORA_LAUNCH(shrink ? "gemm_decode+shrink_rows" : "gemm_decode", gemm_decode<MB>, dim3(ncb * kDecSplit),
-               dim3(64 * kDecWaves), lds, st, X, W, M, K, N, pv, proj, row_key, T, part, shrink ? 1 : 0);
+  if (seg_ws)
+    MLORA_LAUNCH("gemm_decode+seg+shrink_rows", (gemm_decode<MB, true>), dim3(ncb * kDecSplit + 1),
+                 dim3(64 * kDecWaves), lds, st, X, W, M, K, N, pv, proj, row_key, T, part, shrink ? 1 : 0, ids,
+                 seg_ws);
+  else
+    MLORA_LAUNCH(shrink ? "gemm_decode+shrink_rows" : "gemm_decode", (gemm_decode<MB, false>), dim3(ncb * kDecSplit),
+                 dim3(64 * kDecWaves), lds, st, X, W, M, K, N, pv, proj, row_key, T, part, shrink ? 1 : 0,
+                 (const int32_t*)nullptr, (int32_t*)nullptr);
   hipError_t e = launched();
   if (e != hipSuccess) return e;
   const int threads = M * (N / 8);
@@ -1852,6 +1901,23 @@ hipError_t launch_gemm_lora(const PoolView& pv, int proj, const uint16_t* X, con
   }
   return vec ? launch_lora<true>(X, W, Y, M, K, N, pv, proj, row_key, T, stream)
              : launch_lora<false>(X, W, Y, M, K, N, pv, proj, row_key, T, stream);
+}
+
+hipError_t launch_forward_rows(const PoolView& pv, int proj, const uint16_t* X, const uint16_t* W,
+                               const int32_t* ids, int32_t* ws, float* T, float* part, uint16_t* Y, int M,
+                               hipStream_t stream) {
+  if (M <= 0 || M > 64) return hipErrorNotSupported;
+  const int K = pv.din, N = pv.dout;
+  const uintptr_t al = reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(W) |
+                       reinterpret_cast<uintptr_t>(pv.up) | reinterpret_cast<uintptr_t>(Y) |
+                       reinterpret_cast<uintptr_t>(pv.down);
+  const bool vec = (K % 8 == 0) && (N % 8 == 0) && (al % 16 == 0);
+  if (!decode_splitk_ok(M, K, N, vec) || !decode_splitk_enabled()) return hipErrorNotSupported;
+  const int32_t* row_key = ws + MLORA_SEG_ROWKEY(M);
+  if (M <= 16) return launch_decode<1>(X, W, Y, M, K, N, pv, proj, row_key, T, part, true, stream, true, ids, ws);
+  if (M <= 32) return launch_decode<2>(X, W, Y, M, K, N, pv, proj, row_key, T, part, true, stream, true, ids, ws);
+  if (M <= 48) return launch_decode<3>(X, W, Y, M, K, N, pv, proj, row_key, T, part, true, stream, true, ids, ws);
+  return launch_decode<4>(X, W, Y, M, K, N, pv, proj, row_key, T, part, true, stream, true, ids, ws);
 }
 
 size_t gemm_lora_part_floats(int M, int N, int K) {

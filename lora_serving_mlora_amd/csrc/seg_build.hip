@@ -15,6 +15,7 @@
 // same digit (found with ballots), never an atomic's arrival order.  The
 // result is bit-exact and identical run to run.
 #include "internal.h"
+#include "seg_wave.h"
 
 namespace mlora {
 namespace {
@@ -281,107 +282,13 @@ __global__ __launch_bounds__(NT) void seg_build_kernel(const int32_t* __restrict
   }
 }
 
-// ---------------------------------------------------------------------------
-// Batches of at most 64 rows (decode steps): one wave, one row per lane.  A
-// row's sorted position is the number of rows with a smaller (key, row) pair,
-// counted against every other lane's key broadcast from registers; the
-// result is the same stable order as the radix path, with no LDS passes and
-// no barriers across waves.
-// ---------------------------------------------------------------------------
+// Batches of at most 64 rows (decode steps): one wave, one row per lane, no
+// LDS passes and no barriers across waves.
 __global__ __launch_bounds__(64) void seg_build_small(const int32_t* __restrict__ row_adapter, int n,
                                                       const int32_t* __restrict__ pool_rank, int max_adapters,
                                                       int32_t* __restrict__ ws) {
-  __shared__ int s_sorted[65];  // sorted keys, then segment offsets
-  __shared__ int s_rank[64];    // the resident table, when it has at most 64 ids
-  const int lane = threadIdx.x;
-  const bool valid = lane < n;
-  const int A = max_adapters;
-  const bool table = A <= 64;
-  // row id and table entry travel in the same round trip
-  const int a = valid ? row_adapter[lane] : -1;
-  if (table && lane < A) s_rank[lane] = pool_rank[lane];
-  __syncthreads();
-  int key = A + 2, status = 0;  // lanes past n sort after everything
-  if (valid) {
-    if (a == -1) {
-      key = A;
-    } else if (a < -1 || a >= A) {
-      key = A + 1;
-      status = MLORA_SEG_BAD_ID;
-    } else if ((table ? s_rank[a] : pool_rank[a]) <= 0) {
-      key = A + 1;
-      status = MLORA_SEG_NOT_RESIDENT;
-    } else {
-      key = a;
-    }
-    ws[MLORA_SEG_ROWKEY(n) + lane] = key < A ? key : (key == A ? -1 : -2);
-  }
-  int pos = 0;
-  for (int j = 0; j < 64; ++j) {
-    const int kj = __builtin_amdgcn_readlane(key, j);
-    pos += (kj < key) || (kj == key && j < lane);
-  }
-  if (valid) {
-    ws[MLORA_SEG_PERM(n) + pos] = lane;
-    ws[MLORA_SEG_INV(n) + lane] = pos;
-    s_sorted[pos] = key;
-  }
-  const unsigned long long act = __ballot(valid && key < A);
-  const unsigned long long none = __ballot(valid && key == A);
-  const unsigned long long bad = __ballot(valid && key == A + 1);
-  int st = status;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) st |= __shfl_xor(st, m, 64);
-  const int n_act = __popcll(act);
-  __syncthreads();
-  // segment starts among the active sorted positions
-  const int kj = lane < n_act ? s_sorted[lane] : -1;
-  const bool start = lane < n_act && (lane == 0 || s_sorted[lane - 1] != kj);
-  const unsigned long long starts = __ballot(start);
-  const int nseg = __popcll(starts);
-  const int sidx = __popcll(starts & ((1ull << lane) - 1ull));
-  __syncthreads();
-  if (start) {
-    ws[MLORA_SEG_ADAPTER(n) + sidx] = kj;
-    ws[MLORA_SEG_OFF(n) + sidx] = lane;
-    s_sorted[sidx] = lane;
-  }
-  if (lane == 0) {
-    ws[MLORA_SEG_OFF(n) + nseg] = n_act;
-    s_sorted[nseg] = n_act;
-  }
-  __syncthreads();
-  // work items: ceil(len / ITEM_ROWS) per segment, in segment order
-  int tiles = 0;
-  if (lane < nseg) tiles = (s_sorted[lane + 1] - s_sorted[lane] + MLORA_ITEM_ROWS - 1) / MLORA_ITEM_ROWS;
-  int incl = tiles;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += y;
-  }
-  const int n_items = __shfl(incl, 63, 64);
-  int32_t* items = ws + MLORA_SEG_ITEMS(n);
-  for (int t = 0; t < tiles; ++t) {
-    items[2 * (incl - tiles + t)] = lane;
-    items[2 * (incl - tiles + t) + 1] = s_sorted[lane] + t * MLORA_ITEM_ROWS;
-  }
-  if (lane == 0) {
-    ws[MLORA_SEG_NSEG] = nseg;
-    ws[MLORA_SEG_NACT] = n_act;
-    ws[MLORA_SEG_NNONE] = __popcll(none);
-    ws[MLORA_SEG_NBAD] = __popcll(bad);
-    ws[MLORA_SEG_STATUS] = st;
-    ws[MLORA_SEG_NITEMS] = n_items;
-    ws[MLORA_SEG_NROWS] = n;
-    ws[MLORA_SEG_MAXAD] = max_adapters;
-  }
-  // one tile per segment (a segment here has at most 64 rows)
-  if (lane < nseg) {
-    ws[MLORA_SEG_TILES(n) + 2 * lane] = lane;
-    ws[MLORA_SEG_TILES(n) + 2 * lane + 1] = s_sorted[lane];
-  }
-  if (lane >= 8 && lane < MLORA_SEG_HEADER) ws[lane] = lane == MLORA_SEG_NTILES ? nseg : 0;
+  __shared__ int s_sorted[65], s_rank[64];
+  seg_build_wave(row_adapter, n, pool_rank, max_adapters, ws, s_sorted, s_rank);
 }
 
 template <int NT>

@@ -79,6 +79,10 @@ def test_base_and_combined_kernels_match_the_element_count():
     fused_in = algo["gemm_decode+shrink_rows"]
     assert fused_in == (2 * (w0 + x) + 2 * (c["down"] + c["x_act"]) + 4 * c["t"],
                         2 * (dense + c["mac_shrink"]))
+    # the decode launch that also builds the segments: ids in, the
+    # workspace's per-row arrays out (perm, inv, key, item and tile entries)
+    assert algo["gemm_decode+seg+shrink_rows"] == (fused_in[0] + algo["seg_build"][0], fused_in[1])
+    assert algo["seg_build"] == (4 * w.n + 16 * w.n, 0)
     lora = algo["gemm_big_lora"]
     assert lora == (2 * (w0 + x + y) + 2 * c["up"] + 4 * c["t"], 2 * (dense + c["mac_expand"]))
 
