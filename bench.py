@@ -43,7 +43,7 @@ RIDGE = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
 KERNEL_SOURCES = {"seg_build": "seg_build.hip", "gemm_skinny": "base_gemm.hip", "gemm_ksplit": "base_gemm.hip",
                   "gemm_tiled": "base_gemm.hip", "gemm_big": "base_gemm.hip", "gemm_decode": "base_gemm.hip",
                   "gemm_decode+shrink_rows": "base_gemm.hip", "finish_part": "base_gemm.hip",
-                  "gemm_decode+seg+shrink_rows": "base_gemm.hip",
+                  "gemm_decode+seg+shrink_rows": "base_gemm.hip", "gemm_mid+seg+shrink_rows": "base_gemm.hip",
                   "gemm_mid+shrink_rows": "base_gemm.hip",
                   "gemm_mid": "base_gemm.hip", "gemm_skinny_lora": "base_gemm.hip",
                   "gemm_ksplit_lora": "base_gemm.hip", "shrink": "lora_branch.hip", "expand": "lora_branch.hip",
@@ -117,6 +117,7 @@ def algorithmic(w, chunks):
         "gemm_decode+shrink_rows": (split_dense[0] + shrink_rows[0], split_dense[1] + shrink_rows[1]),
         "gemm_mid+shrink_rows": (split_dense[0] + shrink_rows[0], split_dense[1] + shrink_rows[1]),
         "gemm_decode+seg+shrink_rows": (split_dense[0] + shrink_rows[0] + seg[0], split_dense[1] + shrink_rows[1]),
+        "gemm_mid+seg+shrink_rows": (split_dense[0] + shrink_rows[0] + seg[0], split_dense[1] + shrink_rows[1]),
         "finish_part": finish,
         "finish_base": (2 * n * dout, 0),   # the base GEMM's partials summed (scratch) into Y
         "gemm_skinny_lora": gemm_lora, "gemm_ksplit_lora": gemm_lora, "gemm_big_lora": gemm_lora,
@@ -131,7 +132,8 @@ def algorithmic(w, chunks):
 
 
 DENSE = ("gemm_skinny", "gemm_ksplit", "gemm_tiled", "gemm_big", "gemm_decode", "gemm_mid", "gemm_mid+shrink_rows",
-         "gemm_decode+shrink_rows", "gemm_decode+seg+shrink_rows", "gemm_skinny_lora", "gemm_ksplit_lora",
+         "gemm_decode+shrink_rows", "gemm_decode+seg+shrink_rows", "gemm_mid+seg+shrink_rows", "gemm_skinny_lora",
+         "gemm_ksplit_lora",
          "gemm_big_lora")
 
 
@@ -140,7 +142,7 @@ def source_hash(kernel):
     h = hashlib.sha256()
     base = os.path.join(ROOT, "lora_serving_mlora_amd", "csrc")
     src = KERNEL_SOURCES[kernel.split("#")[0]]
-    shared = ("internal.h", "row_kernels.h") + (("seg_wave.h",) if src in ("base_gemm.hip", "seg_build.hip") else ())
+    shared = ("internal.h", "row_kernels.h") + (("seg_device.h",) if src in ("base_gemm.hip", "seg_build.hip") else ())
     for f in (src,) + shared:
         with open(os.path.join(base, f), "rb") as fh:
             h.update(fh.read())

@@ -325,11 +325,13 @@ mlora_status mlora_apply(const mlora_pool* pool, int32_t proj, const uint16_t* X
  *   row_adapter: device int32 [n_rows], as for mlora_build_segments;
  *   seg_ws: device, mlora_segments_bytes(n_rows) bytes, 8-byte aligned;
  *   the other arguments as for mlora_apply.
- * For the per-row plan at decode sizes (n_rows <= 64, 16-byte aligned
- * operands, din a multiple of 2048 up to 4096) the segment build runs as one
- * more workgroup of the base GEMM's launch, whose other workgroups take each
- * row's key from row_adapter and the resident table directly: one launch
- * fewer on the stream.  Otherwise the two calls run one after the other.
+ * For the per-row plan (16-byte aligned operands) at decode sizes
+ * (n_rows <= 64, din a multiple of 2048 up to 4096) and medium ones (65 ..
+ * 1024 rows, din a multiple of 128) the segment build runs in a workgroup
+ * of the base GEMM's launch, whose
+ * other workgroups take each row's key from row_adapter and the resident
+ * table directly: one launch fewer on the stream.  Otherwise the two calls
+ * run one after the other.
  * seg_ws stays valid for mlora_apply on further projections of the batch.
  * Errors: those of the two calls; nothing is launched on an argument error. */
 mlora_status mlora_forward(const mlora_pool* pool, int32_t proj, const uint16_t* X, const uint16_t* W0,

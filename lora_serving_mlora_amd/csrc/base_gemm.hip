@@ -22,7 +22,7 @@
 
 #include "internal.h"
 #include "row_kernels.h"
-#include "seg_wave.h"
+#include "seg_device.h"
 
 namespace mlora {
 namespace {
@@ -1166,21 +1166,59 @@ __device__ __forceinline__ void ring_lora_epilogue(const RingCtx& c, int m0, int
 // two 32 KiB stages, so a shrink workgroup and a tile workgroup fit on one CU
 // together (64 KiB of LDS each, at most 256 registers per lane) and the
 // shrink's Down reads overlap the tiles' work instead of following it.
-template <int TM, int TN, int KD, bool PART, bool LORA, bool CO>
+// The per-row shrink of row k with its key taken from the batch's adapter
+// ids and the resident table (the same key the segment workspace holds).
+template <bool VEC, int NW>
+__device__ __forceinline__ void shrink_row_body_ids(const PoolView& pv, int proj, const uint16_t* __restrict__ X,
+                                                    const int32_t* __restrict__ ids, int k, float* __restrict__ T,
+                                                    int32_t* __restrict__ desc) {
+  const int a = ids[k];
+  const int rk = (a >= 0 && a < pv.max_adapters) ? pv.rank[a] : 0;
+  const int key = row_key_of(a, rk, pv.max_adapters);
+  write_row_desc(pv, proj, key, k, desc);
+  if (key < 0) return;  // base-only or invalid: no low-rank term
+  shrink_row_to<VEC, NW>(pv, pv.down_page + ((size_t)key * pv.n_proj + proj) * pv.max_rank, rk, pv.scale[key],
+                         X + (size_t)k * pv.din, T + (size_t)k * pv.max_rank);
+}
+
+// IDS (co-resident form only): the shrink workgroups take each row's key
+// from the adapter ids `ids`, and the first workgroup dispatched, (0, 0),
+// builds the batch's segment workspace seg_ws (seg_passes radix passes) in
+// the LDS its ring would use, while the rows go to the other n_shrink - 1.
+template <int TM, int TN, int KD, bool PART, bool LORA, bool CO, bool IDS = false>
 __device__ __forceinline__ void gemm_ring_body(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y,
     float* __restrict__ part, int M, int K, int N, int tiles_n, int n_tiles, int per_xcd, int kt_per, PoolView pv,
     const int32_t* __restrict__ row_key, LoraOperands lo, int proj, float* __restrict__ Trows, int n_shrink,
-    int pipe) {
+    int pipe, const int32_t* __restrict__ ids = nullptr, int32_t* __restrict__ seg_ws = nullptr,
+    int seg_passes = 0) {
   static_assert(!(PART && LORA), "the low-rank epilogue needs the whole K range");
   static_assert(!CO || (KD == 64 && TM == 128 && TN == 128), "co-resident form: 128x128 tiles, 64-deep stages");
+  static_assert(!IDS || CO, "the id-based form is the co-resident one");
   constexpr int MI = TM / 64, NJ = TN / 64;
   const int tid = threadIdx.x, lane = tid & 63;
   if constexpr (CO) {
     if ((int)blockIdx.x < n_shrink) {
-      if (blockIdx.y == 0)
-        for (int k = blockIdx.x; k < M; k += n_shrink)
-          shrink_row_body<true, kRingThreads / 64>(pv, proj, X, row_key, k, Trows, row_desc(Trows, M, pv.max_rank));
+      if (blockIdx.y == 0) {
+        if constexpr (IDS) {
+          if (blockIdx.x == 0) {
+            // up to 1024 rows: 2 * 1088 + 4 * kRadix words of scratch
+            static_assert((2 * 1088 + kRadix * (kRingThreads / 64)) * 4 <= sizeof(m64_a0), "segment scratch");
+            static_assert(kMaxWaves + 3 <= sizeof(m64_a1) / 4, "segment scratch");
+            const int cap = ((M + 1) + 63) & ~63;
+            seg_build_block<kRingThreads>(ids, M, pv.rank, pv.max_adapters, seg_passes, cap, seg_ws,
+                                          reinterpret_cast<uint32_t*>(m64_a0), reinterpret_cast<int*>(m64_a1),
+                                          reinterpret_cast<int*>(m64_a1) + kMaxWaves);
+          } else {
+            for (int k = blockIdx.x - 1; k < M; k += n_shrink - 1)
+              shrink_row_body_ids<true, kRingThreads / 64>(pv, proj, X, ids, k, Trows,
+                                                           row_desc(Trows, M, pv.max_rank));
+          }
+        } else {
+          for (int k = blockIdx.x; k < M; k += n_shrink)
+            shrink_row_body<true, kRingThreads / 64>(pv, proj, X, row_key, k, Trows, row_desc(Trows, M, pv.max_rank));
+        }
+      }
       return;
     }
   }
@@ -1322,6 +1360,18 @@ __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(2,
     const int32_t* __restrict__ row_key, int proj, float* __restrict__ Trows, int n_shrink) {
   gemm_ring_body<128, 128, 64, true, false, true>(X, W, Y, part, M, K, N, tiles_n, n_tiles, per_xcd, kt_per, pv,
                                                   row_key, LoraOperands{}, proj, Trows, n_shrink, 1);
+}
+
+// the same, with the row keys from the adapter ids and the segment build in
+// workgroup (0, 0)
+__global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_ring_co_ids(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y,
+    float* __restrict__ part, int M, int K, int N, int tiles_n, int n_tiles, int per_xcd, int kt_per, PoolView pv,
+    int proj, float* __restrict__ Trows, int n_shrink, const int32_t* __restrict__ ids, int32_t* __restrict__ seg_ws,
+    int seg_passes) {
+  gemm_ring_body<128, 128, 64, true, false, true, true>(X, W, Y, part, M, K, N, tiles_n, n_tiles, per_xcd, kt_per,
+                                                        pv, nullptr, LoraOperands{}, proj, Trows, n_shrink, 1, ids,
+                                                        seg_ws, seg_passes);
 }
 
 // MLORA_DECODE_SPLITK=0 keeps decode batches on the one-pass skinny kernel (A/B timing)
@@ -1817,12 +1867,23 @@ bool mid_ring_ok(int M, int K) { return K % (GBK * kRingStages) == 0 && (long)M 
 // after their tiles
 hipError_t launch_mid_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N, const PoolView& pv,
                            int proj, const int32_t* row_key, float* T, float* part, bool shrink, hipStream_t st,
-                           bool lora = true) {
+                           bool lora = true, const int32_t* ids = nullptr, int32_t* seg_ws = nullptr) {
   const int S = mid_split(M, N, K);
   const int tiles_n = (N + 127) / 128, n_tiles = ((M + 127) / 128) * tiles_n;
   const int per_xcd = (n_tiles + 7) / 8;
   const int ns = shrink ? 1 : 0;  // the tile workgroups compute the per-row shrink after their tiles
-  if (ring64_enabled() && mid_co_enabled()) {
+  if (ids != nullptr) {
+    // the segment build takes the first of the co-resident form's shrink
+    // workgroups (at least 72 of them above 64 rows)
+    if (!(ring64_enabled() && mid_co_enabled() && shrink && lora && M > 64 && M <= 1024)) return hipErrorNotSupported;
+    // one more than the rows (the segment build's), up to 264: no shrink
+    // workgroup takes a second row where the plain form gives each its own
+    const int nsw = min((M + 1 + 7) / 8 * 8, 264);
+    const int passes = M <= kRingThreads ? 0 : ((pv.max_adapters + 1 < 256) ? 1 : 2);
+    MLORA_LAUNCH("gemm_mid+seg+shrink_rows", gemm_ring_co_ids, dim3(nsw + per_xcd * 8, S), dim3(kRingThreads), 0,
+                 st, X, W, Y, part, M, K, N, tiles_n, n_tiles, per_xcd, K / GBK64 / S, pv, proj, T, nsw, ids, seg_ws,
+                 passes);
+  } else if (ring64_enabled() && mid_co_enabled()) {
     // shrink workgroups ahead of the tiles: one per row up to one per CU
     // (each then loops over rows, so the tiles still find a free slot on
     // every CU), a multiple of 8 so the tile workgroups keep their XCD mapping
@@ -1906,14 +1967,19 @@ hipError_t launch_gemm_lora(const PoolView& pv, int proj, const uint16_t* X, con
 hipError_t launch_forward_rows(const PoolView& pv, int proj, const uint16_t* X, const uint16_t* W,
                                const int32_t* ids, int32_t* ws, float* T, float* part, uint16_t* Y, int M,
                                hipStream_t stream) {
-  if (M <= 0 || M > 64) return hipErrorNotSupported;
+  if (M <= 0 || M > 1024) return hipErrorNotSupported;
   const int K = pv.din, N = pv.dout;
   const uintptr_t al = reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(W) |
                        reinterpret_cast<uintptr_t>(pv.up) | reinterpret_cast<uintptr_t>(Y) |
                        reinterpret_cast<uintptr_t>(pv.down);
   const bool vec = (K % 8 == 0) && (N % 8 == 0) && (al % 16 == 0);
-  if (!decode_splitk_ok(M, K, N, vec) || !decode_splitk_enabled()) return hipErrorNotSupported;
   const int32_t* row_key = ws + MLORA_SEG_ROWKEY(M);
+  if (M > 64) {
+    if (vec && mid_ring_ok(M, K) && (long)N * K * 2 < (1L << 31) && mid_enabled())
+      return launch_mid_lora(X, W, Y, M, K, N, pv, proj, row_key, T, part, true, stream, true, ids, ws);
+    return hipErrorNotSupported;
+  }
+  if (!decode_splitk_ok(M, K, N, vec) || !decode_splitk_enabled()) return hipErrorNotSupported;
   if (M <= 16) return launch_decode<1>(X, W, Y, M, K, N, pv, proj, row_key, T, part, true, stream, true, ids, ws);
   if (M <= 32) return launch_decode<2>(X, W, Y, M, K, N, pv, proj, row_key, T, part, true, stream, true, ids, ws);
   if (M <= 48) return launch_decode<3>(X, W, Y, M, K, N, pv, proj, row_key, T, part, true, stream, true, ids, ws);

@@ -1,9 +1,9 @@
 """mlora_forward (segment build and the layer for one projection in one call)
 through the C ABI: its Y and segment workspace against mlora_build_segments
 followed by mlora_apply (bit for bit: the same kernels), and its Y against
-the CPU oracle (M031 card, sections 02-03), on decode shapes where the
-segment build rides in the GEMM launch and on shapes that take the two
-calls one after the other."""
+the CPU oracle (M031 card, sections 02-03), on decode and medium shapes
+where the segment build rides in the GEMM launch and on shapes that take
+the two calls one after the other."""
 import numpy as np
 import pytest
 
@@ -60,8 +60,15 @@ CASES = [
     (3, 32, 4096, 4096, {0: 16, 1: 16, 2: 16}, False),
     (4, 48, 2048, 4104, {0: 8, 3: 1, 5: 33}, True),
     (5, 64, 4096, 4096, {i: 16 for i in range(40)}, True),
-    # two calls: above 64 rows, din not a multiple of 2048, unaligned dout
+    # medium batches (65 .. 1024 rows): the segment build in the first
+    # workgroup of the ring GEMM launch (direct ranking up to 256 rows, then
+    # one radix pass, or two with more than 254 ids)
     (6, 65, 4096, 4096, {0: 16, 1: 3}, True),
+    (9, 256, 4096, 1000, {0: 16, 1: 7, 2: 64}, True),
+    (10, 300, 4096, 4096, {i: 16 for i in range(256)}, True),
+    (11, 700, 2048, 512, {i: (16 if i % 3 else 64) for i in range(40)}, True),
+    (12, 1024, 4096, 4096, {0: 16, 1: 8}, True),
+    # two calls: din not a multiple of 128 or 2048, unaligned dout
     (7, 20, 1000, 520, {0: 16, 1: 5}, True),
     (8, 9, 2048, 12, {0: 4}, False),
 ]
@@ -111,8 +118,9 @@ def test_forward_then_apply_on_other_projections(M):
 
 
 def test_forward_launches(M):
-    """Decode shape: two launches (GEMM with the segment build and the
-    shrink, then the finish pass); 65 rows: the segment builder first."""
+    """Decode and medium shapes: two launches (GEMM with the segment build
+    and the shrink, then the finish pass); din not a multiple of 128: the
+    segment builder first."""
     torch = torch_cuda()
     w = synth.decode_3_adapters()
     pool = make_pool(M, w)
@@ -128,6 +136,11 @@ def test_forward_launches(M):
     pool2 = make_pool(M, w2)
     M.timing_arm(8)
     M.forward(pool2, 0, to_dev_bf16(w2.x_bits()), to_dev_bf16(w2.w0_bits()), ids_dev(w2.row_adapter))
+    assert [m[0] for m in M.timing_read()] == ["gemm_mid+seg+shrink_rows", "finish_part"]
+    w3 = _workload(141, 100, 1000, 512, {0: 16})
+    pool3 = make_pool(M, w3)
+    M.timing_arm(8)
+    M.forward(pool3, 0, to_dev_bf16(w3.x_bits()), to_dev_bf16(w3.w0_bits()), ids_dev(w3.row_adapter))
     names = [m[0] for m in M.timing_read()]
     assert names[0] == "seg_build" and len(names) >= 2, names
 
