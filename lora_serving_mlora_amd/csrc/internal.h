@@ -81,11 +81,11 @@ hipError_t launch_base_gemm(const uint16_t* X, const uint16_t* W, uint16_t* Y, i
 // decode form applies.
 hipError_t launch_gemm_lora(const PoolView& pv, int proj, const uint16_t* X, const uint16_t* W, const int32_t* ws,
                             float* T, float* part, uint16_t* Y, int M, bool shrink, hipStream_t stream);
-// The per-row plan of a decode batch (M <= 64) with its segment build in the
-// same GEMM launch: row keys come from the adapter ids `ids` and the
-// resident table, and one more workgroup writes the segment workspace `ws`.
-// hipErrorNotSupported (nothing launched) where the decode form does not
-// apply.
+// The per-row plan of a decode (M <= 64) or medium (M <= 1024) batch with
+// its segment build in the same GEMM launch: row keys come from the adapter
+// ids `ids` and the resident table, and one workgroup of the launch writes
+// the segment workspace `ws`.  hipErrorNotSupported (nothing launched) where
+// neither the split-K decode form nor the co-resident medium form applies.
 hipError_t launch_forward_rows(const PoolView& pv, int proj, const uint16_t* X, const uint16_t* W,
                                const int32_t* ids, int32_t* ws, float* T, float* part, uint16_t* Y, int M,
                                hipStream_t stream);
