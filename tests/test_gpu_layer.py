@@ -349,6 +349,10 @@ def test_zero_rows_is_a_noop(M):
     seg = M.build_segments(pool, torch.empty(0, dtype=torch.int32, device="cuda"))
     Y = M.apply(pool, 0, X, to_dev_bf16(w.w0_bits()), seg)
     assert Y.shape == (0, 64)
+    # the one-call form: the workspace header of an empty batch, no layer work
+    Y, seg = M.forward(pool, 0, X, to_dev_bf16(w.w0_bits()), torch.empty(0, dtype=torch.int32, device="cuda"))
+    h = M.segments_header(seg)
+    assert Y.shape == (0, 64) and h["n_rows"] == 0 and h["nseg"] == 0 and h["n_act"] == 0
 
 
 def test_one_row(M):
