@@ -303,6 +303,31 @@ def test_row_permutation_equivariance():
     assert np.array_equal(Yp, Y[p])
 
 
+def test_zero_padded_rank_changes_nothing():
+    """Padding an adapter to a larger rank with zero Down rows and zero Up
+    columns (the rank-padded baseline of the airsota card's trade-off (4) and
+    the wiblog article's naive shared batch) leaves every output row as it
+    was, in the one-call oracle and in its shrink/expand split; t of a padded
+    adapter is the unpadded t followed by zeros."""
+    ranks = {0: 3, 1: 7, 2: 1}
+    ids = synth.random_ids(47, 19, [0, 1, 2], p_none=0.2)
+    w = synth.custom("pad", 47, 24, 20, ids, ranks, max_adapters=3)
+    X, W0 = O.widen_bf16(w.x_bits()), O.widen_bf16(w.w0_bits())
+    ad = _adapters_f64(w)
+    R = 16
+    padded = {a: (s_, np.vstack([d, np.zeros((R - d.shape[0], d.shape[1]))]),
+                  np.hstack([u, np.zeros((u.shape[0], R - u.shape[1]))])) for a, (s_, d, u) in ad.items()}
+    Y = O.linear(X, W0, ids, ad, 3)
+    np.testing.assert_allclose(O.linear(X, W0, ids, padded, 3), Y, rtol=1e-13, atol=1e-15)
+    t, tp = O.shrink_rows(X, ids, ad, 3), O.shrink_rows(X, ids, padded, 3)
+    assert sorted(t) == sorted(tp)
+    for k in t:
+        r = ranks[int(ids[k])]
+        assert np.array_equal(tp[k][:r], t[k]) and not tp[k][r:].any()
+    base = X @ W0.T
+    np.testing.assert_allclose(O.expand_rows(base, tp, ids, padded, 3), Y, rtol=1e-13, atol=1e-15)
+
+
 def test_linearity_in_scale():
     ranks = {0: 4, 1: 2}
     ids = synth.random_ids(41, 17, [0, 1], p_none=0.2)
