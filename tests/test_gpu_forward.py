@@ -101,10 +101,11 @@ def test_forward_every_variant(M, variant):
     assert np.array_equal(_bits(Yf), _bits(Ya))
 
 
-def test_forward_then_apply_on_other_projections(M):
-    """The workspace forward builds serves apply on the batch's other
-    projections."""
-    w = _workload(130, 40, 4096, 264, {0: 5, 1: 12, 3: 2}, n_proj=3)
+@pytest.mark.parametrize("n", [40, 300])
+def test_forward_then_apply_on_other_projections(M, n):
+    """The workspace forward builds (in the decode or the medium GEMM launch)
+    serves apply on the batch's other projections."""
+    w = _workload(130 + n, n, 4096, 264, {0: 5, 1: 12, 3: 2}, n_proj=3)
     pool = make_pool(M, w)
     X = w.x_bits()
     Xd = to_dev_bf16(X)
