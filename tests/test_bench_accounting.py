@@ -1,5 +1,6 @@
-"""The bench's algorithmic work per launch (the numerator of every roofline
-fraction it reports), checked against a brute-force count on a tiny batch.
+"""Host logic of the bench: its algorithmic work per launch (the numerator
+of every roofline fraction it reports), checked against a brute-force count
+on a tiny batch, and its refusal of more than one GPU.
 
 The count enumerates the distinct elements each step must touch and the
 multiply-adds it must do, straight from the layer's definition: the base
@@ -93,3 +94,13 @@ def test_empty_branch_counts_nothing_low_rank():
     assert algo["fused"] == (0, 0)
     assert algo["shrink_rows"] == (0, 0)
     assert algo["finish_part"] == (2 * w.n * w.dout, 0)
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    """bench.py measures one GPU; asking for more exits with status 2 and says
+    why, before touching any device."""
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
