@@ -107,6 +107,9 @@ def algorithmic(w, chunks):
     finish = (2 * sum_r * dout + 4 * sum_nr + 2 * n * dout, 2 * sum_nr * dout)
     gemm_lora = (base[0] + 2 * sum_r * dout + 4 * sum_nr, base[1] + 2 * sum_nr * dout)
     seg = (4 * n + 4 * 4 * n, 0)   # ids in; perm, inv, row keys and segment tables out
+    # the shrink inside a GEMM launch works from the X rows that launch
+    # already reads for the base product: only the Down rows and T are extra
+    shrink_in_launch = (2 * sum_r * din + 4 * sum_nr, 2 * sum_nr * din)
     out = {
         "seg_build": seg,
         "shrink": (2 * sum_r * din + 2 * n_act * din + 4 * sum_nr * max(chunks, 1), 2 * sum_nr * din),
@@ -114,10 +117,12 @@ def algorithmic(w, chunks):
         "fused": (2 * sum_r * (din + dout) + 2 * n_act * din + 4 * n_act * dout, 2 * sum_nr * (din + dout)),
         "shrink_rows": shrink_rows,
         "gemm_decode": split_dense, "gemm_mid": split_dense,
-        "gemm_decode+shrink_rows": (split_dense[0] + shrink_rows[0], split_dense[1] + shrink_rows[1]),
-        "gemm_mid+shrink_rows": (split_dense[0] + shrink_rows[0], split_dense[1] + shrink_rows[1]),
-        "gemm_decode+seg+shrink_rows": (split_dense[0] + shrink_rows[0] + seg[0], split_dense[1] + shrink_rows[1]),
-        "gemm_mid+seg+shrink_rows": (split_dense[0] + shrink_rows[0] + seg[0], split_dense[1] + shrink_rows[1]),
+        "gemm_decode+shrink_rows": (split_dense[0] + shrink_in_launch[0], split_dense[1] + shrink_in_launch[1]),
+        "gemm_mid+shrink_rows": (split_dense[0] + shrink_in_launch[0], split_dense[1] + shrink_in_launch[1]),
+        "gemm_decode+seg+shrink_rows": (split_dense[0] + shrink_in_launch[0] + seg[0],
+                                        split_dense[1] + shrink_in_launch[1]),
+        "gemm_mid+seg+shrink_rows": (split_dense[0] + shrink_in_launch[0] + seg[0],
+                                     split_dense[1] + shrink_in_launch[1]),
         "finish_part": finish,
         "finish_base": (2 * n * dout, 0),   # the base GEMM's partials summed (scratch) into Y
         "gemm_skinny_lora": gemm_lora, "gemm_ksplit_lora": gemm_lora, "gemm_big_lora": gemm_lora,

@@ -169,6 +169,16 @@ mlora_status mlora_pool_unload(mlora_pool* pool, int32_t adapter_id, void* strea
  * Errors: EINVAL (id range), ENOENT (not resident). */
 mlora_status mlora_pool_ready(mlora_pool* pool, int32_t adapter_id, void* stream);
 
+/* Testing aid for the load's error path: the next mlora_pool_load on this
+ * pool fails with MLORA_EHIP at `step` once its copies are staged (1:
+ * before its last staging flush, whose copies carry the metadata; 2: after
+ * the metadata copies, before the ready event is recorded); 0 turns it off.
+ * A load that fails there, as after any failure once its copies may have
+ * been issued, leaves the adapter not resident on the host and on the
+ * device (its rank is set back to 0 on the stream) and parks its pages
+ * behind an event on the stream, as an unload does.  Errors: EINVAL. */
+mlora_status mlora_pool_fail_next_load(mlora_pool* pool, int32_t step);
+
 /* Host-side view of the pool (no device access). */
 mlora_status mlora_pool_query(const mlora_pool* pool, int32_t adapter_id, int32_t* rank, float* scale);
 mlora_status mlora_pool_free_pages(const mlora_pool* pool, int64_t* free_down, int64_t* free_up,

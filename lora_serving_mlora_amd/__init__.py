@@ -36,6 +36,7 @@ MAX_ROWS = 16384
 MAX_RANK = 128
 SEG = dict(nseg=0, n_act=1, n_none=2, n_bad=3, status=4, n_items=5, n_rows=6, max_adapters=7, n_tiles=8)
 SEG_HEADER = 16
+SEG_BAD_ID, SEG_NOT_RESIDENT = 1, 2  # bits of the status word
 
 _c_void_p, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 _pi32, _pi64, _pf32 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_float)
@@ -60,6 +61,7 @@ EXPORTS = {
     "mlora_pool_ready": (ctypes.c_int, [_c_void_p, _i32, _c_void_p]),
     "mlora_pool_query": (ctypes.c_int, [_c_void_p, _i32, _pi32, _pf32]),
     "mlora_pool_free_pages": (ctypes.c_int, [_c_void_p, _pi64, _pi64, _pi32]),
+    "mlora_pool_fail_next_load": (ctypes.c_int, [_c_void_p, _i32]),
     "mlora_segments_bytes": (_sz, [_i32]),
     "mlora_build_segments": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p]),
     "mlora_segments_header": (ctypes.c_int, [_c_void_p, _pi32, _c_void_p]),
@@ -213,6 +215,11 @@ class Pool:
         _check(lib().mlora_pool_free_pages(self.handle, ctypes.byref(fd), ctypes.byref(fu), ctypes.byref(nr)),
                "mlora_pool_free_pages")
         return fd.value, fu.value, nr.value
+
+    def fail_next_load(self, step: int) -> None:
+        """Testing aid: the next load on this pool fails at `step` (1: before
+        its last staging flush, 2: after its metadata copies; 0: off)."""
+        _check(lib().mlora_pool_fail_next_load(self.handle, step), "mlora_pool_fail_next_load")
 
     def close(self) -> None:
         if getattr(self, "_h", None) is not None:

@@ -184,6 +184,9 @@ struct mlora_pool {
   std::vector<hipEvent_t> ready;
   std::vector<hipEvent_t> spare;  // recorded events no longer referenced
   std::mutex mu;
+  // testing aid (mlora_pool_fail_next_load): the next load fails at this
+  // step once its copies are staged (0 = off)
+  int fail_step = 0;
 
   PoolView view() const {
     PoolView v;
@@ -478,6 +481,32 @@ mlora_status mlora_pool_load(mlora_pool* p, int32_t id, int32_t rank, float scal
     p->ufree.release(ur);
     return s;
   };
+  // the ready event is taken before any device work, so nothing after the
+  // metadata copies can fail for want of an event
+  if (!p->ready[id] && (st = take_event(p, &p->ready[id])) != MLORA_OK) return undo(st);
+  const int fail_step = p->fail_step;
+  p->fail_step = 0;
+  char* meta = static_cast<char*>(d.meta);
+  // A failure once copies may have been issued (page rows by a staging
+  // flush; the page tables, scale and rank by the last one): the device
+  // may already hold this adapter's rank, and copies into its pages may
+  // still be in flight.  So the rank is set back to 0 on the stream, and
+  // the pages are parked behind an event recorded after it, as an unload
+  // parks them: a later load reuses them only once that stream has passed
+  // this point.  Without an event the host waits for the stream instead.
+  auto abort_load = [&](mlora_status s0) {
+    (void)hipMemsetAsync(meta + p->ml.rank + (size_t)id * 4, 0, 4, s);
+    hipEvent_t e = nullptr;
+    if (take_event(p, &e) == MLORA_OK && hipEventRecord(e, s) == hipSuccess) {
+      p->parked.push_back({dr, ur, npages, e});
+    } else {
+      if (e) p->spare.push_back(e);
+      (void)hipStreamSynchronize(s);
+      p->dfree.release(dr);
+      p->ufree.release(ur);
+    }
+    return s0;
+  };
 
   Stager sg(p, s);
   const size_t drow = (size_t)d.din * 2, urow = (size_t)d.dout * 2;
@@ -529,7 +558,7 @@ mlora_status mlora_pool_load(mlora_pool* p, int32_t id, int32_t rank, float scal
   for (int64_t i = 0; i < npages; ++i) {
     const int64_t pg = page_at(dr, i);
     char* h = nullptr;
-    if ((st = sg.reserve(dbase + pg * drow, drow, &h)) != MLORA_OK) return undo(st);
+    if ((st = sg.reserve(dbase + pg * drow, drow, &h)) != MLORA_OK) return abort_load(st);
     fills.push_back({h, i, false});
     dpt[(size_t)(i / rank) * d.max_rank + (i % rank)] = (int32_t)pg;
   }
@@ -537,32 +566,42 @@ mlora_status mlora_pool_load(mlora_pool* p, int32_t id, int32_t rank, float scal
   for (int64_t i = 0; i < npages; ++i) {
     const int64_t pg = page_at(ur, i);
     char* h = nullptr;
-    if ((st = sg.reserve(ubase + pg * urow, urow, &h)) != MLORA_OK) return undo(st);
+    if ((st = sg.reserve(ubase + pg * urow, urow, &h)) != MLORA_OK) return abort_load(st);
     fills.push_back({h, i, true});
     upt[(size_t)(i / rank) * d.max_rank + (i % rank)] = (int32_t)pg;
   }
   // metadata: page tables, scale, then rank (all ordered on the stream)
-  char* meta = static_cast<char*>(d.meta);
   const size_t ptb = dpt.size() * sizeof(int32_t);
   const size_t pt_off = (size_t)id * d.n_proj * d.max_rank * sizeof(int32_t);
   char* h = nullptr;
-  if ((st = sg.reserve(meta + p->ml.dpt + pt_off, ptb, &h)) != MLORA_OK) return undo(st);
+  if ((st = sg.reserve(meta + p->ml.dpt + pt_off, ptb, &h)) != MLORA_OK) return abort_load(st);
   std::memcpy(h, dpt.data(), ptb);
-  if ((st = sg.reserve(meta + p->ml.upt + pt_off, ptb, &h)) != MLORA_OK) return undo(st);
+  if ((st = sg.reserve(meta + p->ml.upt + pt_off, ptb, &h)) != MLORA_OK) return abort_load(st);
   std::memcpy(h, upt.data(), ptb);
-  if ((st = sg.reserve(meta + p->ml.scale + (size_t)id * 4, 4, &h)) != MLORA_OK) return undo(st);
+  if ((st = sg.reserve(meta + p->ml.scale + (size_t)id * 4, 4, &h)) != MLORA_OK) return abort_load(st);
   std::memcpy(h, &scale, 4);
-  if ((st = sg.reserve(meta + p->ml.rank + (size_t)id * 4, 4, &h)) != MLORA_OK) return undo(st);
+  if ((st = sg.reserve(meta + p->ml.rank + (size_t)id * 4, 4, &h)) != MLORA_OK) return abort_load(st);
   std::memcpy(h, &rank, 4);
-  if ((st = sg.flush()) != MLORA_OK) return undo(st);
-  if (!p->ready[id] && (st = take_event(p, &p->ready[id])) != MLORA_OK) return undo(st);
-  if ((st = hip_check(hipEventRecord(p->ready[id], s), "hipEventRecord(ready)")) != MLORA_OK) return undo(st);
+  if (fail_step == 1) return abort_load(fail(MLORA_EHIP, "injected failure before the last staging flush"));
+  if ((st = sg.flush()) != MLORA_OK) return abort_load(st);
+  if (fail_step == 2) return abort_load(fail(MLORA_EHIP, "injected failure after the metadata copies"));
+  if ((st = hip_check(hipEventRecord(p->ready[id], s), "hipEventRecord(ready)")) != MLORA_OK) return abort_load(st);
 
   p->rank[id] = rank;
   p->scale[id] = scale;
   p->druns[id] = dr;
   p->uruns[id] = ur;
   ++p->n_resident;
+  return MLORA_OK;
+}
+
+mlora_status mlora_pool_fail_next_load(mlora_pool* p, int32_t step) {
+  g_err.clear();
+  mlora_status st = check_pool(p);
+  if (st != MLORA_OK) return st;
+  if (step < 0 || step > 2) return fail(MLORA_EINVAL, "failure step %d outside [0, 2]", step);
+  std::lock_guard<std::mutex> lock(p->mu);
+  p->fail_step = step;
   return MLORA_OK;
 }
 

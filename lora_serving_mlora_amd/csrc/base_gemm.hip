@@ -498,37 +498,9 @@ __global__ __launch_bounds__(kTiledThreads) void gemm_tiled(const uint16_t* __re
 // multiple of 32 * NS (per split) and 16-byte aligned rows; rows past M or
 // N read zeros (buffer bounds).
 // ---------------------------------------------------------------------------
-constexpr int GBK = 32, kRingStages = 4;  // 32-deep K tiles, 4 stages (32 KiB / 16 KiB for 256x256 / 128x128)
+constexpr int kRingKAlign = 128;  // K (per split) must be a multiple of two 64-deep stages
 constexpr int kRingThreads = 256;
 constexpr int kGroupM = 4;  // row bands per tile group (large products)
-
-// one array per (operand, stage, tile size): the main loop takes them as
-// distinct restrict pointers, so the compiler knows a DMA into one stage
-// does not write the stage being read
-__shared__ __attribute__((aligned(16))) uint16_t big_a0[256 * GBK];
-__shared__ __attribute__((aligned(16))) uint16_t big_a1[256 * GBK];
-__shared__ __attribute__((aligned(16))) uint16_t big_a2[256 * GBK];
-__shared__ __attribute__((aligned(16))) uint16_t big_a3[256 * GBK];
-__shared__ __attribute__((aligned(16))) uint16_t big_b0[256 * GBK];
-__shared__ __attribute__((aligned(16))) uint16_t big_b1[256 * GBK];
-__shared__ __attribute__((aligned(16))) uint16_t big_b2[256 * GBK];
-__shared__ __attribute__((aligned(16))) uint16_t big_b3[256 * GBK];
-__shared__ __attribute__((aligned(16))) uint16_t mid_a0[128 * GBK];
-__shared__ __attribute__((aligned(16))) uint16_t mid_a1[128 * GBK];
-__shared__ __attribute__((aligned(16))) uint16_t mid_a2[128 * GBK];
-__shared__ __attribute__((aligned(16))) uint16_t mid_a3[128 * GBK];
-__shared__ __attribute__((aligned(16))) uint16_t mid_b0[128 * GBK];
-__shared__ __attribute__((aligned(16))) uint16_t mid_b1[128 * GBK];
-__shared__ __attribute__((aligned(16))) uint16_t mid_b2[128 * GBK];
-__shared__ __attribute__((aligned(16))) uint16_t mid_b3[128 * GBK];
-
-// LDS element offset of 16-byte chunk `chunk` (0..3) of tile row `row`:
-// 64-byte rows, chunks XOR-swizzled by (row >> 2) & 3.  The LDS serves a
-// 128-bit read 16 lanes (256 bytes) per cycle; the 16 lanes of a fragment
-// read are 16 consecutive rows at one logical chunk, which this swizzle
-// spreads over all 16 slots of a 256-byte window (with (row >> 1) & 3 rows
-// r and r + 8 collided: 2-way conflicts, 4 extra cycles per read).
-__device__ __forceinline__ int swz4(int row, int chunk) { return row * GBK + ((chunk ^ ((row >> 2) & 3)) << 3); }
 
 // Workgroup barrier without the release/acquire fences of __syncthreads():
 // those make every wave wait for all of its outstanding DMAs (vmcnt(0)),
@@ -550,180 +522,6 @@ struct RingCtx {
   int voff, voff64, row_bytes, wave, wm, wn, fr, fk;
 };
 
-// DMA of K tile kt (32 deep) into (da, db): instruction j of this wave
-// covers tile rows 16i..16i+15, i = wave + 4j; lane L fills row L >> 2,
-// physical chunk L & 3
-template <int TM, int TN>
-__device__ __forceinline__ void ring_issue(const RingCtx& c, uint16_t* __restrict__ da, uint16_t* __restrict__ db,
-                                           int kt) {
-#pragma unroll
-  for (int j = 0; j < TM / 64; ++j) {
-    const int i = c.wave + 4 * j;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsa, da + i * 16 * GBK, 16, c.voff,
-                                             i * 16 * c.row_bytes + kt * GBK * 2, 0, 0);
-  }
-#pragma unroll
-  for (int j = 0; j < TN / 64; ++j) {
-    const int i = c.wave + 4 * j;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsb, db + i * 16 * GBK, 16, c.voff,
-                                             i * 16 * c.row_bytes + kt * GBK * 2, 0, 0);
-  }
-}
-
-// Consumes K tile kt from stage (ra, rb) while tile kt+NS-1 is sent to
-// stage (na, nb), then waits for tile kt+1 and syncs the workgroup.  Past
-// the end of the K range the DMA re-fetches its last tile into a stage
-// nobody reads again, so every step issues the same number of DMAs and the
-// wait count is constant.
-template <int TM, int TN, int NS>
-__device__ __forceinline__ void ring_step(const RingCtx& c, const uint16_t* __restrict__ ra,
-                                          const uint16_t* __restrict__ rb, uint16_t* __restrict__ na,
-                                          uint16_t* __restrict__ nb, int kt, int kend,
-                                          floatx16 (&acc)[TM / 64][TN / 64]) {
-  constexpr int MI = TM / 64, NJ = TN / 64;
-  uint4 fa0[MI], fb0[NJ], fa1[MI], fb1[NJ];
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-    fa0[i] = *reinterpret_cast<const uint4*>(ra + swz4(c.wm * (TM / 2) + i * 32 + c.fr, c.fk));
-#pragma unroll
-  for (int j = 0; j < NJ; ++j)
-    fb0[j] = *reinterpret_cast<const uint4*>(rb + swz4(c.wn * (TN / 2) + j * 32 + c.fr, c.fk));
-  ring_issue<TM, TN>(c, na, nb, min(kt + NS - 1, kend - 1));
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-    fa1[i] = *reinterpret_cast<const uint4*>(ra + swz4(c.wm * (TM / 2) + i * 32 + c.fr, 2 + c.fk));
-#pragma unroll
-  for (int j = 0; j < NJ; ++j)
-    fb1[j] = *reinterpret_cast<const uint4*>(rb + swz4(c.wn * (TN / 2) + j * 32 + c.fr, 2 + c.fk));
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa0[i]), as_bf16x8(fb0[j]), acc[i][j], 0, 0, 0);
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa1[i]), as_bf16x8(fb1[j]), acc[i][j], 0, 0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  // tile kt+1 has landed once only the DMAs issued after it (tiles kt+2 ..
-  // kt+NS-1) may still be in flight
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * (MI + NJ)));
-  ring_barrier();
-}
-
-// K tiles [kt0, kend) in groups of 4 ((kend - kt0) % 4 == 0), one stage each
-template <int TM, int TN>
-__device__ __forceinline__ void ring_mainloop4(const RingCtx& c, uint16_t* __restrict__ a0, uint16_t* __restrict__ a1,
-                                               uint16_t* __restrict__ a2, uint16_t* __restrict__ a3,
-                                               uint16_t* __restrict__ b0, uint16_t* __restrict__ b1,
-                                               uint16_t* __restrict__ b2, uint16_t* __restrict__ b3, int kt0,
-                                               int kend, floatx16 (&acc)[TM / 64][TN / 64]) {
-  ring_issue<TM, TN>(c, a0, b0, kt0);
-  ring_issue<TM, TN>(c, a1, b1, kt0 + 1);
-  ring_issue<TM, TN>(c, a2, b2, kt0 + 2);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (TM / 64 + TN / 64)));  // tile kt0 has landed
-  ring_barrier();
-  for (int kt = kt0; kt < kend; kt += 4) {
-    ring_step<TM, TN, 4>(c, a0, b0, a3, b3, kt, kend, acc);
-    ring_step<TM, TN, 4>(c, a1, b1, a0, b0, kt + 1, kend, acc);
-    ring_step<TM, TN, 4>(c, a2, b2, a1, b1, kt + 2, kend, acc);
-    ring_step<TM, TN, 4>(c, a3, b3, a2, b2, kt + 3, kend, acc);
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // drain the trailing re-fetches before the workgroup ends
-}
-
-// Fragments of one 32-deep stage, per wave: A rows (MI blocks of 32) and B
-// columns (NJ blocks of 32), for the two 16-deep halves of the stage.
-template <int TM, int TN>
-struct RingFrags {
-  uint4 a[2][TM / 64], b[2][TN / 64];
-};
-
-template <int TM, int TN>
-__device__ __forceinline__ void ring_read(const RingCtx& c, const uint16_t* __restrict__ ra,
-                                          const uint16_t* __restrict__ rb, RingFrags<TM, TN>& f) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int i = 0; i < TM / 64; ++i)
-      f.a[h][i] = *reinterpret_cast<const uint4*>(ra + swz4(c.wm * (TM / 2) + i * 32 + c.fr, 2 * h + c.fk));
-#pragma unroll
-    for (int j = 0; j < TN / 64; ++j)
-      f.b[h][j] = *reinterpret_cast<const uint4*>(rb + swz4(c.wn * (TN / 2) + j * 32 + c.fr, 2 * h + c.fk));
-  }
-}
-
-// Pipelined step k: the MFMAs of stage k run on fragments read during the
-// previous step (cf) while this step reads stage k+1 (ra, rb) into nf and
-// sends the DMA of stage k+4 into the buffer stage k came from (da, db: its
-// data is already in registers).  Then it waits until stage k+2 has landed
-// (stages k+3 and k+4 may still be in flight) and until its own reads of
-// stage k+1 are done (that buffer is overwritten next step), and syncs the
-// workgroup.  The reads are spread over the first MFMAs, so a wave never
-// stalls on a full LDS queue while it could issue matrix work, and the
-// matrix pipe never waits for LDS at the start of a step.
-template <int TM, int TN>
-__device__ __forceinline__ void ring_step_p(const RingCtx& c, const uint16_t* __restrict__ ra,
-                                            const uint16_t* __restrict__ rb, uint16_t* __restrict__ da,
-                                            uint16_t* __restrict__ db, int kt, int kend, const RingFrags<TM, TN>& cf,
-                                            RingFrags<TM, TN>& nf, floatx16 (&acc)[TM / 64][TN / 64]) {
-  constexpr int MI = TM / 64, NJ = TN / 64;
-  constexpr int kReads = 2 * (MI + NJ), kMfma = 2 * MI * NJ, kPer = kMfma / kReads;
-  ring_issue<TM, TN>(c, da, db, min(kt + 4, kend - 1));
-  ring_read<TM, TN>(c, ra, rb, nf);
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cf.a[h][i]), as_bf16x8(cf.b[h][j]), acc[i][j], 0,
-                                                            0, 0);
-  // one DMA per group, spread over the first groups: the memory pipe's
-  // queue drains between issues, so a full queue never holds the wave (and
-  // its matrix work) at an issue
-#pragma unroll
-  for (int r = 0; r < kReads; ++r) {
-    if (r < MI + NJ) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one DMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                   // one fragment read
-    __builtin_amdgcn_sched_group_barrier(0x008, kPer, 0);                // kPer MFMAs
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * (MI + NJ)) & ~(15 << 8));  // + lgkmcnt(0)
-  ring_barrier();
-}
-
-// K tiles [kt0, kend) in groups of 4 ((kend - kt0) % 4 == 0), pipelined
-// form: four stages in flight at the start, fragments double-buffered in
-// registers
-template <int TM, int TN>
-__device__ __forceinline__ void ring_mainloop_p(const RingCtx& c, uint16_t* __restrict__ a0, uint16_t* __restrict__ a1,
-                                                uint16_t* __restrict__ a2, uint16_t* __restrict__ a3,
-                                                uint16_t* __restrict__ b0, uint16_t* __restrict__ b1,
-                                                uint16_t* __restrict__ b2, uint16_t* __restrict__ b3, int kt0,
-                                                int kend, floatx16 (&acc)[TM / 64][TN / 64]) {
-  constexpr int n = TM / 64 + TN / 64;  // DMA instructions per stage and wave
-  ring_issue<TM, TN>(c, a0, b0, kt0);
-  ring_issue<TM, TN>(c, a1, b1, min(kt0 + 1, kend - 1));
-  ring_issue<TM, TN>(c, a2, b2, min(kt0 + 2, kend - 1));
-  ring_issue<TM, TN>(c, a3, b3, min(kt0 + 3, kend - 1));
-  RingFrags<TM, TN> f0, f1;
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * n));  // stage kt0 has landed
-  ring_barrier();
-  ring_read<TM, TN>(c, a0, b0, f0);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * n) & ~(15 << 8));  // stage kt0+1 landed, own reads done
-  ring_barrier();
-  for (int kt = kt0; kt < kend; kt += 4) {
-    ring_step_p<TM, TN>(c, a1, b1, a0, b0, kt, kend, f0, f1, acc);
-    ring_step_p<TM, TN>(c, a2, b2, a1, b1, kt + 1, kend, f1, f0, acc);
-    ring_step_p<TM, TN>(c, a3, b3, a2, b2, kt + 2, kend, f0, f1, acc);
-    ring_step_p<TM, TN>(c, a0, b0, a3, b3, kt + 3, kend, f1, f0, acc);
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // drain the trailing re-fetches before the workgroup ends
-}
-
 // ---------------------------------------------------------------------------
 // ring64: the same pipelined ring with 64-deep stages.  A DMA instruction then
 // covers 8 tile rows x 128 contiguous bytes (8 whole cache lines) instead of
@@ -736,12 +534,6 @@ __device__ __forceinline__ void ring_mainloop_p(const RingCtx& c, uint16_t* __re
 // tiles with 4 stages (32 KiB each).
 // ---------------------------------------------------------------------------
 constexpr int GBK64 = 64;
-__shared__ __attribute__((aligned(16))) uint16_t l64_a0[256 * GBK64];
-__shared__ __attribute__((aligned(16))) uint16_t l64_a1[256 * GBK64];
-__shared__ __attribute__((aligned(16))) uint16_t l64_a2[256 * GBK64];
-__shared__ __attribute__((aligned(16))) uint16_t l64_b0[128 * GBK64];
-__shared__ __attribute__((aligned(16))) uint16_t l64_b1[128 * GBK64];
-__shared__ __attribute__((aligned(16))) uint16_t l64_b2[128 * GBK64];
 __shared__ __attribute__((aligned(16))) uint16_t m64_a0[128 * GBK64];
 __shared__ __attribute__((aligned(16))) uint16_t m64_a1[128 * GBK64];
 __shared__ __attribute__((aligned(16))) uint16_t m64_a2[128 * GBK64];
@@ -829,44 +621,6 @@ __device__ __forceinline__ void ring64_step(const RingCtx& c, const uint16_t* __
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * kDma) & ~(15 << 8));  // + lgkmcnt(0)
   ring_barrier();
-}
-
-// K tiles [kt0, kend) through 3 stages (any count >= 1): six steps per
-// round (three buffers x two fragment sets), later steps of the last round
-// skipped by uniform branches
-template <int TM, int TN>
-__device__ __forceinline__ void ring64_loop3(const RingCtx& c, uint16_t* __restrict__ a0, uint16_t* __restrict__ a1,
-                                             uint16_t* __restrict__ a2, uint16_t* __restrict__ b0,
-                                             uint16_t* __restrict__ b1, uint16_t* __restrict__ b2, int kt0, int kend,
-                                             floatx16 (&acc)[TM / 64][TN / 64]) {
-  constexpr int n = (TM + TN) / 32;
-  ring64_issue<TM, TN>(c, a0, b0, kt0);
-  ring64_issue<TM, TN>(c, a1, b1, min(kt0 + 1, kend - 1));
-  ring64_issue<TM, TN>(c, a2, b2, min(kt0 + 2, kend - 1));
-  Ring64Frags<TM, TN> f0, f1;
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * n));  // stage kt0 has landed
-  ring_barrier();
-  ring64_read<TM, TN>(c, a0, b0, f0);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(n) & ~(15 << 8));  // stage kt0+1 landed, own reads done
-  ring_barrier();
-  // (nested, so that every path into a step passes the previous step's wait)
-  for (int kt = kt0; kt < kend; kt += 6) {
-    ring64_step<TM, TN, 3>(c, a1, b1, a0, b0, kt, kend, f0, f1, acc);
-    if (kt + 1 < kend) {
-      ring64_step<TM, TN, 3>(c, a2, b2, a1, b1, kt + 1, kend, f1, f0, acc);
-      if (kt + 2 < kend) {
-        ring64_step<TM, TN, 3>(c, a0, b0, a2, b2, kt + 2, kend, f0, f1, acc);
-        if (kt + 3 < kend) {
-          ring64_step<TM, TN, 3>(c, a1, b1, a0, b0, kt + 3, kend, f1, f0, acc);
-          if (kt + 4 < kend) {
-            ring64_step<TM, TN, 3>(c, a2, b2, a1, b1, kt + 4, kend, f0, f1, acc);
-            if (kt + 5 < kend) ring64_step<TM, TN, 3>(c, a0, b0, a2, b2, kt + 5, kend, f1, f0, acc);
-          }
-        }
-      }
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // drain the trailing re-fetches before the workgroup ends
 }
 
 // K tiles [kt0, kend) through 4 stages (any count >= 1; later steps of the
@@ -996,36 +750,6 @@ __device__ __forceinline__ void ring64x2_loop(const RingCtx& c, uint16_t* __rest
     ring64x2_stage<TM, TN>(c, a1, b1, a0, b0, kt + 1, kend, h0, h1, acc);
   }
   __builtin_amdgcn_s_waitcnt(0);
-}
-
-// MLORA_RING64X2=0 keeps large products on the 3-stage 256 x 128 ring (A/B timing)
-bool ring64x2_enabled() {
-  static int on = -1;
-  if (on < 0) {
-    const char* e = getenv("MLORA_RING64X2");
-    on = (e && e[0] == '0') ? 0 : 1;
-  }
-  return on == 1;
-}
-
-// MLORA_RING64=0 keeps the GEMMs on 32-deep stages (A/B timing)
-bool ring64_enabled() {
-  static int on = -1;
-  if (on < 0) {
-    const char* e = getenv("MLORA_RING64");
-    on = (e && e[0] == '0') ? 0 : 1;
-  }
-  return on == 1;
-}
-
-// MLORA_RING_PIPE=0 keeps the ring on the unpipelined step (A/B timing)
-int ring_pipe_enabled() {
-  static int on = -1;
-  if (on < 0) {
-    const char* e = getenv("MLORA_RING_PIPE");
-    on = (e && e[0] == '0') ? 0 : 1;
-  }
-  return on;
 }
 
 // The low-rank term added in the GEMM's registers (prefill): for every row
@@ -1185,15 +909,17 @@ __device__ __forceinline__ void shrink_row_body_ids(const PoolView& pv, int proj
 // from the adapter ids `ids`, and the first workgroup dispatched, (0, 0),
 // builds the batch's segment workspace seg_ws (seg_passes radix passes) in
 // the LDS its ring would use, while the rows go to the other n_shrink - 1.
-template <int TM, int TN, int KD, bool PART, bool LORA, bool CO, bool IDS = false>
+template <int TM, int TN, bool PART, bool LORA, bool CO, bool IDS = false>
 __device__ __forceinline__ void gemm_ring_body(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y,
     float* __restrict__ part, int M, int K, int N, int tiles_n, int n_tiles, int per_xcd, int kt_per, PoolView pv,
     const int32_t* __restrict__ row_key, LoraOperands lo, int proj, float* __restrict__ Trows, int n_shrink,
-    int pipe, const int32_t* __restrict__ ids = nullptr, int32_t* __restrict__ seg_ws = nullptr,
+    const int32_t* __restrict__ ids = nullptr, int32_t* __restrict__ seg_ws = nullptr,
     int seg_passes = 0) {
   static_assert(!(PART && LORA), "the low-rank epilogue needs the whole K range");
-  static_assert(!CO || (KD == 64 && TM == 128 && TN == 128), "co-resident form: 128x128 tiles, 64-deep stages");
+  static_assert(!CO || (TM == 128 && TN == 128), "co-resident form: 128x128 tiles");
+  static_assert(!(TM == 256) || TN == 256, "large form: 256x256 tiles");
+  static_assert(!PART || CO, "split-K partials: the co-resident form");
   static_assert(!IDS || CO, "the id-based form is the co-resident one");
   constexpr int MI = TM / 64, NJ = TN / 64;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1270,25 +996,13 @@ __device__ __forceinline__ void gemm_ring_body(
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   const int kt0 = PART ? blockIdx.y * kt_per : 0;
-  const int kend = PART ? kt0 + kt_per : K / KD;
+  const int kend = PART ? kt0 + kt_per : K / GBK64;
   if constexpr (CO) {
     ring64x2_loop<TM, TN>(c, m64_a0, m64_a1, m64_b0, m64_b1, kt0, kend, acc);
-  } else if constexpr (KD == 64 && TM == 256 && TN == 256) {
-    ring64x2_loop<TM, TN>(c, h64_a0, h64_a1, h64_b0, h64_b1, kt0, kend, acc);
-  } else if constexpr (KD == 64 && TM == 256) {
-    ring64_loop3<TM, TN>(c, l64_a0, l64_a1, l64_a2, l64_b0, l64_b1, l64_b2, kt0, kend, acc);
-  } else if constexpr (KD == 64) {
-    ring64_loop4<TM, TN>(c, m64_a0, m64_a1, m64_a2, m64_a3, m64_b0, m64_b1, m64_b2, m64_b3, kt0, kend, acc);
   } else if constexpr (TM == 256) {
-    if (pipe)
-      ring_mainloop_p<TM, TN>(c, big_a0, big_a1, big_a2, big_a3, big_b0, big_b1, big_b2, big_b3, kt0, kend, acc);
-    else
-      ring_mainloop4<TM, TN>(c, big_a0, big_a1, big_a2, big_a3, big_b0, big_b1, big_b2, big_b3, kt0, kend, acc);
+    ring64x2_loop<TM, TN>(c, h64_a0, h64_a1, h64_b0, h64_b1, kt0, kend, acc);
   } else {
-    if (pipe)
-      ring_mainloop_p<TM, TN>(c, mid_a0, mid_a1, mid_a2, mid_a3, mid_b0, mid_b1, mid_b2, mid_b3, kt0, kend, acc);
-    else
-      ring_mainloop4<TM, TN>(c, mid_a0, mid_a1, mid_a2, mid_a3, mid_b0, mid_b1, mid_b2, mid_b3, kt0, kend, acc);
+    ring64_loop4<TM, TN>(c, m64_a0, m64_a1, m64_a2, m64_a3, m64_b0, m64_b1, m64_b2, m64_b3, kt0, kend, acc);
   }
 
   int key[MI];  // low-rank epilogue: the keys of the lane's A-fragment rows
@@ -1319,47 +1033,41 @@ __device__ __forceinline__ void gemm_ring_body(
         }
       }
     }
-  if constexpr (PART && !CO) {
-    if (n_shrink) {
-      const int G = n_tiles * (int)gridDim.y;
-      for (int k = t + n_tiles * (int)blockIdx.y; k < M; k += G)
-        shrink_row_body<true, kRingThreads / 64>(pv, proj, X, row_key, k, Trows, row_desc(Trows, M, pv.max_rank));
-    }
-  }
 }
 
-template <int TM, int TN, int KD, bool PART, bool LORA>
+// one workgroup per CU: 256x256 tiles (large products, with or without the
+// low-rank epilogue) or whole-K 128x128 tiles over a 4-stage ring (plain
+// medium GEMM)
+template <int TM, int TN, bool LORA>
 __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_ring(
-    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y,
-    float* __restrict__ part, int M, int K, int N, int tiles_n, int n_tiles, int per_xcd, int kt_per, PoolView pv,
-    const int32_t* __restrict__ row_key, LoraOperands lo, int proj, float* __restrict__ Trows, int n_shrink,
-    int pipe) {
-  gemm_ring_body<TM, TN, KD, PART, LORA, false>(X, W, Y, part, M, K, N, tiles_n, n_tiles, per_xcd, kt_per, pv,
-                                                row_key, lo, proj, Trows, n_shrink, pipe);
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y, int M, int K, int N,
+    int tiles_n, int n_tiles, int per_xcd, PoolView pv, const int32_t* __restrict__ row_key, LoraOperands lo) {
+  gemm_ring_body<TM, TN, false, LORA, false>(X, W, Y, nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, pv, row_key, lo,
+                                             0, nullptr, 0);
 }
 
 // two workgroups per CU on whole-K 128x128 tiles (plain GEMM, Y in bf16)
 __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_ring_co_whole(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y, int M, int K, int N,
     int tiles_n, int n_tiles, int per_xcd) {
-  gemm_ring_body<128, 128, 64, false, false, true>(X, W, Y, nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0,
-                                                   PoolView{}, nullptr, LoraOperands{}, 0, nullptr, 0, 1);
+  gemm_ring_body<128, 128, false, false, true>(X, W, Y, nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, PoolView{},
+                                               nullptr, LoraOperands{}, 0, nullptr, 0);
 }
 
 // the same with the low-rank epilogue
 __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_ring_co_lora(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y, int M, int K, int N,
     int tiles_n, int n_tiles, int per_xcd, PoolView pv, const int32_t* __restrict__ row_key, LoraOperands lo) {
-  gemm_ring_body<128, 128, 64, false, true, true>(X, W, Y, nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, pv,
-                                                  row_key, lo, 0, nullptr, 0, 1);
+  gemm_ring_body<128, 128, false, true, true>(X, W, Y, nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, pv, row_key,
+                                              lo, 0, nullptr, 0);
 }
 
 __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_ring_co(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y,
     float* __restrict__ part, int M, int K, int N, int tiles_n, int n_tiles, int per_xcd, int kt_per, PoolView pv,
     const int32_t* __restrict__ row_key, int proj, float* __restrict__ Trows, int n_shrink) {
-  gemm_ring_body<128, 128, 64, true, false, true>(X, W, Y, part, M, K, N, tiles_n, n_tiles, per_xcd, kt_per, pv,
-                                                  row_key, LoraOperands{}, proj, Trows, n_shrink, 1);
+  gemm_ring_body<128, 128, true, false, true>(X, W, Y, part, M, K, N, tiles_n, n_tiles, per_xcd, kt_per, pv, row_key,
+                                              LoraOperands{}, proj, Trows, n_shrink);
 }
 
 // the same, with the row keys from the adapter ids and the segment build in
@@ -1369,70 +1077,9 @@ __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(2,
     float* __restrict__ part, int M, int K, int N, int tiles_n, int n_tiles, int per_xcd, int kt_per, PoolView pv,
     int proj, float* __restrict__ Trows, int n_shrink, const int32_t* __restrict__ ids, int32_t* __restrict__ seg_ws,
     int seg_passes) {
-  gemm_ring_body<128, 128, 64, true, false, true, true>(X, W, Y, part, M, K, N, tiles_n, n_tiles, per_xcd, kt_per,
-                                                        pv, nullptr, LoraOperands{}, proj, Trows, n_shrink, 1, ids,
-                                                        seg_ws, seg_passes);
-}
-
-// MLORA_DECODE_SPLITK=0 keeps decode batches on the one-pass skinny kernel (A/B timing)
-bool decode_splitk_enabled() {
-  static int on = -1;
-  if (on < 0) {
-    const char* e = getenv("MLORA_DECODE_SPLITK");
-    on = (e && e[0] == '0') ? 0 : 1;
-  }
-  return on == 1;
-}
-
-// MLORA_GEMM_MID=0 keeps medium per-row batches on the K-split kernel (A/B timing)
-bool mid_enabled() {
-  static int on = -1;
-  if (on < 0) {
-    const char* e = getenv("MLORA_GEMM_MID");
-    on = (e && e[0] == '0') ? 0 : 1;
-  }
-  return on == 1;
-}
-
-// MLORA_GEMM_KSPLIT=0 keeps medium batches on the 128x128 kernel (A/B timing)
-bool ksplit_enabled() {
-  static int on = -1;
-  if (on < 0) {
-    const char* e = getenv("MLORA_GEMM_KSPLIT");
-    on = (e && e[0] == '0') ? 0 : 1;
-  }
-  return on == 1;
-}
-
-// MLORA_GEMM_BIG=0 keeps large products on the 128x128 kernel (for A/B timing)
-bool big_gemm_enabled() {
-  static int on = -1;
-  if (on < 0) {
-    const char* e = getenv("MLORA_GEMM_BIG");
-    on = (e && e[0] == '0') ? 0 : 1;
-  }
-  return on == 1;
-}
-
-// MLORA_MID_CO=0 keeps medium split-K tiles on the 4-stage ring with the
-// shrink after the tiles (A/B timing)
-bool mid_co_enabled() {
-  static int on = -1;
-  if (on < 0) {
-    const char* e = getenv("MLORA_MID_CO");
-    on = (e && e[0] == '0') ? 0 : 1;
-  }
-  return on == 1;
-}
-
-// MLORA_MID_BASE=0 keeps the plain medium GEMM on the K-split kernel (A/B timing)
-bool mid_base_enabled() {
-  static int on = -1;
-  if (on < 0) {
-    const char* e = getenv("MLORA_MID_BASE");
-    on = (e && e[0] == '0') ? 0 : 1;
-  }
-  return on == 1;
+  gemm_ring_body<128, 128, true, false, true, true>(X, W, Y, part, M, K, N, tiles_n, n_tiles, per_xcd, kt_per, pv,
+                                                    nullptr, LoraOperands{}, proj, Trows, n_shrink, ids, seg_ws,
+                                                    seg_passes);
 }
 
 // Large products: 256x256 tiles, one workgroup per CU, unless too few tiles
@@ -1440,7 +1087,6 @@ bool mid_base_enabled() {
 // (measured ~8 % slower per tile-flop at full occupancy, so they win when
 // they fill the machine clearly better: 2048x4096x4096 in 64 us against 91).
 bool big_prefers_co(int M, int N) {
-  if (!ring64_enabled() || !mid_co_enabled()) return false;
   const long t256 = (long)((M + 255) / 256) * ((N + 255) / 256);
   const long t128 = (long)((M + 127) / 128) * ((N + 127) / 128);
   const double e256 = (double)t256 / (((t256 + 255) / 256) * 256);
@@ -1456,23 +1102,10 @@ hipError_t launch_big(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, 
                  tiles_n, n_tiles, per_xcd);
     return launched();
   }
-  const bool r64 = ring64_enabled(), x2 = r64 && ring64x2_enabled();
-  const int TN = (r64 && !x2) ? 128 : 256;
-  const int tiles_m = (M + 255) / 256, tiles_n = (N + TN - 1) / TN;
-  const int n_tiles = tiles_m * tiles_n;
+  const int tiles_n = (N + 255) / 256, n_tiles = ((M + 255) / 256) * tiles_n;
   const int per_xcd = (n_tiles + 7) / 8;
-  if (x2)
-    MLORA_LAUNCH("gemm_big", (gemm_ring<256, 256, 64, false, false>), dim3(per_xcd * 8), dim3(kRingThreads), 0, st,
-                 X, W, Y, (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, PoolView{}, (const int32_t*)nullptr,
-                 LoraOperands{}, 0, (float*)nullptr, 0, 1);
-  else if (r64)
-    MLORA_LAUNCH("gemm_big", (gemm_ring<256, 128, 64, false, false>), dim3(per_xcd * 8), dim3(kRingThreads), 0, st,
-                 X, W, Y, (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, PoolView{}, (const int32_t*)nullptr,
-                 LoraOperands{}, 0, (float*)nullptr, 0, 1);
-  else
-    MLORA_LAUNCH("gemm_big", (gemm_ring<256, 256, 32, false, false>), dim3(per_xcd * 8), dim3(kRingThreads), 0, st,
-                 X, W, Y, (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, PoolView{}, (const int32_t*)nullptr,
-                 LoraOperands{}, 0, (float*)nullptr, 0, ring_pipe_enabled());
+  MLORA_LAUNCH("gemm_big", (gemm_ring<256, 256, false>), dim3(per_xcd * 8), dim3(kRingThreads), 0, st, X, W, Y, M, K,
+               N, tiles_n, n_tiles, per_xcd, PoolView{}, (const int32_t*)nullptr, LoraOperands{});
   return launched();
 }
 
@@ -1485,21 +1118,20 @@ hipError_t launch_gemm(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M,
     else if (M <= 48) MLORA_LAUNCH("gemm_skinny", (gemm_skinny<3, VEC>), grid, block, 0, st, X, W, Y, M, K, N);
     else MLORA_LAUNCH("gemm_skinny", (gemm_skinny<4, VEC>), grid, block, 0, st, X, W, Y, M, K, N);
   } else if (VEC && M <= 1024 && K % (GBK64 * 4) == 0 && (long)M * K * 2 < (1L << 31) &&
-             (long)N * K * 2 < (1L << 31) && ring64_enabled() && mid_base_enabled()) {
+             (long)N * K * 2 < (1L << 31)) {
     // medium batches without scratch for split-K partials: 128x128 ring
     // tiles over the whole K, Y written once in bf16
     const int tiles_n = (N + 127) / 128, n_tiles = ((M + 127) / 128) * tiles_n;
     const int per_xcd = (n_tiles + 7) / 8;
-    MLORA_LAUNCH("gemm_mid", (gemm_ring<128, 128, 64, false, false>), dim3(per_xcd * 8), dim3(kRingThreads), 0, st,
-                 X, W, Y, (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, PoolView{}, (const int32_t*)nullptr,
-                 LoraOperands{}, 0, (float*)nullptr, 0, 1);
+    MLORA_LAUNCH("gemm_mid", (gemm_ring<128, 128, false>), dim3(per_xcd * 8), dim3(kRingThreads), 0, st, X, W, Y, M,
+                 K, N, tiles_n, n_tiles, per_xcd, PoolView{}, (const int32_t*)nullptr, LoraOperands{});
     return launched();
-  } else if (M <= 1024 && (long)((M + 127) / 128) * ((N + 31) / 32) >= 128 && ksplit_enabled()) {
+  } else if (M <= 1024 && (long)((M + 127) / 128) * ((N + 31) / 32) >= 128) {
     const dim3 grid((N + 31) / 32, (M + 32 * KS_MB - 1) / (32 * KS_MB)), block(64 * kKsWaves);
     MLORA_LAUNCH("gemm_ksplit", (gemm_ksplit<VEC, false>), grid, block, 0, st, X, W, Y, M, K, N, PoolView{}, 0, nullptr,
                        nullptr);
-  } else if (VEC && K % (GBK * kRingStages) == 0 && (long)M * N >= 2048L * 2048L && (long)M * K * 2 < (1L << 31) &&
-             (long)N * K * 2 < (1L << 31) && big_gemm_enabled()) {
+  } else if (VEC && K % kRingKAlign == 0 && (long)M * N >= 2048L * 2048L && (long)M * K * 2 < (1L << 31) &&
+             (long)N * K * 2 < (1L << 31)) {
     return launch_big(X, W, Y, M, K, N, st);
   } else {
     const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM), block(kTiledThreads);
@@ -1816,16 +1448,9 @@ hipError_t launch_decode(const uint16_t* X, const uint16_t* W, uint16_t* Y, int 
                          bool lora = true, const int32_t* ids = nullptr, int32_t* seg_ws = nullptr) {
   static_assert(kDecSplit == kRowsTParts, "T partial slices are the K quarters");
   const size_t lds = decode_lds_bytes(M, K, MB);
-  static size_t attr = 0;
-  if (lds > attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_decode<MB, false>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)gemm_decode<MB, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)lds);
-    if (e != hipSuccess) return e;
-    attr = lds;
-  }
+  static LdsLimit limit;
+  const hipError_t le = limit.ensure({(const void*)gemm_decode<MB, false>, (const void*)gemm_decode<MB, true>}, lds);
+  if (le != hipSuccess) return le;
   const int ncb = (N + kDecCols - 1) / kDecCols;
   if (seg_ws)
     MLORA_LAUNCH("gemm_decode+seg+shrink_rows", (gemm_decode<MB, true>), dim3(ncb * kDecSplit + 1),
@@ -1857,25 +1482,24 @@ hipError_t launch_decode(const uint16_t* X, const uint16_t* W, uint16_t* Y, int 
 int mid_split(int M, int N, int K) {
   const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
   int S = 1;
-  while (S < kMidMaxSplit && tiles * S < 256 && K % (GBK * kRingStages * S * 2) == 0) S *= 2;
+  while (S < kMidMaxSplit && tiles * S < 256 && K % (kRingKAlign * S * 2) == 0) S *= 2;
   return S;
 }
 
-bool mid_ring_ok(int M, int K) { return K % (GBK * kRingStages) == 0 && (long)M * K * 2 < (1L << 31); }
+bool mid_ring_ok(int M, int K) { return K % kRingKAlign == 0 && (long)M * K * 2 < (1L << 31); }
 
-// shrink: the per-row shrink (T, one slice) runs in the tile workgroups
-// after their tiles
+// shrink: the per-row shrink (T, one slice) runs in workgroups of its own
+// ahead of the tiles, on the same CUs (co-resident form)
 hipError_t launch_mid_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N, const PoolView& pv,
                            int proj, const int32_t* row_key, float* T, float* part, bool shrink, hipStream_t st,
                            bool lora = true, const int32_t* ids = nullptr, int32_t* seg_ws = nullptr) {
   const int S = mid_split(M, N, K);
   const int tiles_n = (N + 127) / 128, n_tiles = ((M + 127) / 128) * tiles_n;
   const int per_xcd = (n_tiles + 7) / 8;
-  const int ns = shrink ? 1 : 0;  // the tile workgroups compute the per-row shrink after their tiles
   if (ids != nullptr) {
     // the segment build takes the first of the co-resident form's shrink
     // workgroups (at least 72 of them above 64 rows)
-    if (!(ring64_enabled() && mid_co_enabled() && shrink && lora && M > 64 && M <= 1024)) return hipErrorNotSupported;
+    if (!(shrink && lora && M > 64 && M <= 1024)) return hipErrorNotSupported;
     // one more than the rows (the segment build's), up to 264: no shrink
     // workgroup takes a second row where the plain form gives each its own
     const int nsw = min((M + 1 + 7) / 8 * 8, 264);
@@ -1883,7 +1507,7 @@ hipError_t launch_mid_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, in
     MLORA_LAUNCH("gemm_mid+seg+shrink_rows", gemm_ring_co_ids, dim3(nsw + per_xcd * 8, S), dim3(kRingThreads), 0,
                  st, X, W, Y, part, M, K, N, tiles_n, n_tiles, per_xcd, K / GBK64 / S, pv, proj, T, nsw, ids, seg_ws,
                  passes);
-  } else if (ring64_enabled() && mid_co_enabled()) {
+  } else {
     // shrink workgroups ahead of the tiles: one per row up to one per CU
     // (each then loops over rows, so the tiles still find a free slot on
     // every CU), a multiple of 8 so the tile workgroups keep their XCD mapping
@@ -1891,14 +1515,7 @@ hipError_t launch_mid_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, in
     MLORA_LAUNCH(shrink ? "gemm_mid+shrink_rows" : "gemm_mid", gemm_ring_co, dim3(nsw + per_xcd * 8, S),
                  dim3(kRingThreads), 0, st, X, W, Y, part, M, K, N, tiles_n, n_tiles, per_xcd, K / GBK64 / S, pv,
                  row_key, proj, T, nsw);
-  } else if (ring64_enabled())
-    MLORA_LAUNCH(shrink ? "gemm_mid+shrink_rows" : "gemm_mid", (gemm_ring<128, 128, 64, true, false>),
-                 dim3(per_xcd * 8, S), dim3(kRingThreads), 0, st, X, W, Y, part, M, K, N, tiles_n, n_tiles,
-                 per_xcd, K / GBK64 / S, pv, row_key, LoraOperands{}, proj, T, ns, 1);
-  else
-    MLORA_LAUNCH(shrink ? "gemm_mid+shrink_rows" : "gemm_mid", (gemm_ring<128, 128, 32, true, false>),
-                 dim3(per_xcd * 8, S), dim3(kRingThreads), 0, st, X, W, Y, part, M, K, N, tiles_n, n_tiles,
-                 per_xcd, K / GBK / S, pv, row_key, LoraOperands{}, proj, T, ns, ring_pipe_enabled());
+  }
   hipError_t e = launched();
   if (e != hipSuccess) return e;
   const int threads = M * (N / 8);
@@ -1947,14 +1564,14 @@ hipError_t launch_gemm_lora(const PoolView& pv, int proj, const uint16_t* X, con
                        reinterpret_cast<uintptr_t>(pv.up) | reinterpret_cast<uintptr_t>(Y);
   const bool vec = (K % 8 == 0) && (N % 8 == 0) && (al % 16 == 0);
   const bool down_vec = reinterpret_cast<uintptr_t>(pv.down) % 16 == 0;  // the in-launch shrink's loads
-  if (decode_splitk_ok(M, K, N, vec) && (down_vec || !shrink) && decode_splitk_enabled()) {
+  if (decode_splitk_ok(M, K, N, vec) && (down_vec || !shrink)) {
     // the per-row shrink shares the GEMM launch
     if (M <= 16) return launch_decode<1>(X, W, Y, M, K, N, pv, proj, row_key, T, part, shrink, stream);
     if (M <= 32) return launch_decode<2>(X, W, Y, M, K, N, pv, proj, row_key, T, part, shrink, stream);
     if (M <= 48) return launch_decode<3>(X, W, Y, M, K, N, pv, proj, row_key, T, part, shrink, stream);
     return launch_decode<4>(X, W, Y, M, K, N, pv, proj, row_key, T, part, shrink, stream);
   }
-  if (M > 64 && vec && down_vec && mid_ring_ok(M, K) && (long)N * K * 2 < (1L << 31) && mid_enabled())
+  if (M > 64 && vec && down_vec && mid_ring_ok(M, K) && (long)N * K * 2 < (1L << 31))
     return launch_mid_lora(X, W, Y, M, K, N, pv, proj, row_key, T, part, shrink, stream);
   if (shrink) {
     hipError_t e = launch_shrink_rows(pv, proj, X, ws, M, T, stream);
@@ -1975,11 +1592,11 @@ hipError_t launch_forward_rows(const PoolView& pv, int proj, const uint16_t* X, 
   const bool vec = (K % 8 == 0) && (N % 8 == 0) && (al % 16 == 0);
   const int32_t* row_key = ws + MLORA_SEG_ROWKEY(M);
   if (M > 64) {
-    if (vec && mid_ring_ok(M, K) && (long)N * K * 2 < (1L << 31) && mid_enabled())
+    if (vec && mid_ring_ok(M, K) && (long)N * K * 2 < (1L << 31))
       return launch_mid_lora(X, W, Y, M, K, N, pv, proj, row_key, T, part, true, stream, true, ids, ws);
     return hipErrorNotSupported;
   }
-  if (!decode_splitk_ok(M, K, N, vec) || !decode_splitk_enabled()) return hipErrorNotSupported;
+  if (!decode_splitk_ok(M, K, N, vec)) return hipErrorNotSupported;
   if (M <= 16) return launch_decode<1>(X, W, Y, M, K, N, pv, proj, row_key, T, part, true, stream, true, ids, ws);
   if (M <= 32) return launch_decode<2>(X, W, Y, M, K, N, pv, proj, row_key, T, part, true, stream, true, ids, ws);
   if (M <= 48) return launch_decode<3>(X, W, Y, M, K, N, pv, proj, row_key, T, part, true, stream, true, ids, ws);
@@ -1996,33 +1613,23 @@ hipError_t launch_base_split(const uint16_t* X, const uint16_t* W, uint16_t* Y, 
   const uintptr_t al = reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(W) | reinterpret_cast<uintptr_t>(Y);
   const bool vec = (K % 8 == 0) && (N % 8 == 0) && (al % 16 == 0);
   const PoolView none{};
-  if (decode_splitk_ok(M, K, N, vec) && decode_splitk_enabled()) {
+  if (decode_splitk_ok(M, K, N, vec)) {
     if (M <= 16) return launch_decode<1>(X, W, Y, M, K, N, none, 0, nullptr, nullptr, part, false, stream, false);
     if (M <= 32) return launch_decode<2>(X, W, Y, M, K, N, none, 0, nullptr, nullptr, part, false, stream, false);
     if (M <= 48) return launch_decode<3>(X, W, Y, M, K, N, none, 0, nullptr, nullptr, part, false, stream, false);
     return launch_decode<4>(X, W, Y, M, K, N, none, 0, nullptr, nullptr, part, false, stream, false);
   }
-  if (M > 64 && vec && mid_ring_ok(M, K) && (long)N * K * 2 < (1L << 31) && mid_enabled())
+  if (M > 64 && vec && mid_ring_ok(M, K) && (long)N * K * 2 < (1L << 31))
     return launch_mid_lora(X, W, Y, M, K, N, none, 0, nullptr, nullptr, part, false, stream, false);
   return hipErrorNotSupported;
 }
 
-// MLORA_BIG_EPILOGUE=0 keeps large batches on base GEMM + separate expand (A/B timing)
-bool big_epilogue_enabled() {
-  static int on = -1;
-  if (on < 0) {
-    const char* e = getenv("MLORA_BIG_EPILOGUE");
-    on = (e && e[0] == '0') ? 0 : 1;
-  }
-  return on == 1;
-}
 
 bool big_lora_ok(const PoolView& pv, const uint16_t* X, const uint16_t* W, int M) {
-  if (!big_epilogue_enabled()) return false;
   const int K = pv.din, N = pv.dout;
   const bool vec = (K % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(W)) % 16 == 0);
-  return vec && K % (GBK * kRingStages) == 0 && (long)M * N >= 2048L * 2048L && (long)M * K * 2 < (1L << 31) &&
-         (long)N * K * 2 < (1L << 31) && big_gemm_enabled();
+  return vec && K % kRingKAlign == 0 && (long)M * N >= 2048L * 2048L && (long)M * K * 2 < (1L << 31) &&
+         (long)N * K * 2 < (1L << 31);
 }
 
 hipError_t launch_big_lora(const PoolView& pv, const uint16_t* X, const uint16_t* W, const int32_t* ws,
@@ -2035,23 +1642,10 @@ hipError_t launch_big_lora(const PoolView& pv, const uint16_t* X, const uint16_t
                  N, tiles_n, n_tiles, per_xcd, pv, ws + MLORA_SEG_ROWKEY(M), lo);
     return launched();
   }
-  const bool r64 = ring64_enabled(), x2 = r64 && ring64x2_enabled();
-  const int TN = (r64 && !x2) ? 128 : 256;
-  const int tiles_m = (M + 255) / 256, tiles_n = (N + TN - 1) / TN;
-  const int n_tiles = tiles_m * tiles_n;
+  const int tiles_n = (N + 255) / 256, n_tiles = ((M + 255) / 256) * tiles_n;
   const int per_xcd = (n_tiles + 7) / 8;
-  if (x2)
-    MLORA_LAUNCH("gemm_big_lora", (gemm_ring<256, 256, 64, false, true>), dim3(per_xcd * 8), dim3(kRingThreads), 0,
-                 st, X, W, Y, (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, pv, ws + MLORA_SEG_ROWKEY(M), lo,
-                 0, (float*)nullptr, 0, 1);
-  else if (r64)
-    MLORA_LAUNCH("gemm_big_lora", (gemm_ring<256, 128, 64, false, true>), dim3(per_xcd * 8), dim3(kRingThreads), 0,
-                 st, X, W, Y, (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, pv, ws + MLORA_SEG_ROWKEY(M), lo,
-                 0, (float*)nullptr, 0, 1);
-  else
-    MLORA_LAUNCH("gemm_big_lora", (gemm_ring<256, 256, 32, false, true>), dim3(per_xcd * 8), dim3(kRingThreads), 0,
-                 st, X, W, Y, (float*)nullptr, M, K, N, tiles_n, n_tiles, per_xcd, 0, pv, ws + MLORA_SEG_ROWKEY(M), lo,
-                 0, (float*)nullptr, 0, ring_pipe_enabled());
+  MLORA_LAUNCH("gemm_big_lora", (gemm_ring<256, 256, true>), dim3(per_xcd * 8), dim3(kRingThreads), 0, st, X, W, Y, M,
+               K, N, tiles_n, n_tiles, per_xcd, pv, ws + MLORA_SEG_ROWKEY(M), lo);
   return launched();
 }
 

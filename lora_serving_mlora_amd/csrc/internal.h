@@ -6,6 +6,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <initializer_list>
+#include <mutex>
+
 #include "../../include/mlora.h"
 
 namespace mlora {
@@ -56,6 +59,26 @@ __device__ __forceinline__ void load8(const uint16_t* __restrict__ p, int i, int
 // ----------------------------------------------------------------------------
 // host launchers (return hipSuccess or the launch error)
 // ----------------------------------------------------------------------------
+
+// The largest dynamic LDS size a group of kernels has been allowed so far.
+// ensure() raises the limit of every kernel of the group to `bytes` when a
+// launch needs more than before; the check and the raise happen under the
+// mutex, so host threads launching different sizes never leave a kernel's
+// limit below what one of them then requests.
+struct LdsLimit {
+  std::mutex mu;
+  size_t bytes = 0;
+  hipError_t ensure(std::initializer_list<const void*> fns, size_t need) {
+    std::lock_guard<std::mutex> g(mu);
+    if (need <= bytes) return hipSuccess;
+    for (const void* f : fns) {
+      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)need);
+      if (e != hipSuccess) return e;
+    }
+    bytes = need;
+    return hipSuccess;
+  }
+};
 
 // pool metadata view on the device
 struct PoolView {

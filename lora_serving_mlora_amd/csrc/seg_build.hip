@@ -39,14 +39,8 @@ hipError_t launch_nt(const int32_t* row_adapter, int n, const int32_t* pool_rank
   if (lds > 64 * 1024) {
     // a batch near the row limit needs most of the 160 KiB of LDS of a CU;
     // the launch itself reports an error if the device cannot provide it
-    static size_t attr_bytes = 0;
-    if (lds > attr_bytes) {
-      if (hipFuncSetAttribute((const void*)seg_build_kernel<NT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)lds) == hipSuccess)
-        attr_bytes = lds;
-      else
-        (void)hipGetLastError();
-    }
+    static LdsLimit limit;
+    if (limit.ensure({(const void*)seg_build_kernel<NT>}, lds) != hipSuccess) (void)hipGetLastError();
   }
   const int passes = n <= NT ? 0 : ((max_adapters + 1 < 256) ? 1 : 2);
   MLORA_LAUNCH("seg_build", seg_build_kernel<NT>, dim3(1), dim3(NT), lds, stream, row_adapter, n, pool_rank, max_adapters,

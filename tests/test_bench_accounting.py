@@ -77,9 +77,11 @@ def test_base_and_combined_kernels_match_the_element_count():
         assert algo[k] == (2 * (w0 + x + y), 2 * dense)
     # the split-K forms leave Y to the finish pass
     assert algo["gemm_decode"] == (2 * (w0 + x), 2 * dense)
+    # the shrink inside the GEMM launch reads its X rows from what the base
+    # product already reads: X counts once
     fused_in = algo["gemm_decode+shrink_rows"]
-    assert fused_in == (2 * (w0 + x) + 2 * (c["down"] + c["x_act"]) + 4 * c["t"],
-                        2 * (dense + c["mac_shrink"]))
+    assert fused_in == (2 * (w0 + x) + 2 * c["down"] + 4 * c["t"], 2 * (dense + c["mac_shrink"]))
+    assert algo["gemm_mid+shrink_rows"] == fused_in
     # the decode launch that also builds the segments: ids in, the
     # workspace's per-row arrays out (perm, inv, key, item and tile entries)
     assert algo["gemm_decode+seg+shrink_rows"] == (fused_in[0] + algo["seg_build"][0], fused_in[1])

@@ -195,3 +195,35 @@ def test_cross_stream_reuse_waits_for_last_reader(M):
     assert_close(dev_to_f64(Y_b), ref_b, "layer on the adapter loaded on another stream")
     with pytest.raises(M.MloraError):
         pool.ready(0)                             # not resident
+
+
+@pytest.mark.parametrize("step", [1, 2])
+def test_failed_load_leaves_no_resident_adapter_and_parks_its_pages(M, step):
+    """A load that fails once its copies may have been issued (an injected
+    failure before its last staging flush, or after its metadata copies)
+    leaves the id not resident on the host AND on the device (rank 0 in the
+    device table, so an apply treats its rows as invalid, not as reading
+    pages a later load overwrites), and its pages come back for the next
+    load; the retried load then serves the oracle's result."""
+    torch = torch_cuda()
+    w = _w({0: 4, 1: 8}, seed=67)
+    pool = M.Pool(w.din, w.dout, w.n_proj, w.max_adapters, w.max_rank, 40)
+    say(f"pool failed load step {step}")
+    pool.load(0, 4, float(w.scales[0]), w.down_all_bits(0), w.up_all_bits(0))
+    before = pool.free_pages()
+    pool.fail_next_load(step)
+    with pytest.raises(M.MloraError) as e:
+        pool.load(1, 8, float(w.scales[1]), w.down_all_bits(1), w.up_all_bits(1))
+    assert e.value.status == M.EHIP
+    assert pool.query(1) is None
+    torch.cuda.synchronize()
+    dev_rank = pool.meta[: 4 * w.max_adapters].view(torch.int32).cpu().tolist()
+    assert dev_rank[1] == 0 and dev_rank[0] == 4
+    assert pool.free_pages() == before          # the failed load's pages are free again (parked)
+    # rows on the id that failed to load are invalid: NaN, status bit set
+    seg_ws = M.build_segments(pool, ids_dev(w.row_adapter))
+    assert M.segments_header(seg_ws)["status"] & M.SEG_NOT_RESIDENT
+    # the retry takes the parked pages and serves the oracle's result
+    pool.load(1, 8, float(w.scales[1]), w.down_all_bits(1), w.up_all_bits(1))
+    assert pool.free_pages() == (before[0] - 8 * w.n_proj, before[1] - 8 * w.n_proj, before[2] + 1)
+    _apply_matches(M, pool, w, [0, 1])

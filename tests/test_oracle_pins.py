@@ -412,3 +412,211 @@ def test_tolerance_is_nan_aware():
     assert not O.within_tolerance(np.array([np.nan, 1.0]), np.array([1.0, 1.0]))
     assert O.within_tolerance(np.array([1.03]), np.array([1.0]))
     assert not O.within_tolerance(np.array([1.05]), np.array([1.0]))
+
+
+# ---------------------------------------------------------------- bf16 widening
+
+def _bf16_by_definition(bits):
+    """Value of a bf16 pattern from the binary format's definition: sign bit,
+    8 exponent bits (bias 127), 7 fraction bits; exponent 0 is subnormal
+    (no implicit 1, exponent -126), 255 is inf (fraction 0) or NaN."""
+    s = -1.0 if bits >> 15 else 1.0
+    e, f = (bits >> 7) & 0xFF, bits & 0x7F
+    if e == 0xFF:
+        return s * float("inf") if f == 0 else float("nan")
+    if e == 0:
+        return s * float(Fraction(f, 128) * Fraction(2) ** -126)
+    return s * float((1 + Fraction(f, 128)) * Fraction(2) ** (e - 127))
+
+
+def test_widen_bf16_fixed_patterns():
+    cases = {0x3F80: 1.0, 0xC000: -2.0, 0x0000: 0.0, 0x3F81: 1.0 + 2.0 ** -7,
+             0x0001: 2.0 ** -133, 0x8001: -(2.0 ** -133), 0x007F: 127 * 2.0 ** -133,
+             0x0080: 2.0 ** -126, 0x7F7F: (2 - 2.0 ** -7) * 2.0 ** 127,
+             0x7F80: float("inf"), 0xFF80: float("-inf"), 0x4049: 3.140625}
+    got = O.widen_bf16(np.array(list(cases), dtype=np.uint16))
+    assert got.tolist() == list(cases.values())
+    z = O.widen_bf16(np.array([0x8000], dtype=np.uint16))[0]
+    assert z == 0.0 and np.signbit(z)
+    assert np.isnan(O.widen_bf16(np.array([0x7FC0, 0xFFC1, 0x7F81], dtype=np.uint16))).all()
+
+
+def test_widen_bf16_every_pattern_against_definition_and_torch():
+    """All 65536 patterns: the exact value from the format's definition, and
+    torch's own bfloat16 -> float64 conversion (a library routine), agree with
+    the oracle's widening (NaN where they give NaN, sign of zero included)."""
+    import torch
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = O.widen_bf16(bits)
+    ref = np.array([_bf16_by_definition(int(b)) for b in bits.tolist()])
+    lib = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    for want in (ref, lib):
+        nan = np.isnan(want)
+        assert np.array_equal(np.isnan(got), nan)
+        assert np.array_equal(got[~nan], want[~nan])
+        assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+    # float32 widening is the same exact value (every bf16 is a float32)
+    got32 = O.widen_bf16(bits, dtype=np.float32)
+    assert got32.dtype == np.float32
+    assert np.array_equal(got32[~np.isnan(ref)].astype(np.float64), ref[~np.isnan(ref)])
+
+
+def test_widen_bf16_inverts_the_input_rounding():
+    """Widening the generator's RNE-rounded bits gives the float32 value
+    nearest the sample, ties to even: |x - widen(b)| <= half a bf16 ulp."""
+    g = np.random.default_rng(17)
+    x = (g.standard_normal(20000) * np.exp(g.uniform(-30, 30, 20000))).astype(np.float32)
+    b = synth.round_to_bf16_bits(x)
+    w = O.widen_bf16(b)
+    ulp = np.ldexp(1.0, np.frexp(np.abs(x).astype(np.float64))[1] - 8)
+    assert np.all(np.abs(x.astype(np.float64) - w) <= ulp / 2)
+
+
+# ---------------------------------------------------------------- base FLOP count
+
+def _count_matvec_ops(n, din, dout):
+    """Multiplies and adds of the plain row-by-row product y_k = W0 x_k,
+    counted by walking it: each output is a sum of din products, and the
+    count follows the pages' convention of a multiply plus an add per weight
+    (accumulation into zero)."""
+    ops = 0
+    for _k in range(n):
+        for _c in range(dout):
+            for _i in range(din):
+                ops += 2      # acc = acc + w * x
+    return ops
+
+
+@pytest.mark.parametrize("n,din,dout", [(1, 1, 1), (4, 4, 4), (3, 5, 7), (6, 2, 9), (0, 3, 3)])
+def test_base_flops_brute_force(n, din, dout):
+    assert O.base_flops(n, din, dout) == _count_matvec_ops(n, din, dout)
+
+
+def test_base_and_branch_flops_share_the_pages_convention():
+    """On the worked example (din = dout = 4), the page counts 2*r*(din+dout)
+    per active row for the branch; the same convention applied to a rank-r
+    product through a dense din x dout matrix with r = din = dout is the base
+    count of one row, and a merged rank-din adapter costs exactly one base
+    product per row in each factor."""
+    g = _load("worked_example.json")
+    din, dout = g["din"], g["dout"]
+    assert O.base_flops(1, din, dout) == 2 * din * dout
+    assert O.branch_flops([din], din, dout) == O.base_flops(1, din, din) + O.base_flops(1, din, dout)
+    assert O.base_flops(len(g["row_adapter"]), din, dout) == 4 * O.base_flops(1, din, dout)
+
+
+# ---------------------------------------------------------------- mutation check
+
+def _mutants():
+    """Plausible slips planted in the oracle (a dropped term, a wrong sign,
+    order or index, a transposed factor).  Each replaces one oracle function
+    for the duration of one check; every one must make at least one pin
+    above fail."""
+    lin, seg, shr, exp_, mrg = O.linear, O.segments, O.shrink_rows, O.expand_rows, O.merge
+    wid, bfl, brf, adb = O.widen_bf16, O.base_flops, O.branch_flops, O.adapter_bytes
+
+    def unscaled(ad):
+        return {a: (1.0, d, u) for a, (s, d, u) in ad.items()}
+
+    def negated(ad):
+        return {a: (-s, d, u) for a, (s, d, u) in ad.items()}
+
+    def seg_reverse_ties(ids, max_adapters, resident):
+        out = seg(ids, max_adapters, resident)
+        perm = out["perm"].copy()
+        off = out["seg_off"]
+        for s in range(out["nseg"]):
+            perm[off[s]:off[s + 1]] = perm[off[s]:off[s + 1]][::-1].copy()
+        inv = np.empty_like(perm)
+        inv[perm] = np.arange(len(perm), dtype=perm.dtype)
+        return dict(out, perm=perm, inv=inv)
+
+    def seg_inv_is_perm(ids, max_adapters, resident):
+        out = seg(ids, max_adapters, resident)
+        return dict(out, inv=out["perm"].copy())
+
+    def seg_none_first(ids, max_adapters, resident):
+        out = seg(ids, max_adapters, resident)
+        n_act, n_none = out["n_act"], out["n_none"]
+        p = out["perm"]
+        perm = np.concatenate([p[n_act:n_act + n_none], p[:n_act], p[n_act + n_none:]])
+        inv = np.empty_like(perm)
+        inv[perm] = np.arange(len(perm), dtype=perm.dtype)
+        return dict(out, perm=perm, inv=inv)
+
+    def seg_descending(ids, max_adapters, resident):
+        # groups in descending adapter order
+        out = seg(ids, max_adapters, resident)
+        blocks = [out["perm"][out["seg_off"][s]:out["seg_off"][s + 1]] for s in range(out["nseg"])][::-1]
+        rest = out["perm"][out["n_act"]:]
+        perm = np.concatenate(blocks + [rest]).astype(np.int32) if blocks else out["perm"]
+        sa = out["seg_adapter"][::-1].copy()
+        off = np.concatenate([[0], np.cumsum([len(b) for b in blocks])]).astype(np.int32)
+        inv = np.empty_like(perm)
+        inv[perm] = np.arange(len(perm), dtype=perm.dtype)
+        return dict(out, perm=perm, inv=inv, seg_adapter=sa, seg_off=off)
+
+    def shrink_next_row(X, ids, ad, m, rows=None, dtype=np.float64):
+        t = shr(X, ids, ad, m, rows, dtype)
+        n = np.asarray(X).shape[0]
+        return {k: (np.asarray(ad[int(ids[k])][1], dtype) @ np.asarray(X, dtype)[(k + 1) % n]) for k in t}
+
+    return {
+        "linear: scale dropped": ("linear", lambda X, W, i, ad, m, **kw: lin(X, W, i, unscaled(ad), m, **kw)),
+        "linear: delta subtracted": ("linear", lambda X, W, i, ad, m, **kw: lin(X, W, i, negated(ad), m, **kw)),
+        "linear: Up and Down swapped": ("linear", lambda X, W, i, ad, m, **kw: lin(
+            X, W, i, {a: (s, u.T, d.T) for a, (s, d, u) in ad.items()}, m, **kw)),
+        "linear: invalid ids treated as none": ("linear", lambda X, W, i, ad, m, **kw: lin(
+            X, W, [a if (a == -1 or a in ad) else -1 for a in np.asarray(i).tolist()], ad, m, **kw)),
+        "segments: ties in reverse row order": ("segments", seg_reverse_ties),
+        "segments: inverse taken as perm": ("segments", seg_inv_is_perm),
+        "segments: base-only rows first": ("segments", seg_none_first),
+        "segments: groups in descending id order": ("segments", seg_descending),
+        "shrink_rows: next row's x": ("shrink_rows", shrink_next_row),
+        "expand_rows: scale dropped": ("expand_rows", lambda Y, t, i, ad, m, dtype=np.float64: exp_(
+            Y, t, i, unscaled(ad), m, dtype)),
+        "merge: sign ignored": ("merge", lambda W, a, sign=1.0, dtype=np.float64: mrg(W, a, 1.0, dtype)),
+        "merge: factors transposed": ("merge", lambda W, a, sign=1.0, dtype=np.float64: np.asarray(W, dtype) +
+                                      sign * a[0] * (np.asarray(a[1], dtype).T @ np.asarray(a[2], dtype).T)
+                                      if np.asarray(a[1]).shape[1] == np.asarray(a[2]).shape[0]
+                                      else mrg(W, a, sign, dtype)),
+        "widen_bf16: fraction one bit short": ("widen_bf16", lambda b, dtype=np.float64: (
+            (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) & np.uint32(0xFFFE)) << np.uint32(16)
+        ).view(np.float32).astype(dtype)),
+        "widen_bf16: read as float16": ("widen_bf16", lambda b, dtype=np.float64: np.ascontiguousarray(
+            b, dtype=np.uint16).view(np.float16).astype(dtype)),
+        "base_flops: multiply only": ("base_flops", lambda n, din, dout: bfl(n, din, dout) // 2),
+        "branch_flops: Down only": ("branch_flops", lambda r, din, dout: brf(r, din, 0)),
+        "adapter_bytes: one factor": ("adapter_bytes", lambda din, dout, rank, b=2: adb(din, 0, rank, b)),
+    }
+
+
+def _pin_calls():
+    return [
+        test_worked_example_segments_match_page, test_worked_example_flops_match_page,
+        lambda: test_worked_example_values_route_to_the_right_rows(True),
+        lambda: test_worked_example_values_route_to_the_right_rows(False),
+        test_pool_sizes_match_page,
+        lambda: test_merge_identity(11, 16, 16, {0: 1, 1: 4, 2: 8}),
+        lambda: test_merge_serves_its_adapter(31, 16, 24, 3),
+        *[lambda s=s: test_merge_exact_rational(s) for s in range(4)],
+        test_all_rows_one_adapter_is_one_matmul, test_all_rows_base_only_is_plain_gemm,
+        *[lambda s=s: test_exact_rational_brute_force(s) for s in range(6)],
+        test_segments_exhaustive_five_rows, test_segments_invalid_ids_sort_last_and_flag,
+        test_row_permutation_equivariance, test_zero_padded_rank_changes_nothing, test_linearity_in_scale,
+        test_invalid_rows_are_nan_and_others_unaffected, test_widen_bf16_fixed_patterns,
+        lambda: test_base_flops_brute_force(3, 5, 7), test_base_and_branch_flops_share_the_pages_convention,
+    ]
+
+
+@pytest.mark.parametrize("mutant", sorted(_mutants()))
+def test_every_planted_oracle_slip_fails_a_pin(mutant, monkeypatch):
+    name, fn = _mutants()[mutant]
+    monkeypatch.setattr(O, name, fn)
+    caught = []
+    for i, pin in enumerate(_pin_calls()):
+        try:
+            pin()
+        except (AssertionError, ValueError):   # a failed check, or a shape mismatch numpy refuses
+            caught.append(i)
+    assert caught, f"no pin catches the planted slip '{mutant}'"
