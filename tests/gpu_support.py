@@ -69,15 +69,3 @@ def assert_close(Y, ref, what: str, tol: float = TOL):
     err = O.max_scaled_error(Y, ref)
     assert err <= tol, f"{what}: max scaled error {err:.3e} > {tol}"
     return err
-
-
-def sample_rows(n: int, seg: dict, k: int = 48, seed: int = 0):
-    """Rows for full-size checks: random rows plus both ends of every
-    segment and of the base-only block."""
-    g = np.random.default_rng(seed)
-    rows = set(g.choice(n, size=min(k, n), replace=False).tolist())
-    perm = seg["perm"]
-    for j in list(seg["seg_off"][:-1]) + [s - 1 for s in seg["seg_off"][1:]] + [0, n - 1, seg["n_act"]]:
-        if 0 <= j < n:
-            rows.add(int(perm[j]))
-    return sorted(rows)
