@@ -63,6 +63,10 @@ def parse_args():
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of from a HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time only --workload (by default the other workloads where a target is judged are timed "
+                         "too and reported under \"configs\")")
+    ap.add_argument("--config-steps", type=int, default=10, help="timed steps of each of the other workloads")
     ap.add_argument("--separate-build", action="store_true",
                     help="run each step as two library calls (build_segments, then apply) instead of forward")
     ap.add_argument("--copy-only", action="store_true", help="only run the HBM copy calibration kernel")
@@ -257,7 +261,7 @@ def compare_baselines(M, torch, w, pool, X, W0s, R, seg_ws, Y, work, variant, it
     the same outputs, max_rank work per row)."""
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
 
-    def timed(fn):
+    def timed(fn, iters=iters):
         for i in range(min(iters, 2 * R)):
             fn(i)
         torch.cuda.synchronize()
@@ -300,6 +304,24 @@ def compare_baselines(M, torch, w, pool, X, W0s, R, seg_ws, Y, work, variant, it
 
     t_serial = timed(per_group)
 
+    # per-request serial application (wiblog article, baseline methods):
+    # every request through its own layer call (segment build and layer for
+    # its rows alone); its output stays in the request's own buffer
+    reqs = []
+    for rows in synth.request_rows(w):
+        r = torch.from_numpy(rows).cuda()
+        reqs.append((X.index_select(0, r).contiguous(), torch.from_numpy(ids[rows].astype(np.int32)).cuda(),
+                     torch.empty(M.segments_bytes(len(rows)) // 4, dtype=torch.int32, device="cuda"),
+                     torch.empty((len(rows), w.dout), dtype=torch.bfloat16, device="cuda"),
+                     M.new_work(pool, len(rows))))
+
+    def per_request(i):
+        p = i % R
+        for xr, ir, sr, yr, wr in reqs:
+            M.forward(pool, p, xr, W0s[p], ir, seg_ws=sr, Y=yr, work=wr)
+
+    t_per_request = timed(per_request, iters=max(3, min(iters, 3000 // max(len(reqs), 1))))
+
     # every adapter padded to the largest rank with zero factors
     rmax = max(w.ranks.values())
     n_pages = len(w.ranks) * rmax * R
@@ -324,6 +346,7 @@ def compare_baselines(M, torch, w, pool, X, W0s, R, seg_ws, Y, work, variant, it
     del padded
     return {"grouped_step_us": round(t_grouped, 3),
             "per_group_launches_us": round(t_serial, 3), "groups": len(groups),
+            "per_request_serial_us": round(t_per_request, 3), "requests": len(reqs),
             "padded_to_max_rank_us": round(t_padded, 3), "max_rank": rmax,
             "timing": f"torch events on the launch stream around {iters} eager iterations, same W0 rotation"}
 
@@ -397,32 +420,55 @@ def compare_paging(M, torch, w, pool, step_fn, spare_id, R, iters=20):
 
 
 def cpu_baseline(w, seconds):
-    """The oracle as it stands, in fp32, on this host: per-row loop over the
-    workload's rows (projection 0), repeated until `seconds` have passed."""
+    """The oracle as it stands, in fp32, on this host: the per-row loop over
+    the workload's rows (projection 0).  Three runs with the BLAS library's
+    own thread count and three with one thread, each about seconds / 6 long;
+    the medians are reported (tokens/s = rows done / time)."""
     import oracle as O
+    blas = {}
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = {"internal_api": info[0].get("internal_api"), "version": info[0].get("version"),
+                "threading_layer": info[0].get("threading_layer")} if info else {}
     except Exception:
+        threadpool_limits = None
         threads = os.cpu_count() or 1
     X = O.widen_bf16(w.x_bits(), np.float32)
     W0 = O.widen_bf16(w.w0_bits(0), np.float32)
     ad = {a: (float(w.scales[a]), O.widen_bf16(w.down_bits(a, 0), np.float32),
               O.widen_bf16(w.up_bits(a, 0), np.float32)) for a in w.adapter_ids()}
-    rows_done, t0 = 0, time.perf_counter()
     block = min(w.n, 64)
-    start = 0
-    while True:
-        rows = [(start + i) % w.n for i in range(block)]
-        O.linear(X, W0, w.row_adapter, ad, w.max_adapters, rows=rows, dtype=np.float32)
-        rows_done += block
-        start = (start + block) % w.n
-        el = time.perf_counter() - t0
-        if el >= seconds and rows_done >= min(w.n, 64):
-            break
-    return {"value": rows_done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{rows_done} rows of the {w.name} batch (projection 0), per-row fp32 numpy loop "
-                      f"of the oracle, {el:.1f} s on {os.cpu_count()} host cores"}
+
+    def run(budget):
+        rows_done, start, t0 = 0, 0, time.perf_counter()
+        while True:
+            rows = [(start + i) % w.n for i in range(block)]
+            O.linear(X, W0, w.row_adapter, ad, w.max_adapters, rows=rows, dtype=np.float32)
+            rows_done += block
+            start = (start + block) % w.n
+            el = time.perf_counter() - t0
+            if el >= budget and rows_done >= block:
+                return rows_done, el
+
+    per = seconds / 6
+    full = [run(per) for _ in range(3)]
+    single = []
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1, user_api="blas"):
+            single = [run(per) for _ in range(3)]
+    rate = lambda runs: float(np.median([r / el for r, el in runs]))
+    rows_total = sum(r for r, _ in full)
+    out = {"value": rate(full), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"3 runs of about {per:.1f} s ({rows_total} rows in all) of the {w.name} batch "
+                     f"(projection 0), per-row fp32 numpy loop of the oracle, median; "
+                     f"{os.cpu_count()} host cores, BLAS with {threads} threads",
+           "runs_tokens_per_s": [round(r / el, 1) for r, el in full], "blas": blas}
+    if single:
+        out["value_1thread"] = rate(single)
+        out["runs_1thread_tokens_per_s"] = [round(r / el, 1) for r, el in single]
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -430,47 +476,42 @@ def cpu_baseline(w, seconds):
 # ---------------------------------------------------------------------------
 
 def copy_calibration(M, torch, gib=1.0, reps=10):
+    """Achievable HBM rates: the library's streaming copy (1 GiB read + 1 GiB
+    written per launch) and its streaming read (1 GiB read)."""
     nb = int(gib * 2 ** 30)
     src = torch.empty(nb // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
-    M.hbm_copy(dst, src)
-    torch.cuda.synchronize()
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        M.hbm_copy(dst, src)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_copy = timed(lambda: M.hbm_copy(dst, src))
+    ms_read = timed(lambda: M.hbm_read(src, out))
     del src, dst
-    return {"bytes_moved": 2 * nb, "ms": ms, "gbps": 2 * nb / ms / 1e6}
+    return {"bytes_copied": 2 * nb, "copy_ms": ms_copy, "copy_gbps": 2 * nb / ms_copy / 1e6,
+            "bytes_read": nb, "read_ms": ms_read, "read_gbps": nb / ms_read / 1e6}
 
 
-def main():
-    args = parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no multi-GPU path; "
-              "the layer shards by adapter-affine routing or by dout columns with no exchange inside the "
-              "linear (see the design notes)", file=sys.stderr)
-        sys.exit(2)
-    import torch
-    import lora_serving_mlora_amd as M
-    M.lib()
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(2)
-    torch.cuda.set_device(0)
-
-    if args.copy_only:
-        cal = copy_calibration(M, torch)
-        print(json.dumps({"copy_calibration": cal}))
-        return
-
-    w = synth.NAMED[args.workload]()
+def run_workload(M, torch, name, steps, warmup, variant_arg="auto", rotate_bytes=1.0, separate_build=False,
+                 no_graph=False, spare_adapter=False):
+    """Builds the workload on the device and times K steps of it (segment
+    build + layer for one projection per step, from a captured HIP graph),
+    then the same steps eagerly with the library's launch timing.  Returns
+    the measured figures and the objects the comparisons reuse."""
+    w = synth.NAMED[name]()
     n = w.n
     # rotation: distinct projections of one pool, each with its own W0 copy
     per_proj = 2 * w.din * w.dout + 2 * sum(w.ranks.values()) * (w.din + w.dout)
-    R = max(1, math.ceil(args.rotate_bytes * 2 ** 30 / per_proj))
+    R = max(1, math.ceil(rotate_bytes * 2 ** 30 / per_proj))
     if w.n_proj > 1:
         R = w.n_proj   # the workload is a layer stack: rotate over its own projections
     print(f"[bench] workload {w.name}: n={n} din={w.din} dout={w.dout} adapters={len(w.ranks)} "
@@ -478,7 +519,7 @@ def main():
 
     n_pages = sum(w.ranks.values()) * R
     max_adapters = w.max_adapters
-    if args.compare_paging:
+    if spare_adapter:
         # one more id (no row uses it) and pages for a spare adapter
         max_adapters += 1
         n_pages += max(w.ranks.values()) * R
@@ -500,13 +541,13 @@ def main():
     ids = torch.from_numpy(w.row_adapter.astype(np.int32)).cuda()
     seg_ws = M.build_segments(pool, ids)
     Y = torch.empty((n, w.dout), dtype=torch.bfloat16, device="cuda")
-    variant, chunks = M.plan(pool, n, args.variant)
+    variant, chunks = M.plan(pool, n, variant_arg)
     torch.cuda.synchronize()
     print(f"[bench] plan: variant={variant} shrink_chunks={chunks}", file=sys.stderr, flush=True)
 
     work = M.new_work(pool, n)
 
-    if args.separate_build:
+    if separate_build:
         def step(i):
             p = i % R
             M.build_segments(pool, ids, seg_ws)
@@ -518,13 +559,13 @@ def main():
             p = i % R
             M.forward(pool, p, X, W0s[p], ids, seg_ws=seg_ws, Y=Y, work=work, variant=variant)
 
-    K, W = args.steps, args.warmup
+    K, W = steps, warmup
     for i in range(W):
         step(i)
     torch.cuda.synchronize()
 
     # ---- timed region: K steps replayed from one captured HIP graph
-    use_graph = not args.no_graph
+    use_graph = not no_graph
     graph = None
     if use_graph:
         try:
@@ -601,9 +642,59 @@ def main():
         ach, peak, unit = b / t_s / 1e9, HBM_PEAK_GBS, "GB/s"
     roofline = {"bound": "mfma" if mfma_bound else "hbm", "kernel": dom, "achieved": round(ach, 2),
                 "peak": peak, "unit": unit, "frac": round(ach / peak, 4),
-                "traffic": measured_traffic(dom, args.workload),
+                "traffic": measured_traffic(dom, name),
                 "algorithmic_bytes": b, "algorithmic_flops": f, "avg_us": round(timed[dom] * 1e3, 3),
                 "timing": timing}
+
+    ctx = dict(w=w, pool=pool, X=X, W0s=W0s, R=R, seg_ws=seg_ws, Y=Y, work=work, variant=variant, step=step,
+               max_adapters=max_adapters, spin=spin, spin_cycles=spin_cycles if spin is not None else 0, K=K,
+               use_graph=use_graph)
+    meas = dict(n=n, ms_per_step=ms_per_step, per_kernel_ms=per_kernel_ms, kernel_sum_ms=kernel_sum_ms,
+                roofline=roofline, chunks=chunks, variant=variant, R=R, use_graph=use_graph)
+    return meas, ctx
+
+
+def config_summary(name, meas):
+    """The figures of one workload for the bench line."""
+    n, t = meas["n"], meas["ms_per_step"] * 1e-3
+    out = {"tokens_per_s": round(n / t, 1), "us_per_step": round(t * 1e6, 3), "n_tokens": n,
+           "variant": meas["variant"], "launch": "hipgraph" if meas["use_graph"] else "eager",
+           "per_kernel_us": {k: (round(v * 1e3, 3) if v else None) for k, v in meas["per_kernel_ms"].items()},
+           "roofline": meas["roofline"]}
+    if name == "layer_stack":
+        # the step is one of the stack's 64 projections (all independent,
+        # one X): the stack takes 64 steps
+        out["stack_tokens_per_s"] = round(n / (64 * t), 1)
+        out["stack_us"] = round(64 * t * 1e6, 2)
+    return out
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no multi-GPU path; "
+              "the layer shards by adapter-affine routing or by dout columns with no exchange inside the "
+              "linear (see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import lora_serving_mlora_amd as M
+    M.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+
+    if args.copy_only:
+        cal = copy_calibration(M, torch)
+        print(json.dumps({"copy_calibration": cal}))
+        return
+
+    meas, ctx = run_workload(M, torch, args.workload, args.steps, args.warmup, args.variant, args.rotate_bytes,
+                             args.separate_build, args.no_graph, args.compare_paging)
+    w, pool, X, W0s, R = ctx["w"], ctx["pool"], ctx["X"], ctx["W0s"], ctx["R"]
+    seg_ws, Y, work, variant = ctx["seg_ws"], ctx["Y"], ctx["work"], ctx["variant"]
+    n, K, W = w.n, args.steps, args.warmup
+    ms_per_step = meas["ms_per_step"]
 
     yardstick = None
     if args.yardstick:
@@ -614,8 +705,8 @@ def main():
         for i in range(min(K, 2 * R)):
             F.linear(X, W0s[i % R])
         torch.cuda.synchronize()
-        if spin is not None:
-            spin(spin_cycles)
+        if ctx["spin"] is not None:
+            ctx["spin"](ctx["spin_cycles"])
         ev[0].record()
         for i in range(K):
             F.linear(X, W0s[i % R])
@@ -624,21 +715,19 @@ def main():
         yardstick = round(ev[0].elapsed_time(ev[1]) / K * 1e3, 3)
 
     tokens_per_s = n / (ms_per_step * 1e-3)
-    cal = copy_calibration(M, torch)
     result = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": W, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "n_tokens": n, "din": w.din, "dout": w.dout,
                    "adapters": len(w.ranks), "ranks": sorted(set(w.ranks.values())),
-                   "variant": variant, "shrink_chunks": chunks, "rotation_projections": R,
+                   "variant": variant, "shrink_chunks": meas["chunks"], "rotation_projections": R,
                    "step": "build_segments+apply" if args.separate_build else "forward",
-                   "launch": "hipgraph" if use_graph else "eager", "parallelism": "single-gpu"},
-        "roofline": roofline,
-        "per_kernel_us": {k: (round(v * 1e3, 3) if v else None) for k, v in per_kernel_ms.items()},
-        "kernel_sum_us": round(kernel_sum_ms * 1e3, 3),
+                   "launch": "hipgraph" if meas["use_graph"] else "eager", "parallelism": "single-gpu"},
+        "roofline": meas["roofline"],
+        "per_kernel_us": {k: (round(v * 1e3, 3) if v else None) for k, v in meas["per_kernel_ms"].items()},
+        "kernel_sum_us": round(meas["kernel_sum_ms"] * 1e3, 3),
         "gpu_name": torch.cuda.get_device_name(0),
-        "hbm_copy_gbps": round(cal["gbps"], 1),
     }
     if yardstick is not None:
         result["vendor_gemm_us"] = yardstick
@@ -648,7 +737,24 @@ def main():
         result["merged_comparison"] = compare_merged(M, torch, w, pool, X, W0s, R, seg_ws, Y, work, variant)
     if args.compare_paging:
         result["paging_comparison"] = (None if w.n_proj > 1 else
-                                       compare_paging(M, torch, w, pool, step, max_adapters - 1, R))
+                                       compare_paging(M, torch, w, pool, ctx["step"], ctx["max_adapters"] - 1, R))
+    del ctx, pool, X, W0s, seg_ws, Y, work
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        # the other workloads where a target is judged, each timed the same
+        # way (its own seeded inputs, its own rotation) with fewer steps
+        configs = {}
+        for other in ("decode_frag", "prefill", "layer_stack"):
+            if other == args.workload:
+                continue
+            m2, c2 = run_workload(M, torch, other, max(3, min(K, args.config_steps)), min(W, 3))
+            configs[other] = config_summary(other, m2)
+            del c2
+            torch.cuda.empty_cache()
+        result["configs"] = configs
+    cal = copy_calibration(M, torch)
+    result["hbm_copy_gbps"] = round(cal["copy_gbps"], 1)
+    result["hbm_read_gbps"] = round(cal["read_gbps"], 1)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result))

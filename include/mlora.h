@@ -367,11 +367,17 @@ mlora_status mlora_merge(const mlora_pool* pool, int32_t adapter_id, int32_t pro
                          void* stream);
 
 /* ---------------------------------------------------------------------------
- * Measurement helper: a plain streaming copy (dst = src, `bytes` a multiple
+ * Measurement helpers: a plain streaming copy (dst = src, `bytes` a multiple
  * of 16, both 16-byte aligned), used to calibrate achievable HBM bandwidth
  * and hardware byte counters against a kernel of known traffic.
  * ------------------------------------------------------------------------- */
 mlora_status mlora_hbm_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+/* The read half of the same measurement: streams `bytes` from src (a
+ * multiple of 16, 16-byte aligned) and XORs every 32-bit word read into
+ * *out (device uint32, caller-owned; the caller clears it first), so the
+ * achievable streaming read rate can be measured.  Errors: EINVAL, EHIP. */
+mlora_status mlora_hbm_read(const void* src, size_t bytes, uint32_t* out, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Launch timing, a measurement aid that changes no result.

@@ -1043,6 +1043,13 @@ mlora_status mlora_hbm_copy(void* dst, const void* src, size_t bytes, void* stre
   return hip_check(mlora::launch_hbm_copy(dst, src, bytes, as_stream(stream)), "copy launch");
 }
 
+mlora_status mlora_hbm_read(const void* src, size_t bytes, uint32_t* out, void* stream) {
+  g_err.clear();
+  if (!src || !out || bytes % 16 != 0 || !aligned16(src))
+    return fail(MLORA_EINVAL, "read needs a non-NULL 16-byte aligned source, a multiple of 16 bytes and an output word");
+  return hip_check(mlora::launch_hbm_read(src, bytes, out, as_stream(stream)), "read launch");
+}
+
 }  // extern "C"
 
 namespace mlora {

@@ -770,11 +770,12 @@ __device__ __forceinline__ int32_t uniform_load(const int32_t* p, size_t i) {
   return ((const __attribute__((address_space(4))) int32_t*)p)[i];
 }
 
-template <int TM, int TN>
-__device__ __forceinline__ void ring_lora_epilogue(const RingCtx& c, int m0, int n0, int M, int N, const PoolView& pv,
+// The wave owns MI x NJ blocks of 32 x 32 outputs: rows wr + 32 i, columns
+// wc + 32 j (wr, wc absolute).
+template <int MI, int NJ>
+__device__ __forceinline__ void ring_lora_epilogue(int wr, int wc, int M, int N, const PoolView& pv,
                                                    const int32_t* __restrict__ row_key, const LoraOperands& lo,
-                                                   floatx16 (&acc)[TM / 64][TN / 64], int (&key)[TM / 64]) {
-  constexpr int MI = TM / 64, NJ = TN / 64;
+                                                   floatx16 (&acc)[MI][NJ], int (&key)[MI]) {
   // kBad: the pseudo adapter of rows with an invalid id, walked after the
   // real ones; its step multiplies NaN into those rows' accumulators
   constexpr int kNone = 0x7fffffff, kBad = 0x7ffffffe, kBatch = 4;
@@ -783,7 +784,7 @@ __device__ __forceinline__ void ring_lora_epilogue(const RingCtx& c, int m0, int
   int trow[MI];  // element offset of the lane's t piece (rows past M read row M-1: never stored)
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
-    const int r = m0 + c.wm * (TM / 2) + i * 32 + (lane & 31);
+    const int r = wr + i * 32 + (lane & 31);
     key[i] = r < M ? row_key[r] : -1;
     if (key[i] == -2) key[i] = kBad;
     pend[i] = (key[i] >= 0) ? key[i] : kNone;
@@ -791,7 +792,7 @@ __device__ __forceinline__ void ring_lora_epilogue(const RingCtx& c, int m0, int
   }
   int col[NJ];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) col[j] = min(n0 + c.wn * (TN / 2) + j * 32 + (lane & 31), N - 1);
+  for (int j = 0; j < NJ; ++j) col[j] = min(wc + j * 32 + (lane & 31), N - 1);
   // the wave's next adapter (smallest pending key), taken off the pending set
   auto next_key = [&]() {
     int a = pend[0];
@@ -1008,7 +1009,7 @@ __device__ __forceinline__ void gemm_ring_body(
   int key[MI];  // low-rank epilogue: the keys of the lane's A-fragment rows
   if constexpr (LORA) {
     __builtin_amdgcn_sched_barrier(0);
-    ring_lora_epilogue<TM, TN>(c, m0, n0, M, N, pv, row_key, lo, acc, key);
+    ring_lora_epilogue<MI, NJ>(m0 + c.wm * (TM / 2), n0 + c.wn * (TN / 2), M, N, pv, row_key, lo, acc, key);
   }
 
   // C layout of a 32x32 tile: lane l holds column l%32, rows 8*(v/4) + 4*(l/32) + v%4.

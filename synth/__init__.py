@@ -211,7 +211,8 @@ def prefill_hetero() -> Workload:
         name="prefill_4096tok_4096x11008_r8-16-64", seed=seed, din=4096, dout=11008, n_proj=1,
         row_adapter=ids, ranks=ranks, scales={a: 2.0 for a in ranks},
         max_adapters=6, max_rank=64,
-        extra=dict(lengths=lengths, request_adapter=[int(a) for a in req_ad]),
+        extra=dict(lengths=lengths, request_adapter=[int(a) for a in req_ad],
+                   request=np.array(order, dtype=np.int32)),
         **_DECODE_STD)
 
 
@@ -233,10 +234,11 @@ def layer_stack() -> Workload:
     n = ids.shape[0]
     none_rows = g.choice(n, size=round(0.05 * n), replace=False)
     ids[none_rows] = NONE
+    request = np.concatenate([np.repeat(np.arange(4), 96), np.arange(4, 132)]).astype(np.int32)
     return Workload(
         name="layerstack_64proj_100ad_512tok", seed=seed, din=4096, dout=4096, n_proj=64,
         row_adapter=ids, ranks={a: 16 for a in range(100)}, scales={a: 2.0 for a in range(100)},
-        max_adapters=100, max_rank=16, **_DECODE_STD)
+        max_adapters=100, max_rank=16, extra=dict(request=request), **_DECODE_STD)
 
 
 NAMED: Dict[str, Callable[[], Workload]] = {
@@ -247,6 +249,16 @@ NAMED: Dict[str, Callable[[], Workload]] = {
     "layer_stack": layer_stack,
 }
 ORDER = ["worked_example", "decode_3", "decode_frag", "prefill", "layer_stack"]
+
+
+def request_rows(w: Workload) -> List[np.ndarray]:
+    """The rows of each request of the batch, in request order (each request
+    in its original row order).  Workloads that record no request map
+    (decode steps, custom batches) have one token per request."""
+    req = w.extra.get("request")
+    if req is None:
+        return [np.array([k]) for k in range(w.n)]
+    return [np.flatnonzero(req == r) for r in range(int(req.max()) + 1)]
 
 
 def custom(name: str, seed: int, din: int, dout: int, row_adapter, ranks: Dict[int, int],

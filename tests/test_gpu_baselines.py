@@ -69,3 +69,35 @@ def test_padded_pool_matches_oracle(M):
         Y = M.apply(pool, 0, Xd, Wd, seg, variant=variant)
         torch.cuda.synchronize()
         assert_close(dev_to_f64(Y), ref, f"padded {variant}")
+
+
+@pytest.mark.parametrize("name,n_rows", [("decode_3", None), ("prefill", 1200)])
+def test_per_request_serial_matches_oracle(M, name, n_rows):
+    """The per-request serial baseline (wiblog article, baseline methods):
+    every request through its own layer call on its own rows.  Each
+    request's output equals the oracle's rows of that request.  (The
+    prefill case keeps its first requests up to about n_rows rows, so the
+    fp64 oracle stays quick.)"""
+    torch = torch_cuda()
+    w = synth.NAMED[name]()
+    reqs = synth.request_rows(w)
+    if n_rows is not None:
+        keep, total = [], 0
+        for rows in reqs:
+            if total >= n_rows:
+                break
+            keep.append(rows)
+            total += len(rows)
+        reqs = keep
+    pool = make_pool(M, w)
+    X, W0 = w.x_bits(), w.w0_bits()
+    Wd = to_dev_bf16(W0)
+    sel = np.concatenate(reqs)
+    ref = O.linear(O.widen_bf16(X), O.widen_bf16(W0), w.row_adapter, oracle_adapters(w), w.max_adapters,
+                   rows=sel.tolist(), base_batched=True)
+    at = {int(k): i for i, k in enumerate(sel)}
+    for r, rows in enumerate(reqs):
+        say(f"per-request {name} request={r} rows={len(rows)}")
+        Y, _ = M.forward(pool, 0, to_dev_bf16(X[rows]), Wd, ids_dev(w.row_adapter[rows]))
+        torch.cuda.synchronize()
+        assert_close(dev_to_f64(Y), ref[[at[int(k)] for k in rows]], f"request {r}")

@@ -28,8 +28,10 @@ GEMM_SHAPES = [(1, 4, 4), (4, 4, 4), (3, 5, 7), (16, 64, 16), (17, 72, 33), (32,
                (256, 4096, 4096), (513, 264, 392),
                # medium batches on the K-split kernel, incl. K tails and unaligned K
                (65, 4096, 4096), (129, 520, 4104), (700, 1000, 2000), (100, 20, 4096), (512, 4096, 4096),
-               # 256x256 LDS-DMA kernel (M*N >= 2048^2): full tiles, ragged M and N, odd K-tile count
-               (2048, 1024, 2048), (2100, 640, 2200), (1030, 4096, 4104)]
+               # large products: 128x128 co-resident tiles where 256x256 tiles would underfill the chip
+               (2048, 1024, 2048), (2100, 640, 2200), (1030, 4096, 4104),
+               # 256x256 tiles: full tiles, ragged M and N, the shortest K (two stages)
+               (4096, 256, 4096), (4000, 384, 4000), (4096, 128, 4096)]
 
 
 @pytest.mark.parametrize("m,k,n", GEMM_SHAPES)
@@ -74,6 +76,8 @@ SMALL = [
     (8, 512, 1000, 700, {i: (16 if i % 3 else 64) for i in range(40)}),
     (9, 1000, 520, 260, {0: 16, 1: 3, 2: 64}),        # din not a multiple of 32: vector-ALU shrink
     (10, 520, 1000, 13, {0: 16, 1: 5, 2: 9}),          # ranks <= 16, din and dout <= 4096: fused fast form
+    # large batch on the 256x256 GEMM with the low-rank epilogue, ragged rows and columns
+    (11, 512, 4000, 4000, {0: 8, 1: 16, 2: 64, 3: 1, 4: 33}),
 ]
 
 

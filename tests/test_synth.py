@@ -69,3 +69,23 @@ def test_value_distributions():
     assert abs(w.w0_f32().std() - 0.02) < 1e-4
     assert abs(w.down_f32(0).std() - 1 / 64) < 5e-4
     assert abs(w.up_f32(1).std() - 0.02) < 5e-4
+
+
+def test_request_rows_follow_the_workload_recipes():
+    """Requests of the prefill batch: the recipe's lengths, each request's
+    rows on its adapter or base-only, round-robin interleaving; the layer
+    stack: 4 contiguous prefill requests of 96 rows, then one decode token
+    each; decode batches: one token per request."""
+    w = synth.prefill_hetero()
+    rr = synth.request_rows(w)
+    assert [len(r) for r in rr] == w.extra["lengths"]
+    for r, rows in enumerate(rr):
+        a = w.extra["request_adapter"][r]
+        assert set(w.row_adapter[rows].tolist()) <= {a, -1}
+    assert [int(np.flatnonzero([k in rows for rows in rr])[0]) for k in range(8)] == list(range(8))
+    ls = synth.layer_stack()
+    rr = synth.request_rows(ls)
+    assert len(rr) == 132 and [len(r) for r in rr[:5]] == [96, 96, 96, 96, 1]
+    assert rr[0].tolist() == list(range(96)) and rr[4].tolist() == [384]
+    assert all(len(r) == 1 for r in synth.request_rows(synth.decode_fragmented()))
+    assert sorted(np.concatenate(rr).tolist()) == list(range(ls.n))
