@@ -76,6 +76,8 @@ SMALL = [
     (8, 512, 1000, 700, {i: (16 if i % 3 else 64) for i in range(40)}),
     (9, 1000, 520, 260, {0: 16, 1: 3, 2: 64}),        # din not a multiple of 32: vector-ALU shrink
     (10, 520, 1000, 13, {0: 16, 1: 5, 2: 9}),          # ranks <= 16, din and dout <= 4096: fused fast form
+]
+LARGE = [
     # large batch on the 256x256 GEMM with the low-rank epilogue, ragged rows and columns
     (11, 512, 4000, 4000, {0: 8, 1: 16, 2: 64, 3: 1, 4: 33}),
 ]
@@ -211,7 +213,7 @@ def test_apply_layer_stack(M):
     check_apply(M, synth.layer_stack(), projs=(0, 37, 63))
 
 
-@pytest.mark.parametrize("case", SMALL, ids=lambda c: str(c[0]))
+@pytest.mark.parametrize("case", SMALL + LARGE, ids=lambda c: str(c[0]))
 def test_apply_small(M, case):
     check_apply(M, small_workload(*case))
 
