@@ -348,6 +348,28 @@ mlora_status mlora_forward(const mlora_pool* pool, int32_t proj, const uint16_t*
                            const int32_t* row_adapter, void* seg_ws, uint16_t* Y, int32_t n_rows, void* work,
                            size_t work_bytes, int32_t variant, void* stream);
 
+/* mlora_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and results as mlora_forward, with the `work` buffer
+ * replaced by scratch the library owns, a static device array of
+ * MLORA_STATIC_SCRATCH_BYTES on each GPU it runs on (held until the process
+ * ends).  The call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine); the caller still passes X, W0, row_adapter, seg_ws and
+ * Y as for mlora_forward.  Every call on a GPU uses that GPU's one scratch
+ * array, whose contents stay from the last call: calls that overlap on one
+ * GPU (concurrent streams or host threads) race and must be ordered by the
+ * caller.  Errors: those of mlora_forward, and MLORA_EINVAL for a batch
+ * whose launch plan needs more scratch than MLORA_STATIC_SCRATCH_BYTES
+ * (nothing is launched then).  The per-row plan of 256 rows at dout = 4096
+ * needs 16.1 MiB (512 rows, which split K in two, about the same); the
+ * split plan of 4096 rows over six adapters of rank <= 64 at dout = 11008
+ * needs 17 MB; pools with many adapter slots of large rank need more (the
+ * split plan's per-adapter Up blocks) and take mlora_forward. */
+#define MLORA_STATIC_SCRATCH_BYTES (20u << 20)
+mlora_status mlora_forward_static(const mlora_pool* pool, int32_t proj, const uint16_t* X, const uint16_t* W0,
+                                  const int32_t* row_adapter, void* seg_ws, uint16_t* Y, int32_t n_rows,
+                                  int32_t variant, void* stream);
+
 /* ---------------------------------------------------------------------------
  * The merged alternative (M031 card, section 04: W_merged = W_base + scale *
  * Up Down serves that one adapter with a plain GEMM; airsota card, section

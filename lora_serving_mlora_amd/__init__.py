@@ -23,7 +23,7 @@ import numpy as np
 __all__ = [
     "MloraError", "lib", "Pool", "build_segments", "segments_header", "read_segments",
     "base_gemm", "shrink", "shrink_max_chunks", "expand", "fused", "shrink_rows", "gemm_lora", "new_work", "rows_t", "apply", "forward", "plan", "work_bytes",
-    "merge", "hbm_copy", "hbm_read", "timing_arm", "timing_read", "VARIANTS", "ITEM_ROWS", "TILE_ROWS", "MAX_ROWS", "MAX_RANK", "SEG", "EXPORTS", "LIB_PATH",
+    "forward_static", "STATIC_SCRATCH_BYTES", "merge", "hbm_copy", "hbm_read", "timing_arm", "timing_read", "VARIANTS", "ITEM_ROWS", "TILE_ROWS", "MAX_ROWS", "MAX_RANK", "SEG", "EXPORTS", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmlora.so")
@@ -79,6 +79,8 @@ EXPORTS = {
                                    _sz, _i32, _c_void_p]),
     "mlora_forward": (ctypes.c_int, [_c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32,
                                      _c_void_p, _sz, _i32, _c_void_p]),
+    "mlora_forward_static": (ctypes.c_int, [_c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                            _i32, _i32, _c_void_p]),
     "mlora_merge": (ctypes.c_int, [_c_void_p, _i32, _i32, _c_void_p, _f32, _c_void_p]),
     "mlora_hbm_copy": (ctypes.c_int, [_c_void_p, _c_void_p, _sz, _c_void_p]),
     "mlora_hbm_read": (ctypes.c_int, [_c_void_p, _sz, _c_void_p, _c_void_p]),
@@ -433,6 +435,35 @@ def forward(pool: Pool, proj: int, X, W0, row_adapter, seg_ws=None, Y=None, work
                                _ptr(work), work.numel() * work.element_size(), VARIANTS[variant], _stream()),
            "mlora_forward")
     return Y, seg_ws
+
+
+def forward_static(pool: Pool, proj: int, X, W0, row_adapter, seg_ws=None, Y=None, variant: str = "auto"):
+    """forward() with the library's static scratch in place of a work buffer
+    (the call allocates no device memory).  Returns (Y, seg_ws)."""
+    torch = _torch()
+    n = X.shape[0]
+    _rows_check(pool, X, n)
+    _bf16_dev(W0, "W0")
+    if tuple(W0.shape) != (pool.dout, pool.din):
+        raise ValueError(f"W0 must be [{pool.dout}][{pool.din}]")
+    if row_adapter.dtype != torch.int32 or not row_adapter.is_cuda or not row_adapter.is_contiguous():
+        raise TypeError("row_adapter must be a contiguous int32 CUDA tensor")
+    if row_adapter.shape[0] != n:
+        raise ValueError("row_adapter must have one id per row of X")
+    nb = segments_bytes(n)
+    if seg_ws is None:
+        seg_ws = torch.empty(nb // 4, dtype=torch.int32, device=X.device)
+    elif seg_ws.numel() * seg_ws.element_size() < nb:
+        raise ValueError("seg_ws too small")
+    if Y is None:
+        Y = torch.empty((n, pool.dout), dtype=torch.bfloat16, device=X.device)
+    _bf16_dev(Y, "Y")
+    _check(lib().mlora_forward_static(pool.handle, proj, _ptr(X), _ptr(W0), _ptr(row_adapter), _ptr(seg_ws), _ptr(Y),
+                                      n, VARIANTS[variant], _stream()), "mlora_forward_static")
+    return Y, seg_ws
+
+
+STATIC_SCRATCH_BYTES = 20 << 20
 
 
 def merge(pool: Pool, adapter_id: int, proj: int, W0, sign: float = 1.0):

@@ -35,6 +35,37 @@ mlora_status fail(mlora_status s, const char* fmt, ...) {
   return s;
 }
 
+// Scratch of the entry point that allocates nothing (mlora_forward_static):
+// device memory the library owns for the life of the process, one copy per
+// GPU (each device holds its own at its own address), shared by every call
+// on that GPU.  In host code `scratch` names a host-side stand-in, not the
+// device memory: its device address comes from hipGetSymbolAddress, taken
+// once per device with that device current.
+constexpr size_t kStaticScratchBytes = size_t(20) << 20;
+constexpr int kMaxDevices = 64;
+static_assert(kStaticScratchBytes == MLORA_STATIC_SCRATCH_BYTES, "the header states the scratch size");
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the device address of `scratch` on device `dev` (the current device)
+mlora_status static_scratch(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(MLORA_EINVAL, "device %d outside [0, %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return fail(MLORA_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLORA_OK;
+}
+
 // armed launch timing: launch i gets events ev[2i] (kernel start) and
 // ev[2i+1] (kernel end)
 constexpr int kTimingMax = 2048;
@@ -859,16 +890,27 @@ int32_t auto_variant(const mlora_pool* p, int n) {
 }
 }  // namespace
 
-size_t mlora_work_bytes(const mlora_pool* p, int32_t n) {
-  if (!p || n < 0) return 0;
-  // the larger of the split variant's partial t and the per-row path's layout
+namespace {
+// Bytes of `work` the launch plan of `variant` (AUTO resolved) uses for n
+// rows: ROWS its T region and split-K partials; FUSED the same partials
+// (its base GEMM splits K through them when the buffer holds them, else it
+// takes the one-pass form); SPLIT its shrink slices, plus the epilogue's
+// operands for large batches, and the split-K partials of its base GEMM.
+size_t plan_work_bytes(const mlora_pool* p, int n, int variant) {
+  if (n <= 0) return 0;
+  const size_t rows = n <= kRowsMax ? rows_work_bytes(p, n) : 0;
+  if (variant != MLORA_VARIANT_SPLIT) return rows;
   const int chunks = std::max(split_chunks(p, n), 1);
-  // split: the shrink's partial t, then t per row for a GEMM that adds the
-  // low-rank term in its epilogue (large batches)
   size_t b = align256((size_t)chunks * n * p->d.max_rank * sizeof(float));
   if (big_epilogue_fits(p, n)) b += lora_operands_bytes(p, n);
-  if (n <= kRowsMax) b = std::max(b, rows_work_bytes(p, n));
-  return b;
+  return std::max(b, rows);
+}
+}  // namespace
+
+size_t mlora_work_bytes(const mlora_pool* p, int32_t n) {
+  if (!p || n < 0) return 0;
+  // the largest need among the variants (so one buffer serves them all)
+  return std::max(plan_work_bytes(p, n, MLORA_VARIANT_SPLIT), plan_work_bytes(p, n, MLORA_VARIANT_ROWS));
 }
 
 mlora_status mlora_plan(const mlora_pool* p, int32_t n, int32_t variant, int32_t* out_variant, int32_t* out_chunks) {
@@ -901,7 +943,7 @@ mlora_status mlora_apply(const mlora_pool* p, int32_t proj, const uint16_t* X, c
   const int32_t* ws = static_cast<const int32_t*>(seg_ws);
   if (variant == MLORA_VARIANT_AUTO) variant = auto_variant(p, n);
   if (variant == MLORA_VARIANT_SPLIT || variant == MLORA_VARIANT_ROWS) {
-    const size_t need = mlora_work_bytes(p, n);
+    const size_t need = plan_work_bytes(p, n, variant);
     if (!work || work_bytes < need) return fail(MLORA_EINVAL, "work: %zu bytes given, %zu needed", work_bytes, need);
     if (!aligned16(work)) return fail(MLORA_EINVAL, "work must be 16-byte aligned");
   }
@@ -965,7 +1007,7 @@ mlora_status mlora_forward(const mlora_pool* p, int32_t proj, const uint16_t* X,
   const int32_t resolved = variant == MLORA_VARIANT_AUTO ? auto_variant(p, n) : variant;
   if (n > 0 && (resolved == MLORA_VARIANT_SPLIT || resolved == MLORA_VARIANT_ROWS)) {
     // the work checks of mlora_apply, before anything is launched
-    const size_t need = mlora_work_bytes(p, n);
+    const size_t need = plan_work_bytes(p, n, resolved);
     if (!work || work_bytes < need) return fail(MLORA_EINVAL, "work: %zu bytes given, %zu needed", work_bytes, need);
     if (!aligned16(work)) return fail(MLORA_EINVAL, "work must be 16-byte aligned");
     if (resolved == MLORA_VARIANT_ROWS && (st = check_rows_work(p, n, work, work_bytes)) != MLORA_OK) return st;
@@ -978,6 +1020,23 @@ mlora_status mlora_forward(const mlora_pool* p, int32_t proj, const uint16_t* X,
   }
   if ((st = mlora_build_segments(p, row_adapter, n, seg_ws, stream)) != MLORA_OK) return st;
   return mlora_apply(p, proj, X, W0, seg_ws, Y, n, work, work_bytes, variant, stream);
+}
+
+mlora_status mlora_forward_static(const mlora_pool* p, int32_t proj, const uint16_t* X, const uint16_t* W0,
+                                  const int32_t* row_adapter, void* seg_ws, uint16_t* Y, int32_t n, int32_t variant,
+                                  void* stream) {
+  g_err.clear();
+  mlora_status st = check_pool(p);
+  if (st != MLORA_OK) return st;
+  if (n < 0 || n > MLORA_MAX_ROWS) return fail(MLORA_EINVAL, "n_rows %d outside [0, %d]", n, MLORA_MAX_ROWS);
+  if (variant < MLORA_VARIANT_AUTO || variant > MLORA_VARIANT_ROWS) return fail(MLORA_EINVAL, "unknown variant %d", variant);
+  const size_t need = plan_work_bytes(p, n, variant == MLORA_VARIANT_AUTO ? auto_variant(p, n) : variant);
+  if (need > kStaticScratchBytes)
+    return fail(MLORA_EINVAL, "a batch of %d rows needs %zu bytes of scratch; the static scratch holds %zu "
+                "(use mlora_forward with a work buffer)", n, need, kStaticScratchBytes);
+  void* work = nullptr;
+  if ((st = static_scratch(p->device, &work)) != MLORA_OK) return st;
+  return mlora_forward(p, proj, X, W0, row_adapter, seg_ws, Y, n, work, kStaticScratchBytes, variant, stream);
 }
 
 mlora_status mlora_timing_arm(int32_t n_launches) {
