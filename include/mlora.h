@@ -336,7 +336,7 @@ mlora_status mlora_apply(const mlora_pool* pool, int32_t proj, const uint16_t* X
  *   seg_ws: device, mlora_segments_bytes(n_rows) bytes, 8-byte aligned;
  *   the other arguments as for mlora_apply.
  * For the per-row plan (16-byte aligned operands) at decode sizes
- * (n_rows <= 64, din a multiple of 2048 up to 4096) and medium ones (65 ..
+ * (n_rows <= 64, din a multiple of 128 from 512 to 16384) and medium ones (65 ..
  * 1024 rows, din a multiple of 128) the segment build runs in a workgroup
  * of the base GEMM's launch, whose
  * other workgroups take each row's key from row_adapter and the resident

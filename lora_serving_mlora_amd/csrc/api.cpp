@@ -794,10 +794,10 @@ struct RowsWork {
   float* T;
   float* part;
 };
-// T region: room for the decode form's K-quarter partials of T as well, then
+// T region: room for the decode form's K-slice partials of T as well, then
 // the per-row descriptors
 size_t rows_t_bytes(const mlora_pool* p, int n) {
-  return align256((size_t)mlora::kRowsTParts * n * p->d.max_rank * sizeof(float) +
+  return align256((size_t)mlora::rows_t_slices(n) * n * p->d.max_rank * sizeof(float) +
                   (size_t)n * mlora::row_desc_words(p->d.max_rank) * sizeof(int32_t));
 }
 size_t rows_work_bytes(const mlora_pool* p, int n) {

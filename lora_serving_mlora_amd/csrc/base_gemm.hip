@@ -1147,22 +1147,41 @@ hipError_t launch_gemm(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M,
 //
 // Every workgroup reading all of X made X (L2-resident, but read 256 times)
 // cost as much as streaming W0 from HBM.  Here a workgroup owns 64 columns
-// and one quarter of K: its X slice (M x K/4) is brought into LDS once by
-// LDS DMA and shared by the 4 column-group waves, so each X byte is read by 64
-// workgroups instead of 256, while the 256 workgroups still cover the chip.
-// 8 GEMM waves = 4 column groups x 2 halves of the quarter; each wave issues
-// all 16 of its W0 loads at once.  The quarter's fp32 partial goes to `part`
-// and a second kernel (finish_part) sums the 4 partials in quarter order,
-// adds the low-rank term and writes Y: deterministic.  (Finishing in the last
-// workgroup of a column block behind an atomic counter cost more: the
-// device-scope release/acquire writes back and invalidates the L2s.)  The
-// per-row shrink of the batch rides along as extra workgroups of the launch:
-// independent work, and one launch less per step.
-// LDS: X slice [M][K/4] in 1 KiB blocks whose 16-byte chunks are XOR-swizzled
-// by (row & 15), so the 16 rows an MFMA fragment read touches hit 16
-// different chunk positions.
+// and one of S slices of K (at most 1024 deep, a whole number of 128-wide
+// units; S = 4 up to din 4096, then one slice per 1024): its X slice
+// (M x slice) is brought into LDS once by LDS DMA and shared by the 4
+// column-group waves, so each X byte is read by N/64 workgroups instead of
+// N/16, while 64 * S workgroups still cover the chip.  8 GEMM waves = 4
+// column groups x 2 halves of the slice (the halves take alternate 64-wide
+// segments); each wave issues all 16 of its W0 loads at once.  The slice's
+// fp32 partial goes to `part` and a second kernel (finish_part) sums the S
+// partials in slice order, adds the low-rank term and writes Y:
+// deterministic.  (Finishing in the last workgroup of a column block behind
+// an atomic counter cost more: the device-scope release/acquire writes back
+// and invalidates the L2s.)  The per-row shrink of the batch rides along as
+// extra work of the same workgroups: independent work, and one launch less
+// per step.
+// LDS: X slice [M][xs_stride] in 1 KiB blocks whose 16-byte chunks are
+// XOR-swizzled by (row & 15), so the 16 rows an MFMA fragment read touches
+// hit 16 different chunk positions.
 // ---------------------------------------------------------------------------
-constexpr int kDecCols = 64, kDecSplit = 4, kDecWaves = 8;
+constexpr int kDecCols = 64, kDecWaves = 8;
+constexpr int kDecMinSlices = 4, kDecMaxDepth = 1024, kDecUnit = 128;
+
+// Number of K slices of the decode form for din K (a multiple of kDecUnit,
+// at most kDecMaxSlices * kDecMaxDepth).
+int dec_slices(int K) {
+  const int s = (K + kDecMaxDepth - 1) / kDecMaxDepth;
+  return s > kDecMinSlices ? s : kDecMinSlices;
+}
+// Slice s of S over U units: units [U s / S, U (s + 1) / S), so slices differ
+// by at most one unit.
+__host__ __device__ __forceinline__ int dec_slice_unit(int U, int S, int s) { return (int)(((long)U * s) / S); }
+// LDS row stride of the X slice: the deepest slice rounded up to 1 KiB blocks.
+int dec_xs_stride(int K, int S) {
+  const int units = (K / kDecUnit + S - 1) / S;
+  return (units * kDecUnit + 511) / 512 * 512;
+}
 constexpr int kMidMaxSplit = 8;
 
 // Row r's key and its adapter's rank (0 for a key < 0) from the batch's
@@ -1185,20 +1204,19 @@ __device__ __forceinline__ KeyRank key_rank_from_ids(const int32_t* __restrict__
 template <int MB, bool IDS>
 __global__ __launch_bounds__(64 * kDecWaves) void gemm_decode(const uint16_t* __restrict__ X,
                                                              const uint16_t* __restrict__ W, int M, int K, int N,
-                                                             PoolView pv, int proj,
+                                                             int S, int xs_stride, PoolView pv, int proj,
                                                              const int32_t* __restrict__ row_key,
                                                              float* __restrict__ Tp, float* __restrict__ part,
                                                              int shrink, const int32_t* __restrict__ ids,
                                                              int32_t* __restrict__ seg_ws) {
   extern __shared__ __attribute__((aligned(16))) uint16_t dec_lds[];
-  if (IDS && (int)blockIdx.x == ((N + kDecCols - 1) / kDecCols) * kDecSplit) {
+  if (IDS && (int)blockIdx.x == ((N + kDecCols - 1) / kDecCols) * S) {
     int* scratch_lds = reinterpret_cast<int*>(dec_lds);  // 516 bytes of at least 4 KiB (the reduction area alone)
     seg_build_wave(ids, M, pv.rank, pv.max_adapters, seg_ws, scratch_lds, scratch_lds + 65);
     return;
   }
-  const int Kq = K / kDecSplit;
-  uint16_t* xs = dec_lds;                                               // [M][Kq]
-  floatx4* red = reinterpret_cast<floatx4*>(dec_lds + (size_t)M * Kq);  // [4][MB][64]
+  uint16_t* xs = dec_lds;                                                      // [M][xs_stride]
+  floatx4* red = reinterpret_cast<floatx4*>(dec_lds + (size_t)M * xs_stride);  // [4][MB][64]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1206,40 +1224,50 @@ __global__ __launch_bounds__(64 * kDecWaves) void gemm_decode(const uint16_t* __
   const int cb = blockIdx.x % ncb, kq = blockIdx.x / ncb;
   const int n0 = cb * kDecCols;
   const int cg = wave & 3, kh = wave >> 2;
-  const int nseg = Kq / 128;  // 64-element K segments in a wave's half of the quarter (<= 8)
+  // this workgroup's slice: [k0, k0 + Kq), nseg 128-wide units; each half
+  // of the waves takes one 64-wide segment of every unit (nseg <= 8)
+  const int U = K / kDecUnit;
+  const int u0 = dec_slice_unit(U, S, kq), nseg = dec_slice_unit(U, S, kq + 1) - u0;
+  const int k0 = u0 * kDecUnit, Kq = nseg * kDecUnit;
 
   // X slice -> LDS first (an L2 hit for all but the first workgroups of a
-  // quarter): instruction (row r, 1 KiB block b); lane l fetches logical
-  // chunk l ^ (r & 15) of the block into physical chunk l
+  // slice): instruction (row r, 1 KiB block b); lane l fetches logical
+  // chunk l ^ (r & 15) of the block into physical chunk l.  In the last
+  // block of a slice that is not a whole number of blocks, lanes whose
+  // chunk lies past the slice fetch nothing (those LDS chunks are never
+  // read), so no load leaves the slice.
   const __amdgpu_buffer_rsrc_t rx =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(X), (short)0, M * K * 2, 0x00020000);
-  const int blocks = Kq / 512;
+  const int blocks = (Kq + 511) / 512;
   for (int i = wave; i < M * blocks; i += kDecWaves) {
     const int r = i / blocks, bl = i % blocks;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, xs + (size_t)r * Kq + bl * 512, 16, (lane ^ (r & 15)) * 16,
-                                             (r * K + kq * Kq + bl * 512) * 2, 0, 0);
+    if (bl * 64 + (lane ^ (r & 15)) < Kq / 8)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, xs + (size_t)r * xs_stride + bl * 512, 16,
+                                               (lane ^ (r & 15)) * 16, (r * K + k0 + bl * 512) * 2, 0, 0);
   }
   // then W0, all 16 loads of the wave at once.  Instruction 2s+h reads rows
-  // 8h + (l & 7) of the column group, 16-byte chunk l >> 3 of K segment s:
-  // 128 contiguous bytes per row (64-byte row pieces cost 30 % more HBM time).
-  // Segments are consumed as they land (the compiler's waits count the
-  // loads in issue order).
-  const size_t kbase = (size_t)kq * Kq + kh * (Kq / 2) + (lane >> 3) * 8;
+  // 8h + (l & 7) of the column group, 16-byte chunk l >> 3 of the wave's
+  // half of unit s: 128 contiguous bytes per row (64-byte row pieces cost
+  // 30 % more HBM time), next to the other half's 128.  Segments are
+  // consumed as they land (the compiler's waits count the loads in issue
+  // order).
+  const size_t kbase = (size_t)k0 + kh * 64 + (lane >> 3) * 8;
   const uint16_t* w0p = W + (size_t)min(n0 + 16 * cg + (lane & 7), N - 1) * K + kbase;
   const uint16_t* w1p = W + (size_t)min(n0 + 16 * cg + 8 + (lane & 7), N - 1) * K + kbase;
   uint4 wv[16];
 #pragma unroll
   for (int sg = 0; sg < 8; ++sg) {
-    wv[2 * sg] = *reinterpret_cast<const uint4*>(w0p + min(sg, nseg - 1) * 64);
-    wv[2 * sg + 1] = *reinterpret_cast<const uint4*>(w1p + min(sg, nseg - 1) * 64);
+    wv[2 * sg] = *reinterpret_cast<const uint4*>(w0p + min(sg, nseg - 1) * kDecUnit);
+    wv[2 * sg + 1] = *reinterpret_cast<const uint4*>(w1p + min(sg, nseg - 1) * kDecUnit);
   }
-  // The per-row shrink rides along: this workgroup computes the quarter-kq
+  // The per-row shrink rides along: this workgroup computes the slice-kq
   // partial of T for rows cb, cb + ncb, ... from the X slice it already
   // holds.  Key, rank and pages are uniform (scalar loads, which do not wait
   // for the vector loads in flight); the first 16 ranks of the first row
-  // are fetched now: each wave takes ranks wave and wave + 8, each lane
-  // Kq / 64 consecutive elements (cpl 16-byte chunks).
-  const int cpl = Kq / 512;  // 1 or 2
+  // are fetched now: each wave takes ranks wave and wave + 8, each lane the
+  // 16-byte chunks lane and lane + 64 of the slice (nch chunks in all; a
+  // lane past them re-reads the last one and adds nothing).
+  const int nch = Kq / 8;
   int key0 = -1, rank0 = 0;
   uint4 dn[2][2];
   if (shrink && cb < M) {
@@ -1257,9 +1285,10 @@ __global__ __launch_bounds__(64 * kDecWaves) void gemm_decode(const uint16_t* __
       for (int i = 0; i < 2; ++i) {
         int pg = dpage[min(wave + 8 * i, pv.max_rank - 1)];
         pg = pg < 0 ? dpage[0] : pg;
-        const uint16_t* dr = pv.down + (size_t)pg * pv.din + (size_t)kq * Kq + lane * cpl * 8;
+        const uint16_t* dr = pv.down + (size_t)pg * pv.din + k0;
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) dn[i][cc] = *reinterpret_cast<const uint4*>(dr + min(cc, cpl - 1) * 8);
+        for (int cc = 0; cc < 2; ++cc)
+          dn[i][cc] = *reinterpret_cast<const uint4*>(dr + min(lane + 64 * cc, nch - 1) * 8);
       }
     }
   }
@@ -1291,12 +1320,12 @@ __global__ __launch_bounds__(64 * kDecWaves) void gemm_decode(const uint16_t* __
       f1.w = __builtin_amdgcn_update_dpp((int)B.w, (int)A.w, 0x108, 0xf, 0x3, false);
 #pragma unroll
       for (int odd = 0; odd < 2; ++odd) {
-        const int c = kh * (Kq / 16) + sg * 8 + 2 * (lane >> 4) + odd;  // logical 16-byte chunk in the slice row
+        const int c = (2 * sg + kh) * 8 + 2 * (lane >> 4) + odd;  // logical 16-byte chunk in the slice row
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           const int r = min(mb * 16 + (lane & 15), M - 1);
-          const uint4 a =
-              *reinterpret_cast<const uint4*>(xs + (size_t)r * Kq + (c >> 6) * 512 + (((c & 63) ^ (r & 15)) << 3));
+          const uint4 a = *reinterpret_cast<const uint4*>(xs + (size_t)r * xs_stride + (c >> 6) * 512 +
+                                                          (((c & 63) ^ (r & 15)) << 3));
           acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(odd ? f1 : f0), acc[mb], 0, 0, 0);
         }
       }
@@ -1329,9 +1358,10 @@ __global__ __launch_bounds__(64 * kDecWaves) void gemm_decode(const uint16_t* __
         for (int i = 0; i < 2; ++i) {
           int pg = dpage[min(q0 + wave + 8 * i, pv.max_rank - 1)];
           pg = pg < 0 ? dpage[0] : pg;
-          const uint16_t* dr = pv.down + (size_t)pg * pv.din + (size_t)kq * Kq + lane * cpl * 8;
+          const uint16_t* dr = pv.down + (size_t)pg * pv.din + k0;
 #pragma unroll
-          for (int cc = 0; cc < 2; ++cc) d[i][cc] = *reinterpret_cast<const uint4*>(dr + min(cc, cpl - 1) * 8);
+          for (int cc = 0; cc < 2; ++cc)
+            d[i][cc] = *reinterpret_cast<const uint4*>(dr + min(lane + 64 * cc, nch - 1) * 8);
         }
       };
       if (first) {
@@ -1346,10 +1376,10 @@ __global__ __launch_bounds__(64 * kDecWaves) void gemm_decode(const uint16_t* __
         float v[2] = {0.f, 0.f};
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
-          if (cc < cpl) {
-            const int c = lane * cpl + cc;  // logical chunk of row r's slice
-            const uint4 xa = *reinterpret_cast<const uint4*>(xs + (size_t)r * Kq + (c >> 6) * 512 +
-                                                             (((c & 63) ^ (r & 15)) << 3));
+          const int c = lane + 64 * cc;  // logical chunk of row r's slice
+          if (c < nch) {
+            const uint4 xa = *reinterpret_cast<const uint4*>(xs + (size_t)r * xs_stride + cc * 512 +
+                                                             ((lane ^ (r & 15)) << 3));
             const uint32_t xw[4] = {xa.x, xa.y, xa.z, xa.w};
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
@@ -1383,7 +1413,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void gemm_decode(const uint16_t* __
   }
   __syncthreads();
   if (kh == 0) {
-    // the quarter's partial: both halves
+    // the slice's partial: both halves
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const floatx4 o = red[(cg * MB + mb) * 64 + lane];
@@ -1400,10 +1430,35 @@ __global__ __launch_bounds__(64 * kDecWaves) void gemm_decode(const uint16_t* __
 // Sums the S split-K partials of a tile in split order, adds the row's
 // low-rank term when LORA (sum_q T[r][q] Up_a[c][q], Up streamed here), and
 // writes Y (bf16 RNE); 8 columns per thread, so each Up page row is read as
-// coalesced 16-byte pieces.
+// coalesced 16-byte pieces.  TPARTS: T holds S partial slices of t (the
+// split-K slices of the decode form's shrink), summed and scaled here.
 constexpr int kFinishThreads = 64;  // one wave per workgroup: the decode grid spreads over every CU
 
-template <bool LORA, int TP, int QG = 8>
+// sum[0..8) = the S slices (stride apart) of 8 fp32 at p, added in slice
+// order; the loads of B slices go out together.
+template <int B>
+__device__ __forceinline__ void sum_parts(const float* __restrict__ p, size_t stride, int S, float (&sum)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sum[e] = 0.f;
+  for (int q0 = 0; q0 < S; q0 += B) {
+    float4 v[B][2];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const float* pp = p + min(q0 + u, S - 1) * stride;
+      v[u][0] = *reinterpret_cast<const float4*>(pp);
+      v[u][1] = *reinterpret_cast<const float4*>(pp + 4);
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      if (q0 + u < S) {
+        sum[0] += v[u][0].x; sum[1] += v[u][0].y; sum[2] += v[u][0].z; sum[3] += v[u][0].w;
+        sum[4] += v[u][1].x; sum[5] += v[u][1].y; sum[6] += v[u][1].z; sum[7] += v[u][1].w;
+      }
+    }
+  }
+}
+
+template <bool LORA, bool TPARTS, int QG = 8>
 __global__ __launch_bounds__(kFinishThreads) void finish_part(const float* __restrict__ part, int S,
                                                               uint16_t* __restrict__ Y, int M, int N, PoolView pv,
                                                               int proj, const int32_t* __restrict__ row_key,
@@ -1412,20 +1467,17 @@ __global__ __launch_bounds__(kFinishThreads) void finish_part(const float* __res
   const int per_row = N / 8;
   if (t >= M * per_row) return;
   const int r = t / per_row, c0 = (t % per_row) * 8;
-  // the partials' loads go out before the low-rank term's dependent chain
+  // the partials' loads go out before the low-rank term's dependent chain,
+  // 4 or 8 slices' loads at once (summed in slice order)
   float sum[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) sum[e] = 0.f;
-  for (int q = 0; q < S; ++q) {
-    const float* pp = part + ((size_t)q * M + r) * N + c0;
-    const float4 p0 = *reinterpret_cast<const float4*>(pp);
-    const float4 p1 = *reinterpret_cast<const float4*>(pp + 4);
-    sum[0] += p0.x; sum[1] += p0.y; sum[2] += p0.z; sum[3] += p0.w;
-    sum[4] += p1.x; sum[5] += p1.y; sum[6] += p1.z; sum[7] += p1.w;
-  }
+  const float* pr = part + (size_t)r * N + c0;
+  if (S <= 4)
+    sum_parts<4>(pr, (size_t)M * N, S, sum);
+  else
+    sum_parts<8>(pr, (size_t)M * N, S, sum);
   float y[8];
   if (LORA) {
-    lora_delta8_desc<true, TP, QG>(pv, row_desc(const_cast<float*>(T), M, pv.max_rank), T, r, M, c0, N, y);
+    lora_delta8_desc<true, TPARTS, QG>(pv, row_desc(const_cast<float*>(T), M, pv.max_rank), T, r, M, c0, N, y, S);
   } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = 0.f;
@@ -1438,43 +1490,44 @@ __global__ __launch_bounds__(kFinishThreads) void finish_part(const float* __res
   *reinterpret_cast<uint4*>(Y + (size_t)r * N + c0) = w;
 }
 
-size_t decode_lds_bytes(int M, int K, int MB) { return (size_t)M * (K / kDecSplit) * 2 + (size_t)4 * MB * 64 * 16; }
+size_t decode_lds_bytes(int M, int xs_stride, int MB) {
+  return (size_t)M * xs_stride * 2 + (size_t)4 * MB * 64 * 16;
+}
 
-// shrink: the workgroups also compute T as K-quarter partials (kRowsTParts
-// slices of [M][max_rank] in T), which the finish pass sums and scales;
-// otherwise T holds the finished t (scale folded).
+// shrink: the workgroups also compute T as K-slice partials (S slices of
+// [M][max_rank] in T), which the finish pass sums and scales; otherwise T
+// holds the finished t (scale folded).
 template <int MB>
 hipError_t launch_decode(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N, const PoolView& pv,
                          int proj, const int32_t* row_key, float* T, float* part, bool shrink, hipStream_t st,
                          bool lora = true, const int32_t* ids = nullptr, int32_t* seg_ws = nullptr) {
-  static_assert(kDecSplit == kRowsTParts, "T partial slices are the K quarters");
-  const size_t lds = decode_lds_bytes(M, K, MB);
+  const int S = dec_slices(K), xs_stride = dec_xs_stride(K, S);
+  if (S > rows_t_slices(M)) return hipErrorNotSupported;
+  const size_t lds = decode_lds_bytes(M, xs_stride, MB);
   static LdsLimit limit;
   const hipError_t le = limit.ensure({(const void*)gemm_decode<MB, false>, (const void*)gemm_decode<MB, true>}, lds);
   if (le != hipSuccess) return le;
   const int ncb = (N + kDecCols - 1) / kDecCols;
   if (seg_ws)
-    MLORA_LAUNCH("gemm_decode+seg+shrink_rows", (gemm_decode<MB, true>), dim3(ncb * kDecSplit + 1),
-                 dim3(64 * kDecWaves), lds, st, X, W, M, K, N, pv, proj, row_key, T, part, shrink ? 1 : 0, ids,
-                 seg_ws);
+    MLORA_LAUNCH("gemm_decode+seg+shrink_rows", (gemm_decode<MB, true>), dim3(ncb * S + 1), dim3(64 * kDecWaves),
+                 lds, st, X, W, M, K, N, S, xs_stride, pv, proj, row_key, T, part, shrink ? 1 : 0, ids, seg_ws);
   else
-    MLORA_LAUNCH(shrink ? "gemm_decode+shrink_rows" : "gemm_decode", (gemm_decode<MB, false>), dim3(ncb * kDecSplit),
-                 dim3(64 * kDecWaves), lds, st, X, W, M, K, N, pv, proj, row_key, T, part, shrink ? 1 : 0,
-                 (const int32_t*)nullptr, (int32_t*)nullptr);
+    MLORA_LAUNCH(shrink ? "gemm_decode+shrink_rows" : "gemm_decode", (gemm_decode<MB, false>), dim3(ncb * S),
+                 dim3(64 * kDecWaves), lds, st, X, W, M, K, N, S, xs_stride, pv, proj, row_key, T, part,
+                 shrink ? 1 : 0, (const int32_t*)nullptr, (int32_t*)nullptr);
   hipError_t e = launched();
   if (e != hipSuccess) return e;
   const int threads = M * (N / 8);
   // a decode batch's finish has few waves per SIMD: ranks in rounds of 16
   if (!lora)
-    MLORA_LAUNCH("finish_base", (finish_part<false, 1>), dim3((threads + kFinishThreads - 1) / kFinishThreads),
-                 dim3(kFinishThreads), 0, st, part, kDecSplit, Y, M, N, pv, proj, row_key, T);
+    MLORA_LAUNCH("finish_base", (finish_part<false, false>), dim3((threads + kFinishThreads - 1) / kFinishThreads),
+                 dim3(kFinishThreads), 0, st, part, S, Y, M, N, pv, proj, row_key, T);
   else if (shrink)
-    MLORA_LAUNCH("finish_part", (finish_part<true, kRowsTParts, 16>),
-                 dim3((threads + kFinishThreads - 1) / kFinishThreads), dim3(kFinishThreads), 0, st, part, kDecSplit,
-                 Y, M, N, pv, proj, row_key, T);
+    MLORA_LAUNCH("finish_part", (finish_part<true, true, 16>), dim3((threads + kFinishThreads - 1) / kFinishThreads),
+                 dim3(kFinishThreads), 0, st, part, S, Y, M, N, pv, proj, row_key, T);
   else
-    MLORA_LAUNCH("finish_part", (finish_part<true, 1, 16>), dim3((threads + kFinishThreads - 1) / kFinishThreads),
-                 dim3(kFinishThreads), 0, st, part, kDecSplit, Y, M, N, pv, proj, row_key, T);
+    MLORA_LAUNCH("finish_part", (finish_part<true, false, 16>), dim3((threads + kFinishThreads - 1) / kFinishThreads),
+                 dim3(kFinishThreads), 0, st, part, S, Y, M, N, pv, proj, row_key, T);
   return launched();
 }
 
@@ -1521,10 +1574,10 @@ hipError_t launch_mid_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, in
   if (e != hipSuccess) return e;
   const int threads = M * (N / 8);
   if (!lora)
-    MLORA_LAUNCH("finish_base", (finish_part<false, 1>), dim3((threads + kFinishThreads - 1) / kFinishThreads),
+    MLORA_LAUNCH("finish_base", (finish_part<false, false>), dim3((threads + kFinishThreads - 1) / kFinishThreads),
                  dim3(kFinishThreads), 0, st, part, S, Y, M, N, pv, proj, row_key, T);
   else
-    MLORA_LAUNCH("finish_part", (finish_part<true, 1>), dim3((threads + kFinishThreads - 1) / kFinishThreads),
+    MLORA_LAUNCH("finish_part", (finish_part<true, false>), dim3((threads + kFinishThreads - 1) / kFinishThreads),
                  dim3(kFinishThreads), 0, st, part, S, Y, M, N, pv, proj, row_key, T);
   return launched();
 }
@@ -1552,8 +1605,10 @@ hipError_t launch_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M,
 }  // namespace
 
 bool decode_splitk_ok(int M, int K, int N, bool vec) {
-  // X slice in 1 KiB blocks, each wave's half of a quarter in <= 16 steps
-  return vec && M <= 64 && K % (kDecSplit * 512) == 0 && K <= kDecSplit * 1024 && (long)M * K * 2 < (1L << 31);
+  // whole 128-wide units, at least one per slice, every slice at most 1024
+  // deep (each wave's half in <= 8 segments, 16 loads)
+  return vec && M <= 64 && K % kDecUnit == 0 && K >= kDecMinSlices * kDecUnit &&
+         K <= kDecMaxSlices * kDecMaxDepth && (long)M * K * 2 < (1L << 31);
 }
 
 hipError_t launch_gemm_lora(const PoolView& pv, int proj, const uint16_t* X, const uint16_t* W, const int32_t* ws,
@@ -1605,7 +1660,7 @@ hipError_t launch_forward_rows(const PoolView& pv, int proj, const uint16_t* X, 
 }
 
 size_t gemm_lora_part_floats(int M, int N, int K) {
-  return (size_t)(M > 64 ? mid_split(M, N, K) : kDecSplit) * M * N;
+  return (size_t)(M > 64 ? mid_split(M, N, K) : dec_slices(K)) * M * N;
 }
 
 hipError_t launch_base_split(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N, float* part,

@@ -112,20 +112,23 @@ hipError_t launch_gemm_lora(const PoolView& pv, int proj, const uint16_t* X, con
 hipError_t launch_forward_rows(const PoolView& pv, int proj, const uint16_t* X, const uint16_t* W,
                                const int32_t* ids, int32_t* ws, float* T, float* part, uint16_t* Y, int M,
                                hipStream_t stream);
-// T's region in the per-row work holds up to this many [M][max_rank] slices
-// (the decode form computes T as K-quarter partials inside its GEMM launch)
-constexpr int kRowsTParts = 4;
+// T's region in the per-row work holds rows_t_slices(M) [M][max_rank]
+// slices: a batch of at most 64 rows may take the decode form, which computes
+// T as partials over its K slices (at most kDecMaxSlices) inside its GEMM
+// launch; larger batches keep one slice (the finished T).
+constexpr int kDecMaxSlices = 16;
+__host__ __device__ constexpr int rows_t_slices(int M) { return M <= 64 ? kDecMaxSlices : 1; }
 // Per-row descriptor of the per-row path, written by whichever kernel runs a
 // row's shrink and read by the pass that adds the low-rank term (one
 // dependent load less there: the adapter's pages come with the row instead
 // of through the row's key): word 0 the row key (adapter id, -1 base-only,
 // -2 invalid id), 1 the rank, 2 the scale (fp32 bits), 3 unused, 4.. the
 // adapter's Up page ids for the projection (entries past the rank repeat the
-// first page).  The descriptors follow the kRowsTParts slices of T in T's
+// first page).  The descriptors follow the rows_t_slices(M) slices of T in T's
 // region of the work buffer.
 __host__ __device__ constexpr int row_desc_words(int max_rank) { return 4 + max_rank; }
 __host__ __device__ inline int32_t* row_desc(float* T, int M, int max_rank) {
-  return reinterpret_cast<int32_t*>(T + (size_t)kRowsTParts * M * max_rank);
+  return reinterpret_cast<int32_t*>(T + (size_t)rows_t_slices(M) * M * max_rank);
 }
 size_t gemm_lora_part_floats(int M, int N, int K);
 // Y = X W^T alone on the split-K decode / medium forms, with fp32 scratch

@@ -7,14 +7,12 @@
 namespace mlora {
 namespace {
 
-// The low-rank term of row r at columns [c0, c0+8): sum_q t_q Up_a[c][q].
-// TP == 1: T [M][max_rank] holds t with the scale folded in; TP > 1: T
-// holds TP partial slices [TP][M][max_rank] (K ranges of the shrink),
-// summed here in slice order and then scaled.  Zero for a
+// The low-rank term of row r at columns [c0, c0+8): sum_q t_q Up_a[c][q],
+// with T [M][max_rank] holding t with the scale folded in.  Zero for a
 // base-only row or a row past M, NaN for a row with an invalid id.  Ranks
 // past the adapter's rank read its last column with weight 0, so each group
 // of 8 page loads goes out at once.
-template <bool VEC, int TP = 1>
+template <bool VEC>
 __device__ __forceinline__ void lora_delta8(const PoolView& pv, int proj, const int32_t* __restrict__ row_key,
                                             const float* __restrict__ T, int r, int M, int c0, int N,
                                             float (&acc8)[8]) {
@@ -23,11 +21,9 @@ __device__ __forceinline__ void lora_delta8(const PoolView& pv, int proj, const 
   const int key = (r < M && c0 < N) ? row_key[r] : -1;
   if (key >= 0) {
     const int rank = pv.rank[key];
-    const float tscale = TP > 1 ? pv.scale[key] : 1.f;
     const int32_t* upage = pv.up_page + ((size_t)key * pv.n_proj + proj) * pv.max_rank;
     const float* tr = T + (size_t)r * pv.max_rank;
-    const size_t tstride = (size_t)M * pv.max_rank;
-    // t rows of 8 ranks as two 16-byte loads per slice when they are aligned
+    // t rows of 8 ranks as two 16-byte loads when they are aligned
     const bool tvec = (pv.max_rank & 7) == 0;
     // page indices and t are read without waiting for the rank: entries past
     // it fall back to the group's first page and weigh zero (a select, so an
@@ -44,26 +40,16 @@ __device__ __forceinline__ void lora_delta8(const PoolView& pv, int proj, const 
       for (int q = 0; q < 8; ++q) load8<VEC>(pv.up + (size_t)pg[q] * pv.dout, c0, N, u8[q]);
       if (tvec) {
         // q0 + 7 < max_rank here: q0 < rank <= max_rank and both multiples of 8
-#pragma unroll
-        for (int q = 0; q < 8; ++q) tv[q] = 0.f;
-#pragma unroll
-        for (int p = 0; p < TP; ++p) {
-          const float4 a = *reinterpret_cast<const float4*>(tr + p * tstride + q0);
-          const float4 b = *reinterpret_cast<const float4*>(tr + p * tstride + q0 + 4);
-          tv[0] += a.x; tv[1] += a.y; tv[2] += a.z; tv[3] += a.w;
-          tv[4] += b.x; tv[5] += b.y; tv[6] += b.z; tv[7] += b.w;
-        }
+        const float4 a = *reinterpret_cast<const float4*>(tr + q0);
+        const float4 b = *reinterpret_cast<const float4*>(tr + q0 + 4);
+        tv[0] = a.x; tv[1] = a.y; tv[2] = a.z; tv[3] = a.w;
+        tv[4] = b.x; tv[5] = b.y; tv[6] = b.z; tv[7] = b.w;
       } else {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int qq = min(q0 + q, pv.max_rank - 1);
-          tv[q] = tr[qq];
-#pragma unroll
-          for (int p = 1; p < TP; ++p) tv[q] += tr[p * tstride + qq];
-        }
+        for (int q = 0; q < 8; ++q) tv[q] = tr[min(q0 + q, pv.max_rank - 1)];
       }
 #pragma unroll
-      for (int q = 0; q < 8; ++q) tq[q] = (q0 + q < rank) ? tscale * tv[q] : 0.f;
+      for (int q = 0; q < 8; ++q) tq[q] = (q0 + q < rank) ? tv[q] : 0.f;
 #pragma unroll
       for (int q = 0; q < 8; ++q)
 #pragma unroll
@@ -82,11 +68,13 @@ __device__ __forceinline__ void lora_delta8(const PoolView& pv, int proj, const 
 // go in rounds of QG (8 or 16): each round's QG page loads go out at once,
 // so a rank-16 row takes one round with QG = 16; QG = 8 keeps the register
 // count low where many waves must share each SIMD.  The sum over ranks runs
-// in rank order either way.
-template <bool VEC, int TP = 1, int QG = 8>
+// in rank order either way.  PARTS: T holds tp partial slices
+// [tp][M][max_rank] (K ranges of the shrink), summed here in slice order and
+// then scaled; otherwise T [M][max_rank] holds t with the scale folded in.
+template <bool VEC, bool PARTS = false, int QG = 8>
 __device__ __forceinline__ void lora_delta8_desc(const PoolView& pv, const int32_t* __restrict__ desc,
                                                  const float* __restrict__ T, int r, int M, int c0, int N,
-                                                 float (&acc8)[8]) {
+                                                 float (&acc8)[8], int tp = 1) {
   static_assert(QG == 8 || QG == 16, "rank rounds of 8 or 16");
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc8[e] = 0.f;
@@ -95,7 +83,8 @@ __device__ __forceinline__ void lora_delta8_desc(const PoolView& pv, const int32
   const int32_t* d = desc + (size_t)r * words;
   const int key = d[0];
   const int rank = d[1];
-  const float tscale = TP > 1 ? __int_as_float(d[2]) : 1.f;
+  const float tscale = PARTS ? __int_as_float(d[2]) : 1.f;
+  if (!PARTS) tp = 1;
   if (key >= 0) {
     const float* tr = T + (size_t)r * pv.max_rank;
     const size_t tstride = (size_t)M * pv.max_rank;
@@ -109,8 +98,8 @@ __device__ __forceinline__ void lora_delta8_desc(const PoolView& pv, const int32
       if (tvec && q0 + QG <= pv.max_rank) {
 #pragma unroll
         for (int q = 0; q < QG; ++q) tv[q] = 0.f;
-#pragma unroll
-        for (int p = 0; p < TP; ++p) {
+#pragma unroll 4
+        for (int p = 0; p < tp; ++p) {
 #pragma unroll
           for (int h = 0; h < QG / 4; ++h) {
             const float4 a = *reinterpret_cast<const float4*>(tr + p * tstride + q0 + 4 * h);
@@ -122,8 +111,7 @@ __device__ __forceinline__ void lora_delta8_desc(const PoolView& pv, const int32
         for (int q = 0; q < QG; ++q) {
           const int qq = min(q0 + q, pv.max_rank - 1);
           tv[q] = tr[qq];
-#pragma unroll
-          for (int p = 1; p < TP; ++p) tv[q] += tr[p * tstride + qq];
+          for (int p = 1; p < tp; ++p) tv[q] += tr[p * tstride + qq];
         }
       }
 #pragma unroll

@@ -68,7 +68,13 @@ CASES = [
     (10, 300, 4096, 4096, {i: 16 for i in range(256)}, True),
     (11, 700, 2048, 512, {i: (16 if i % 3 else 64) for i in range(40)}, True),
     (12, 1024, 4096, 4096, {0: 16, 1: 8}, True),
-    # two calls: din not a multiple of 128 or 2048, unaligned dout
+    # decode shapes with wider or ragged din (8 to 16 K slices; slices of
+    # unequal depth)
+    (13, 32, 11008, 4096, {0: 16, 1: 16, 2: 16}, True),
+    (14, 64, 8192, 1000, {0: 8, 1: 64, 4: 3}, True),
+    (15, 5, 2560, 520, {0: 16}, False),
+    (16, 48, 16384, 264, {i: 16 for i in range(12)}, True),
+    # two calls: din not a multiple of 128, unaligned dout
     (7, 20, 1000, 520, {0: 16, 1: 5}, True),
     (8, 9, 2048, 12, {0: 4}, False),
 ]

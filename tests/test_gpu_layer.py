@@ -231,9 +231,12 @@ def test_delta_only(M, name):
 
 
 @pytest.mark.parametrize("n,din,dout", [(40, 520, 264), (300, 520, 4104), (1024, 520, 1000),
-                                        # split-K decode form: K multiple of 2048, up to 64 rows
+                                        # split-K decode form: up to 64 rows, K a multiple of 128 from
+                                        # 512 to 16384 (4 slices up to 4096, then one per 1024; slices of
+                                        # unequal depth where the 128-wide units do not divide evenly)
                                         (1, 4096, 4096), (17, 2048, 1000), (32, 4096, 136), (48, 2048, 4096),
-                                        (64, 4096, 4104),
+                                        (64, 4096, 4104), (1, 640, 1000), (13, 2560, 264), (32, 11008, 4096),
+                                        (48, 8192, 520), (64, 16384, 1000),
                                         # medium batches on the split-K tiled kernel + finish pass
                                         (130, 512, 1000), (700, 1024, 2000), (256, 4096, 4096)])
 def test_gemm_lora_with_synthetic_t(M, n, din, dout):
@@ -260,13 +263,28 @@ def test_gemm_lora_with_synthetic_t(M, n, din, dout):
 
 
 @pytest.mark.parametrize("n,din,dout", [(1, 2048, 1000), (17, 2048, 1000), (33, 4096, 136), (48, 4096, 4104),
-                                        (64, 4096, 4096), (65, 4096, 4096)])
+                                        (64, 4096, 4096), (65, 4096, 4096),
+                                        # wider K: 8 to 16 slices, and depths that leave a ragged 1 KiB block
+                                        (13, 640, 264), (1, 8192, 1000), (32, 11008, 4096), (17, 2560, 1000),
+                                        (48, 14336, 136), (64, 16384, 4104)])
 def test_apply_rows_decode_forms(M, n, din, dout):
     """The per-row variant end to end where the per-row shrink shares the
-    split-K GEMM launch (K a multiple of 2048, up to 64 rows; 65 rows takes
-    the separate shrink), mixed ranks up to 64 and base-only rows."""
+    split-K GEMM launch (K a multiple of 128 from 512 to 16384, up to 64
+    rows; 65 rows takes the separate shrink), mixed ranks up to 64 and
+    base-only rows."""
     w = small_workload(71 + n, din, dout, n, {0: 16, 1: 3, 2: 64}, p_none=0.2)
     check_apply(M, w, variants=("rows",))
+
+
+@pytest.mark.parametrize("din", [8192, 11008])
+def test_apply_decode_wide_din(M, din):
+    """A down projection's decode step (din 8192 or 11008 -> 4096, 32 rows
+    split 20/8/4 over three rank-16 adapters): every variant against the
+    oracle; the split and fused variants take the same split-K base GEMM
+    without the low-rank term."""
+    ids = np.array([0] * 20 + [1] * 8 + [2] * 4, dtype=np.int32)
+    w = synth.custom(f"decode_din{din}", 81, din, 4096, ids, {0: 16, 1: 16, 2: 16})
+    check_apply(M, w)
 
 
 def test_launch_timing_marks_every_launch(M):
@@ -291,6 +309,15 @@ def test_launch_timing_marks_every_launch(M):
     M.apply(pool, 0, Xd, W0d, seg, Y=Y, work=work, variant="rows")
     torch.cuda.synchronize()
     assert [m[0] for m in M.timing_read()] == [m[0] for m in marks]
+    # a down projection's din (11008 = 86 units of 128) takes the same form
+    w2 = synth.custom("timing_din11008", 82, 11008, 1024, np.array([0, 1, -1, 0] * 4, dtype=np.int32),
+                      {0: 16, 1: 8})
+    pool2 = make_pool(M, w2)
+    seg2 = M.build_segments(pool2, ids_dev(w2.row_adapter))
+    torch.cuda.synchronize()
+    M.timing_arm(8)
+    M.apply(pool2, 0, to_dev_bf16(w2.x_bits()), to_dev_bf16(w2.w0_bits()), seg2, variant="rows")
+    assert [m[0] for m in M.timing_read()] == ["gemm_decode+shrink_rows", "finish_part"]
 
 
 @pytest.mark.parametrize("variant", ["split", "fused", "rows"])
