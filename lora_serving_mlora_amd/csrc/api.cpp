@@ -852,17 +852,37 @@ namespace {
 // over the chip, never more than kMaxSplitChunks
 // the large-batch epilogue's operands (t per row in bf16, adapter offsets,
 // Up blocks with ranks contiguous)
-size_t lora_operands_bytes(const mlora_pool* p, int n) {
-  const int wt = mlora::t_rows_width(p->d.max_rank);
-  return align256((size_t)n * wt * 2) + align256((size_t)p->d.max_adapters * 4) +
-         align256(mlora::lora_upt_bytes(n, p->d.max_adapters, p->d.max_rank, p->d.dout));
-}
-// The GEMM epilogue takes the low-rank term of batches with at most 256
-// adapters (one prep block per adapter and column chunk) whose operands
-// stay within 256 MiB; others take the separate expand.
+// Operands of the large-batch GEMM's low-rank epilogue, in `work` after the
+// shrink's slices: tb [n][wt] bf16 | koff [max_adapters] | over (one word) |
+// upt, room for upt_units rank rows of dout.  upt_units is every adapter of
+// the batch padded to the largest rank, or as many rank rows as fit in a
+// 256 MiB budget for the operands if that is less: then a batch whose
+// distinct adapters (known only on the device) need more has its low-rank
+// term added by a separate expand instead of the epilogue (may_overrun).
 constexpr size_t kMaxEpilogueBytes = 256u << 20;
+struct EpilogueLayout {
+  size_t koff, over, upt, total;
+  long upt_units;
+  bool may_overrun;
+};
+EpilogueLayout epilogue_layout(const mlora_pool* p, int n) {
+  const int wt = mlora::t_rows_width(p->d.max_rank);
+  EpilogueLayout L{};
+  L.koff = align256((size_t)n * wt * 2);
+  L.over = L.koff + align256((size_t)p->d.max_adapters * 4);
+  L.upt = L.over + 256;
+  const size_t row = (size_t)p->d.dout * 2;
+  const long worst = (long)mlora::lora_upt_units(n, p->d.max_adapters, p->d.max_rank);
+  const long budget = L.upt < kMaxEpilogueBytes ? (long)((kMaxEpilogueBytes - L.upt) / row) / 16 * 16 : 0;
+  L.upt_units = std::min(worst, budget);
+  L.may_overrun = L.upt_units < worst;
+  L.total = L.upt + align256((size_t)L.upt_units * row);
+  return L;
+}
+size_t lora_operands_bytes(const mlora_pool* p, int n) { return epilogue_layout(p, n).total; }
+// The GEMM epilogue needs room for at least one adapter of the largest rank.
 bool big_epilogue_fits(const mlora_pool* p, int n) {
-  return std::min(n, p->d.max_adapters) <= 256 && lora_operands_bytes(p, n) <= kMaxEpilogueBytes &&
+  return epilogue_layout(p, n).upt_units >= mlora::t_rows_width(p->d.max_rank) &&
          (size_t)p->d.n_up_pages * p->d.dout < (1u << 31);
 }
 
@@ -960,17 +980,20 @@ mlora_status mlora_apply(const mlora_pool* p, int32_t proj, const uint16_t* X, c
     float* T = static_cast<float*>(work);
     char* w = static_cast<char*>(work) + align256((size_t)chunks * n * d.max_rank * sizeof(float));
     const int wt = mlora::t_rows_width(d.max_rank);
+    const EpilogueLayout L = epilogue_layout(p, n);
     uint16_t* tb = reinterpret_cast<uint16_t*>(w);
-    w += align256((size_t)n * wt * 2);
-    int32_t* koff = reinterpret_cast<int32_t*>(w);
-    w += align256((size_t)d.max_adapters * 4);
-    uint16_t* upt = reinterpret_cast<uint16_t*>(w);
+    int32_t* koff = reinterpret_cast<int32_t*>(w + L.koff);
+    int32_t* over = reinterpret_cast<int32_t*>(w + L.over);
+    uint16_t* upt = reinterpret_cast<uint16_t*>(w + L.upt);
     st = hip_check(mlora::launch_shrink(v, proj, X, ws, n, T, chunks, chunk_elems_for(d.din, chunks), s), "shrink launch");
     if (st != MLORA_OK) return st;
-    st = hip_check(mlora::launch_lora_prep(v, proj, ws, n, T, chunks, tb, wt, koff, upt, s), "low-rank operand launch");
+    st = hip_check(mlora::launch_lora_prep(v, proj, ws, n, T, chunks, tb, wt, koff, upt, L.upt_units, over, s),
+                   "low-rank operand launch");
     if (st != MLORA_OK) return st;
-    const mlora::LoraOperands lo{tb, koff, upt, wt};
-    return hip_check(mlora::launch_big_lora(v, X, W0, ws, lo, Y, n, s), "GEMM + low-rank epilogue launch");
+    const mlora::LoraOperands lo{tb, koff, upt, wt, L.may_overrun ? over : nullptr};
+    st = hip_check(mlora::launch_big_lora(v, X, W0, ws, lo, Y, n, s), "GEMM + low-rank epilogue launch");
+    if (st != MLORA_OK || !L.may_overrun) return st;
+    return hip_check(mlora::launch_expand_over(v, proj, T, chunks, ws, Y, n, over, s), "overrun expand launch");
   }
   // the base GEMM: split over K with its partials in `work` (per-row
   // layout) when the batch and the buffer allow, else the plain form

@@ -1009,7 +1009,10 @@ __device__ __forceinline__ void gemm_ring_body(
   int key[MI];  // low-rank epilogue: the keys of the lane's A-fragment rows
   if constexpr (LORA) {
     __builtin_amdgcn_sched_barrier(0);
-    ring_lora_epilogue<MI, NJ>(m0 + c.wm * (TM / 2), n0 + c.wn * (TN / 2), M, N, pv, row_key, lo, acc, key);
+    // (left out when the batch's Up blocks overran the operand buffer: a
+    // separate expand then adds the term)
+    if (lo.over == nullptr || uniform_load(lo.over, 0) == 0)
+      ring_lora_epilogue<MI, NJ>(m0 + c.wm * (TM / 2), n0 + c.wn * (TN / 2), M, N, pv, row_key, lo, acc, key);
   }
 
   // C layout of a 32x32 tile: lane l holds column l%32, rows 8*(v/4) + 4*(l/32) + v%4.

@@ -148,18 +148,23 @@ hipError_t launch_shrink_rows(const PoolView& pv, int proj, const uint16_t* X, c
 //        rank row of its block in upt (other entries are not written),
 //   upt  bf16: per adapter a block [dout][r_pad(a)] at element koff[a] * dout
 //        (Up with ranks contiguous, r_pad = rank rounded up to 16, zeros
-//        past the rank).
+//        past the rank), room for upt_units rank rows in all,
+//   over int32 (when not null): written by lora_prep, nonzero when the
+//        batch's blocks need more than upt_units rank rows; then upt is
+//        incomplete, the GEMM leaves the low-rank term out and
+//        launch_expand_over adds it.
 struct LoraOperands {
   const uint16_t* tb;
   const int32_t* koff;
   const uint16_t* upt;
   int wt;
+  const int32_t* over = nullptr;
 };
 inline int t_rows_width(int max_rank) { return (max_rank + 15) / 16 * 16; }
-// Bytes of upt for a batch of n rows: every adapter of the batch padded to
-// the largest rank.
-inline size_t lora_upt_bytes(int n, int max_adapters, int max_rank, int dout) {
-  return (size_t)(n < max_adapters ? n : max_adapters) * t_rows_width(max_rank) * dout * 2;
+// Rank rows of upt for a batch of n rows at most: every adapter of the
+// batch padded to the largest rank.
+inline size_t lora_upt_units(int n, int max_adapters, int max_rank) {
+  return (size_t)(n < max_adapters ? n : max_adapters) * t_rows_width(max_rank);
 }
 
 // Large batches: Y = X W^T plus every row's low-rank term, added in the
@@ -168,10 +173,12 @@ inline size_t lora_upt_bytes(int n, int max_adapters, int max_rank, int dout) {
 bool big_lora_ok(const PoolView& pv, const uint16_t* X, const uint16_t* W, int M);
 hipError_t launch_big_lora(const PoolView& pv, const uint16_t* X, const uint16_t* W, const int32_t* ws,
                            const LoraOperands& lo, uint16_t* Y, int M, hipStream_t stream);
-// Writes tb, koff and upt (see LoraOperands) from the shrink's slices Ts
-// [n_chunks][n][max_rank] (sorted positions; t = sum over slices in order).
+// Writes tb, koff, upt and *over (see LoraOperands) from the shrink's slices
+// Ts [n_chunks][n][max_rank] (sorted positions; t = sum over slices in
+// order); upt has room for upt_units rank rows.
 hipError_t launch_lora_prep(const PoolView& pv, int proj, const int32_t* ws, int n, const float* Ts, int n_chunks,
-                            uint16_t* tb, int wt, int32_t* koff, uint16_t* upt, hipStream_t stream);
+                            uint16_t* tb, int wt, int32_t* koff, uint16_t* upt, long upt_units, int32_t* over,
+                            hipStream_t stream);
 
 hipError_t launch_shrink(const PoolView& pv, int proj, const uint16_t* X, const int32_t* ws, int n,
                          float* T, int n_chunks, int chunk_elems, hipStream_t stream);
@@ -183,6 +190,10 @@ int shrink_tile_cap(const PoolView& pv, int n);
 
 hipError_t launch_expand(const PoolView& pv, int proj, const float* T, int n_chunks, const int32_t* ws,
                          uint16_t* Y, int n, hipStream_t stream);
+// launch_expand whose workgroups return at once unless *over is nonzero (the
+// large-batch GEMM then left the low-rank term out)
+hipError_t launch_expand_over(const PoolView& pv, int proj, const float* T, int n_chunks, const int32_t* ws,
+                              uint16_t* Y, int n, const int32_t* over, hipStream_t stream);
 
 hipError_t launch_fused(const PoolView& pv, int proj, const uint16_t* X, const int32_t* ws, uint16_t* Y,
                         int n, hipStream_t stream);

@@ -206,9 +206,12 @@ __global__ __launch_bounds__(64) void shrink_kernel(PoolView pv, int proj, const
 // ---------------------------------------------------------------------------
 // expand: grid (items + invalid rows, column chunks of 512), one wave
 // ---------------------------------------------------------------------------
+// over (when not null): nothing to do unless *over is nonzero.
 template <bool VEC>
 __global__ __launch_bounds__(64) void expand_kernel(PoolView pv, int proj, const float* __restrict__ T, int n_chunks,
-                                                    const int32_t* __restrict__ ws, uint16_t* __restrict__ Y, int n) {
+                                                    const int32_t* __restrict__ ws, uint16_t* __restrict__ Y, int n,
+                                                    const int32_t* __restrict__ over) {
+  if (over != nullptr && *over == 0) return;
   __shared__ float ts[R][MLORA_MAX_RANK];
   const int lane = threadIdx.x;
   const int n_items = ws[MLORA_SEG_NITEMS];
@@ -684,14 +687,18 @@ __global__ __launch_bounds__(64 * kTileWaves) void shrink_tiles_kernel(PoolView 
 // to bf16 and zero-padded to wt.  Blocks [nt, ...): one per (segment,
 // kPrepCols columns): the adapter's Up columns as a [dout][r_pad] block (ranks
 // contiguous, zeros past the rank) at koff * dout, koff = the sum of r_pad
-// over the segments before it, and koff recorded per adapter id.
+// over the segments before it, and koff recorded per adapter id.  A block
+// that would end past upt_units rank rows writes nothing; the first column
+// block of the last segment (of the first, with no segment) records in
+// *over whether the batch's blocks overran.
 // ---------------------------------------------------------------------------
 constexpr int kPrepCols = 64;
 
 __global__ __launch_bounds__(256) void lora_prep_kernel(PoolView pv, int proj, const int32_t* __restrict__ ws, int n,
                                                         const float* __restrict__ Ts, int n_chunks,
                                                         uint16_t* __restrict__ tb, int wt, int nt,
-                                                        int32_t* __restrict__ koff_out, uint16_t* __restrict__ upt) {
+                                                        int32_t* __restrict__ koff_out, uint16_t* __restrict__ upt,
+                                                        long upt_units, int32_t* __restrict__ over) {
   const int tid = threadIdx.x;
   if ((int)blockIdx.x < nt) {
     const int n_act = ws[MLORA_SEG_NACT];
@@ -716,12 +723,14 @@ __global__ __launch_bounds__(256) void lora_prep_kernel(PoolView pv, int proj, c
   const int chunks = (pv.dout + kPrepCols - 1) / kPrepCols;
   const int sidx = (blockIdx.x - nt) / chunks, cc = (blockIdx.x - nt) % chunks;
   const int nseg = ws[MLORA_SEG_NSEG];
+  if (nseg == 0 && sidx == 0 && cc == 0 && tid == 0) *over = 0;
   if (sidx >= nseg) return;
   const int32_t* seg_adapter = ws + MLORA_SEG_ADAPTER(n);
-  // koff = sum of r_pad over the segments before this one (at most 255 of
-  // them: one per thread, then a block sum)
+  // koff = sum of r_pad over the segments before this one (each thread sums
+  // every 256th, then a block sum)
   __shared__ int part[4];
-  int mine = tid < sidx ? (pv.rank[seg_adapter[tid]] + 15) & ~15 : 0;
+  int mine = 0;
+  for (int s2 = tid; s2 < sidx; s2 += 256) mine += (pv.rank[seg_adapter[s2]] + 15) & ~15;
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) mine += __shfl_xor(mine, m, 64);
   if ((tid & 63) == 0) part[tid >> 6] = mine;
@@ -729,7 +738,12 @@ __global__ __launch_bounds__(256) void lora_prep_kernel(PoolView pv, int proj, c
   const int koff = part[0] + part[1] + part[2] + part[3];
   const int a = seg_adapter[sidx];
   const int rank = pv.rank[a], rp = (rank + 15) & ~15;
-  if (cc == 0 && tid == 0) koff_out[a] = koff;
+  const bool fits = koff + rp <= upt_units;
+  if (cc == 0 && tid == 0) {
+    koff_out[a] = koff;
+    if (sidx == nseg - 1) *over = fits ? 0 : 1;
+  }
+  if (!fits) return;
   const int c0 = cc * kPrepCols, ncol = min(kPrepCols, pv.dout - c0);
   const int32_t* upage = pv.up_page + ((size_t)a * pv.n_proj + proj) * pv.max_rank;
   // rank rows in: 8 columns per thread-chunk (one 16-byte load when the
@@ -819,10 +833,22 @@ hipError_t launch_shrink_rows(const PoolView& pv, int proj, const uint16_t* X, c
 hipError_t launch_expand(const PoolView& pv, int proj, const float* T, int n_chunks, const int32_t* ws, uint16_t* Y,
                          int n, hipStream_t stream) {
   const dim3 grid(item_grid(n), (pv.dout + 511) / 512), block(64);
+  const int32_t* none = nullptr;
   if (vec_ok(pv, Y, Y))
-    MLORA_LAUNCH("expand", (expand_kernel<true>), grid, block, 0, stream, pv, proj, T, n_chunks, ws, Y, n);
+    MLORA_LAUNCH("expand", (expand_kernel<true>), grid, block, 0, stream, pv, proj, T, n_chunks, ws, Y, n, none);
   else
-    MLORA_LAUNCH("expand", (expand_kernel<false>), grid, block, 0, stream, pv, proj, T, n_chunks, ws, Y, n);
+    MLORA_LAUNCH("expand", (expand_kernel<false>), grid, block, 0, stream, pv, proj, T, n_chunks, ws, Y, n, none);
+  return launched();
+}
+
+hipError_t launch_expand_over(const PoolView& pv, int proj, const float* T, int n_chunks, const int32_t* ws,
+                              uint16_t* Y, int n, const int32_t* over, hipStream_t stream) {
+  const dim3 grid(item_grid(n), (pv.dout + 511) / 512), block(64);
+  if (vec_ok(pv, Y, Y))
+    MLORA_LAUNCH("expand_over", (expand_kernel<true>), grid, block, 0, stream, pv, proj, T, n_chunks, ws, Y, n, over);
+  else
+    MLORA_LAUNCH("expand_over", (expand_kernel<false>), grid, block, 0, stream, pv, proj, T, n_chunks, ws, Y, n,
+                 over);
   return launched();
 }
 
@@ -839,13 +865,15 @@ hipError_t launch_fused(const PoolView& pv, int proj, const uint16_t* X, const i
 }
 
 hipError_t launch_lora_prep(const PoolView& pv, int proj, const int32_t* ws, int n, const float* Ts, int n_chunks,
-                            uint16_t* tb, int wt, int32_t* koff, uint16_t* upt, hipStream_t stream) {
+                            uint16_t* tb, int wt, int32_t* koff, uint16_t* upt, long upt_units, int32_t* over,
+                            hipStream_t stream) {
   const long total = (long)n * wt;
   const int nt = (int)((total + 255) / 256 < 1024 ? (total + 255) / 256 : 1024);
-  const int segs = n < pv.max_adapters ? n : pv.max_adapters;  // segments of the batch, at most
-  const int blocks = (nt > 0 ? nt : 1) + segs * ((pv.dout + kPrepCols - 1) / kPrepCols);
-  MLORA_LAUNCH("lora_prep", lora_prep_kernel, dim3(blocks), dim3(256), 0, stream, pv, proj, ws, n, Ts, n_chunks, tb,
-               wt, nt > 0 ? nt : 1, koff, upt);
+  const long segs = n < pv.max_adapters ? n : pv.max_adapters;  // segments of the batch, at most
+  const long blocks = (nt > 0 ? nt : 1) + segs * ((pv.dout + kPrepCols - 1) / kPrepCols);
+  if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
+  MLORA_LAUNCH("lora_prep", lora_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, pv, proj, ws, n, Ts,
+               n_chunks, tb, wt, nt > 0 ? nt : 1, koff, upt, upt_units, over);
   return launched();
 }
 

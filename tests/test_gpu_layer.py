@@ -360,6 +360,54 @@ def test_apply_large_batch_epilogue(M, n, dout):
     check_apply(M, w, variants=("split",))
 
 
+def _apply_launches(M, w, pool):
+    """Kernel names of one split-variant apply call."""
+    torch = torch_cuda()
+    Xd, W0d = to_dev_bf16(w.x_bits()), to_dev_bf16(w.w0_bits())
+    seg = M.build_segments(pool, ids_dev(w.row_adapter))
+    torch.cuda.synchronize()
+    M.timing_arm(16)
+    M.apply(pool, 0, Xd, W0d, seg, variant="split")
+    return [m[0] for m in M.timing_read()]
+
+
+def test_apply_large_batch_many_adapters(M):
+    """A large batch spread over 300 adapters: more segments than the
+    operand preparation has threads per block (256), all within the
+    epilogue's operand budget, so the GEMM epilogue adds every row's term."""
+    ranks = {i: (8 if i % 3 else 16) for i in range(300)}
+    ids = synth.random_ids(92, 2048, list(range(300)), 0.05)
+    ids[[3, 999]] = [300, -3]  # an id of the table that is not resident, and an invalid one
+    w = synth.custom("large_300ad", 92, 512, 4096, ids, ranks, max_adapters=301)
+    pool = make_pool(M, w)
+    say("many adapters: launches")
+    names = _apply_launches(M, w, pool)
+    assert "gemm_big_lora" in names and "expand" not in names and "expand_over" not in names, names
+    check_apply(M, w, variants=("split",), pool=pool)
+
+
+def test_apply_large_batch_epilogue_overrun(M):
+    """200 rank-64 adapters at dout 11008: one batch touching all of them
+    needs 200 * 64 = 12800 rank rows of packed Up (22016 bytes each), more
+    than the 256 MiB operand budget holds (12176), so the GEMM leaves the
+    low-rank term out and the expand that follows adds it; a batch of the
+    same pool over 40 of them fits, the epilogue adds the term and that
+    expand does nothing.  Every row against the oracle in both."""
+    ranks = {i: 64 for i in range(200)}
+    ids = (np.arange(1024) % 200).astype(np.int32)
+    ids[[7, 500]] = [-1, -3]  # a base-only row and an invalid id
+    w = synth.custom("overrun_200ad", 93, 512, 11008, ids, ranks)
+    pool = make_pool(M, w)
+    say("overrun: launches")
+    names = _apply_launches(M, w, pool)
+    assert names[-2:] == ["gemm_big_lora", "expand_over"], names
+    check_apply(M, w, variants=("split",), pool=pool)
+    ids40 = (np.arange(1024) % 40).astype(np.int32)
+    w40 = synth.custom("overrun_200ad", 93, 512, 11008, ids40, ranks)
+    say("overrun pool, 40 adapters in the batch")
+    check_apply(M, w40, variants=("split",), pool=pool)
+
+
 def test_invalid_ids_give_nan_rows(M):
     w = small_workload(31, 136, 72, 40, {0: 4, 2: 8}, p_none=0.1)
     ids = w.row_adapter.copy()
