@@ -13,8 +13,8 @@
 // radix pass is stable by construction: every wave owns a contiguous range
 // of entries, per-(digit, wave) counts are scanned digit-major, and inside a
 // 64-entry slice a lane's place among equal digits is the popcount of the
-// lower lanes holding the same digit (found with ballots), never an atomic's
-// arrival order.  The result is bit-exact and identical run to run.
+// lower lanes holding the same digit (found with one ballot per digit bit),
+// never an atomic's arrival order.  The result is bit-exact and identical run to run.
 #pragma once
 
 #include "internal.h"
@@ -29,6 +29,18 @@ __device__ __forceinline__ int row_key_of(int a, int rank_of_a, int max_adapters
   if (a == -1) return -1;
   if (a < -1 || a >= max_adapters) return -2;
   return rank_of_a > 0 ? a : -2;
+}
+
+// Workgroup barrier for the builder's LDS data only: the builder writes its
+// global outputs and never reads them back, so its barriers wait for the
+// LDS operations in flight but not for those stores (a __syncthreads()
+// would hold every wave until all its global stores were acknowledged).
+__device__ __forceinline__ void seg_sync() {
+  asm volatile("" ::: "memory");
+  // s_waitcnt lgkmcnt(0) (vmcnt and expcnt not waited)
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Writes the whole segment workspace `ws` for rows row_adapter[0, n), n <= 64.
@@ -52,7 +64,7 @@ __device__ __forceinline__ void seg_build_wave(const int32_t* __restrict__ row_a
   // row id and table entry travel in the same round trip
   const int a = valid ? row_adapter[lane] : -1;
   if (table && lane < A) s_rank[lane] = pool_rank[lane];
-  __syncthreads();
+  seg_sync();
   int key = A + 2, status = 0;  // lanes past n sort after everything
   if (valid) {
     const bool in_range = a >= 0 && a < A;
@@ -84,14 +96,14 @@ __device__ __forceinline__ void seg_build_wave(const int32_t* __restrict__ row_a
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) st |= __shfl_xor(st, m, 64);
   const int n_act = __popcll(act);
-  __syncthreads();
+  seg_sync();
   // segment starts among the active sorted positions
   const int kj = w0 && lane < n_act ? s_sorted[lane] : -1;
   const bool start = w0 && lane < n_act && (lane == 0 || s_sorted[lane - 1] != kj);
   const unsigned long long starts = __ballot(start);
   const int nseg = __popcll(starts);
   const int sidx = __popcll(starts & ((1ull << (lane & 63)) - 1ull));
-  __syncthreads();
+  seg_sync();
   if (start) {
     ws[MLORA_SEG_ADAPTER(n) + sidx] = kj;
     ws[MLORA_SEG_OFF(n) + sidx] = lane;
@@ -101,7 +113,7 @@ __device__ __forceinline__ void seg_build_wave(const int32_t* __restrict__ row_a
     ws[MLORA_SEG_OFF(n) + nseg] = n_act;
     s_sorted[nseg] = n_act;
   }
-  __syncthreads();
+  seg_sync();
   if (!w0) return;  // no barriers below
   // work items: ceil(len / ITEM_ROWS) per segment, in segment order
   int tiles = 0;
@@ -112,7 +124,7 @@ __device__ __forceinline__ void seg_build_wave(const int32_t* __restrict__ row_a
     const int y = __shfl_up(incl, d, 64);
     if (lane >= d) incl += y;
   }
-  const int n_items = __shfl(incl, 63, 64);
+  const int n_items = __builtin_amdgcn_readlane(incl, 63);
   int32_t* items = ws + MLORA_SEG_ITEMS(n);
   for (int t = 0; t < tiles; ++t) {
     items[2 * (incl - tiles + t)] = lane;
@@ -136,6 +148,27 @@ __device__ __forceinline__ void seg_build_wave(const int32_t* __restrict__ row_a
   if (lane >= 8 && lane < MLORA_SEG_HEADER) ws[lane] = lane == MLORA_SEG_NTILES ? nseg : 0;
 }
 
+// The valid lanes of the wave whose digit d (nbits <= 8 significant bits)
+// equals this lane's: those that agree with it on each of those bits (one
+// ballot per bit, whatever the number of distinct digits).
+__device__ __forceinline__ unsigned long long same_digit_lanes(bool valid, int d, int nbits) {
+  unsigned long long peers = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = ((d >> b) & 1) != 0;
+    const unsigned long long m = __ballot(valid && bit);
+    peers &= bit ? m : ~m;
+  }
+  return peers;
+}
+
+// Sum over the wave of v, 0 <= v < 32 (one ballot per bit).
+__device__ __forceinline__ int wave_sum_small(int v) {
+  int sum = 0;
+#pragma unroll
+  for (int b = 0; b < 5; ++b) sum += __popcll(__ballot(((v >> b) & 1) != 0)) << b;
+  return sum;
+}
+
 constexpr int kRadix = 256;
 constexpr int kMaxWaves = 16;
 
@@ -152,7 +185,7 @@ __device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
     if (lane >= d) x += y;
   }
   if (lane == 63) s_wave[wave] = x;
-  __syncthreads();
+  seg_sync();
   if (wave == 0) {
     int w = (lane < kWaves) ? s_wave[lane] : 0;
 #pragma unroll
@@ -162,10 +195,10 @@ __device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
     }
     if (lane < kWaves) s_wave[lane] = w;
   }
-  __syncthreads();
+  seg_sync();
   const int wave_prefix = wave ? s_wave[wave - 1] : 0;
   *total = s_wave[kWaves - 1];
-  __syncthreads();
+  seg_sync();
   return wave_prefix + x - v;
 }
 
@@ -205,34 +238,54 @@ __device__ __forceinline__ void seg_build_block(const int32_t* __restrict__ row_
   const int a_first = tid < n ? row_adapter[tid] : -1;
   if (table && tid < max_adapters) rank_tab[tid] = pool_rank[tid];
   if (tid < 3) s_cnt[tid] = 0;
-  __syncthreads();
+  seg_sync();
 
-  // 1. key of every row, packed with its index: (key << 16) | row
+  // 1. key of every row, packed with its index: (key << 16) | row; a
+  // thread's ids are fetched four rows at a time (one round trip each)
   int my_none = 0, my_bad = 0, my_status = 0;
-  for (int k = tid; k < n; k += kThreads) {
-    const int a = k == tid ? a_first : row_adapter[k];
-    uint32_t key;
-    if (a == -1) {
-      key = A;
-      ++my_none;
-    } else if (a < -1 || a >= max_adapters) {
-      key = A + 1;
-      ++my_bad;
-      my_status |= MLORA_SEG_BAD_ID;
-    } else if ((table ? rank_tab[a] : pool_rank[a]) <= 0) {
-      key = A + 1;
-      ++my_bad;
-      my_status |= MLORA_SEG_NOT_RESIDENT;
-    } else {
-      key = (uint32_t)a;
+  for (int k0 = tid; k0 < n; k0 += 4 * kThreads) {
+    int ids[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int k = k0 + u * kThreads;
+      ids[u] = k == tid ? a_first : (k < n ? row_adapter[k] : -1);
     }
-    bufA[k] = (key << 16) | (uint32_t)k;
-    row_key[k] = key < A ? (int32_t)key : (key == A ? -1 : -2);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int k = k0 + u * kThreads;
+      if (k >= n) break;
+      const int a = ids[u];
+      uint32_t key;
+      if (a == -1) {
+        key = A;
+        ++my_none;
+      } else if (a < -1 || a >= max_adapters) {
+        key = A + 1;
+        ++my_bad;
+        my_status |= MLORA_SEG_BAD_ID;
+      } else if ((table ? rank_tab[a] : pool_rank[a]) <= 0) {
+        key = A + 1;
+        ++my_bad;
+        my_status |= MLORA_SEG_NOT_RESIDENT;
+      } else {
+        key = (uint32_t)a;
+      }
+      bufA[k] = (key << 16) | (uint32_t)k;
+      row_key[k] = key < A ? (int32_t)key : (key == A ? -1 : -2);
+    }
   }
-  if (my_none) atomicAdd(&s_cnt[0], my_none);
-  if (my_bad) atomicAdd(&s_cnt[1], my_bad);
-  if (my_status) atomicOr(&s_cnt[2], my_status);
-  __syncthreads();
+  // one LDS atomic per wave for each count (a thread has at most 16 rows)
+  {
+    const int w_none = wave_sum_small(my_none), w_bad = wave_sum_small(my_bad);
+    const int w_status = (__ballot((my_status & MLORA_SEG_BAD_ID) != 0) ? MLORA_SEG_BAD_ID : 0) |
+                         (__ballot((my_status & MLORA_SEG_NOT_RESIDENT) != 0) ? MLORA_SEG_NOT_RESIDENT : 0);
+    if (lane == 0) {
+      if (w_none) atomicAdd(&s_cnt[0], w_none);
+      if (w_bad) atomicAdd(&s_cnt[1], w_bad);
+      if (w_status) atomicOr(&s_cnt[2], w_status);
+    }
+  }
+  seg_sync();
 
   // 2. stable sort of the packed (key, row) values, which are all distinct.
   // passes == 0 (at most one row per thread, up to 256 rows): a row's sorted
@@ -251,18 +304,21 @@ __device__ __forceinline__ void seg_build_block(const int32_t* __restrict__ row_
       for (int l = 0; l < 64; ++l) pos += (int)(__builtin_amdgcn_readlane(other, l) < me);
     }
     if (tid < n) bufB[pos] = me;
-    __syncthreads();
+    seg_sync();
     src = bufB;
     dst = bufA;
   }
   const int per = (((n + kWaves - 1) / kWaves) + 63) & ~63;
   const int beg = min(n, wave * per), end = min(n, wave * per + per);
+  // significant bits of the largest key, A + 1 (the invalid rows' key)
+  const int key_bits = 32 - __builtin_clz(A + 1u);
   for (int pass = 0; pass < passes; ++pass) {
     const int shift = 16 + 8 * pass;
+    const int nbits = min(8, key_bits - 8 * pass);
     for (int i = tid; i < kRadix * kWaves; i += kThreads) hist[i] = 0;
-    __syncthreads();
+    seg_sync();
     for (int i = beg + lane; i < end; i += 64) atomicAdd(&hist[((src[i] >> shift) & 255u) * kWaves + wave], 1u);
-    __syncthreads();
+    seg_sync();
     {
       const uint32_t v0 = hist[4 * tid], v1 = hist[4 * tid + 1], v2 = hist[4 * tid + 2], v3 = hist[4 * tid + 3];
       int total;
@@ -272,29 +328,20 @@ __device__ __forceinline__ void seg_build_block(const int32_t* __restrict__ row_
       hist[4 * tid + 2] = ex + v0 + v1;
       hist[4 * tid + 3] = ex + v0 + v1 + v2;
     }
-    __syncthreads();
+    seg_sync();
     for (int base = beg; base < end; base += 64) {
       const int i = base + lane;
       const bool valid = i < end;
       const uint32_t e = valid ? src[i] : 0u;
       const int d = (int)((e >> shift) & 255u);
-      // lanes holding the same digit as this lane
-      unsigned long long peers = 0ull;
-      unsigned long long todo = __ballot(valid);
-      while (todo) {
-        const int leader = __ffsll(todo) - 1;
-        const int dl = __shfl(d, leader, 64);
-        const unsigned long long m = __ballot(valid && d == dl);
-        if (valid && d == dl) peers = m;
-        todo &= ~m;
-      }
+      const unsigned long long peers = same_digit_lanes(valid, d, nbits);
       const unsigned long long below = peers & ((1ull << lane) - 1ull);
       if (valid) dst[hist[d * kWaves + wave] + (uint32_t)__popcll(below)] = e;
       // the lowest lane of each digit advances that digit's cursor (after
       // every lane of the wave has read it: LDS ops of one wave are ordered)
       if (valid && below == 0ull) hist[d * kWaves + wave] += (uint32_t)__popcll(peers);
     }
-    __syncthreads();
+    seg_sync();
     uint32_t* t = src;
     src = dst;
     dst = t;
@@ -312,30 +359,33 @@ __device__ __forceinline__ void seg_build_block(const int32_t* __restrict__ row_
     inv[k] = j;
   }
 
-  // 4. segments: a new one starts wherever the key changes among active rows
-  int nseg = 0;
-  for (int base = 0; base < n_act; base += kThreads) {
-    const int j = base + tid;
-    int flag = 0;
-    uint32_t key = 0;
-    if (j < n_act) {
-      key = sorted[j] >> 16;
-      flag = (j == 0) || ((sorted[j - 1] >> 16) != key);
-    }
+  // 4. segments: a new one starts wherever the key changes among active rows.
+  // Each thread takes a run of E consecutive sorted positions, so one block
+  // scan numbers them all.
+  int nseg;
+  {
+    const int E = (n_act + kThreads - 1) / kThreads;
+    const int j0 = tid * E, j1 = min(n_act, j0 + E);
+    int cnt = 0;
+    for (int j = j0; j < j1; ++j) cnt += (j == 0) || ((sorted[j - 1] >> 16) != (sorted[j] >> 16));
     int total;
-    const int ex = block_exclusive_scan<NT>(flag, s_wave, &total);
-    if (flag) {
-      offs[nseg + ex] = (uint32_t)j;
-      seg_adapter[nseg + ex] = (int32_t)key;
-      seg_off[nseg + ex] = j;
+    int at = block_exclusive_scan<NT>(cnt, s_wave, &total);
+    for (int j = j0; j < j1; ++j) {
+      const uint32_t key = sorted[j] >> 16;
+      if ((j == 0) || ((sorted[j - 1] >> 16) != key)) {
+        offs[at] = (uint32_t)j;
+        seg_adapter[at] = (int32_t)key;
+        seg_off[at] = j;
+        ++at;
+      }
     }
-    nseg += total;
+    nseg = total;
   }
   if (tid == 0) {
     offs[nseg] = (uint32_t)n_act;
     seg_off[nseg] = n_act;
   }
-  __syncthreads();
+  seg_sync();
 
   // 5. work items: ceil(len / ITEM_ROWS) per segment, in segment order
   uint32_t* item_end = sorted;  // the sorted keys are no longer needed
@@ -349,7 +399,7 @@ __device__ __forceinline__ void seg_build_block(const int32_t* __restrict__ row_
     if (s < nseg) item_end[s] = (uint32_t)(n_items + ex + t);
     n_items += total;
   }
-  __syncthreads();
+  seg_sync();
   for (int i = tid; i < n_items; i += kThreads) {
     int lo = 0, hi = nseg - 1;
     while (lo < hi) {
@@ -360,7 +410,7 @@ __device__ __forceinline__ void seg_build_block(const int32_t* __restrict__ row_
     items[2 * i] = lo;
     items[2 * i + 1] = (int)offs[lo] + (i - first) * MLORA_ITEM_ROWS;
   }
-  __syncthreads();
+  seg_sync();
 
   // 6. tiles: ceil(len / TILE_ROWS) per segment, in segment order
   int32_t* tiles = ws + MLORA_SEG_TILES(n);
@@ -375,7 +425,7 @@ __device__ __forceinline__ void seg_build_block(const int32_t* __restrict__ row_
     if (s < nseg) tile_end[s] = (uint32_t)(n_tiles + ex + t);
     n_tiles += total;
   }
-  __syncthreads();
+  seg_sync();
   for (int i = tid; i < n_tiles; i += kThreads) {
     int lo = 0, hi = nseg - 1;
     while (lo < hi) {
