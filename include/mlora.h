@@ -130,11 +130,20 @@ typedef struct mlora_pool_desc {
 
 size_t mlora_pool_meta_bytes(int32_t max_adapters, int32_t n_proj, int32_t max_rank);
 
-/* Creates the host handle, binds it to the current device and clears the
- * device metadata on `stream` (no adapter resident).  The three device
- * buffers stay owned by the caller and must outlive the pool. */
+/* Creates the host handle of an adapter pool in HBM (M031 card, section
+ * 06: adapters kept in GPU memory as pages, the pool sized by max_adapters
+ * and max_rank; wiblog article, memory cost: one paged pool for every
+ * adapter), binds it to the current device and clears the device metadata
+ * on `stream` (no adapter resident).  The three device buffers stay owned
+ * by the caller and must outlive the pool.  Errors: MLORA_EINVAL for a
+ * descriptor outside the documented ranges or misaligned buffers,
+ * MLORA_EHIP. */
 mlora_status mlora_pool_create(const mlora_pool_desc* desc, void* stream, mlora_pool** out);
-mlora_status mlora_pool_destroy(mlora_pool* pool); /* waits for its own pending copies */
+/* Releases the host handle after waiting for the pool's own pending copies
+ * (M031 card, section 07: an adapter's storage goes only after its last
+ * reader); the caller frees the device buffers afterwards.  Errors:
+ * MLORA_EINVAL for NULL, MLORA_EHIP if a pending copy failed. */
+mlora_status mlora_pool_destroy(mlora_pool* pool);
 
 /* Loads adapter `adapter_id` with the given rank and scale:
  *   down: host bf16 [n_proj][rank][din]   (Down, the "lora A" layout)
@@ -241,6 +250,15 @@ mlora_status mlora_build_segments(const mlora_pool* pool, const int32_t* row_ada
  * stream (for tests and for callers that want to check the status word). */
 mlora_status mlora_segments_header(const void* seg_ws, int32_t* header, void* stream);
 
+/* The batch's status word alone (MLORA_SEG_BAD_ID | MLORA_SEG_NOT_RESIDENT,
+ * 0 when every id was -1 or a resident adapter) copied to host `status`;
+ * SYNCHRONISES the stream.  The rows behind a nonzero status are NaN rows in
+ * Y: a request bound to an id that is not loaded is reported, never served
+ * by another adapter (M031 card, section 03: a wrong write-back is wrong
+ * semantics even without a shape error; section 07: weights resident
+ * before use).  Errors: MLORA_EINVAL for a NULL pointer, MLORA_EHIP. */
+mlora_status mlora_segments_status(const void* seg_ws, int32_t* status, void* stream);
+
 /* ---------------------------------------------------------------------------
  * The steps of the layer, each usable on its own
  * ------------------------------------------------------------------------- */
@@ -303,7 +321,9 @@ mlora_status mlora_gemm_lora(const mlora_pool* pool, int32_t proj, const uint16_
                              void* stream);
 
 /* ---------------------------------------------------------------------------
- * The whole layer for one projection of one batch:
+ * The whole layer for one projection of one batch (M031 card, section 02:
+ * one base product shared by all rows, each row's low-rank term from its
+ * own adapter written back at its original row; section 03 worked example):
  *   Y = X W0^T, then every row's low-rank term added at its original row.
  *   X: device bf16 [n_rows][din]; W0: device bf16 [dout][din] (projection
  *   `proj`'s base weight); Y: device bf16 [n_rows][dout] (overwritten);
@@ -312,6 +332,9 @@ mlora_status mlora_gemm_lora(const mlora_pool* pool, int32_t proj, const uint16_
  *   mlora_work_bytes(pool, n_rows) bytes, 256-byte aligned.
  * n_rows = 0 is a no-op.
  * ------------------------------------------------------------------------- */
+/* mlora_work_bytes: the scratch any variant of mlora_apply needs for a batch
+ * of n_rows on this pool (t per row and rank, split-K partials, the
+ * epilogue's operands); 0 for a NULL pool or n_rows < 0.  Host only. */
 size_t mlora_work_bytes(const mlora_pool* pool, int32_t n_rows);
 
 /* The launch plan mlora_apply follows for `variant` (AUTO resolved) on a

@@ -21,7 +21,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = [
-    "MloraError", "lib", "Pool", "build_segments", "segments_header", "read_segments",
+    "MloraError", "lib", "Pool", "build_segments", "segments_header", "segments_status", "read_segments",
     "base_gemm", "shrink", "shrink_max_chunks", "expand", "fused", "shrink_rows", "gemm_lora", "new_work", "rows_t", "apply", "forward", "plan", "work_bytes",
     "forward_static", "STATIC_SCRATCH_BYTES", "merge", "hbm_copy", "hbm_read", "timing_arm", "timing_read", "VARIANTS", "ITEM_ROWS", "TILE_ROWS", "MAX_ROWS", "MAX_RANK", "SEG", "EXPORTS", "LIB_PATH",
 ]
@@ -65,6 +65,7 @@ EXPORTS = {
     "mlora_segments_bytes": (_sz, [_i32]),
     "mlora_build_segments": (ctypes.c_int, [_c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p]),
     "mlora_segments_header": (ctypes.c_int, [_c_void_p, _pi32, _c_void_p]),
+    "mlora_segments_status": (ctypes.c_int, [_c_void_p, _pi32, _c_void_p]),
     "mlora_base_gemm": (ctypes.c_int, [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _c_void_p]),
     "mlora_shrink_max_chunks": (_i32, [_i32]),
     "mlora_shrink": (ctypes.c_int, [_c_void_p, _i32, _c_void_p, _c_void_p, _i32, _c_void_p, _i32, _c_void_p]),
@@ -261,6 +262,13 @@ def segments_header(seg_ws) -> dict:
     h = (ctypes.c_int32 * SEG_HEADER)()
     _check(lib().mlora_segments_header(_ptr(seg_ws), h, _stream()), "mlora_segments_header")
     return {k: int(h[i]) for k, i in SEG.items()}
+
+
+def segments_status(seg_ws) -> int:
+    """The batch's status word (SEG_BAD_ID | SEG_NOT_RESIDENT bits; synchronises the stream)."""
+    st = ctypes.c_int32(0)
+    _check(lib().mlora_segments_status(_ptr(seg_ws), ctypes.byref(st), _stream()), "mlora_segments_status")
+    return int(st.value)
 
 
 def read_segments(seg_ws, n: int) -> dict:

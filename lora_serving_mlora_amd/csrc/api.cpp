@@ -722,6 +722,15 @@ mlora_status mlora_segments_header(const void* seg_ws, int32_t* header, void* st
   return MLORA_OK;
 }
 
+mlora_status mlora_segments_status(const void* seg_ws, int32_t* status, void* stream) {
+  g_err.clear();
+  if (!seg_ws || !status) return fail(MLORA_EINVAL, "seg_ws and status must not be NULL");
+  HIP_TRY(hipMemcpyAsync(status, static_cast<const int32_t*>(seg_ws) + MLORA_SEG_STATUS, sizeof(int32_t),
+                         hipMemcpyDeviceToHost, as_stream(stream)));
+  HIP_TRY(hipStreamSynchronize(as_stream(stream)));
+  return MLORA_OK;
+}
+
 mlora_status mlora_base_gemm(const uint16_t* X, const uint16_t* W0, uint16_t* Y, int32_t n, int32_t din,
                              int32_t dout, void* stream) {
   g_err.clear();

@@ -417,7 +417,12 @@ def test_invalid_ids_give_nan_rows(M):
     seg_ws = M.build_segments(pool, ids_dev(ids))
     h = M.segments_header(seg_ws)
     assert h["status"] == O.STATUS_BAD_ID | O.STATUS_NOT_RESIDENT and h["n_bad"] == 3
+    assert M.segments_status(seg_ws) == h["status"]
     check_apply(M, w, pool=pool)
+    # a batch of resident and base-only rows reports no problem
+    ok = ids.copy()
+    ok[[3, 7, 11]] = [0, -1, 2]
+    assert M.segments_status(M.build_segments(pool, ids_dev(ok))) == 0
 
 
 def test_zero_rows_is_a_noop(M):

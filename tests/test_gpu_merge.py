@@ -49,6 +49,10 @@ MERGE_CASES = [
     (4, 4096, 512, {0: 16, 1: 64}, 1, 0),      # several column blocks, 16-row tail-free
     (5, 2056, 1000, {0: 128, 2: 1}, 1, 0),     # largest rank; dout not a multiple of 16
     (6, 4096, 4096, {0: 16, 1: 16, 2: 16}, 1, 0),  # the decode workload's shape
+    # rank <= 16 on 16-byte rows (Down held in registers over 16 rows): a
+    # partial column block (din 2056) and a ragged last row block (dout 1000)
+    (7, 2056, 1000, {0: 5, 1: 9}, 2, 1),
+    (8, 512, 24, {0: 17}, 1, 0),               # rank 17: the general form on 16-byte rows
 ]
 
 
