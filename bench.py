@@ -741,10 +741,11 @@ def main():
     del ctx, pool, X, W0s, seg_ws, Y, work
     torch.cuda.empty_cache()
     if not args.no_configs:
-        # the other workloads where a target is judged, each timed the same
-        # way (its own seeded inputs, its own rotation) with fewer steps
+        # the other workloads where a target is judged, and the decode step
+        # on a down projection (din 11008), each timed the same way (its own
+        # seeded inputs, its own rotation) with fewer steps
         configs = {}
-        for other in ("decode_frag", "prefill", "layer_stack"):
+        for other in ("decode_frag", "prefill", "layer_stack", "decode_down"):
             if other == args.workload:
                 continue
             m2, c2 = run_workload(M, torch, other, max(3, min(K, args.config_steps)), min(W, 3))

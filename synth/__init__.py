@@ -174,6 +174,23 @@ def decode_fragmented() -> Workload:
         max_adapters=256, max_rank=16, **_DECODE_STD)
 
 
+def decode_down_projection() -> Workload:
+    """The 32-token decode step of decode_3_adapters (20/8/4 over three
+    rank-16 adapters, rows shuffled) on the down projection of the prefill
+    workload's MLP: din 11008 -> dout 4096, the transpose of its 4096 ->
+    11008 shape.  The same distributions as decode_3_adapters (Down ~
+    N(0, 1/din) with din = 11008)."""
+    seed = 1006
+    g = _rng(seed, _TAG_IDS)
+    ids = np.array([0] * 20 + [1] * 8 + [2] * 4, dtype=np.int32)
+    ids = g.permutation(ids).astype(np.int32)
+    std = dict(_DECODE_STD, down_std=1.0 / np.sqrt(11008.0))
+    return Workload(
+        name="decode_32tok_3ad_down_11008x4096", seed=seed, din=11008, dout=4096, n_proj=1,
+        row_adapter=ids, ranks={a: 16 for a in range(3)}, scales={a: 2.0 for a in range(3)},
+        max_adapters=3, max_rank=16, **std)
+
+
 def prefill_hetero() -> Workload:
     """Heterogeneous-rank prefill: din 4096, dout 11008, 4096 tokens in 8
     requests over 6 adapters of ranks {8, 16, 64}; 10% of rows base-only;
@@ -247,8 +264,9 @@ NAMED: Dict[str, Callable[[], Workload]] = {
     "decode_frag": decode_fragmented,
     "prefill": prefill_hetero,
     "layer_stack": layer_stack,
+    "decode_down": decode_down_projection,
 }
-ORDER = ["worked_example", "decode_3", "decode_frag", "prefill", "layer_stack"]
+ORDER = ["worked_example", "decode_3", "decode_frag", "prefill", "layer_stack", "decode_down"]
 
 
 def request_rows(w: Workload) -> List[np.ndarray]:

@@ -35,6 +35,13 @@ def test_decode_3_split():
     assert w.row_adapter.tolist() != sorted(w.row_adapter.tolist())
 
 
+def test_decode_down_is_the_decode_split_on_the_down_projection():
+    w = synth.decode_down_projection()
+    assert (w.din, w.dout, w.n) == (11008, 4096, 32)
+    assert np.bincount(w.row_adapter).tolist() == [20, 8, 4]
+    assert w.down_std == pytest.approx(1.0 / np.sqrt(11008.0))
+
+
 def test_decode_frag_is_a_permutation():
     w = synth.decode_fragmented()
     assert sorted(w.row_adapter.tolist()) == list(range(256))
