@@ -619,8 +619,8 @@ def run_workload(M, torch, name, steps, warmup, variant_arg="auto", rotate_bytes
     per_step = len(marks) // KT
     kernels = [marks[j][0] for j in range(per_step)]
     per_kernel_ms = {}
-    for j, name in enumerate(kernels):
-        key = name if name not in per_kernel_ms else f"{name}#{j}"
+    for j, kname in enumerate(kernels):
+        key = kname if kname not in per_kernel_ms else f"{kname}#{j}"
         per_kernel_ms[key] = float(np.mean([marks[i * per_step + j][1] for i in range(KT)]))
     kernel_sum_ms = float(np.mean([sum(m[1] for m in marks[i * per_step:(i + 1) * per_step]) for i in range(KT)]))
     queue_ok = spin is not None and host_enqueue_s * 1e3 < (0.05 + 100e-6 * K) * 1e3

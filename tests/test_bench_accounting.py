@@ -106,3 +106,29 @@ def test_more_than_one_gpu_is_refused_with_a_message():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_run_workload_keeps_the_workload_name_for_the_traffic_lookup():
+    """The measured-traffic lookup is keyed by (kernel, workload): nothing in
+    run_workload may rebind its `name` parameter (a loop variable of that
+    name once made every lookup miss)."""
+    import ast
+    tree = ast.parse(open(os.path.join(ROOT, "bench.py")).read())
+    fn = next(n for n in ast.walk(tree) if isinstance(n, ast.FunctionDef) and n.name == "run_workload")
+    assert "name" in [a.arg for a in fn.args.args]
+    rebound = [n.lineno for n in ast.walk(fn)
+               if isinstance(n, ast.Name) and n.id == "name" and isinstance(n.ctx, ast.Store)]
+    assert rebound == [], f"`name` rebound at bench.py lines {rebound}"
+
+
+def test_traffic_lookup_resolves_committed_records():
+    """Every record in profiles/traffic.json is found under its own (kernel,
+    workload) key whenever its source hash is current."""
+    import json
+    recs = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+    for key, rec in recs.items():
+        kernel, workload = key.rsplit("/", 1)
+        got = bench.measured_traffic(kernel, workload)
+        want = rec["bytes_per_launch"] if rec["source_sha256_16"] == bench.source_hash(kernel) else None
+        assert got == want, key
+
