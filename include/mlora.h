@@ -63,7 +63,9 @@ typedef enum mlora_variant {
   MLORA_VARIANT_AUTO = 0,  /* ROWS up to 1024 rows, SPLIT above                  */
   MLORA_VARIANT_SPLIT = 1, /* base GEMM, then shrink kernel -> fp32 t in `work`
                               -> expand kernel (large batches: the expand in the
-                              GEMM's epilogue instead)                           */
+                              GEMM's epilogue instead, unless the batch's Up
+                              blocks overrun the epilogue's 256 MiB operand
+                              budget; then an expand follows the GEMM)           */
   MLORA_VARIANT_FUSED = 2, /* base GEMM, then one kernel per work item of up to
                               MLORA_ITEM_ROWS rows: t stays on chip              */
   MLORA_VARIANT_ROWS = 3   /* n_rows <= 1024: the per-row shrink inside the
