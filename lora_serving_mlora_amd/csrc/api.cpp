@@ -861,17 +861,21 @@ namespace {
 // over the chip, never more than kMaxSplitChunks
 // the large-batch epilogue's operands (t per row in bf16, adapter offsets,
 // Up blocks with ranks contiguous)
-// Operands of the large-batch GEMM's low-rank epilogue, in `work` after the
-// shrink's slices: tb [n][wt] bf16 | koff [max_adapters] | over (one word) |
-// upt, room for upt_units rank rows of dout.  upt_units is every adapter of
-// the batch padded to the largest rank, or as many rank rows as fit in a
-// 256 MiB budget for the operands if that is less: then a batch whose
-// distinct adapters (known only on the device) need more has its low-rank
-// term added by a separate expand instead of the epilogue (may_overrun).
+// Operands of the large-batch GEMM's low-rank term, in `work` after the
+// shrink's slices: tb [n][wt] bf16 | koff [max_adapters] | over, kx (one
+// word each) | tx [n][txw] bf16 | upt, room for upt_units rank rows of dout.
+// upt_units is every adapter of the batch padded to the largest rank, or as
+// many rank rows as fit in a 256 MiB budget for the operands if that is
+// less: then a batch whose distinct adapters (known only on the device) need
+// more has its low-rank term added by a separate expand instead of the
+// epilogue (may_overrun).  txw (the widest rank-concatenated batch, Ux
+// living in the upt region) is the largest multiple of 64 up to
+// kMaxConcatRanks that upt_units holds.
 constexpr size_t kMaxEpilogueBytes = 256u << 20;
 struct EpilogueLayout {
-  size_t koff, over, upt, total;
+  size_t koff, over, kx, tx, upt, total;
   long upt_units;
+  int txw;
   bool may_overrun;
 };
 EpilogueLayout epilogue_layout(const mlora_pool* p, int n) {
@@ -879,11 +883,15 @@ EpilogueLayout epilogue_layout(const mlora_pool* p, int n) {
   EpilogueLayout L{};
   L.koff = align256((size_t)n * wt * 2);
   L.over = L.koff + align256((size_t)p->d.max_adapters * 4);
-  L.upt = L.over + 256;
-  const size_t row = (size_t)p->d.dout * 2;
+  L.kx = L.over + 4;
   const long worst = (long)mlora::lora_upt_units(n, p->d.max_adapters, p->d.max_rank);
+  L.txw = (int)std::min<long>(mlora::kMaxConcatRanks, worst / 64 * 64);
+  L.tx = L.over + 256;
+  L.upt = L.tx + align256((size_t)n * L.txw * 2);
+  const size_t row = (size_t)p->d.dout * 2;
   const long budget = L.upt < kMaxEpilogueBytes ? (long)((kMaxEpilogueBytes - L.upt) / row) / 16 * 16 : 0;
   L.upt_units = std::min(worst, budget);
+  if (L.upt_units < L.txw) L.txw = (int)(L.upt_units / 64 * 64);
   L.may_overrun = L.upt_units < worst;
   L.total = L.upt + align256((size_t)L.upt_units * row);
   return L;
@@ -993,13 +1001,16 @@ mlora_status mlora_apply(const mlora_pool* p, int32_t proj, const uint16_t* X, c
     uint16_t* tb = reinterpret_cast<uint16_t*>(w);
     int32_t* koff = reinterpret_cast<int32_t*>(w + L.koff);
     int32_t* over = reinterpret_cast<int32_t*>(w + L.over);
+    int32_t* kx = reinterpret_cast<int32_t*>(w + L.kx);
+    uint16_t* tx = L.txw > 0 ? reinterpret_cast<uint16_t*>(w + L.tx) : nullptr;
     uint16_t* upt = reinterpret_cast<uint16_t*>(w + L.upt);
     st = hip_check(mlora::launch_shrink(v, proj, X, ws, n, T, chunks, chunk_elems_for(d.din, chunks), s), "shrink launch");
     if (st != MLORA_OK) return st;
-    st = hip_check(mlora::launch_lora_prep(v, proj, ws, n, T, chunks, tb, wt, koff, upt, L.upt_units, over, s),
+    st = hip_check(mlora::launch_lora_prep(v, proj, ws, n, T, chunks, tb, wt, koff, upt, L.upt_units, over, tx,
+                                           L.txw, kx, s),
                    "low-rank operand launch");
     if (st != MLORA_OK) return st;
-    const mlora::LoraOperands lo{tb, koff, upt, wt, L.may_overrun ? over : nullptr};
+    const mlora::LoraOperands lo{tb, koff, upt, wt, L.may_overrun ? over : nullptr, tx, L.txw, tx ? kx : nullptr};
     st = hip_check(mlora::launch_big_lora(v, X, W0, ws, lo, Y, n, s), "GEMM + low-rank epilogue launch");
     if (st != MLORA_OK || !L.may_overrun) return st;
     return hip_check(mlora::launch_expand_over(v, proj, T, chunks, ws, Y, n, over, s), "overrun expand launch");

@@ -520,6 +520,9 @@ constexpr int vmcnt_imm(int v) { return (v & 15) | ((v >> 4) << 14) | (7 << 4) |
 struct RingCtx {
   __amdgpu_buffer_rsrc_t rsa, rsb;
   int voff, voff64, row_bytes, wave, wm, wn, fr, fk;
+  // rank-concatenated stages (kt >= kmain): Tx and Ux rows, xrow_bytes long
+  __amdgpu_buffer_rsrc_t rsx, rsu;
+  int voffx, xrow_bytes, kmain;
 };
 
 // ---------------------------------------------------------------------------
@@ -549,21 +552,32 @@ __device__ __forceinline__ int swz8(int row, int chunk) { return row * GBK64 + (
 // DMA of 64-deep K tile kt into (da, db): instruction j of this wave covers
 // tile rows 8i..8i+7, i = wave + 4j; lane L fills row L >> 3 of the group,
 // physical chunk L & 7 (voff64: the logical chunk that slot holds, which
-// depends on the row's parity group, the same for all i of a wave)
-template <int TM, int TN>
+// depends on the row's parity group, the same for all i of a wave).
+// EXT: tiles kt >= kmain come from the rank-concatenated operands (tile
+// kt - kmain of Tx and Ux), chosen by selects, not a branch, so the DMAs stay
+// in the block the callers' schedule interleaves with the MFMAs.
+template <int TM, int TN, bool EXT = false>
 __device__ __forceinline__ void ring64_issue(const RingCtx& c, uint16_t* __restrict__ da, uint16_t* __restrict__ db,
                                              int kt) {
+  __amdgpu_buffer_rsrc_t ra = c.rsa, rb = c.rsb;
+  int voff = c.voff64, rbytes = c.row_bytes, ko = kt * GBK64 * 2;
+  if constexpr (EXT) {
+    const bool x = kt >= c.kmain;
+    ra = x ? c.rsx : c.rsa;
+    rb = x ? c.rsu : c.rsb;
+    voff = x ? c.voffx : c.voff64;
+    rbytes = x ? c.xrow_bytes : c.row_bytes;
+    ko = (x ? kt - c.kmain : kt) * GBK64 * 2;
+  }
 #pragma unroll
   for (int j = 0; j < TM / 32; ++j) {
     const int i = c.wave + 4 * j;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsa, da + i * 8 * GBK64, 16, c.voff64,
-                                             i * 8 * c.row_bytes + kt * GBK64 * 2, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, da + i * 8 * GBK64, 16, voff, i * 8 * rbytes + ko, 0, 0);
   }
 #pragma unroll
   for (int j = 0; j < TN / 32; ++j) {
     const int i = c.wave + 4 * j;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsb, db + i * 8 * GBK64, 16, c.voff64,
-                                             i * 8 * c.row_bytes + kt * GBK64 * 2, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, db + i * 8 * GBK64, 16, voff, i * 8 * rbytes + ko, 0, 0);
   }
 }
 
@@ -607,7 +621,7 @@ __device__ __forceinline__ void ring64_step(const RingCtx& c, const uint16_t* __
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cf.a[q][i]), as_bf16x8(cf.b[q][j]), acc[i][j], 0,
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cf.b[q][j]), as_bf16x8(cf.a[q][i]), acc[i][j], 0,
                                                             0, 0);
 #pragma unroll
   for (int r = 0; r < kReads; ++r) {
@@ -695,12 +709,12 @@ __device__ __forceinline__ void ring64_mfma_half(const RingHalf<TM, TN>& f, floa
 #pragma unroll
       for (int j = 0; j < TN / 64; ++j)
         acc[i][j] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(f.a[q][i]), as_bf16x8(f.b[q][j]), acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(f.b[q][j]), as_bf16x8(f.a[q][i]), acc[i][j], 0, 0, 0);
 }
 
 // stage k in (ca, cb), the other buffer (oa, ob) holds stage k+1 (landed
 // before this call); h0 holds the first half of stage k
-template <int TM, int TN>
+template <int TM, int TN, bool EXT>
 __device__ __forceinline__ void ring64x2_stage(const RingCtx& c, uint16_t* __restrict__ ca, uint16_t* __restrict__ cb,
                                                const uint16_t* __restrict__ oa, const uint16_t* __restrict__ ob,
                                                int kt, int kend, RingHalf<TM, TN>& h0, RingHalf<TM, TN>& h1,
@@ -722,7 +736,7 @@ __device__ __forceinline__ void ring64x2_stage(const RingCtx& c, uint16_t* __res
   ring_barrier();
   // second half: DMA of stage k+2 into this buffer, MFMAs on h1, reads of
   // the next stage's first half into h0
-  ring64_issue<TM, TN>(c, ca, cb, min(kt + 2, kend - 1));
+  ring64_issue<TM, TN, EXT>(c, ca, cb, min(kt + 2, kend - 1));
   ring64_read_half<TM, TN>(c, oa, ob, 0, h0);
   ring64_mfma_half<TM, TN>(h1, acc);
 #pragma unroll
@@ -734,20 +748,22 @@ __device__ __forceinline__ void ring64x2_stage(const RingCtx& c, uint16_t* __res
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int TM, int TN>
+// EXT: K tiles [kt0, c.kmain) of X and W, then [c.kmain, kend) of the
+// rank-concatenated operands (kend - kt0 may then be odd; c.kmain - kt0 >= 2)
+template <int TM, int TN, bool EXT = false>
 __device__ __forceinline__ void ring64x2_loop(const RingCtx& c, uint16_t* __restrict__ a0, uint16_t* __restrict__ a1,
                                               uint16_t* __restrict__ b0, uint16_t* __restrict__ b1, int kt0, int kend,
                                               floatx16 (&acc)[TM / 64][TN / 64]) {
   constexpr int n = (TM + TN) / 32;
   ring64_issue<TM, TN>(c, a0, b0, kt0);
-  ring64_issue<TM, TN>(c, a1, b1, min(kt0 + 1, kend - 1));
+  ring64_issue<TM, TN>(c, a1, b1, min(kt0 + 1, (EXT ? c.kmain : kend) - 1));
   RingHalf<TM, TN> h0, h1;
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(n));  // stage kt0 has landed
   ring_barrier();
   ring64_read_half<TM, TN>(c, a0, b0, 0, h0);
-  for (int kt = kt0; kt < kend; kt += 2) {  // (kend - kt0) even: K is a multiple of 128
-    ring64x2_stage<TM, TN>(c, a0, b0, a1, b1, kt, kend, h0, h1, acc);
-    ring64x2_stage<TM, TN>(c, a1, b1, a0, b0, kt + 1, kend, h0, h1, acc);
+  for (int kt = kt0; kt < kend; kt += 2) {  // (without EXT kend - kt0 is even: K is a multiple of 128)
+    ring64x2_stage<TM, TN, EXT>(c, a0, b0, a1, b1, kt, kend, h0, h1, acc);
+    if (!EXT || kt + 1 < kend) ring64x2_stage<TM, TN, EXT>(c, a1, b1, a0, b0, kt + 1, kend, h0, h1, acc);
   }
   __builtin_amdgcn_s_waitcnt(0);
 }
@@ -873,7 +889,7 @@ __device__ __forceinline__ void ring_lora_epilogue(int wr, int wc, int M, int N,
       for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[k][i]), as_bf16x8(fb[k][j]), acc[i][j],
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fb[k][j]), as_bf16x8(fa[k][i]), acc[i][j],
                                                               0, 0, 0);
     }
   }
@@ -904,6 +920,70 @@ __device__ __forceinline__ void shrink_row_body_ids(const PoolView& pv, int proj
   if (key < 0) return;  // base-only or invalid: no low-rank term
   shrink_row_to<VEC, NW>(pv, pv.down_page + ((size_t)key * pv.n_proj + proj) * pv.max_rank, rk, pv.scale[key],
                          X + (size_t)k * pv.din, T + (size_t)k * pv.max_rank);
+}
+
+// The store of a wave's MI x NJ accumulator blocks (rows wr + 32 i, columns
+// wc + 32 j) through LDS, `st` being the wave's own buffer of at least
+// MI 32 rows x NJ 32 elements (bf16 Y, or fp32 partials `pt` when PART).
+// Rows of the buffer are RB bytes, CH 16-byte chunks, XOR-swizzled by
+// row % CH so that both the scattered piece writes and the row reads spread
+// over the banks.  Each read pass covers 64 / CH rows, one 16-byte piece per
+// lane; pieces past N, and every piece when N or the output is not aligned
+// to 16 bytes per piece, go out element by element.
+template <int MI, int NJ, bool PART>
+__device__ __forceinline__ void ring_store_tile(int wave, int wr, int wc, int M, int N, uint16_t* __restrict__ Y,
+                                                float* __restrict__ pt, floatx16 (&acc)[MI][NJ], uint16_t* st16) {
+  constexpr int ES = PART ? 4 : 2;  // bytes per element
+  constexpr int RB = NJ * 32 * ES, CH = RB / 16, EPC = 16 / ES, RPP = 64 / CH;
+  static_assert(CH == 8 || CH == 16, "rows of 128 or 256 bytes");
+  char* st = reinterpret_cast<char*>(st16);
+  const int lane = threadIdx.x & 63, h = lane >> 5, lr = lane & 31;
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int R = i * 32 + lr, off = (j * 32 + 8 * g + 4 * h) * ES;
+        char* d = st + R * RB + (((off >> 4) ^ (R % CH)) << 4) + (off & 15);
+        const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1], v2 = acc[i][j][4 * g + 2],
+                    v3 = acc[i][j][4 * g + 3];
+        if constexpr (PART)
+          *reinterpret_cast<float4*>(d) = make_float4(v0, v1, v2, v3);
+        else
+          *reinterpret_cast<uint2*>(d) = make_uint2(pack_bf2(v0, v1), pack_bf2(v2, v3));
+      }
+  // the wave's own LDS writes before its reads: DS instructions of a wave
+  // complete in order, the fence keeps the compiler from reordering them
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int cc = lane % CH, rr = lane / CH;
+  const int col = wc + cc * EPC;
+  const bool vec = N % EPC == 0 && (PART ? reinterpret_cast<uintptr_t>(pt) : reinterpret_cast<uintptr_t>(Y)) % 16 == 0;
+#pragma unroll
+  for (int p = 0; p < MI * 32 / RPP; ++p) {
+    const int R = p * RPP + rr, row = wr + R;
+    const uint4 v = *reinterpret_cast<const uint4*>(st + R * RB + ((cc ^ (R % CH)) << 4));
+    if (row >= M || col >= N) continue;
+    if (vec) {
+      if constexpr (PART)
+        *reinterpret_cast<uint4*>(pt + (size_t)row * N + col) = v;
+      else
+        *reinterpret_cast<uint4*>(Y + (size_t)row * N + col) = v;
+    } else {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        if (col + e < N) {
+          if constexpr (PART)
+            pt[(size_t)row * N + col + e] = __uint_as_float(w[e]);
+          else
+            Y[(size_t)row * N + col + e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
+  }
 }
 
 // IDS (co-resident form only): the shrink workgroups take each row's key
@@ -997,11 +1077,31 @@ __device__ __forceinline__ void gemm_ring_body(
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   const int kt0 = PART ? blockIdx.y * kt_per : 0;
-  const int kend = PART ? kt0 + kt_per : K / GBK64;
+  int kend = PART ? kt0 + kt_per : K / GBK64;
+  // LORA: a batch in the rank-concatenated form (kx > 0) runs kx / 64 more
+  // K tiles from Tx and Ux, and no epilogue
+  int kx = 0;
+  c.kmain = kend;
+  c.rsx = c.rsa;
+  c.rsu = c.rsb;
+  c.voffx = c.voff64;
+  c.xrow_bytes = c.row_bytes;
+  if constexpr (LORA) {
+    if (lo.kx != nullptr) {
+      kx = uniform_load(lo.kx, 0);
+      c.xrow_bytes = lo.txw * 2;
+      c.rsx = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(lo.tx + (size_t)m0 * lo.txw), (short)0,
+                                                (M - m0) * c.xrow_bytes, 0x00020000);
+      c.rsu = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(lo.upt + (size_t)n0 * lo.txw), (short)0,
+                                                (N - n0) * c.xrow_bytes, 0x00020000);
+      c.voffx = (lane >> 3) * c.xrow_bytes + (((lane & 7) ^ ((4 * (c.wave & 1) + (lane >> 4)) & 7)) << 4);
+      kend += kx / GBK64;
+    }
+  }
   if constexpr (CO) {
-    ring64x2_loop<TM, TN>(c, m64_a0, m64_a1, m64_b0, m64_b1, kt0, kend, acc);
+    ring64x2_loop<TM, TN, LORA>(c, m64_a0, m64_a1, m64_b0, m64_b1, kt0, kend, acc);
   } else if constexpr (TM == 256) {
-    ring64x2_loop<TM, TN>(c, h64_a0, h64_a1, h64_b0, h64_b1, kt0, kend, acc);
+    ring64x2_loop<TM, TN, LORA>(c, h64_a0, h64_a1, h64_b0, h64_b1, kt0, kend, acc);
   } else {
     ring64_loop4<TM, TN>(c, m64_a0, m64_a1, m64_a2, m64_a3, m64_b0, m64_b1, m64_b2, m64_b3, kt0, kend, acc);
   }
@@ -1011,32 +1111,26 @@ __device__ __forceinline__ void gemm_ring_body(
     __builtin_amdgcn_sched_barrier(0);
     // (left out when the batch's Up blocks overran the operand buffer: a
     // separate expand then adds the term)
-    if (lo.over == nullptr || uniform_load(lo.over, 0) == 0)
+    if (kx == 0 && (lo.over == nullptr || uniform_load(lo.over, 0) == 0))
       ring_lora_epilogue<MI, NJ>(m0 + c.wm * (TM / 2), n0 + c.wn * (TN / 2), M, N, pv, row_key, lo, acc, key);
   }
 
-  // C layout of a 32x32 tile: lane l holds column l%32, rows 8*(v/4) + 4*(l/32) + v%4.
-  // The lane index passes through an empty asm statement, so the stores'
-  // addresses are computed here and not hoisted above the main loop, where
-  // they would hold registers the fragments need.
-  int sl = lane;
-  asm volatile("" : "+v"(sl));
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int col = n0 + c.wn * (TN / 2) + j * 32 + (sl & 31);
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = m0 + c.wm * (TM / 2) + i * 32 + 8 * (v >> 2) + 4 * (sl >> 5) + (v & 3);
-        if (r < M && col < N) {
-          if (PART)
-            part[((size_t)blockIdx.y * M + r) * N + col] = acc[i][j][v];
-          else
-            Y[(size_t)r * N + col] = (uint16_t)f2bf(acc[i][j][v]);
-        }
-      }
-    }
+  // Output through LDS.  The ring's MFMAs take the W0 fragment as A and the
+  // X fragment as B, so each 32x32 accumulator block is the transposed
+  // output: lane l holds output row l % 32 and columns 8 (v / 4) + 4 (l / 32)
+  // + v % 4, four consecutive columns per v / 4, one 8-byte (bf16) or 16-byte
+  // (fp32 partials) piece.  Straight to memory every store instruction would
+  // scatter over 32 rows; instead each wave writes its (MI 32) x (NJ 32)
+  // block into a ring buffer of its own (idle once every wave has passed the
+  // barrier below: the rings' DMAs were waited for) and reads it back as
+  // 16-byte row pieces, so one store instruction covers whole rows.
+  static_assert(MI * 32 * NJ * 32 * (PART ? 4 : 2) <= (TM == 256 ? sizeof(h64_a0) : sizeof(m64_a0)),
+                "a wave's output block fits its ring buffer");
+  ring_barrier();
+  ring_store_tile<MI, NJ, PART>(c.wave, m0 + c.wm * (TM / 2), n0 + c.wn * (TN / 2), M, N, Y,
+                                PART ? part + (size_t)blockIdx.y * M * N : nullptr, acc,
+                                TM == 256 ? (c.wave == 0 ? h64_a0 : c.wave == 1 ? h64_a1 : c.wave == 2 ? h64_b0 : h64_b1)
+                                          : (c.wave == 0 ? m64_a0 : c.wave == 1 ? m64_a1 : c.wave == 2 ? m64_b0 : m64_b1));
 }
 
 // one workgroup per CU: 256x256 tiles (large products, with or without the

@@ -153,13 +153,30 @@ hipError_t launch_shrink_rows(const PoolView& pv, int proj, const uint16_t* X, c
 //        batch's blocks need more than upt_units rank rows; then upt is
 //        incomplete, the GEMM leaves the low-rank term out and
 //        launch_expand_over adds it.
+// The rank-concatenated form, for batches whose adapters' r_pad sum to at
+// most txw ranks (txw a multiple of 64, 0 = never): the low-rank term is
+// then the product of two more K stages, [X | Tx] [W0 | Ux]^T, in the
+// GEMM's own pipeline instead of its epilogue.
+//   kx   int32 (when not null): written by lora_prep, the extra depth Kx
+//        (the batch's r_pad sum rounded up to 64) or 0 when the batch does
+//        not take this form; then tb and upt above are written instead,
+//   tx   bf16 [M][txw]: row r holds s_a * t of its adapter a at columns
+//        koff[a] .. koff[a] + rank - 1, zeros elsewhere below Kx; NaN below
+//        Kx for a row with an invalid id,
+//   Ux   bf16 [dout][txw] in the upt region: Up_a[c][q] at column
+//        koff[a] + q, zeros elsewhere below Kx.
 struct LoraOperands {
   const uint16_t* tb;
   const int32_t* koff;
   const uint16_t* upt;
   int wt;
   const int32_t* over = nullptr;
+  const uint16_t* tx = nullptr;
+  int txw = 0;
+  const int32_t* kx = nullptr;
 };
+// the largest extra depth of the rank-concatenated form
+constexpr int kMaxConcatRanks = 256;
 inline int t_rows_width(int max_rank) { return (max_rank + 15) / 16 * 16; }
 // Rank rows of upt for a batch of n rows at most: every adapter of the
 // batch padded to the largest rank.
@@ -178,7 +195,7 @@ hipError_t launch_big_lora(const PoolView& pv, const uint16_t* X, const uint16_t
 // order); upt has room for upt_units rank rows.
 hipError_t launch_lora_prep(const PoolView& pv, int proj, const int32_t* ws, int n, const float* Ts, int n_chunks,
                             uint16_t* tb, int wt, int32_t* koff, uint16_t* upt, long upt_units, int32_t* over,
-                            hipStream_t stream);
+                            uint16_t* tx, int txw, int32_t* kx, hipStream_t stream);
 
 hipError_t launch_shrink(const PoolView& pv, int proj, const uint16_t* X, const int32_t* ws, int n,
                          float* T, int n_chunks, int chunk_elems, hipStream_t stream);

@@ -679,66 +679,134 @@ __global__ __launch_bounds__(64 * kTileWaves) void shrink_tiles_kernel(PoolView 
 }
 
 // ---------------------------------------------------------------------------
-// lora_prep: the operands of the large-batch GEMM's low-rank epilogue.
+// lora_prep: the operands of the large-batch GEMM's low-rank term.
 // (Columns per gather block: small enough that the LDS tile lets the
 // launch's blocks all be resident at once.)
+// Every block first sums r_pad (rank rounded up to 16) over the batch's
+// segments: when the sum, rounded up to 64, is at most txw, the batch takes
+// the rank-concatenated form (Tx, Ux: extra K stages of the GEMM), else the
+// epilogue form (tb, upt).  Adapter a's ranks start at koff[a] = the sum of
+// r_pad over the segments before a's, in both forms.
 // Blocks [0, nt): t per original row, the scaled sum of the shrink's din
 // slices in slice order (the same arithmetic the expand applies), rounded
-// to bf16 and zero-padded to wt.  Blocks [nt, ...): one per (segment,
-// kPrepCols columns): the adapter's Up columns as a [dout][r_pad] block (ranks
-// contiguous, zeros past the rank) at koff * dout, koff = the sum of r_pad
-// over the segments before it, and koff recorded per adapter id.  A block
-// that would end past upt_units rank rows writes nothing; the first column
-// block of the last segment (of the first, with no segment) records in
-// *over whether the batch's blocks overran.
+// to bf16: compact and zero-padded to wt (epilogue form), or at the
+// adapter's columns of a Kx-wide row, zeros elsewhere and NaN for a row with
+// an invalid id (concatenated form).  Block 0 records Kx (0: epilogue form).
+// Blocks [nt, ...): one per (segment, kPrepCols columns): the adapter's Up
+// columns, ranks contiguous and zeros past the rank, as a [dout][r_pad] block
+// at koff * dout (epilogue form) or at columns koff .. koff + r_pad - 1 of
+// the [dout][txw] rows of Ux, the last segment's blocks also zeroing the
+// columns up to Kx (concatenated form); koff recorded per adapter id.  In
+// the epilogue form a block that would end past upt_units rank rows writes
+// nothing, and the first column block of the last segment (of the first,
+// with no segment) records in *over whether the batch's blocks overran.
 // ---------------------------------------------------------------------------
 constexpr int kPrepCols = 64;
+constexpr int kConcatSegs = kMaxConcatRanks / 16;  // segments of a concatenated batch, at most
+
+__device__ __forceinline__ int rank_pad16(int r) { return (r + 15) & ~15; }
 
 __global__ __launch_bounds__(256) void lora_prep_kernel(PoolView pv, int proj, const int32_t* __restrict__ ws, int n,
                                                         const float* __restrict__ Ts, int n_chunks,
                                                         uint16_t* __restrict__ tb, int wt, int nt,
                                                         int32_t* __restrict__ koff_out, uint16_t* __restrict__ upt,
-                                                        long upt_units, int32_t* __restrict__ over) {
+                                                        long upt_units, int32_t* __restrict__ over,
+                                                        uint16_t* __restrict__ tx, int txw, int32_t* __restrict__ kx_out) {
   const int tid = threadIdx.x;
-  if ((int)blockIdx.x < nt) {
+  const int nseg = ws[MLORA_SEG_NSEG];
+  const int32_t* seg_adapter = ws + MLORA_SEG_ADAPTER(n);
+  const int chunks = (pv.dout + kPrepCols - 1) / kPrepCols;
+  const bool tpart = (int)blockIdx.x < nt;
+  const int sidx = tpart ? 0 : (blockIdx.x - nt) / chunks, cc = tpart ? 0 : (blockIdx.x - nt) % chunks;
+  // r_pad over all segments, and over those before this block's (each
+  // thread sums every 256th, then block sums)
+  __shared__ int part[2][4];
+  int all = 0, before = 0;
+  for (int s2 = tid; s2 < nseg; s2 += 256) {
+    const int rp = rank_pad16(pv.rank[seg_adapter[s2]]);
+    all += rp;
+    before += s2 < sidx ? rp : 0;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    all += __shfl_xor(all, m, 64);
+    before += __shfl_xor(before, m, 64);
+  }
+  if ((tid & 63) == 0) {
+    part[0][tid >> 6] = all;
+    part[1][tid >> 6] = before;
+  }
+  __syncthreads();
+  const int total = part[0][0] + part[0][1] + part[0][2] + part[0][3];
+  const int koff = part[1][0] + part[1][1] + part[1][2] + part[1][3];
+  const int kx = (tx != nullptr && total > 0 && ((total + 63) & ~63) <= txw) ? (total + 63) & ~63 : 0;
+  const size_t cs = (size_t)n * pv.max_rank;
+
+  if (tpart) {
+    if (blockIdx.x == 0 && tid == 0 && kx_out != nullptr) *kx_out = kx;
+    if (kx) {
+      // the batch's adapters and their first columns (kx > 0: at most kConcatSegs)
+      __shared__ int tab_ad[kConcatSegs], tab_koff[kConcatSegs];
+      if (tid < nseg) {
+        int ko = 0;
+        for (int s2 = 0; s2 < tid; ++s2) ko += rank_pad16(pv.rank[seg_adapter[s2]]);
+        tab_ad[tid] = seg_adapter[tid];
+        tab_koff[tid] = ko;
+      }
+      __syncthreads();
+      const int32_t* row_key = ws + MLORA_SEG_ROWKEY(n);
+      const int32_t* inv = ws + MLORA_SEG_INV(n);
+      const int per_row = kx / 8;
+      for (long idx = (long)blockIdx.x * 256 + tid; idx < (long)n * per_row; idx += (long)nt * 256) {
+        const int r = (int)(idx / per_row), c0 = (int)(idx % per_row) * 8;
+        const int key = row_key[r];
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = key == -2 ? 0x7fc0u : 0u;
+        if (key >= 0) {
+          int ko = 0;
+          for (int s2 = 0; s2 < nseg; ++s2) ko = tab_ad[s2] == key ? tab_koff[s2] : ko;
+          const int rank = pv.rank[key];
+          const float sc = pv.scale[key];
+          const float* tp = Ts + (size_t)inv[r] * pv.max_rank;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int q = c0 + e - ko;
+            if (q >= 0 && q < rank) {
+              float v = 0.f;
+              for (int ch = 0; ch < n_chunks; ++ch) v += tp[ch * cs + q];
+              h[e] = f2bf(v * sc);
+            }
+          }
+        }
+        *reinterpret_cast<uint4*>(tx + (size_t)r * txw + c0) =
+            make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+      }
+      return;
+    }
     const int n_act = ws[MLORA_SEG_NACT];
     const int32_t* perm = ws + MLORA_SEG_PERM(n);
     const int32_t* row_key = ws + MLORA_SEG_ROWKEY(n);
-    const size_t cs = (size_t)n * pv.max_rank;
     for (int idx = blockIdx.x * 256 + tid; idx < n_act * wt; idx += nt * 256) {
       const int j = idx / wt, q = idx % wt;
       const int row = perm[j];
       const int key = row_key[row];  // >= 0: sorted positions below n_act are rows on resident adapters
-      float s = 0.f;
+      float v = 0.f;
       if (q < pv.rank[key]) {
         const float* tp = Ts + (size_t)j * pv.max_rank + q;
-        for (int ch = 0; ch < n_chunks; ++ch) s += tp[ch * cs];
-        s *= pv.scale[key];
+        for (int ch = 0; ch < n_chunks; ++ch) v += tp[ch * cs];
+        v *= pv.scale[key];
       }
-      tb[(size_t)row * wt + q] = (uint16_t)f2bf(s);
+      tb[(size_t)row * wt + q] = (uint16_t)f2bf(v);
     }
     return;
   }
   __shared__ __attribute__((aligned(16))) uint16_t tile[MLORA_MAX_RANK][kPrepCols];  // Up rows of the block's columns
-  const int chunks = (pv.dout + kPrepCols - 1) / kPrepCols;
-  const int sidx = (blockIdx.x - nt) / chunks, cc = (blockIdx.x - nt) % chunks;
-  const int nseg = ws[MLORA_SEG_NSEG];
   if (nseg == 0 && sidx == 0 && cc == 0 && tid == 0) *over = 0;
   if (sidx >= nseg) return;
-  const int32_t* seg_adapter = ws + MLORA_SEG_ADAPTER(n);
-  // koff = sum of r_pad over the segments before this one (each thread sums
-  // every 256th, then a block sum)
-  __shared__ int part[4];
-  int mine = 0;
-  for (int s2 = tid; s2 < sidx; s2 += 256) mine += (pv.rank[seg_adapter[s2]] + 15) & ~15;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) mine += __shfl_xor(mine, m, 64);
-  if ((tid & 63) == 0) part[tid >> 6] = mine;
-  __syncthreads();
-  const int koff = part[0] + part[1] + part[2] + part[3];
   const int a = seg_adapter[sidx];
-  const int rank = pv.rank[a], rp = (rank + 15) & ~15;
-  const bool fits = koff + rp <= upt_units;
+  const int rank = pv.rank[a], rp = rank_pad16(rank);
+  const bool fits = kx > 0 || koff + rp <= upt_units;
   if (cc == 0 && tid == 0) {
     koff_out[a] = koff;
     if (sidx == nseg - 1) *over = fits ? 0 : 1;
@@ -766,15 +834,25 @@ __global__ __launch_bounds__(256) void lora_prep_kernel(PoolView pv, int proj, c
     *reinterpret_cast<uint4*>(&tile[q][cl]) = v;
   }
   __syncthreads();
-  // columns out: the block [dout][rp] at koff * dout, 8 ranks per 16-byte store
-  uint16_t* dst = upt + (size_t)koff * pv.dout + (size_t)c0 * rp;
+  // columns out, 8 ranks per 16-byte store: the block [dout][rp] at
+  // koff * dout, or columns koff.. of the txw-wide rows
+  const int stride = kx ? txw : rp;
+  uint16_t* dst = kx ? upt + (size_t)c0 * txw + koff : upt + (size_t)koff * pv.dout + (size_t)c0 * rp;
   for (int idx = tid; idx < ncol * (rp / 8); idx += 256) {
     const int cl = idx / (rp / 8), q0 = (idx % (rp / 8)) * 8;
     uint32_t h[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) h[e] = tile[q0 + e][cl];
-    *reinterpret_cast<uint4*>(dst + (size_t)cl * rp + q0) =
+    *reinterpret_cast<uint4*>(dst + (size_t)cl * stride + q0) =
         make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+  }
+  if (kx && sidx == nseg - 1) {
+    // zeros from the last adapter's columns up to Kx
+    const int tail = (kx - total) / 8;
+    for (int idx = tid; idx < ncol * tail; idx += 256) {
+      const int cl = idx / tail, q0 = total + (idx % tail) * 8;
+      *reinterpret_cast<uint4*>(upt + (size_t)(c0 + cl) * txw + q0) = make_uint4(0u, 0u, 0u, 0u);
+    }
   }
 }
 
@@ -866,14 +944,16 @@ hipError_t launch_fused(const PoolView& pv, int proj, const uint16_t* X, const i
 
 hipError_t launch_lora_prep(const PoolView& pv, int proj, const int32_t* ws, int n, const float* Ts, int n_chunks,
                             uint16_t* tb, int wt, int32_t* koff, uint16_t* upt, long upt_units, int32_t* over,
-                            hipStream_t stream) {
+                            uint16_t* tx, int txw, int32_t* kx, hipStream_t stream) {
+  if (tx != nullptr && (txw % 64 != 0 || txw > kMaxConcatRanks || (long)txw > upt_units))
+    return hipErrorInvalidValue;
   const long total = (long)n * wt;
   const int nt = (int)((total + 255) / 256 < 1024 ? (total + 255) / 256 : 1024);
   const long segs = n < pv.max_adapters ? n : pv.max_adapters;  // segments of the batch, at most
   const long blocks = (nt > 0 ? nt : 1) + segs * ((pv.dout + kPrepCols - 1) / kPrepCols);
   if (blocks > 0x7fffffffL) return hipErrorInvalidConfiguration;
   MLORA_LAUNCH("lora_prep", lora_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, pv, proj, ws, n, Ts,
-               n_chunks, tb, wt, nt > 0 ? nt : 1, koff, upt, upt_units, over);
+               n_chunks, tb, wt, nt > 0 ? nt : 1, koff, upt, upt_units, over, tx, txw, kx);
   return launched();
 }
 

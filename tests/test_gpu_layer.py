@@ -31,7 +31,9 @@ GEMM_SHAPES = [(1, 4, 4), (4, 4, 4), (3, 5, 7), (16, 64, 16), (17, 72, 33), (32,
                # large products: 128x128 co-resident tiles where 256x256 tiles would underfill the chip
                (2048, 1024, 2048), (2100, 640, 2200), (1030, 4096, 4104),
                # 256x256 tiles: full tiles, ragged M and N, the shortest K (two stages)
-               (4096, 256, 4096), (4000, 384, 4000), (4096, 128, 4096)]
+               (4096, 256, 4096), (4000, 384, 4000), (4096, 128, 4096),
+               # ring tiles with N % 4 != 0: element stores instead of 4-column stores
+               (100, 512, 777), (2100, 512, 2203)]
 
 
 @pytest.mark.parametrize("m,k,n", GEMM_SHAPES)
@@ -42,6 +44,23 @@ def test_base_gemm(M, m, k, n):
     Y = M.base_gemm(to_dev_bf16(X), to_dev_bf16(W0))
     ref = O.widen_bf16(X) @ O.widen_bf16(W0).T
     assert_close(dev_to_f64(Y), ref, f"gemm {m}x{k}x{n}")
+
+
+@pytest.mark.parametrize("m,k,n", [(100, 512, 776), (2100, 512, 2200)])
+def test_base_gemm_unaligned_output(M, m, k, n):
+    """Y two bytes past an 8-byte boundary: the ring tiles' 4-column stores
+    need 8-byte alignment and fall back to element stores."""
+    import torch
+    w = synth.custom("gemm", 3100 + m + n, k, n, np.full(m, -1, np.int32), {0: 1})
+    X, W0 = w.x_bits(), w.w0_bits()
+    say(f"base_gemm unaligned Y M={m} K={k} N={n}")
+    buf = torch.full((m * n + 4,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    Y = buf[1:1 + m * n].view(m, n)
+    M.base_gemm(to_dev_bf16(X), to_dev_bf16(W0), Y)
+    ref = O.widen_bf16(X) @ O.widen_bf16(W0).T
+    assert_close(dev_to_f64(Y), ref, f"gemm unaligned {m}x{k}x{n}")
+    edges = buf[[0, m * n + 1, m * n + 2, m * n + 3]].float()
+    assert torch.isnan(edges).all(), "a store left the output"
 
 
 def test_base_gemm_prefill_full_size(M):
@@ -345,14 +364,24 @@ def test_base_only_rows_bitwise_and_deterministic(M, variant):
     assert_close(dev_to_f64(Yb), dev_to_f64(M.base_gemm(Xd, W0d)), f"{variant} all-none", tol=1e-2)
 
 
+# ranks padded to 16 sum to 272 (> 256: the epilogue form), 144 (the
+# rank-concatenated form, 192 deep with 48 zero columns) and exactly 256
+LARGE_RANKS = {"epilogue": {0: 1, 1: 8, 2: 17, 3: 64, 4: 128, 6: 16},
+               "concat": {0: 1, 1: 8, 2: 17, 3: 64, 6: 16},
+               "concat256": {0: 64, 1: 48, 2: 64, 3: 64, 6: 16}}
+
+
+@pytest.mark.parametrize("form", list(LARGE_RANKS))
 @pytest.mark.parametrize("n,dout", [(2100, 2200),   # few 256x256 tiles: 128x128 tiles, two per CU
                                     (4090, 4090)])  # 16 x 16 tiles of 256x256
-def test_apply_large_batch_epilogue(M, n, dout):
+def test_apply_large_batch_epilogue(M, n, dout, form):
     """Batches large enough for the large GEMM take the split variant with
-    the low-rank term added in the GEMM's epilogue: ragged M and N, ranks 1
-    to 128 (up to 8 groups of 16), base-only rows and invalid ids (NaN), all
-    rows checked, on both tile shapes of the large GEMM."""
-    w = small_workload(91, 640, dout, n, {0: 1, 1: 8, 2: 17, 3: 64, 4: 128, 6: 16}, p_none=0.1)
+    the low-rank term added inside the GEMM: in its epilogue, or as extra K
+    stages over the rank-concatenated operands when the batch's ranks
+    (padded to 16) sum to at most 256.  Ragged M and N, ranks 1 to 128,
+    base-only rows and invalid ids (NaN), all rows checked, on both tile
+    shapes of the large GEMM."""
+    w = small_workload(91, 640, dout, n, LARGE_RANKS[form], p_none=0.1)
     ids = w.row_adapter.copy()
     ids[[5, 700, n - 1]] = [5, 99, -3]      # 5 not resident, 99 out of range, -3 invalid
     w = synth.custom("large_epi", w.seed, w.din, w.dout, ids, w.ranks, scales=w.scales, max_adapters=7,
