@@ -706,6 +706,24 @@ constexpr int kConcatSegs = kMaxConcatRanks / 16;  // segments of a concatenated
 
 __device__ __forceinline__ int rank_pad16(int r) { return (r + 15) & ~15; }
 
+// The sum of the shrink's n_chunks din slices of one t entry (slice stride
+// cs), in slice order.  Up to 8 slices the loads are all issued before the
+// first add (a load-add loop would wait out one round trip per slice).
+__device__ __forceinline__ float sum_slices(const float* __restrict__ p, size_t cs, int n_chunks) {
+  float v = 0.f;
+  if (n_chunks <= 8) {
+    float x[8];
+#pragma unroll
+    for (int ch = 0; ch < 8; ++ch) x[ch] = p[(size_t)min(ch, n_chunks - 1) * cs];
+#pragma unroll
+    for (int ch = 0; ch < 8; ++ch)
+      if (ch < n_chunks) v += x[ch];
+  } else {
+    for (int ch = 0; ch < n_chunks; ++ch) v += p[(size_t)ch * cs];
+  }
+  return v;
+}
+
 __global__ __launch_bounds__(256) void lora_prep_kernel(PoolView pv, int proj, const int32_t* __restrict__ ws, int n,
                                                         const float* __restrict__ Ts, int n_chunks,
                                                         uint16_t* __restrict__ tb, int wt, int nt,
@@ -719,11 +737,20 @@ __global__ __launch_bounds__(256) void lora_prep_kernel(PoolView pv, int proj, c
   const bool tpart = (int)blockIdx.x < nt;
   const int sidx = tpart ? 0 : (blockIdx.x - nt) / chunks, cc = tpart ? 0 : (blockIdx.x - nt) % chunks;
   // r_pad over all segments, and over those before this block's (each
-  // thread sums every 256th, then block sums)
+  // thread sums every 256th, then block sums); the first kConcatSegs
+  // segments' adapters and r_pad kept for the concatenated form's rows
   __shared__ int part[2][4];
+  __shared__ int tab_ad[kConcatSegs], tab_rank[kConcatSegs];
+  __shared__ float tab_scale[kConcatSegs];
   int all = 0, before = 0;
   for (int s2 = tid; s2 < nseg; s2 += 256) {
-    const int rp = rank_pad16(pv.rank[seg_adapter[s2]]);
+    const int ad = seg_adapter[s2];
+    const int rk = pv.rank[ad], rp = rank_pad16(rk);
+    if (s2 < kConcatSegs) {
+      tab_ad[s2] = ad;
+      tab_rank[s2] = rk;
+      tab_scale[s2] = pv.scale[ad];
+    }
     all += rp;
     before += s2 < sidx ? rp : 0;
   }
@@ -745,37 +772,54 @@ __global__ __launch_bounds__(256) void lora_prep_kernel(PoolView pv, int proj, c
   if (tpart) {
     if (blockIdx.x == 0 && tid == 0 && kx_out != nullptr) *kx_out = kx;
     if (kx) {
-      // the batch's adapters and their first columns (kx > 0: at most kConcatSegs)
-      __shared__ int tab_ad[kConcatSegs], tab_koff[kConcatSegs];
-      if (tid < nseg) {
-        int ko = 0;
-        for (int s2 = 0; s2 < tid; ++s2) ko += rank_pad16(pv.rank[seg_adapter[s2]]);
-        tab_ad[tid] = seg_adapter[tid];
-        tab_koff[tid] = ko;
-      }
-      __syncthreads();
+      // (kx > 0: at most kConcatSegs segments, all in the table)
       const int32_t* row_key = ws + MLORA_SEG_ROWKEY(n);
       const int32_t* inv = ws + MLORA_SEG_INV(n);
       const int per_row = kx / 8;
       for (long idx = (long)blockIdx.x * 256 + tid; idx < (long)n * per_row; idx += (long)nt * 256) {
         const int r = (int)(idx / per_row), c0 = (int)(idx % per_row) * 8;
         const int key = row_key[r];
+        const int j = inv[r];
         uint32_t h[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) h[e] = key == -2 ? 0x7fc0u : 0u;
         if (key >= 0) {
-          int ko = 0;
-          for (int s2 = 0; s2 < nseg; ++s2) ko = tab_ad[s2] == key ? tab_koff[s2] : ko;
-          const int rank = pv.rank[key];
-          const float sc = pv.scale[key];
-          const float* tp = Ts + (size_t)inv[r] * pv.max_rank;
+          // the adapter's rank, scale and first column (r_pad of the segments before its own)
+          int ko = 0, run = 0, rank = 0;
+          float sc = 0.f;
+          for (int s2 = 0; s2 < nseg; ++s2) {
+            if (tab_ad[s2] == key) {
+              ko = run;
+              rank = tab_rank[s2];
+              sc = tab_scale[s2];
+            }
+            run += rank_pad16(tab_rank[s2]);
+          }
+          const float* tp = Ts + (size_t)j * pv.max_rank;
+          if (n_chunks <= 8) {
+            // all 8 x n_chunks loads first, then the sums in slice order
+            float x[8][8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int q = c0 + e - ko;
-            if (q >= 0 && q < rank) {
+            for (int ch = 0; ch < 8; ++ch)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const int q = c0 + e - ko;
+                x[ch][e] = (q >= 0 && q < rank && ch < n_chunks) ? tp[(size_t)ch * cs + q] : 0.f;
+              }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int q = c0 + e - ko;
               float v = 0.f;
-              for (int ch = 0; ch < n_chunks; ++ch) v += tp[ch * cs + q];
-              h[e] = f2bf(v * sc);
+#pragma unroll
+              for (int ch = 0; ch < 8; ++ch)
+                if (ch < n_chunks) v += x[ch][e];
+              if (q >= 0 && q < rank) h[e] = f2bf(v * sc);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int q = c0 + e - ko;
+              if (q >= 0 && q < rank) h[e] = f2bf(sum_slices(tp + q, cs, n_chunks) * sc);
             }
           }
         }
@@ -792,11 +836,7 @@ __global__ __launch_bounds__(256) void lora_prep_kernel(PoolView pv, int proj, c
       const int row = perm[j];
       const int key = row_key[row];  // >= 0: sorted positions below n_act are rows on resident adapters
       float v = 0.f;
-      if (q < pv.rank[key]) {
-        const float* tp = Ts + (size_t)j * pv.max_rank + q;
-        for (int ch = 0; ch < n_chunks; ++ch) v += tp[ch * cs];
-        v *= pv.scale[key];
-      }
+      if (q < pv.rank[key]) v = sum_slices(Ts + (size_t)j * pv.max_rank + q, cs, n_chunks) * pv.scale[key];
       tb[(size_t)row * wt + q] = (uint16_t)f2bf(v);
     }
     return;
