@@ -62,10 +62,13 @@ typedef enum mlora_status {
 typedef enum mlora_variant {
   MLORA_VARIANT_AUTO = 0,  /* ROWS up to 1024 rows, SPLIT above                  */
   MLORA_VARIANT_SPLIT = 1, /* base GEMM, then shrink kernel -> fp32 t in `work`
-                              -> expand kernel (large batches: the expand in the
-                              GEMM's epilogue instead, unless the batch's Up
-                              blocks overrun the epilogue's 256 MiB operand
-                              budget; then an expand follows the GEMM)           */
+                              -> expand kernel (large batches: the expand inside
+                              the GEMM instead, as extra K stages over the
+                              ranks concatenated when the batch's ranks, each
+                              rounded up to 16, sum to at most 256, else in its
+                              epilogue, unless the batch's Up blocks overrun
+                              the epilogue's 256 MiB operand budget; then an
+                              expand follows the GEMM)                           */
   MLORA_VARIANT_FUSED = 2, /* base GEMM, then one kernel per work item of up to
                               MLORA_ITEM_ROWS rows: t stays on chip              */
   MLORA_VARIANT_ROWS = 3   /* n_rows <= 1024: the per-row shrink inside the
@@ -336,7 +339,8 @@ mlora_status mlora_gemm_lora(const mlora_pool* pool, int32_t proj, const uint16_
  * ------------------------------------------------------------------------- */
 /* mlora_work_bytes: the scratch any variant of mlora_apply needs for a batch
  * of n_rows on this pool (t per row and rank, split-K partials, the
- * epilogue's operands); 0 for a NULL pool or n_rows < 0.  Host only. */
+ * large GEMM's low-rank operands); 0 for a NULL pool or n_rows < 0.  Host
+ * only. */
 size_t mlora_work_bytes(const mlora_pool* pool, int32_t n_rows);
 
 /* The launch plan mlora_apply follows for `variant` (AUTO resolved) on a
