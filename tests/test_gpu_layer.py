@@ -389,6 +389,20 @@ def test_apply_large_batch_epilogue(M, n, dout, form):
     check_apply(M, w, variants=("split",))
 
 
+@pytest.mark.parametrize("n,dout", [(2100, 2200), (4090, 4090)])
+def test_apply_large_batch_concat_narrow(M, n, dout):
+    """A pool of two adapters of rank at most 32 gives the low-rank
+    operands room for 2 x 32 = 64 rank rows only: the rank-concatenated
+    operands are then 64 wide, and ranks 16 + 32 fill 48 of them.  Base-only
+    rows and invalid ids (NaN), all rows checked, both tile shapes."""
+    w = small_workload(94, 512, dout, n, {0: 16, 1: 32}, p_none=0.1)
+    ids = w.row_adapter.copy()
+    ids[[3, n // 2]] = [2, -5]  # out of range, invalid
+    w = synth.custom("concat_narrow", w.seed, w.din, w.dout, ids, w.ranks, scales=w.scales, max_adapters=2,
+                     max_rank=32)
+    check_apply(M, w, variants=("split",))
+
+
 def _apply_launches(M, w, pool):
     """Kernel names of one split-variant apply call."""
     torch = torch_cuda()
