@@ -537,6 +537,7 @@ struct RingCtx {
 // tiles with 4 stages (32 KiB each).
 // ---------------------------------------------------------------------------
 constexpr int GBK64 = 64;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __shared__ __attribute__((aligned(16))) uint16_t m64_a0[128 * GBK64];
 __shared__ __attribute__((aligned(16))) uint16_t m64_a1[128 * GBK64];
 __shared__ __attribute__((aligned(16))) uint16_t m64_a2[128 * GBK64];
@@ -929,7 +930,10 @@ __device__ __forceinline__ void shrink_row_body_ids(const PoolView& pv, int proj
 // row % CH so that both the scattered piece writes and the row reads spread
 // over the banks.  Each read pass covers 64 / CH rows, one 16-byte piece per
 // lane; pieces past N, and every piece when N or the output is not aligned
-// to 16 bytes per piece, go out element by element.
+// to 16 bytes per piece, go out element by element.  The 16-byte pieces are
+// non-temporal stores: every CU writes its tile at about the same moment,
+// and streaming them past the L2 shortened the medium split-K launches by
+// 3-14 % (their finish pass reads the partials back a little slower).
 template <int MI, int NJ, bool PART>
 __device__ __forceinline__ void ring_store_tile(int wave, int wr, int wc, int M, int N, uint16_t* __restrict__ Y,
                                                 float* __restrict__ pt, floatx16 (&acc)[MI][NJ], uint16_t* st16) {
@@ -967,10 +971,8 @@ __device__ __forceinline__ void ring_store_tile(int wave, int wr, int wc, int M,
     const uint4 v = *reinterpret_cast<const uint4*>(st + R * RB + ((cc ^ (R % CH)) << 4));
     if (row >= M || col >= N) continue;
     if (vec) {
-      if constexpr (PART)
-        *reinterpret_cast<uint4*>(pt + (size_t)row * N + col) = v;
-      else
-        *reinterpret_cast<uint4*>(Y + (size_t)row * N + col) = v;
+      void* dst = PART ? static_cast<void*>(pt + (size_t)row * N + col) : static_cast<void*>(Y + (size_t)row * N + col);
+      __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, static_cast<u32x4*>(dst));
     } else {
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
