@@ -10,9 +10,10 @@
 //
 // The update reads and writes every element of W0 once and does rank
 // multiply-adds per element, so it is bound by HBM traffic (4 bytes per
-// element against 2 * rank flops: 8 flop/B at rank 16), not by arithmetic:
-// plain vector FMAs, no matrix cores.  (Ranks <= 16: merge_kernel_r16
-// below.)  A workgroup owns 4 rows of W0 and
+// element against 2 * rank flops: 8 flop/B at rank 16).  Rows of 16-byte
+// pieces take merge_kernel_mfma below, which does the rank products on the
+// matrix cores; the vector-ALU form here serves din % 8 != 0 and unaligned
+// weights.  It gives a workgroup 4 rows of W0 and
 // 2048 columns (8 per thread): small, so the ~8 workgroups a CU holds are in
 // different phases (loading, summing, storing) and the HBM stream does not
 // stall while they all sum at once.  It stages its rows' Up entries (4 x rank,
@@ -101,92 +102,112 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(PoolView pv, int a
   }
 }
 
-// Ranks <= 16 with 16-byte rows.  The vector ALU work (rank multiply-adds
-// per element plus the bf16 unpacking, with no packed fp32 math) took as
-// long as the HBM traffic, so this form sums the ranks in pairs with the
-// bf16 dot instruction (two exact bf16 products and an fp32 add each): each
-// thread loads its 8 columns of all 16 Down rows once, repacks them into
-// rank pairs per column, and applies them to kMergeRows16 rows of W0, whose
-// pieces it loads first; the rows' Up entries are staged in LDS as rank
-// pairs.  Ranks past the adapter's weigh 0.
-constexpr int kMergeRows16 = 4;
+// 16-byte rows (din % 8 == 0, aligned W0): the rank product on the matrix
+// cores.  Up Down is a contraction over the ranks, 16 per 32x32x16
+// MFMA, so a workgroup owns a 128 x 128 tile of W0 (rows c, columns i) and
+// each of its four waves 32 rows of it.  Per 16 ranks the workgroup stages
+// Down^T [i][q] and Up^T [c][q] of its tile in LDS (zeros past the rank and
+// the matrix edges) and every wave runs one MFMA per 32x32 block with A =
+// Down^T rows (M = i), B = Up^T rows (N = c), so that a lane's accumulator
+// holds one row c and four consecutive columns i per group.  The W0 tile
+// goes through LDS too: the wave's 32 rows are loaded as 16-byte row pieces
+// (coalesced), stored with their 16-byte chunks XOR-swizzled by row, updated
+// in place in the accumulator layout (8-byte pieces) and written back as the
+// same row pieces.  At most 128 registers, so that four workgroups share a CU
+// (four tiles of W0 in flight): 23.9 us at 4096 x 4096 and rank 16, as the
+// vector-ALU form, and 38 / 58 us at ranks 64 / 128 against 51 / 87 us.
+// (Persistent workgroups over several tiles, the next tile's W0 loaded during
+// this one, held two per CU and took 26 / 51 / 82 us.)
+constexpr int kMergeTile = 128;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
-                                         false);
-}
-
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel_r16(PoolView pv, int adapter, int proj, int rank,
-                                                                  float f, uint16_t* __restrict__ W) {
-  __shared__ uint32_t up_p[kMergeRows16][8];  // (Up[c][2p], Up[c][2p+1]) as two bf16
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void merge_kernel_mfma(
+    PoolView pv, int adapter, int proj, int rank, float f, uint16_t* __restrict__ W) {
+  __shared__ __attribute__((aligned(16))) uint16_t wt[kMergeTile * kMergeTile];  // W0 tile, swizzled rows
+  __shared__ __attribute__((aligned(16))) uint16_t dT[kMergeTile * 16];          // Down^T [i][q]
+  __shared__ __attribute__((aligned(16))) uint16_t uT[kMergeTile * 16];          // Up^T [c][q]
   const int din = pv.din, dout = pv.dout;
-  const int tid = threadIdx.x;
-  const int c0 = blockIdx.y * kMergeRows16;
-  const int i0 = blockIdx.x * (kMergeThreads * 8) + tid * 8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i0 = blockIdx.x * kMergeTile, c0 = blockIdx.y * kMergeTile;
   const size_t pt = ((size_t)adapter * pv.n_proj + proj) * pv.max_rank;
   const int32_t* dpage = pv.down_page + pt;
   const int32_t* upage = pv.up_page + pt;
-  const bool live = i0 < din;
-  const int nrows = min(kMergeRows16, dout - c0);
+  char* wtb = reinterpret_cast<char*>(wt);
 
-  uint4 w[kMergeRows16];
-  uint4 d[16];
-  if (live) {
+  // the wave's 32 rows of W0: 512 pieces of 16 bytes, 8 per lane, 16 lanes per row
+  uint4 wv[8];
 #pragma unroll
-    for (int c = 0; c < kMergeRows16; ++c)
-      w[c] = *reinterpret_cast<const uint4*>(W + (size_t)(c0 + min(c, nrows - 1)) * din + i0);
-#pragma unroll
-    for (int q = 0; q < 16; ++q)
-      d[q] = *reinterpret_cast<const uint4*>(pv.down + (size_t)dpage[min(q, rank - 1)] * din + i0);
+  for (int k = 0; k < 8; ++k) {
+    const int e = lane + 64 * k, r = 32 * wave + (e >> 4), ch = e & 15;
+    const int c = c0 + r, i = i0 + 8 * ch;
+    wv[k] = (c < dout && i < din) ? *reinterpret_cast<const uint4*>(W + (size_t)c * din + i) : make_uint4(0u, 0u, 0u, 0u);
   }
-  for (int e = tid; e < kMergeRows16 * 8; e += kMergeThreads) {
-    const int c = e >> 3, q = 2 * (e & 7);
-    const uint32_t lo = (q < rank && c < nrows) ? pv.up[(size_t)upage[q] * dout + c0 + c] : 0u;
-    const uint32_t hi = (q + 1 < rank && c < nrows) ? pv.up[(size_t)upage[q + 1] * dout + c0 + c] : 0u;
-    up_p[c][e & 7] = lo | (hi << 16);
-  }
-  __syncthreads();
-  if (!live) return;
 
-  // rank pairs per column: dl[p][j] = (D[2p][2j], D[2p+1][2j]), dh[p][j] =
-  // (D[2p][2j+1], D[2p+1][2j+1]) for the thread's columns 2j, 2j+1
-  uint32_t dl[8][4], dh[8][4];
+  floatx16 acc[4];
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const uint32_t a[4] = {d[2 * p].x, d[2 * p].y, d[2 * p].z, d[2 * p].w};
-    const uint32_t b[4] = {d[2 * p + 1].x, d[2 * p + 1].y, d[2 * p + 1].z, d[2 * p + 1].w};
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      dl[p][j] = __builtin_amdgcn_perm(b[j], a[j], 0x05040100u);
-      dh[p][j] = __builtin_amdgcn_perm(b[j], a[j], 0x07060302u);
+    for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+  // staging: thread t fills row t & 127 of Down^T and of Up^T, ranks 8 (t >> 7) .. + 7
+  const int sr = tid & 127, sq = 8 * (tid >> 7);
+  for (int q0 = 0; q0 < rank; q0 += 16) {
+    if (q0 > 0) __syncthreads();  // every wave is done with the previous ranks
+    uint32_t hd[8], hu[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int q = q0 + sq + e;
+      hd[e] = (q < rank && i0 + sr < din) ? pv.down[(size_t)dpage[q] * din + i0 + sr] : 0u;
+      hu[e] = (q < rank && c0 + sr < dout) ? pv.up[(size_t)upage[q] * dout + c0 + sr] : 0u;
     }
-  }
+    if (q0 == 0) {
+      // W0 rows into the wave's LDS rows (row r, chunk ch at physical chunk
+      // ch ^ (r & 15)), their loads having gone out with the first ranks'
 #pragma unroll
-  for (int c = 0; c < kMergeRows16; ++c) {
-    if (c >= nrows) continue;  // (not break: the loop must unroll, w[] stays in registers)
-    uint32_t u[8];
-#pragma unroll
-    for (int p = 0; p < 8; ++p) u[p] = up_p[c][p];
-    float acc[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float lo = 0.f, hi = 0.f;
-#pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        lo = dot2_bf16(u[p], dl[p][j], lo);
-        hi = dot2_bf16(u[p], dh[p][j], hi);
+      for (int k = 0; k < 8; ++k) {
+        const int e = lane + 64 * k, r = 32 * wave + (e >> 4), ch = e & 15;
+        *reinterpret_cast<uint4*>(wtb + r * 256 + ((ch ^ (r & 15)) << 4)) = wv[k];
       }
-      acc[2 * j] = lo;
-      acc[2 * j + 1] = hi;
     }
-    const uint4 o = w[c];
-    uint4 r;
-    r.x = pack_bf2(fmaf(f, acc[0], lo_bf(o.x)), fmaf(f, acc[1], hi_bf(o.x)));
-    r.y = pack_bf2(fmaf(f, acc[2], lo_bf(o.y)), fmaf(f, acc[3], hi_bf(o.y)));
-    r.z = pack_bf2(fmaf(f, acc[4], lo_bf(o.z)), fmaf(f, acc[5], hi_bf(o.z)));
-    r.w = pack_bf2(fmaf(f, acc[6], lo_bf(o.w)), fmaf(f, acc[7], hi_bf(o.w)));
-    *reinterpret_cast<uint4*>(W + (size_t)(c0 + c) * din + i0) = r;
+    *reinterpret_cast<uint4*>(dT + sr * 16 + sq) =
+        make_uint4(hd[0] | (hd[1] << 16), hd[2] | (hd[3] << 16), hd[4] | (hd[5] << 16), hd[6] | (hd[7] << 16));
+    *reinterpret_cast<uint4*>(uT + sr * 16 + sq) =
+        make_uint4(hu[0] | (hu[1] << 16), hu[2] | (hu[3] << 16), hu[4] | (hu[5] << 16), hu[6] | (hu[7] << 16));
+    __syncthreads();
+    const uint4 b = *reinterpret_cast<const uint4*>(uT + (32 * wave + (lane & 31)) * 16 + 8 * (lane >> 5));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 a = *reinterpret_cast<const uint4*>(dT + (32 * j + (lane & 31)) * 16 + 8 * (lane >> 5));
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                       acc[j], 0, 0, 0);
+    }
+  }
+
+  // update in the accumulator layout: row r = 32 wave + lane % 32, columns
+  // 32 j + 8 g + 4 (lane / 32) + 0..3 (one 8-byte piece per group g)
+  {
+    const int r = 32 * wave + (lane & 31), h = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        char* p = wtb + r * 256 + (((4 * j + g) ^ (r & 15)) << 4) + 8 * h;
+        const uint2 o = *reinterpret_cast<const uint2*>(p);
+        *reinterpret_cast<uint2*>(p) =
+            make_uint2(pack_bf2(fmaf(f, acc[j][4 * g], lo_bf(o.x)), fmaf(f, acc[j][4 * g + 1], hi_bf(o.x))),
+                       pack_bf2(fmaf(f, acc[j][4 * g + 2], lo_bf(o.y)), fmaf(f, acc[j][4 * g + 3], hi_bf(o.y))));
+      }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int e = lane + 64 * k, r = 32 * wave + (e >> 4), ch = e & 15;
+    const int c = c0 + r, i = i0 + 8 * ch;
+    if (c < dout && i < din)
+      *reinterpret_cast<uint4*>(W + (size_t)c * din + i) =
+          *reinterpret_cast<const uint4*>(wtb + r * 256 + ((ch ^ (r & 15)) << 4));
   }
 }
 
@@ -194,17 +215,14 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel_r16(PoolView pv, i
 
 hipError_t launch_merge(const PoolView& pv, int adapter, int proj, int rank, float f, uint16_t* W,
                         hipStream_t stream) {
-  const dim3 grid((pv.din + kMergeThreads * 8 - 1) / (kMergeThreads * 8), (pv.dout + kMergeRows - 1) / kMergeRows);
-  const bool vec = pv.din % 8 == 0 && reinterpret_cast<uintptr_t>(W) % 16 == 0 &&
-                   reinterpret_cast<uintptr_t>(pv.down) % 16 == 0;
-  if (vec && rank <= 16) {
-    const dim3 grid16((pv.din + kMergeThreads * 8 - 1) / (kMergeThreads * 8),
-                      (pv.dout + kMergeRows16 - 1) / kMergeRows16);
-    MLORA_LAUNCH("merge", merge_kernel_r16, grid16, dim3(kMergeThreads), 0, stream, pv, adapter, proj, rank, f, W);
-  } else if (vec)
-    MLORA_LAUNCH("merge", (merge_kernel<true>), grid, dim3(kMergeThreads), 0, stream, pv, adapter, proj, rank, f, W);
-  else
+  const bool vec = pv.din % 8 == 0 && reinterpret_cast<uintptr_t>(W) % 16 == 0;
+  if (vec) {
+    const dim3 grid((pv.din + kMergeTile - 1) / kMergeTile, (pv.dout + kMergeTile - 1) / kMergeTile);
+    MLORA_LAUNCH("merge", merge_kernel_mfma, grid, dim3(256), 0, stream, pv, adapter, proj, rank, f, W);
+  } else {
+    const dim3 grid((pv.din + kMergeThreads * 8 - 1) / (kMergeThreads * 8), (pv.dout + kMergeRows - 1) / kMergeRows);
     MLORA_LAUNCH("merge", (merge_kernel<false>), grid, dim3(kMergeThreads), 0, stream, pv, adapter, proj, rank, f, W);
+  }
   return launched();
 }
 
