@@ -477,7 +477,8 @@ def cpu_baseline(w, seconds):
 
 def copy_calibration(M, torch, gib=1.0, reps=10):
     """Achievable HBM rates: the library's streaming copy (1 GiB read + 1 GiB
-    written per launch) and its streaming read (1 GiB read)."""
+    written per launch), its streaming read (1 GiB read) and the same read
+    through LDS DMA (the ring GEMMs' operand path)."""
     nb = int(gib * 2 ** 30)
     src = torch.empty(nb // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
@@ -496,9 +497,11 @@ def copy_calibration(M, torch, gib=1.0, reps=10):
 
     ms_copy = timed(lambda: M.hbm_copy(dst, src))
     ms_read = timed(lambda: M.hbm_read(src, out))
+    ms_read_lds = timed(lambda: M.hbm_read_lds(src, out))
     del src, dst
     return {"bytes_copied": 2 * nb, "copy_ms": ms_copy, "copy_gbps": 2 * nb / ms_copy / 1e6,
-            "bytes_read": nb, "read_ms": ms_read, "read_gbps": nb / ms_read / 1e6}
+            "bytes_read": nb, "read_ms": ms_read, "read_gbps": nb / ms_read / 1e6,
+            "read_lds_ms": ms_read_lds, "read_lds_gbps": nb / ms_read_lds / 1e6}
 
 
 def run_workload(M, torch, name, steps, warmup, variant_arg="auto", rotate_bytes=1.0, separate_build=False,
@@ -756,6 +759,7 @@ def main():
     cal = copy_calibration(M, torch)
     result["hbm_copy_gbps"] = round(cal["copy_gbps"], 1)
     result["hbm_read_gbps"] = round(cal["read_gbps"], 1)
+    result["hbm_read_lds_gbps"] = round(cal["read_lds_gbps"], 1)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result))

@@ -430,6 +430,14 @@ mlora_status mlora_hbm_copy(void* dst, const void* src, size_t bytes, void* stre
  * achievable streaming read rate can be measured.  Errors: EINVAL, EHIP. */
 mlora_status mlora_hbm_read(const void* src, size_t bytes, uint32_t* out, void* stream);
 
+/* The same read through LDS DMA (buffer loads into LDS, the path by which
+ * the ring GEMMs fetch X, W0 and the rank-concatenated operands), so that a
+ * byte counter's reading for that path can be calibrated as well: streams
+ * `bytes` from src (a multiple of 1024 up to 2^31 - 1, 16-byte aligned) in
+ * 1 KiB pieces and XORs a few of the words received into *out (device
+ * uint32, caller-owned).  Errors: EINVAL, EHIP. */
+mlora_status mlora_hbm_read_lds(const void* src, size_t bytes, uint32_t* out, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Launch timing, a measurement aid that changes no result.
  * mlora_timing_arm(n) arms the library's next n kernel launches (1..2048),

@@ -23,7 +23,7 @@ import numpy as np
 __all__ = [
     "MloraError", "lib", "Pool", "build_segments", "segments_header", "segments_status", "read_segments",
     "base_gemm", "shrink", "shrink_max_chunks", "expand", "fused", "shrink_rows", "gemm_lora", "new_work", "rows_t", "apply", "forward", "plan", "work_bytes",
-    "forward_static", "STATIC_SCRATCH_BYTES", "merge", "hbm_copy", "hbm_read", "timing_arm", "timing_read", "VARIANTS", "ITEM_ROWS", "TILE_ROWS", "MAX_ROWS", "MAX_RANK", "SEG", "EXPORTS", "LIB_PATH",
+    "forward_static", "STATIC_SCRATCH_BYTES", "merge", "hbm_copy", "hbm_read", "hbm_read_lds", "timing_arm", "timing_read", "VARIANTS", "ITEM_ROWS", "TILE_ROWS", "MAX_ROWS", "MAX_RANK", "SEG", "EXPORTS", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmlora.so")
@@ -85,6 +85,7 @@ EXPORTS = {
     "mlora_merge": (ctypes.c_int, [_c_void_p, _i32, _i32, _c_void_p, _f32, _c_void_p]),
     "mlora_hbm_copy": (ctypes.c_int, [_c_void_p, _c_void_p, _sz, _c_void_p]),
     "mlora_hbm_read": (ctypes.c_int, [_c_void_p, _sz, _c_void_p, _c_void_p]),
+    "mlora_hbm_read_lds": (ctypes.c_int, [_c_void_p, _sz, _c_void_p, _c_void_p]),
     "mlora_timing_arm": (ctypes.c_int, [ctypes.c_int32]),
     "mlora_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float), ctypes.c_int32,
                                          ctypes.POINTER(ctypes.c_int32)]),
@@ -496,6 +497,13 @@ def hbm_read(src, out, nbytes: Optional[int] = None):
     """Streams src and XORs its 32-bit words into out[0] (device int32)."""
     nb = src.numel() * src.element_size() if nbytes is None else nbytes
     _check(lib().mlora_hbm_read(_ptr(src), nb, _ptr(out), _stream()), "mlora_hbm_read")
+    return out
+
+
+def hbm_read_lds(src, out, nbytes: Optional[int] = None):
+    """Streams src through LDS DMA in 1 KiB pieces (mlora_hbm_read_lds)."""
+    nb = src.numel() * src.element_size() if nbytes is None else nbytes
+    _check(lib().mlora_hbm_read_lds(_ptr(src), nb, _ptr(out), _stream()), "mlora_hbm_read_lds")
     return out
 
 

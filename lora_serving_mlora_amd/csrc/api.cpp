@@ -1152,6 +1152,15 @@ mlora_status mlora_hbm_read(const void* src, size_t bytes, uint32_t* out, void* 
   return hip_check(mlora::launch_hbm_read(src, bytes, out, as_stream(stream)), "read launch");
 }
 
+mlora_status mlora_hbm_read_lds(const void* src, size_t bytes, uint32_t* out, void* stream) {
+  g_err.clear();
+  if (!src || !out || bytes % 1024 != 0 || bytes > 0x7fffffffu || !aligned16(src))
+    return fail(MLORA_EINVAL,
+                "LDS-DMA read needs a non-NULL 16-byte aligned source, a multiple of 1024 bytes below 2 GiB and an "
+                "output word");
+  return hip_check(mlora::launch_hbm_read_lds(src, bytes, out, as_stream(stream)), "LDS-DMA read launch");
+}
+
 }  // extern "C"
 
 namespace mlora {

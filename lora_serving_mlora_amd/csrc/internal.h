@@ -217,6 +217,7 @@ hipError_t launch_fused(const PoolView& pv, int proj, const uint16_t* X, const i
 
 hipError_t launch_hbm_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
 hipError_t launch_hbm_read(const void* src, size_t bytes, uint32_t* out, hipStream_t stream);
+hipError_t launch_hbm_read_lds(const void* src, size_t bytes, uint32_t* out, hipStream_t stream);
 // W (bf16 [dout][din], in place) += f * Up_a Down_a for adapter a's rank-r
 // factors of projection proj (f = +-scale), fp32 sum, bf16 RNE store
 hipError_t launch_merge(const PoolView& pv, int adapter, int proj, int rank, float f, uint16_t* W,

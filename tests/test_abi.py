@@ -57,6 +57,9 @@ def test_host_only_calls():
     assert L.mlora_base_gemm(None, None, None, 0, 4, 4, None) == M.OK     # n = 0 is a no-op
     assert L.mlora_base_gemm(None, None, None, 1, 0, 4, None) == M.EINVAL
     assert L.mlora_hbm_copy(None, None, 16, None) == M.EINVAL
+    assert L.mlora_hbm_read_lds(None, 1024, None, None) == M.EINVAL
+    assert L.mlora_hbm_read_lds(ctypes.c_void_p(256), 1000, ctypes.c_void_p(256), None) == M.EINVAL  # not KiB
+    assert L.mlora_hbm_read_lds(ctypes.c_void_p(256), 1 << 31, ctypes.c_void_p(256), None) == M.EINVAL
     # the layer's entry points reject a NULL pool before touching the device
     assert L.mlora_apply(None, 0, None, None, None, None, 1, None, 0, 0, None) == M.EINVAL
     assert L.mlora_forward(None, 0, None, None, None, None, None, 1, None, 0, 0, None) == M.EINVAL

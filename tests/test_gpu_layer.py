@@ -63,6 +63,23 @@ def test_base_gemm_unaligned_output(M, m, k, n):
     assert torch.isnan(edges).all(), "a store left the output"
 
 
+def test_hbm_read_kernels(M):
+    """The calibration reads run to completion on a buffer of known size:
+    the plain read's XOR of all words is the host's, and the LDS-DMA read
+    (1 KiB pieces) accepts whole KiB only."""
+    import torch
+    src = torch.arange(1 << 20, dtype=torch.int32, device="cuda")  # 4 MiB
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    M.hbm_read(src, out)
+    want = np.bitwise_xor.reduce(np.arange(1 << 20, dtype=np.int64)).astype(np.int32)
+    assert int(out.item()) == int(want)
+    out.zero_()
+    M.hbm_read_lds(src, out)
+    torch.cuda.synchronize()
+    with pytest.raises(M.MloraError):
+        M.hbm_read_lds(src, out, nbytes=1000)
+
+
 def test_base_gemm_prefill_full_size(M):
     """The prefill workload's base product (4096 x 4096 -> 11008) at full
     size, every element against the fp64 product."""
