@@ -130,7 +130,7 @@ def algorithmic(w, chunks):
         "finish_part": finish,
         "finish_base": (2 * n * dout, 0),   # the base GEMM's partials summed (scratch) into Y
         "gemm_skinny_lora": gemm_lora, "gemm_ksplit_lora": gemm_lora, "gemm_big_lora": gemm_lora,
-        # the epilogue's operands: chunk partials in, bf16 t per row out; Up
+        # the large GEMM's low-rank operands: chunk partials in, bf16 t per row out; Up
         # pages in, the same Up with ranks contiguous out
         "lora_prep": (4 * sum_nr * max(chunks, 1) + 2 * sum_nr + 4 * sum_r * dout, sum_nr * max(chunks, 1)),
         "shrink_tiles": (2 * sum_r * din + 2 * n_act * din + 4 * sum_nr * max(chunks, 1), 2 * sum_nr * din),

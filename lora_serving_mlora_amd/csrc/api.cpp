@@ -859,8 +859,6 @@ mlora_status mlora_gemm_lora(const mlora_pool* p, int32_t proj, const uint16_t* 
 namespace {
 // din slices for the split variant: enough waves to spread a small batch
 // over the chip, never more than kMaxSplitChunks
-// the large-batch epilogue's operands (t per row in bf16, adapter offsets,
-// Up blocks with ranks contiguous)
 // Operands of the large-batch GEMM's low-rank term, in `work` after the
 // shrink's slices: tb [n][wt] bf16 | koff [max_adapters] | over, kx (one
 // word each) | tx [n][txw] bf16 | upt, room for upt_units rank rows of dout.
@@ -991,8 +989,8 @@ mlora_status mlora_apply(const mlora_pool* p, int32_t proj, const uint16_t* X, c
                      "per-row shrink + GEMM + expand launch");
   }
   if (variant == MLORA_VARIANT_SPLIT && big_epilogue_fits(p, n) && mlora::big_lora_ok(v, X, W0, n)) {
-    // large batch: shrink, the epilogue's operands, then one GEMM that adds
-    // the low-rank term in its epilogue (Y written once)
+    // large batch: shrink, the low-rank operands, then one GEMM that adds
+    // the low-rank term itself (Y written once)
     const int chunks = split_chunks(p, n);
     float* T = static_cast<float*>(work);
     char* w = static_cast<char*>(work) + align256((size_t)chunks * n * d.max_rank * sizeof(float));
@@ -1011,7 +1009,7 @@ mlora_status mlora_apply(const mlora_pool* p, int32_t proj, const uint16_t* X, c
                    "low-rank operand launch");
     if (st != MLORA_OK) return st;
     const mlora::LoraOperands lo{tb, koff, upt, wt, L.may_overrun ? over : nullptr, tx, L.txw, tx ? kx : nullptr};
-    st = hip_check(mlora::launch_big_lora(v, X, W0, ws, lo, Y, n, s), "GEMM + low-rank epilogue launch");
+    st = hip_check(mlora::launch_big_lora(v, X, W0, ws, lo, Y, n, s), "GEMM + low-rank term launch");
     if (st != MLORA_OK || !L.may_overrun) return st;
     return hip_check(mlora::launch_expand_over(v, proj, T, chunks, ws, Y, n, over, s), "overrun expand launch");
   }

@@ -896,8 +896,10 @@ __device__ __forceinline__ void ring_lora_epilogue(int wr, int wc, int M, int N,
   }
 }
 
-// LORA (whole-K form only): the low-rank term of every row is added in the
-// epilogue (ring_lora_epilogue) and rows with an invalid id become NaN.
+// LORA (whole-K form only): the low-rank term of every row is added as
+// extra K tiles over the rank-concatenated operands (when lora_prep wrote
+// Kx > 0) or else in the epilogue (ring_lora_epilogue); rows with an invalid
+// id become NaN.
 // n_shrink > 0 (split-K form): after its tile, every workgroup also computes
 // the per-row shrink T[k] = s_a Down_a x_k for rows k = g, g + G, ... (g its
 // index among the G = n_tiles * S tile workgroups): independent work that
@@ -1136,7 +1138,7 @@ __device__ __forceinline__ void gemm_ring_body(
 }
 
 // one workgroup per CU: 256x256 tiles (large products, with or without the
-// low-rank epilogue) or whole-K 128x128 tiles over a 4-stage ring (plain
+// low-rank term) or whole-K 128x128 tiles over a 4-stage ring (plain
 // medium GEMM)
 template <int TM, int TN, bool LORA>
 __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_ring(
@@ -1154,7 +1156,7 @@ __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(2,
                                                nullptr, LoraOperands{}, 0, nullptr, 0);
 }
 
-// the same with the low-rank epilogue
+// the same with the low-rank term
 __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_ring_co_lora(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y, int M, int K, int N,
     int tiles_n, int n_tiles, int per_xcd, PoolView pv, const int32_t* __restrict__ row_key, LoraOperands lo) {

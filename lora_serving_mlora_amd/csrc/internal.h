@@ -140,7 +140,7 @@ hipError_t launch_base_split(const uint16_t* X, const uint16_t* W, uint16_t* Y, 
 hipError_t launch_shrink_rows(const PoolView& pv, int proj, const uint16_t* X, const int32_t* ws, int n, float* T,
                               hipStream_t stream);
 
-// Operands of the large-batch GEMM's low-rank epilogue, prepared per batch
+// Operands of the large-batch GEMM's low-rank term, prepared per batch
 // and projection by launch_lora_prep from the shrink's slices and the pool:
 //   tb   bf16 [M][wt]: s_a * t per original row (ranks past the adapter's
 //        are zero; rows not on a resident adapter are not written),
@@ -184,9 +184,9 @@ inline size_t lora_upt_units(int n, int max_adapters, int max_rank) {
   return (size_t)(n < max_adapters ? n : max_adapters) * t_rows_width(max_rank);
 }
 
-// Large batches: Y = X W^T plus every row's low-rank term, added in the
-// 256x256 GEMM's epilogue (no read-modify-write of Y); invalid rows become
-// NaN.  big_lora_ok: the shapes and pointers this kernel takes.
+// Large batches: Y = X W^T plus every row's low-rank term, added inside the
+// large GEMM (extra K tiles over the rank-concatenated operands, or its
+// epilogue; no read-modify-write of Y); invalid rows become NaN.  big_lora_ok: the shapes and pointers this kernel takes.
 bool big_lora_ok(const PoolView& pv, const uint16_t* X, const uint16_t* W, int M);
 hipError_t launch_big_lora(const PoolView& pv, const uint16_t* X, const uint16_t* W, const int32_t* ws,
                            const LoraOperands& lo, uint16_t* Y, int M, hipStream_t stream);
