@@ -301,7 +301,7 @@ __device__ __forceinline__ void seg_build_block(const int32_t* __restrict__ row_
     for (int base = 0; base < n; base += 64) {
       const uint32_t other = base + lane < n ? bufA[base + lane] : 0xffffffffu;  // above every packed value
 #pragma unroll 16
-      for (int l = 0; l < 64; ++l) pos += (int)(__builtin_amdgcn_readlane(other, l) < me);
+      for (int l = 0; l < 64; ++l) pos += (int)((uint32_t)__builtin_amdgcn_readlane((int)other, l) < me);
     }
     if (tid < n) bufB[pos] = me;
     seg_sync();
