@@ -994,7 +994,9 @@ __device__ __forceinline__ void ring_store_tile(int wave, int wr, int wc, int M,
 // from the adapter ids `ids`, and the first workgroup dispatched, (0, 0),
 // builds the batch's segment workspace seg_ws (seg_passes radix passes) in
 // the LDS its ring would use, while the rows go to the other n_shrink - 1.
-template <int TM, int TN, bool PART, bool LORA, bool CO, bool IDS = false>
+// S4 (co-resident mapping, split-K partials): the tiles run over the 4-stage
+// ring (128 KiB of LDS) and the launch has no shrink workgroups.
+template <int TM, int TN, bool PART, bool LORA, bool CO, bool IDS = false, bool S4 = false>
 __device__ __forceinline__ void gemm_ring_body(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y,
     float* __restrict__ part, int M, int K, int N, int tiles_n, int n_tiles, int per_xcd, int kt_per, PoolView pv,
@@ -1102,7 +1104,10 @@ __device__ __forceinline__ void gemm_ring_body(
       kend += kx / GBK64;
     }
   }
-  if constexpr (CO) {
+  if constexpr (S4) {
+    static_assert(CO && PART && !LORA, "the 4-stage form: split-K partials of 128x128 tiles");
+    ring64_loop4<TM, TN>(c, m64_a0, m64_a1, m64_a2, m64_a3, m64_b0, m64_b1, m64_b2, m64_b3, kt0, kend, acc);
+  } else if constexpr (CO) {
     ring64x2_loop<TM, TN, LORA>(c, m64_a0, m64_a1, m64_b0, m64_b1, kt0, kend, acc);
   } else if constexpr (TM == 256) {
     ring64x2_loop<TM, TN, LORA>(c, h64_a0, h64_a1, h64_b0, h64_b1, kt0, kend, acc);
@@ -1183,6 +1188,22 @@ __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(2,
                                                     nullptr, LoraOperands{}, proj, Trows, n_shrink, ids, seg_ws,
                                                     seg_passes);
 }
+
+// Medium products without the low-rank term, from kMidS4Rows rows: split-K
+// 128x128 tiles over the 4-stage ring (128 KiB of LDS, one workgroup per
+// CU), three stages of lookahead where the co-resident form has one.
+// Against that form: 24.1 against 32.4 us at 512 x 4096 x 4096, 40.5
+// against 58.6 us at 1024 rows; no gain at 256 rows.  (The layer with its
+// per-row shrink keeps the co-resident form: the shrink workgroups no
+// longer fit beside 128 KiB tiles, and run on a second stream they started
+// only as the tiles ended, the cross-stream waits costing about 10 us each.)
+__global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_ring_split4(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, float* __restrict__ part, int M, int K, int N,
+    int tiles_n, int n_tiles, int per_xcd, int kt_per) {
+  gemm_ring_body<128, 128, true, false, true, false, true>(X, W, nullptr, part, M, K, N, tiles_n, n_tiles, per_xcd,
+                                                           kt_per, PoolView{}, nullptr, LoraOperands{}, 0, nullptr, 0);
+}
+
 
 // Large products: 256x256 tiles, one workgroup per CU, unless too few tiles
 // fill the chip's 256 slots; then 128x128 tiles two workgroups per CU
@@ -1643,6 +1664,11 @@ int mid_split(int M, int N, int K) {
 
 bool mid_ring_ok(int M, int K) { return K % kRingKAlign == 0 && (long)M * K * 2 < (1L << 31); }
 
+// rows from which a medium product without the low-rank term (the base GEMM
+// of the split and fused plans) takes the 4-stage split-K tiles (the product
+// alone: 18.5 us either way at 256 rows, 24.1 against 32.4 us at 512)
+constexpr int kMidS4Rows = 384;
+
 // shrink: the per-row shrink (T, one slice) runs in workgroups of its own
 // ahead of the tiles, on the same CUs (co-resident form)
 hipError_t launch_mid_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M, int K, int N, const PoolView& pv,
@@ -1651,6 +1677,16 @@ hipError_t launch_mid_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, in
   const int S = mid_split(M, N, K);
   const int tiles_n = (N + 127) / 128, n_tiles = ((M + 127) / 128) * tiles_n;
   const int per_xcd = (n_tiles + 7) / 8;
+  if (!lora && !shrink && ids == nullptr && M >= kMidS4Rows) {
+    MLORA_LAUNCH("gemm_mid", gemm_ring_split4, dim3(per_xcd * 8, S), dim3(kRingThreads), 0, st, X, W, part, M, K, N,
+                 tiles_n, n_tiles, per_xcd, K / GBK64 / S);
+    const hipError_t e = launched();
+    if (e != hipSuccess) return e;
+    const int threads = M * (N / 8);
+    MLORA_LAUNCH("finish_base", (finish_part<false, false>), dim3((threads + kFinishThreads - 1) / kFinishThreads),
+                 dim3(kFinishThreads), 0, st, part, S, Y, M, N, pv, proj, row_key, T);
+    return launched();
+  }
   if (ids != nullptr) {
     // the segment build takes the first of the co-resident form's shrink
     // workgroups (at least 72 of them above 64 rows)
