@@ -328,10 +328,12 @@ __device__ __forceinline__ void reduce_scatter_step(float (&v)[G], int lane) {
 // issue order, so the Down stream is not queued behind the Up stream, and
 // the Y read is not a round trip of its own at the end.  The arithmetic is
 // that of shrink_row_to and expand_cols_pre.
+// row0: the item's first original row when the caller already has it, else
+// -1 (read from perm here).
 __device__ __forceinline__ void fused_item_fast(const PoolView& pv, const Item& m, const int32_t* __restrict__ dpage,
                                                 const int32_t* __restrict__ upage, const uint16_t* __restrict__ X,
                                                 const int32_t* __restrict__ perm, uint16_t* __restrict__ Y,
-                                                float (*ts)[MLORA_MAX_RANK], float (*red)[G]) {
+                                                float (*ts)[MLORA_MAX_RANK], float (*red)[G], int row0) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k0 = tid * 8;  // this thread's din elements and dout columns
   const bool kin = k0 < pv.din, cin = k0 < pv.dout;
@@ -348,7 +350,8 @@ __device__ __forceinline__ void fused_item_fast(const PoolView& pv, const Item& 
     up[q] = up[q] < 0 ? up[0] : up[q];
   }
 #pragma unroll
-  for (int i = 0; i < R; ++i) row[i] = __builtin_amdgcn_readfirstlane(perm[m.j0 + min(i, m.nr - 1)]);
+  for (int i = 0; i < R; ++i)
+    row[i] = (i == 0 && row0 >= 0) ? row0 : __builtin_amdgcn_readfirstlane(perm[m.j0 + min(i, m.nr - 1)]);
   // the first row's X and Y pieces go out with the weights; an item's
   // further rows (same adapter) load theirs when they come up
   // loads are unconditional (threads past din or dout read the last piece;
@@ -439,14 +442,36 @@ __global__ __launch_bounds__(kFusedThreads) void fused_fast_kernel(PoolView pv, 
                                                                    uint16_t* __restrict__ Y, int n) {
   __shared__ float ts[R][MLORA_MAX_RANK];
   __shared__ float red[kFusedThreads / 64][G];
+  const int32_t* perm = ws + MLORA_SEG_PERM(n);
+  // The first item's entries are read together with the counts, and so are
+  // the entries of segment b and sorted position b (b = this workgroup):
+  // when the item is (segment b, first position b), as every item is where
+  // each row has an adapter of its own, its adapter, end and first row
+  // arrive two dependent loads earlier than through load_item.  (Indices are
+  // clamped to the arrays; the values are used only when the item matches.)
+  const int b = blockIdx.x;
+  const int bi = min(b, MLORA_SEG_MAX_ITEMS(n) - 1), bs = min(b, n - 1);
+  const int g_seg = ws[MLORA_SEG_ITEMS(n) + 2 * bi], g_j0 = ws[MLORA_SEG_ITEMS(n) + 2 * bi + 1];
+  const int g_ad = ws[MLORA_SEG_ADAPTER(n) + bs], g_end = ws[MLORA_SEG_OFF(n) + bs + 1], g_row = perm[bs];
   const int n_items = ws[MLORA_SEG_NITEMS];
   const int n_bad = ws[MLORA_SEG_NBAD];
-  const int32_t* perm = ws + MLORA_SEG_PERM(n);
-  for (int it = blockIdx.x; it < n_items + n_bad; it += gridDim.x) {
+  for (int it = b; it < n_items + n_bad; it += gridDim.x) {
     if (it < n_items) {
-      const Item m = load_item(pv, ws, n, it);
+      Item m;
+      int row0 = -1;
+      if (it == b && g_seg == b && g_j0 == b) {
+        m.seg = b;
+        m.j0 = b;
+        m.nr = min(R, g_end - b);
+        m.adapter = g_ad;
+        m.rank = pv.rank[g_ad];
+        m.scale = pv.scale[g_ad];
+        row0 = g_row;
+      } else {
+        m = load_item(pv, ws, n, it);
+      }
       const size_t pt = ((size_t)m.adapter * pv.n_proj + proj) * pv.max_rank;
-      fused_item_fast(pv, m, pv.down_page + pt, pv.up_page + pt, X, perm, Y, ts, red);
+      fused_item_fast(pv, m, pv.down_page + pt, pv.up_page + pt, X, perm, Y, ts, red, row0);
       __syncthreads();
     } else {
       uint16_t* y = Y + (size_t)perm[n - n_bad + (it - n_items)] * pv.dout;

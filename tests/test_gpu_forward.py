@@ -68,6 +68,9 @@ CASES = [
     (10, 300, 4096, 4096, {i: 16 for i in range(256)}, True),
     (11, 700, 2048, 512, {i: (16 if i % 3 else 64) for i in range(40)}, True),
     (12, 1024, 4096, 4096, {0: 16, 1: 8}, True),
+    (17, 200, 2048, 1000, {0: 8, 1: 3, 2: 5}, True),
+    (18, 520, 4096, 4096, {i: 16 for i in range(60)}, True),
+    (19, 128, 1024, 4096, {0: 16, 1: 1}, False),
     # decode shapes with wider or ragged din (8 to 16 K slices; slices of
     # unequal depth)
     (13, 32, 11008, 4096, {0: 16, 1: 16, 2: 16}, True),

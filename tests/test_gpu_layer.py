@@ -112,6 +112,7 @@ SMALL = [
     (8, 512, 1000, 700, {i: (16 if i % 3 else 64) for i in range(40)}),
     (9, 1000, 520, 260, {0: 16, 1: 3, 2: 64}),        # din not a multiple of 32: vector-ALU shrink
     (10, 520, 1000, 13, {0: 16, 1: 5, 2: 9}),          # ranks <= 16, din and dout <= 4096: fused fast form
+    (12, 640, 1000, 200, {0: 16, 1: 5, 2: 9}),         # medium rows, K one ring split deep, ranks <= 16
 ]
 LARGE = [
     # large batch on the 256x256 GEMM with the low-rank epilogue, ragged rows and columns
