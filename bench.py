@@ -48,7 +48,7 @@ KERNEL_SOURCES = {"seg_build": "seg_build.hip", "gemm_skinny": "base_gemm.hip", 
                   "gemm_mid": "base_gemm.hip", "gemm_skinny_lora": "base_gemm.hip",
                   "gemm_ksplit_lora": "base_gemm.hip", "shrink": "lora_branch.hip", "expand": "lora_branch.hip",
                   "fused": "lora_branch.hip", "shrink_rows": "lora_branch.hip", "shrink_tiles": "lora_branch.hip",
-                  "gemm_big_lora": "base_gemm.hip", "lora_prep": "lora_branch.hip"}
+                  "gemm_big_lora": "base_gemm.hip", "lora_prep": "lora_branch.hip", "finish_base": "base_gemm.hip"}
 DEFAULT_WORKLOAD = "decode_3"
 
 
