@@ -900,16 +900,13 @@ __device__ __forceinline__ void ring_lora_epilogue(int wr, int wc, int M, int N,
 // extra K tiles over the rank-concatenated operands (when lora_prep wrote
 // Kx > 0) or else in the epilogue (ring_lora_epilogue); rows with an invalid
 // id become NaN.
-// n_shrink > 0 (split-K form): after its tile, every workgroup also computes
-// the per-row shrink T[k] = s_a Down_a x_k for rows k = g, g + G, ... (g its
-// index among the G = n_tiles * S tile workgroups): independent work that
-// shares the launch.  (As workgroups of their own, ahead of the tiles, the
-// rows held whole CUs: a workgroup of this kernel reserves the ring's LDS.)
-// CO (medium split-K tiles only): the per-row shrink runs in n_shrink
-// workgroups of its own ahead of the tiles, and the tiles take the ring with
-// two 32 KiB stages, so a shrink workgroup and a tile workgroup fit on one CU
-// together (64 KiB of LDS each, at most 256 registers per lane) and the
-// shrink's Down reads overlap the tiles' work instead of following it.
+// CO (medium split-K tiles only): the per-row shrink T[k] = s_a Down_a x_k
+// runs in n_shrink workgroups of its own ahead of the tiles, and the tiles
+// take the ring with two 32 KiB stages, so a shrink workgroup and a tile
+// workgroup fit on one CU together (64 KiB of LDS each, at most 256
+// registers per lane) and the shrink's Down reads overlap the tiles' work
+// instead of following it.  (Run by the tile workgroups after their tiles,
+// the shrink's latency showed in full.)
 // The per-row shrink of row k with its key taken from the batch's adapter
 // ids and the resident table (the same key the segment workspace holds).
 template <bool VEC, int NW>
