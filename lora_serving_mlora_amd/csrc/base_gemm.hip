@@ -1688,9 +1688,13 @@ hipError_t launch_mid_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, in
     // the segment build takes the first of the co-resident form's shrink
     // workgroups (at least 72 of them above 64 rows)
     if (!(shrink && lora && M > 64 && M <= 1024)) return hipErrorNotSupported;
-    // one more than the rows (the segment build's), up to 264: no shrink
-    // workgroup takes a second row where the plain form gives each its own
-    const int nsw = min((M + 1 + 7) / 8 * 8, 264);
+    // one more than the rows (the segment build's), a multiple of 8, up to
+    // 256 workgroups for at most 256 rows (so that all 256 tile workgroups
+    // find a free slot beside one: the row workgroups that overflowed onto
+    // a CU of their own held 8 tiles back, 25.9-26.3 against 22.9-23.8 us
+    // at 256 rows), else up to 264 (at 512 rows 264 keep every shrink
+    // workgroup at two rows; 256 gave two of them three: 34 against 37 us)
+    const int nsw = min((M + 1 + 7) / 8 * 8, M <= 256 ? 256 : 264);
     const int passes = M <= kRingThreads ? 0 : ((pv.max_adapters + 1 < 256) ? 1 : 2);
     MLORA_LAUNCH("gemm_mid+seg+shrink_rows", gemm_ring_co_ids, dim3(nsw + per_xcd * 8, S), dim3(kRingThreads), 0,
                  st, X, W, Y, part, M, K, N, tiles_n, n_tiles, per_xcd, K / GBK64 / S, pv, proj, T, nsw, ids, seg_ws,
