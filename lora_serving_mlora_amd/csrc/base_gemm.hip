@@ -990,7 +990,8 @@ __device__ __forceinline__ void ring_store_tile(int wave, int wr, int wc, int M,
 // IDS (co-resident form only): the shrink workgroups take each row's key
 // from the adapter ids `ids`, and the first workgroup dispatched, (0, 0),
 // builds the batch's segment workspace seg_ws (seg_passes radix passes) in
-// the LDS its ring would use, while the rows go to the other n_shrink - 1.
+// the LDS its ring would use, while the rows go to the other n_shrink - 1
+// (seg_rows: to all n_shrink, that workgroup's share last).
 // S4 (co-resident mapping, split-K partials): the tiles run over the 4-stage
 // ring (128 KiB of LDS) and the launch has no shrink workgroups.
 template <int TM, int TN, bool PART, bool LORA, bool CO, bool IDS = false, bool S4 = false>
@@ -999,7 +1000,7 @@ __device__ __forceinline__ void gemm_ring_body(
     float* __restrict__ part, int M, int K, int N, int tiles_n, int n_tiles, int per_xcd, int kt_per, PoolView pv,
     const int32_t* __restrict__ row_key, LoraOperands lo, int proj, float* __restrict__ Trows, int n_shrink,
     const int32_t* __restrict__ ids = nullptr, int32_t* __restrict__ seg_ws = nullptr,
-    int seg_passes = 0) {
+    int seg_passes = 0, int seg_rows = 0) {
   static_assert(!(PART && LORA), "the low-rank epilogue needs the whole K range");
   static_assert(!CO || (TM == 128 && TN == 128), "co-resident form: 128x128 tiles");
   static_assert(!(TM == 256) || TN == 256, "large form: 256x256 tiles");
@@ -1019,8 +1020,13 @@ __device__ __forceinline__ void gemm_ring_body(
             seg_build_block<kRingThreads>(ids, M, pv.rank, pv.max_adapters, seg_passes, cap, seg_ws,
                                           reinterpret_cast<uint32_t*>(m64_a0), reinterpret_cast<int*>(m64_a1),
                                           reinterpret_cast<int*>(m64_a1) + kMaxWaves);
-          } else {
-            for (int k = blockIdx.x - 1; k < M; k += n_shrink - 1)
+          }
+          // the rows: over the other workgroups, or (seg_rows) over all of
+          // them, the segment build's taking the last share
+          if (blockIdx.x != 0 || seg_rows) {
+            const int nw = seg_rows ? n_shrink : n_shrink - 1;
+            const int i0 = seg_rows ? ((int)blockIdx.x + n_shrink - 1) % n_shrink : (int)blockIdx.x - 1;
+            for (int k = i0; k < M; k += nw)
               shrink_row_body_ids<true, kRingThreads / 64>(pv, proj, X, ids, k, Trows,
                                                            row_desc(Trows, M, pv.max_rank));
           }
@@ -1180,10 +1186,10 @@ __global__ __launch_bounds__(kRingThreads) __attribute__((amdgpu_waves_per_eu(2,
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y,
     float* __restrict__ part, int M, int K, int N, int tiles_n, int n_tiles, int per_xcd, int kt_per, PoolView pv,
     int proj, float* __restrict__ Trows, int n_shrink, const int32_t* __restrict__ ids, int32_t* __restrict__ seg_ws,
-    int seg_passes) {
+    int seg_passes, int seg_rows) {
   gemm_ring_body<128, 128, true, false, true, true>(X, W, Y, part, M, K, N, tiles_n, n_tiles, per_xcd, kt_per, pv,
                                                     nullptr, LoraOperands{}, proj, Trows, n_shrink, ids, seg_ws,
-                                                    seg_passes);
+                                                    seg_passes, seg_rows);
 }
 
 // Medium products without the low-rank term, from kMidS4Rows rows: split-K
@@ -1688,17 +1694,19 @@ hipError_t launch_mid_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, in
     // the segment build takes the first of the co-resident form's shrink
     // workgroups (at least 72 of them above 64 rows)
     if (!(shrink && lora && M > 64 && M <= 1024)) return hipErrorNotSupported;
-    // one more than the rows (the segment build's), a multiple of 8, up to
-    // 256 workgroups for at most 256 rows (so that all 256 tile workgroups
-    // find a free slot beside one: the row workgroups that overflowed onto
-    // a CU of their own held 8 tiles back, 25.9-26.3 against 22.9-23.8 us
-    // at 256 rows), else up to 264 (at 512 rows 264 keep every shrink
-    // workgroup at two rows; 256 gave two of them three: 34 against 37 us)
-    const int nsw = min((M + 1 + 7) / 8 * 8, M <= 256 ? 256 : 264);
+    // Up to 256 rows: one workgroup per row (a multiple of 8, at most 256),
+    // the segment build's taking a row too, so that all 256 tile workgroups
+    // find a free slot beside one (257-264 of them, one more for the build,
+    // held tiles back: 256 rows, 25.9-26.3 against 22.0-22.9 us).  Above:
+    // one more than the rows, up to 264 (at 512 rows every row workgroup then
+    // takes two rows; 256 of them, the build's with rows or without, took
+    // 35.7-37.2 us against 34.1-34.9).
+    const int seg_rows = M <= 256 ? 1 : 0;
+    const int nsw = seg_rows ? min((M + 7) / 8 * 8, 256) : min((M + 1 + 7) / 8 * 8, 264);
     const int passes = M <= kRingThreads ? 0 : ((pv.max_adapters + 1 < 256) ? 1 : 2);
     MLORA_LAUNCH("gemm_mid+seg+shrink_rows", gemm_ring_co_ids, dim3(nsw + per_xcd * 8, S), dim3(kRingThreads), 0,
                  st, X, W, Y, part, M, K, N, tiles_n, n_tiles, per_xcd, K / GBK64 / S, pv, proj, T, nsw, ids, seg_ws,
-                 passes);
+                 passes, seg_rows);
   } else {
     // shrink workgroups ahead of the tiles: one per row up to one per CU
     // (each then loops over rows, so the tiles still find a free slot on
