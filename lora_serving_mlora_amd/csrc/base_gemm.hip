@@ -1010,7 +1010,7 @@ __device__ __forceinline__ void gemm_ring_body(
   const int tid = threadIdx.x, lane = tid & 63;
   if constexpr (CO) {
     if ((int)blockIdx.x < n_shrink) {
-      if (blockIdx.y == 0) {
+      {
         if constexpr (IDS) {
           if (blockIdx.x == 0) {
             // up to 1024 rows: 2 * 1088 + 4 * kRadix words of scratch
@@ -1038,7 +1038,13 @@ __device__ __forceinline__ void gemm_ring_body(
       return;
     }
   }
-  const int bx = (int)blockIdx.x - (CO ? n_shrink : 0);
+  // the tile workgroups follow the shrink workgroups in a one-dimensional
+  // grid, K slice by K slice (no idle shrink slots per slice to dispatch);
+  // n_shrink and per_xcd * 8 are multiples of 8, so a workgroup's XCD is
+  // bx & 7 either way
+  const int b = (int)blockIdx.x - (CO ? n_shrink : 0);
+  const int ks = PART ? b / (per_xcd * 8) : 0;
+  const int bx = PART ? b % (per_xcd * 8) : b;
   const int t = (bx & 7) * per_xcd + (bx >> 3);
   if (t >= n_tiles) return;
   // large: groups of kGroupM row bands walked column by column, so the
@@ -1085,7 +1091,7 @@ __device__ __forceinline__ void gemm_ring_body(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int kt0 = PART ? blockIdx.y * kt_per : 0;
+  const int kt0 = PART ? ks * kt_per : 0;
   int kend = PART ? kt0 + kt_per : K / GBK64;
   // LORA: a batch in the rank-concatenated form (kx > 0) runs kx / 64 more
   // K tiles from Tx and Ux, and no epilogue
@@ -1140,7 +1146,7 @@ __device__ __forceinline__ void gemm_ring_body(
                 "a wave's output block fits its ring buffer");
   ring_barrier();
   ring_store_tile<MI, NJ, PART>(c.wave, m0 + c.wm * (TM / 2), n0 + c.wn * (TN / 2), M, N, Y,
-                                PART ? part + (size_t)blockIdx.y * M * N : nullptr, acc,
+                                PART ? part + (size_t)ks * M * N : nullptr, acc,
                                 TM == 256 ? (c.wave == 0 ? h64_a0 : c.wave == 1 ? h64_a1 : c.wave == 2 ? h64_b0 : h64_b1)
                                           : (c.wave == 0 ? m64_a0 : c.wave == 1 ? m64_a1 : c.wave == 2 ? m64_b0 : m64_b1));
 }
@@ -1681,7 +1687,7 @@ hipError_t launch_mid_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, in
   const int tiles_n = (N + 127) / 128, n_tiles = ((M + 127) / 128) * tiles_n;
   const int per_xcd = (n_tiles + 7) / 8;
   if (!lora && !shrink && ids == nullptr && M >= kMidS4Rows) {
-    MLORA_LAUNCH("gemm_mid", gemm_ring_split4, dim3(per_xcd * 8, S), dim3(kRingThreads), 0, st, X, W, part, M, K, N,
+    MLORA_LAUNCH("gemm_mid", gemm_ring_split4, dim3(per_xcd * 8 * S), dim3(kRingThreads), 0, st, X, W, part, M, K, N,
                  tiles_n, n_tiles, per_xcd, K / GBK64 / S);
     const hipError_t e = launched();
     if (e != hipSuccess) return e;
@@ -1704,7 +1710,7 @@ hipError_t launch_mid_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, in
     const int seg_rows = M <= 256 ? 1 : 0;
     const int nsw = seg_rows ? min((M + 7) / 8 * 8, 256) : min((M + 1 + 7) / 8 * 8, 264);
     const int passes = M <= kRingThreads ? 0 : ((pv.max_adapters + 1 < 256) ? 1 : 2);
-    MLORA_LAUNCH("gemm_mid+seg+shrink_rows", gemm_ring_co_ids, dim3(nsw + per_xcd * 8, S), dim3(kRingThreads), 0,
+    MLORA_LAUNCH("gemm_mid+seg+shrink_rows", gemm_ring_co_ids, dim3(nsw + per_xcd * 8 * S), dim3(kRingThreads), 0,
                  st, X, W, Y, part, M, K, N, tiles_n, n_tiles, per_xcd, K / GBK64 / S, pv, proj, T, nsw, ids, seg_ws,
                  passes, seg_rows);
   } else {
@@ -1712,7 +1718,7 @@ hipError_t launch_mid_lora(const uint16_t* X, const uint16_t* W, uint16_t* Y, in
     // (each then loops over rows, so the tiles still find a free slot on
     // every CU), a multiple of 8 so the tile workgroups keep their XCD mapping
     const int nsw = shrink ? min((M + 7) / 8 * 8, 256) : 0;
-    MLORA_LAUNCH(shrink ? "gemm_mid+shrink_rows" : "gemm_mid", gemm_ring_co, dim3(nsw + per_xcd * 8, S),
+    MLORA_LAUNCH(shrink ? "gemm_mid+shrink_rows" : "gemm_mid", gemm_ring_co, dim3(nsw + per_xcd * 8 * S),
                  dim3(kRingThreads), 0, st, X, W, Y, part, M, K, N, tiles_n, n_tiles, per_xcd, K / GBK64 / S, pv,
                  row_key, proj, T, nsw);
   }
