@@ -66,7 +66,7 @@ def parse_args():
     ap.add_argument("--no-configs", action="store_true",
                     help="time only --workload (by default the other workloads where a target is judged are timed "
                          "too and reported under \"configs\")")
-    ap.add_argument("--config-steps", type=int, default=10, help="timed steps of each of the other workloads")
+    ap.add_argument("--config-steps", type=int, default=50, help="timed steps of each of the other workloads")
     ap.add_argument("--separate-build", action="store_true",
                     help="run each step as two library calls (build_segments, then apply) instead of forward")
     ap.add_argument("--copy-only", action="store_true", help="only run the HBM copy calibration kernel")
@@ -751,7 +751,7 @@ def main():
         for other in ("decode_frag", "prefill", "layer_stack", "decode_down"):
             if other == args.workload:
                 continue
-            m2, c2 = run_workload(M, torch, other, max(3, min(K, args.config_steps)), min(W, 3))
+            m2, c2 = run_workload(M, torch, other, max(3, min(K, args.config_steps)), min(W, 5))
             configs[other] = config_summary(other, m2)
             del c2
             torch.cuda.empty_cache()
