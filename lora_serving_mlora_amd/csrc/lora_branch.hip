@@ -997,6 +997,7 @@ hipError_t launch_expand_over(const PoolView& pv, int proj, const float* T, int 
 
 hipError_t launch_fused(const PoolView& pv, int proj, const uint16_t* X, const int32_t* ws, uint16_t* Y, int n,
                         hipStream_t stream) {
+  if (n <= 0) return hipSuccess;  // (the fast form's first-item reads index sorted position min(b, n - 1))
   const dim3 grid(item_grid(n)), block(kFusedThreads);
   if (vec_ok(pv, X, Y) && pv.max_rank <= G && pv.din <= 8 * kFusedThreads && pv.dout <= 8 * kFusedThreads)
     MLORA_LAUNCH("fused", fused_fast_kernel, grid, block, 0, stream, pv, proj, X, ws, Y, n);
