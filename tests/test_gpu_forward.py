@@ -71,6 +71,11 @@ CASES = [
     (17, 200, 2048, 1000, {0: 8, 1: 3, 2: 5}, True),
     (18, 520, 4096, 4096, {i: 16 for i in range(60)}, True),
     (19, 128, 1024, 4096, {0: 16, 1: 1}, False),
+    # up to 256 rows the segment build's workgroup takes a share of the rows
+    # too: 250 rows over 256 workgroups leaves it none, 257 rows takes the
+    # other form
+    (20, 250, 2048, 1000, {i: 16 for i in range(30)}, True),
+    (21, 257, 2048, 1000, {i: 16 for i in range(30)}, True),
     # decode shapes with wider or ragged din (8 to 16 K slices; slices of
     # unequal depth)
     (13, 32, 11008, 4096, {0: 16, 1: 16, 2: 16}, True),
