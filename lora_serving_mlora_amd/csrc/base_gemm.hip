@@ -1399,22 +1399,28 @@ __global__ __launch_bounds__(64 * kDecWaves) void gemm_decode(const uint16_t* __
   // 16-byte chunks lane and lane + 64 of the slice (nch chunks in all; a
   // lane past them re-reads the last one and adds nothing).
   const int nch = Kq / 8;
+  // halves (at most half as many rows as column blocks): each row's shrink
+  // is shared by two column blocks, 8 of every 16 ranks each, one rank per
+  // wave, so that every workgroup carries the same shrink work
+  const bool halves = shrink && 2 * M <= ncb;
+  const int srow = halves ? (cb >> 1) : cb, hq = halves ? 8 * (cb & 1) : 0;
   int key0 = -1, rank0 = 0;
   uint4 dn[2][2];
-  if (shrink && cb < M) {
+  if (shrink && srow < M) {
     if (IDS) {
-      const KeyRank kr = key_rank_from_ids(ids, pv, cb);
+      const KeyRank kr = key_rank_from_ids(ids, pv, srow);
       key0 = kr.key;
       rank0 = kr.rank;
     } else {
-      key0 = __builtin_amdgcn_readfirstlane(row_key[cb]);
+      key0 = __builtin_amdgcn_readfirstlane(row_key[srow]);
     }
     if (key0 >= 0) {
       if (!IDS) rank0 = __builtin_amdgcn_readfirstlane(pv.rank[key0]);
       const int32_t* dpage = pv.down_page + ((size_t)key0 * pv.n_proj + proj) * pv.max_rank;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        int pg = dpage[min(wave + 8 * i, pv.max_rank - 1)];
+        if (halves && i > 0) break;
+        int pg = dpage[min(hq + wave + 8 * i, pv.max_rank - 1)];
         pg = pg < 0 ? dpage[0] : pg;
         const uint16_t* dr = pv.down + (size_t)pg * pv.din + k0;
 #pragma unroll
@@ -1463,7 +1469,46 @@ __global__ __launch_bounds__(64 * kDecWaves) void gemm_decode(const uint16_t* __
     }
   }
 
-  if (shrink) {
+  if (halves) {
+    if (srow < M) {
+      const int r = srow, key = key0, rank = rank0;
+      if (kq == 0 && hq == 0) write_row_desc(pv, proj, key, r, row_desc(Tp, M, pv.max_rank));
+      if (key >= 0) {
+        const int32_t* dpage = pv.down_page + ((size_t)key * pv.n_proj + proj) * pv.max_rank;
+        uint4 d[2] = {dn[0][0], dn[0][1]};
+        for (int q0 = 0; q0 < rank; q0 += 16) {
+          if (q0 > 0) {
+            int pg = dpage[min(q0 + hq + wave, pv.max_rank - 1)];
+            pg = pg < 0 ? dpage[0] : pg;
+            const uint16_t* dr = pv.down + (size_t)pg * pv.din + k0;
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+              d[cc] = *reinterpret_cast<const uint4*>(dr + min(lane + 64 * cc, nch - 1) * 8);
+          }
+          float v = 0.f;
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            const int c = lane + 64 * cc;  // logical chunk of row r's slice
+            if (c < nch) {
+              const uint4 xa = *reinterpret_cast<const uint4*>(xs + (size_t)r * xs_stride + cc * 512 +
+                                                               ((lane ^ (r & 15)) << 3));
+              const uint32_t xw[4] = {xa.x, xa.y, xa.z, xa.w};
+              const uint32_t dw[4] = {d[cc].x, d[cc].y, d[cc].z, d[cc].w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                v = fmaf(lo_bf(dw[e]), lo_bf(xw[e]), v);
+                v = fmaf(hi_bf(dw[e]), hi_bf(xw[e]), v);
+              }
+            }
+          }
+#pragma unroll
+          for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+          const int q = q0 + hq + wave;
+          if (lane == 0 && q < rank) Tp[((size_t)kq * M + r) * pv.max_rank + q] = v;
+        }
+      }
+    }
+  } else if (shrink) {
     for (int r = cb; r < M; r += ncb) {
       const bool first = r == cb;
       int key, rank;
